@@ -1,0 +1,423 @@
+// svt_api.cpp - host side of the C ABI declared in include/svt.h: argument validation, the
+// cluster-contiguous HBM layout built at upload, per-search workspace carving and kernel launches,
+// the Bloom signature helpers and stage timing.  Device work is enqueued on the caller's stream.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <set>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include "svt.h"
+#include "svt_internal.h"
+
+using namespace svt;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int fail_hip(hipError_t e, const char *what) {
+  return fail(e == hipErrorOutOfMemory ? SVT_ENOMEM : SVT_EDEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr uint32_t kMagic = 0x53565449u;   // "SVTI"
+
+std::mutex g_live_mu;
+std::set<const void *> g_live;
+
+bool is_live(const void *p) {
+  std::lock_guard<std::mutex> lk(g_live_mu);
+  return g_live.count(p) != 0;
+}
+
+bool supported_dim(int32_t d) { return d == 16 || d == 32 || d == 64 || d == 128 || d == 256; }
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// stage timing (per process switch, per thread results)
+std::atomic<int> g_prof_on{0};
+struct ProfState {
+  std::vector<hipEvent_t> ev;
+  std::vector<const char *> names;
+  int n = 0;
+  ~ProfState() {
+    for (auto e : ev) (void)hipEventDestroy(e);
+  }
+};
+thread_local ProfState g_prof;
+
+}  // namespace
+
+struct svt_index {
+  uint32_t magic;
+  int device;
+  DevIndex dev;
+  int8_t *d_items = nullptr;
+  uint64_t *d_sigs = nullptr;
+  int32_t *d_perm = nullptr;
+  int32_t *d_offsets = nullptr;
+  int8_t *d_centroids = nullptr;
+  int32_t scan_wgs;                 // persistent workgroups of the fused kernel
+};
+
+// ------------------------------------------------------------------------------------------------
+extern "C" const char *svt_last_error(void) { return g_err.c_str(); }
+
+static void free_index_memory(svt_index *ix) {
+  if (ix->d_items) (void)hipFree(ix->d_items);
+  if (ix->d_sigs) (void)hipFree(ix->d_sigs);
+  if (ix->d_perm) (void)hipFree(ix->d_perm);
+  if (ix->d_offsets) (void)hipFree(ix->d_offsets);
+  if (ix->d_centroids) (void)hipFree(ix->d_centroids);
+}
+
+extern "C" int svt_index_upload(const svt_index_desc *d, void *hip_stream, svt_index **out) {
+  g_err.clear();
+  if (!d || !out) return fail(SVT_EINVAL, "svt_index_upload: NULL desc or out");
+  *out = nullptr;
+  if (d->n_items < 0 || d->n_items >= (int64_t(1) << 31))
+    return fail(SVT_EINVAL, "svt_index_upload: n_items %lld out of [0, 2^31)", (long long)d->n_items);
+  if (!supported_dim(d->dim)) return fail(SVT_EUNSUPPORTED, "svt_index_upload: dim %d not in {16,32,64,128,256}", d->dim);
+  if (d->sig_words != 1 && d->sig_words != 2)
+    return fail(SVT_EUNSUPPORTED, "svt_index_upload: sig_words %d not in {1,2}", d->sig_words);
+  if (d->nlist < 1 || d->nlist > 65536) return fail(SVT_EINVAL, "svt_index_upload: nlist %d out of [1, 65536]", d->nlist);
+  if (!(d->item_scale > 0.f)) return fail(SVT_EINVAL, "svt_index_upload: item_scale must be > 0");
+  if (!d->centroids) return fail(SVT_EINVAL, "svt_index_upload: NULL centroids");
+  if (d->n_items > 0 && (!d->items || !d->sigs || !d->list_of))
+    return fail(SVT_EINVAL, "svt_index_upload: NULL items, sigs or list_of");
+  const int64_t n = d->n_items;
+  const int32_t dim = d->dim, W = d->sig_words, nlist = d->nlist;
+  hipStream_t s = (hipStream_t)hip_stream;
+
+  // host: cluster sizes, offsets, stable cluster-contiguous order
+  std::vector<int32_t> offsets(nlist + 1, 0);
+  for (int64_t i = 0; i < n; ++i) {
+    const int32_t c = d->list_of[i];
+    if (c < 0 || c >= nlist) return fail(SVT_EINVAL, "svt_index_upload: list_of[%lld] = %d out of range", (long long)i, c);
+    ++offsets[c + 1];
+  }
+  for (int32_t c = 0; c < nlist; ++c) offsets[c + 1] += offsets[c];
+  std::vector<int32_t> perm((size_t)n), pos_of((size_t)n);
+  {
+    std::vector<int32_t> cur(offsets.begin(), offsets.end() - 1);
+    for (int64_t i = 0; i < n; ++i) {
+      const int32_t p = cur[d->list_of[i]]++;
+      perm[(size_t)p] = (int32_t)i;
+      pos_of[(size_t)i] = p;
+    }
+  }
+
+  svt_index *ix = new (std::nothrow) svt_index();
+  if (!ix) return fail(SVT_ENOMEM, "svt_index_upload: host allocation");
+  ix->magic = kMagic;
+  hipError_t e = hipGetDevice(&ix->device);
+  if (e != hipSuccess) { delete ix; return fail_hip(e, "hipGetDevice"); }
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, ix->device);
+  if (e != hipSuccess) { delete ix; return fail_hip(e, "hipGetDeviceProperties"); }
+  ix->scan_wgs = std::min(kMaxScanWGs, std::max(64, prop.multiProcessorCount * 4));
+
+  int32_t *d_pos_of = nullptr;
+  int8_t *stage_rows = nullptr;
+  uint64_t *stage_sigs = nullptr;
+  auto cleanup_fail = [&](hipError_t err, const char *what) {
+    if (d_pos_of) (void)hipFree(d_pos_of);
+    if (stage_rows) (void)hipFree(stage_rows);
+    if (stage_sigs) (void)hipFree(stage_sigs);
+    free_index_memory(ix);
+    delete ix;
+    return fail_hip(err, what);
+  };
+  const size_t nb = (size_t)std::max<int64_t>(n, 1);
+  if ((e = hipMalloc(&ix->d_items, nb * dim)) != hipSuccess) return cleanup_fail(e, "hipMalloc(items)");
+  if ((e = hipMalloc(&ix->d_sigs, nb * W * sizeof(uint64_t))) != hipSuccess) return cleanup_fail(e, "hipMalloc(sigs)");
+  if ((e = hipMalloc(&ix->d_perm, nb * sizeof(int32_t))) != hipSuccess) return cleanup_fail(e, "hipMalloc(perm)");
+  if ((e = hipMalloc(&ix->d_offsets, (nlist + 1) * sizeof(int32_t))) != hipSuccess) return cleanup_fail(e, "hipMalloc(offsets)");
+  if ((e = hipMalloc(&ix->d_centroids, (size_t)nlist * dim)) != hipSuccess) return cleanup_fail(e, "hipMalloc(centroids)");
+  if ((e = hipMemcpyAsync(ix->d_offsets, offsets.data(), (nlist + 1) * sizeof(int32_t), hipMemcpyHostToDevice, s)) != hipSuccess)
+    return cleanup_fail(e, "copy offsets");
+  if ((e = hipMemcpyAsync(ix->d_centroids, d->centroids, (size_t)nlist * dim, hipMemcpyHostToDevice, s)) != hipSuccess)
+    return cleanup_fail(e, "copy centroids");
+  if (n > 0) {
+    if ((e = hipMemcpyAsync(ix->d_perm, perm.data(), (size_t)n * sizeof(int32_t), hipMemcpyHostToDevice, s)) != hipSuccess)
+      return cleanup_fail(e, "copy perm");
+    // rows and signatures: staged in bounded chunks, scattered on the device to their positions
+    if ((e = hipMalloc(&d_pos_of, (size_t)n * sizeof(int32_t))) != hipSuccess) return cleanup_fail(e, "hipMalloc(pos_of)");
+    if ((e = hipMemcpyAsync(d_pos_of, pos_of.data(), (size_t)n * sizeof(int32_t), hipMemcpyHostToDevice, s)) != hipSuccess)
+      return cleanup_fail(e, "copy pos_of");
+    const int64_t chunk = std::min<int64_t>(n, std::max<int64_t>(1, (int64_t(256) << 20) / dim));
+    if ((e = hipMalloc(&stage_rows, (size_t)chunk * dim)) != hipSuccess) return cleanup_fail(e, "hipMalloc(stage)");
+    if ((e = hipMalloc(&stage_sigs, (size_t)chunk * W * sizeof(uint64_t))) != hipSuccess) return cleanup_fail(e, "hipMalloc(stage)");
+    for (int64_t i0 = 0; i0 < n; i0 += chunk) {
+      const int64_t m = std::min(chunk, n - i0);
+      if ((e = hipMemcpyAsync(stage_rows, d->items + (size_t)i0 * dim, (size_t)m * dim, hipMemcpyHostToDevice, s)) != hipSuccess)
+        return cleanup_fail(e, "copy rows");
+      if ((e = hipMemcpyAsync(stage_sigs, d->sigs + (size_t)i0 * W, (size_t)m * W * sizeof(uint64_t), hipMemcpyHostToDevice, s)) != hipSuccess)
+        return cleanup_fail(e, "copy sigs");
+      if ((e = launch_scatter_rows(stage_rows, stage_sigs, d_pos_of, i0, m, dim, W, ix->d_items, ix->d_sigs, s)) != hipSuccess)
+        return cleanup_fail(e, "scatter rows");
+      // the staging buffers are reused by the next chunk
+      if ((e = hipStreamSynchronize(s)) != hipSuccess) return cleanup_fail(e, "upload sync");
+    }
+  }
+  if ((e = hipStreamSynchronize(s)) != hipSuccess) return cleanup_fail(e, "upload sync");
+  if (d_pos_of) (void)hipFree(d_pos_of);
+  if (stage_rows) (void)hipFree(stage_rows);
+  if (stage_sigs) (void)hipFree(stage_sigs);
+
+  ix->dev.items = ix->d_items;
+  ix->dev.sigs = ix->d_sigs;
+  ix->dev.perm = ix->d_perm;
+  ix->dev.offsets = ix->d_offsets;
+  ix->dev.centroids = ix->d_centroids;
+  ix->dev.n_items = n;
+  ix->dev.dim = dim;
+  ix->dev.sig_words = W;
+  ix->dev.nlist = nlist;
+  ix->dev.item_scale = d->item_scale;
+  {
+    std::lock_guard<std::mutex> lk(g_live_mu);
+    g_live.insert(ix);
+  }
+  *out = ix;
+  return SVT_OK;
+}
+
+extern "C" int svt_index_free(svt_index *ix) {
+  g_err.clear();
+  if (!ix) return SVT_OK;
+  {
+    std::lock_guard<std::mutex> lk(g_live_mu);
+    if (!g_live.count(ix) || ix->magic != kMagic) return fail(SVT_ESTATE, "svt_index_free: not a live index");
+    g_live.erase(ix);
+  }
+  (void)hipDeviceSynchronize();
+  free_index_memory(ix);
+  ix->magic = 0;
+  delete ix;
+  return SVT_OK;
+}
+
+extern "C" int svt_index_info(const svt_index *ix, int64_t *n_items, int32_t *dim, int32_t *sig_words, int32_t *nlist) {
+  g_err.clear();
+  if (!ix || !is_live(ix)) return fail(SVT_ESTATE, "svt_index_info: not a live index");
+  if (n_items) *n_items = ix->dev.n_items;
+  if (dim) *dim = ix->dev.dim;
+  if (sig_words) *sig_words = ix->dev.sig_words;
+  if (nlist) *nlist = ix->dev.nlist;
+  return SVT_OK;
+}
+
+// ------------------------------------------------------------------------------------------------
+// workspace layout
+
+namespace {
+
+struct Layout {
+  size_t coarse_keys, probes, seg, qlen, qstart, thr, counter, slot_cnt, slot_keys, stats, total;
+};
+
+Layout layout(const svt_index *ix, int32_t B, int32_t nprobe, int32_t k) {
+  Layout L{};
+  const size_t P = (size_t)ix->scan_wgs, nlist = (size_t)ix->dev.nlist;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o += align256(bytes);
+    return at;
+  };
+  L.coarse_keys = take((size_t)B * nlist * sizeof(uint64_t));
+  L.probes = take((size_t)B * nprobe * sizeof(int32_t));
+  L.seg = take((size_t)B * (nprobe + 1) * sizeof(int32_t));
+  L.qlen = take((size_t)B * sizeof(int64_t));
+  L.qstart = take((size_t)(B + 1) * sizeof(int64_t));
+  L.thr = take((size_t)B * sizeof(int32_t));
+  L.counter = take(sizeof(uint32_t));
+  L.slot_cnt = take((P + B) * sizeof(int32_t));
+  L.slot_keys = take((P + B) * (size_t)k * sizeof(uint64_t));
+  L.stats = take((size_t)B * 2 * sizeof(int64_t));
+  L.total = o;
+  return L;
+}
+
+// SVT_OK or the error code (message set)
+int check_search_args(const svt_index *ix, int32_t B, int32_t nprobe, int32_t k, const char *who) {
+  if (!ix || !is_live(ix) || ix->magic != kMagic) return fail(SVT_ESTATE, "%s: not a live index", who);
+  if (B < 0 || B > 65535) return fail(SVT_EINVAL, "%s: n_queries %d out of [0, 65535]", who, B);
+  if (nprobe < 1 || nprobe > ix->dev.nlist) return fail(SVT_EINVAL, "%s: nprobe %d out of [1, %d]", who, nprobe, ix->dev.nlist);
+  if (k < 1 || k > SVT_MAX_K) return fail(SVT_EINVAL, "%s: k %d out of [1, %d]", who, k, SVT_MAX_K);
+  return SVT_OK;
+}
+
+}  // namespace
+
+extern "C" size_t svt_search_workspace_size(const svt_index *ix, int32_t n_queries, int32_t nprobe, int32_t k) {
+  g_err.clear();
+  if (check_search_args(ix, n_queries, nprobe, k, "svt_search_workspace_size") != SVT_OK) return 0;
+  return layout(ix, n_queries, nprobe, k).total;
+}
+
+extern "C" int svt_search(const svt_index *ix, int32_t B, const int8_t *queries, const uint64_t *masks,
+                          const float *query_scales, int32_t nprobe, int32_t k, int64_t *out_ids, int32_t *out_scores,
+                          float *out_fscores, int32_t *out_counts, int64_t *out_stats, void *workspace,
+                          size_t workspace_bytes, void *hip_stream) {
+  g_err.clear();
+  const int rc = check_search_args(ix, B, nprobe, k, "svt_search");
+  if (rc != SVT_OK) return rc;
+  if (B == 0) return SVT_OK;
+  if (!queries || !masks || !out_ids || !out_scores || !workspace)
+    return fail(SVT_EINVAL, "svt_search: NULL queries, masks, out_ids, out_scores or workspace");
+  if (((uintptr_t)workspace & 255) != 0) return fail(SVT_EINVAL, "svt_search: workspace not 256-byte aligned");
+  if (((uintptr_t)queries & 15) != 0) return fail(SVT_EINVAL, "svt_search: queries not 16-byte aligned");
+  if (((uintptr_t)masks & 7) != 0) return fail(SVT_EINVAL, "svt_search: masks not 8-byte aligned");
+  const Layout L = layout(ix, B, nprobe, k);
+  if (workspace_bytes < L.total)
+    return fail(SVT_EINVAL, "svt_search: workspace %zu bytes < required %zu", workspace_bytes, L.total);
+  hipStream_t s = (hipStream_t)hip_stream;
+  char *base = (char *)workspace;
+  Work w;
+  w.coarse_keys = (uint64_t *)(base + L.coarse_keys);
+  w.probes = (int32_t *)(base + L.probes);
+  w.seg = (int32_t *)(base + L.seg);
+  w.qlen = (int64_t *)(base + L.qlen);
+  w.qstart = (int64_t *)(base + L.qstart);
+  w.thr = (int32_t *)(base + L.thr);
+  w.counter = (uint32_t *)(base + L.counter);
+  w.slot_cnt = (int32_t *)(base + L.slot_cnt);
+  w.slot_keys = (uint64_t *)(base + L.slot_keys);
+  w.stats = out_stats ? out_stats : (int64_t *)(base + L.stats);
+  SearchShape sh{B, nprobe, k, ix->scan_wgs};
+
+  const bool prof = g_prof_on.load(std::memory_order_relaxed) != 0;
+  ProfState &ps = g_prof;
+  ps.n = 0;
+  auto mark = [&](const char *name) -> hipError_t {
+    if (!prof) return hipSuccess;
+    while ((int)ps.ev.size() <= ps.n) {
+      hipEvent_t ev;
+      hipError_t er = hipEventCreate(&ev);
+      if (er != hipSuccess) return er;
+      ps.ev.push_back(ev);
+      ps.names.push_back(nullptr);
+    }
+    ps.names[ps.n] = name;
+    return hipEventRecord(ps.ev[ps.n++], s);
+  };
+  hipError_t e;
+  if ((e = mark("start")) != hipSuccess) return fail_hip(e, "event");
+  if ((e = launch_coarse_keys(ix->dev, queries, B, w, s)) != hipSuccess) return fail_hip(e, "launch coarse_keys");
+  if ((e = mark("coarse")) != hipSuccess) return fail_hip(e, "event");
+  if ((e = launch_coarse_select(ix->dev, sh, w, s)) != hipSuccess) return fail_hip(e, "launch coarse_select");
+  if ((e = mark("select")) != hipSuccess) return fail_hip(e, "event");
+  if ((e = launch_scan(ix->dev, queries, masks, sh, w, s)) != hipSuccess) return fail_hip(e, "launch scan");
+  if ((e = mark("scan")) != hipSuccess) return fail_hip(e, "event");
+  if ((e = launch_merge(ix->dev, query_scales, sh, w, out_ids, out_scores, out_fscores, out_counts, s)) != hipSuccess)
+    return fail_hip(e, "launch merge");
+  if ((e = mark("merge")) != hipSuccess) return fail_hip(e, "event");
+  return SVT_OK;
+}
+
+extern "C" int svt_profile_enable(int on) {
+  g_prof_on.store(on ? 1 : 0);
+  return SVT_OK;
+}
+
+extern "C" int svt_profile_read(float *stage_ms, const char **stage_names, int32_t max_stages, int32_t *n_stages) {
+  g_err.clear();
+  ProfState &ps = g_prof;
+  const int n = ps.n > 1 ? ps.n - 1 : 0;
+  if (n_stages) *n_stages = n;
+  if (n == 0) return SVT_OK;
+  hipError_t e = hipEventSynchronize(ps.ev[ps.n - 1]);
+  if (e != hipSuccess) return fail_hip(e, "hipEventSynchronize");
+  for (int i = 0; i < n && i < max_stages; ++i) {
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, ps.ev[i], ps.ev[i + 1]);
+    if (e != hipSuccess) return fail_hip(e, "hipEventElapsedTime");
+    if (stage_ms) stage_ms[i] = ms;
+    if (stage_names) stage_names[i] = ps.names[i + 1];
+  }
+  return SVT_OK;
+}
+
+// ------------------------------------------------------------------------------------------------
+// Bloom signature helpers (host).  splitmix64 (Steele, Lea, Flood, OOPSLA 2014) seeded with the token
+// key; output j selects bit out_j >> (64 - log2(64 * sig_words)).
+
+namespace {
+
+inline uint64_t sm64_next(uint64_t &st) {
+  uint64_t z = (st += 0x9E3779B97F4A7C15ULL);
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ULL;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBULL;
+  return z ^ (z >> 31);
+}
+
+inline void token_bits(uint64_t key, int h, int W, uint64_t *sig) {
+  const int shift = 64 - (W == 1 ? 6 : 7);
+  uint64_t st = key;
+  for (int j = 0; j < h; ++j) {
+    const uint64_t b = sm64_next(st) >> shift;
+    sig[b >> 6] |= 1ULL << (b & 63);
+  }
+}
+
+}  // namespace
+
+extern "C" int svt_bloom_mask(const uint64_t *token_keys, int32_t n_tokens, int32_t n_hashes, int32_t sig_words,
+                              uint64_t *out) {
+  g_err.clear();
+  if (!out || n_tokens < 0 || (n_tokens > 0 && !token_keys) || n_hashes < 1 || n_hashes > 16)
+    return fail(SVT_EINVAL, "svt_bloom_mask: invalid arguments");
+  if (sig_words != 1 && sig_words != 2) return fail(SVT_EUNSUPPORTED, "svt_bloom_mask: sig_words %d", sig_words);
+  uint64_t m[2] = {0, 0};
+  for (int32_t t = 0; t < n_tokens; ++t) token_bits(token_keys[t], n_hashes, sig_words, m);
+  for (int32_t w = 0; w < sig_words; ++w) out[w] = m[w];
+  return SVT_OK;
+}
+
+extern "C" int svt_bloom_sign(const uint64_t *token_keys, int64_t n_items, int32_t tokens_per_item, int32_t n_hashes,
+                              int32_t sig_words, uint64_t *out, int32_t n_threads) {
+  g_err.clear();
+  if (n_items < 0 || tokens_per_item < 0 || (n_items > 0 && (!out || (tokens_per_item > 0 && !token_keys))) ||
+      n_hashes < 1 || n_hashes > 16)
+    return fail(SVT_EINVAL, "svt_bloom_sign: invalid arguments");
+  if (sig_words != 1 && sig_words != 2) return fail(SVT_EUNSUPPORTED, "svt_bloom_sign: sig_words %d", sig_words);
+  int nt = n_threads > 0 ? n_threads : (int)std::max(1u, std::thread::hardware_concurrency());
+  nt = (int)std::min<int64_t>(nt, std::max<int64_t>(1, n_items / 4096));
+  auto work = [&](int64_t i0, int64_t i1) {
+    for (int64_t i = i0; i < i1; ++i) {
+      uint64_t m[2] = {0, 0};
+      for (int32_t t = 0; t < tokens_per_item; ++t)
+        token_bits(token_keys[i * tokens_per_item + t], n_hashes, sig_words, m);
+      for (int32_t w = 0; w < sig_words; ++w) out[i * sig_words + w] = m[w];
+    }
+  };
+  if (nt <= 1) {
+    work(0, n_items);
+    return SVT_OK;
+  }
+  std::vector<std::thread> th;
+  for (int t = 0; t < nt; ++t) th.emplace_back(work, n_items * t / nt, n_items * (t + 1) / nt);
+  for (auto &x : th) x.join();
+  return SVT_OK;
+}

@@ -1,0 +1,197 @@
+"""GPU vs CPU oracle, element by element, on small seeded inputs that span several workgroup chunks,
+LDS list cuts and ragged tails; plus the degenerate cases of the method."""
+import numpy as np
+import pytest
+
+import oracle
+import oracle_pins as P
+import synth
+from gpu_common import check_invariants, compare, gpu_search, oracle_search, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def svt():
+    import torch
+    assert torch.cuda.is_available()
+    torch.cuda.set_device(0)
+    from int8_ivf_ann_amd import svt as m
+    m.lib()
+    return m
+
+
+def _run(svt, items, sigs, list_of, cent, scale, q, masks, nprobe, k, label, query_scales=None, invariants=True):
+    say(f"case {label}: n={items.shape[0]} d={items.shape[1]} W={sigs.shape[1]} nlist={cent.shape[0]} "
+        f"B={q.shape[0]} nprobe={nprobe} k={k}")
+    ix = svt.Index(items, sigs, list_of, cent, scale)
+    try:
+        got = gpu_search(ix, q, masks, nprobe, k, query_scales)
+    finally:
+        ix.close()
+    ref = oracle_search(items, sigs, list_of, cent, scale, q, masks, nprobe, k, query_scales)
+    compare(got, ref, k, label)
+    if invariants:
+        check_invariants(items, sigs, list_of, got, masks, q, k)
+    return got
+
+
+def test_tiny_preset(svt):
+    cat = synth.catalogue("tiny")
+    cfg = cat.cfg
+    W, h = cfg["sig_words"], cfg["n_hashes"]
+    qs = synth.queries(cat, 4)
+    sigs = svt.svt_bloom_sign(cat.tokens, h, W)
+    masks = np.stack([svt.svt_bloom_mask(qs.required(b), h, W) for b in range(4)])
+    orc = oracle.Oracle()
+    assert np.array_equal(sigs, orc.signatures(cat.tokens, h, W))
+    assert np.array_equal(masks, orc.masks(qs, h, W))
+    _run(svt, cat.items, sigs, cat.list_of, cat.centroids, cat.item_scale, qs.queries, masks, cfg["nprobe"],
+         cfg["k"], "tiny")
+
+
+def test_tiny_preset_more_queries(svt):
+    cat = synth.catalogue("tiny")
+    cfg = cat.cfg
+    W, h = cfg["sig_words"], cfg["n_hashes"]
+    qs = synth.queries(cat, 300, offset=1000)
+    sigs = svt.svt_bloom_sign(cat.tokens, h, W)
+    masks = np.stack([svt.svt_bloom_mask(qs.required(b), h, W) for b in range(300)])
+    for nprobe, k in ((1, 1), (8, 100), (64, 2048)):
+        _run(svt, cat.items, sigs, cat.list_of, cat.centroids, cat.item_scale, qs.queries, masks, nprobe, k,
+             f"tiny300-{nprobe}-{k}")
+
+
+def test_handworked_example(svt):
+    items, sigs, cl, cent, q, cases = P.load_handworked()
+    pad = lambda a: np.concatenate([a, np.zeros((a.shape[0], 12), np.int8)], axis=1)  # d 4 -> 16, same dots
+    items, cent, q = pad(items), pad(cent), pad(q)
+    ix = svt.Index(items, sigs, cl, cent, 2.0)
+    try:
+        for c in cases:
+            masks = np.array([[c["mask"]]], np.uint64)
+            ids, sc, fs, cnt, _ = gpu_search(ix, q, masks, c["nprobe"], c["k"], np.array([4.0], np.float32))
+            assert ids[0].tolist() == c["ids"] and sc[0].tolist() == c["scores"] and int(cnt[0]) == c["count"], c
+            assert fs[0].tolist() == c["fscores"], c
+    finally:
+        ix.close()
+
+
+@pytest.mark.parametrize("d", [16, 32, 64, 128, 256])
+@pytest.mark.parametrize("W", [1, 2])
+def test_random_shapes(svt, d, W):
+    rng = np.random.default_rng(100 + d + W)
+    items, sigs, cl, cent = P.small_catalogue(rng, n=7001, d=d, nlist=37, W=W, empty_clusters=4)
+    B = 9
+    q = rng.integers(-127, 128, (B, d)).astype(np.int8)
+    masks = P.random_masks(rng, B, W)
+    for nprobe, k in ((1, 1), (5, 37), (37, 300)):
+        _run(svt, items, sigs, cl, cent, 3.0, q, masks, nprobe, k, f"rand-d{d}-W{W}-{nprobe}-{k}")
+
+
+def test_large_k_many_candidates(svt):
+    # every query keeps ~40k candidates: LDS lists are cut many times and the merge selects
+    rng = np.random.default_rng(7)
+    items, sigs, cl, cent = P.small_catalogue(rng, n=120_000, d=64, nlist=8, W=1)
+    q = rng.integers(-127, 128, (5, 64)).astype(np.int8)
+    masks = np.zeros((5, 1), np.uint64)
+    masks[1, 0] = 1
+    masks[2, 0] = 0b101
+    _run(svt, items, sigs, cl, cent, 1.0, q, masks, 8, 2048, "largek")
+    _run(svt, items, sigs, cl, cent, 1.0, q, masks, 3, 2047, "largek-odd")
+
+
+def test_tie_heavy(svt):
+    rng = np.random.default_rng(8)
+    items, sigs, cl, cent = P.small_catalogue(rng, n=50_000, d=16, nlist=16, W=2, tie_heavy=True)
+    q = rng.integers(-1, 2, (6, 16)).astype(np.int8)
+    masks = np.zeros((6, 2), np.uint64)
+    _run(svt, items, sigs, cl, cent, 1.0, q, masks, 16, 2048, "ties-all")
+    _run(svt, items, sigs, cl, cent, 1.0, q, masks, 3, 500, "ties-ivf")
+
+
+def test_all_zero_items(svt):
+    # every score is 0: the result is the k lowest eligible ids of the probed clusters
+    rng = np.random.default_rng(9)
+    n, d = 30_000, 32
+    items = np.zeros((n, d), np.int8)
+    cl = rng.integers(0, 10, n).astype(np.int32)
+    cent = rng.integers(-5, 6, (10, d)).astype(np.int8)
+    sigs = rng.integers(0, 2**63, (n, 1), dtype=np.uint64)
+    q = rng.integers(-127, 128, (3, d)).astype(np.int8)
+    masks = np.zeros((3, 1), np.uint64)
+    got = _run(svt, items, sigs, cl, cent, 1.0, q, masks, 10, 2048, "zeros")
+    assert np.array_equal(got[0][0], np.arange(2048))
+
+
+def test_empty_and_degenerate(svt):
+    rng = np.random.default_rng(10)
+    items, sigs, cl, cent = P.small_catalogue(rng, n=3000, d=16, nlist=12, W=1, empty_clusters=6)
+    q = rng.integers(-127, 128, (4, 16)).astype(np.int8)
+    masks = np.zeros((4, 1), np.uint64)
+    masks[1, 0] = np.uint64(0xFFFFFFFFFFFFFFFF)        # nothing eligible
+    # query 2 prefers the empty clusters only
+    cent[6:] = 100
+    cent[:6] = -100
+    q[2] = 1
+    _run(svt, items, sigs, cl, cent, 1.0, q, masks, 1, 10, "degenerate-1")
+    _run(svt, items, sigs, cl, cent, 1.0, q, masks, 6, 10, "degenerate-6")
+    # single item, single cluster
+    _run(svt, items[:1], sigs[:1], np.zeros(1, np.int32), cent[:1], 1.0, q, masks, 1, 5, "single")
+
+
+def test_zero_queries(svt):
+    import torch
+    rng = np.random.default_rng(11)
+    items, sigs, cl, cent = P.small_catalogue(rng, n=100, d=16, nlist=4, W=1)
+    ix = svt.Index(items, sigs, cl, cent, 1.0)
+    q = torch.zeros((0, 16), dtype=torch.int8, device="cuda")
+    m = torch.zeros((0, 1), dtype=torch.int64, device="cuda")
+    ids, sc, fs, cnt, st = ix.search(q, m, 2, 5)
+    torch.cuda.synchronize()
+    assert ids.shape == (0, 5)
+    ix.close()
+
+
+def test_query_scales(svt):
+    rng = np.random.default_rng(12)
+    items, sigs, cl, cent = P.small_catalogue(rng, n=5000, d=32, nlist=8, W=1)
+    q = rng.integers(-127, 128, (4, 32)).astype(np.int8)
+    masks = P.random_masks(rng, 4, 1)
+    qs = np.array([1.0, 0.37, 250.0, 3.5], np.float32)
+    _run(svt, items, sigs, cl, cent, 17.25, q, masks, 4, 64, "qscales", query_scales=qs)
+
+
+def test_batch_composition_invariance(svt):
+    """A query's result does not depend on the other queries of its batch."""
+    rng = np.random.default_rng(13)
+    items, sigs, cl, cent = P.small_catalogue(rng, n=40_000, d=64, nlist=32, W=2)
+    B = 40
+    q = rng.integers(-127, 128, (B, 64)).astype(np.int8)
+    masks = P.random_masks(rng, B, 2)
+    ix = svt.Index(items, sigs, cl, cent, 1.0)
+    try:
+        full = gpu_search(ix, q, masks, 6, 500)
+        for b in (0, 17, 39):
+            one = gpu_search(ix, q[b:b + 1], masks[b:b + 1], 6, 500)
+            for a, c in zip(one, full):
+                assert np.array_equal(a[0], c[b])
+        again = gpu_search(ix, q, masks, 6, 500)
+        for a, c in zip(again, full):
+            assert np.array_equal(a, c)
+    finally:
+        ix.close()
+
+
+def test_zipf_skewed_cluster(svt):
+    rng = np.random.default_rng(14)
+    n, d, nlist = 200_000, 32, 64
+    items = rng.integers(-127, 128, (n, d)).astype(np.int8)
+    p = 1.0 / np.arange(1, nlist + 1) ** 1.5
+    cl = rng.choice(nlist, size=n, p=p / p.sum()).astype(np.int32)
+    cent = rng.integers(-127, 128, (nlist, d)).astype(np.int8)
+    sigs = rng.integers(0, 2**63, (n, 2), dtype=np.uint64)
+    q = rng.integers(-127, 128, (12, d)).astype(np.int8)
+    q[:6] = cent[0]      # half the queries probe the giant cluster first
+    masks = P.random_masks(rng, 12, 2, nbits_max=2)
+    _run(svt, items, sigs, cl, cent, 1.0, q, masks, 4, 2048, "zipf")
