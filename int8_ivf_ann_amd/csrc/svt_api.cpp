@@ -53,17 +53,19 @@ bool supported_dim(int32_t d) { return d == 16 || d == 32 || d == 64 || d == 128
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// stage timing (per process switch, per thread results)
+// stage timing: per-process switch; per-thread record of the searches since the last read
 std::atomic<int> g_prof_on{0};
+constexpr int kStages = 4;
+const char *const kStageNames[kStages] = {"coarse", "select", "scan", "merge"};
 struct ProfState {
-  std::vector<hipEvent_t> ev;
-  std::vector<const char *> names;
-  int n = 0;
+  std::vector<hipEvent_t> pool;   // kStages + 1 events per recorded search
+  int searches = 0;
   ~ProfState() {
-    for (auto e : ev) (void)hipEventDestroy(e);
+    for (auto e : pool) (void)hipEventDestroy(e);
   }
 };
 thread_local ProfState g_prof;
+constexpr int kMaxProfiledSearches = 100000;
 
 }  // namespace
 
@@ -307,32 +309,31 @@ extern "C" int svt_search(const svt_index *ix, int32_t B, const int8_t *queries,
   w.stats = out_stats ? out_stats : (int64_t *)(base + L.stats);
   SearchShape sh{B, nprobe, k, ix->scan_wgs};
 
-  const bool prof = g_prof_on.load(std::memory_order_relaxed) != 0;
+  const bool prof = g_prof_on.load(std::memory_order_relaxed) != 0 && g_prof.searches < kMaxProfiledSearches;
   ProfState &ps = g_prof;
-  ps.n = 0;
-  auto mark = [&](const char *name) -> hipError_t {
-    if (!prof) return hipSuccess;
-    while ((int)ps.ev.size() <= ps.n) {
+  int ev0 = 0, evn = 0;
+  if (prof) {
+    ev0 = ps.searches * (kStages + 1);
+    while ((int)ps.pool.size() < ev0 + kStages + 1) {
       hipEvent_t ev;
       hipError_t er = hipEventCreate(&ev);
-      if (er != hipSuccess) return er;
-      ps.ev.push_back(ev);
-      ps.names.push_back(nullptr);
+      if (er != hipSuccess) return fail_hip(er, "hipEventCreate");
+      ps.pool.push_back(ev);
     }
-    ps.names[ps.n] = name;
-    return hipEventRecord(ps.ev[ps.n++], s);
-  };
+  }
+  auto mark = [&]() -> hipError_t { return prof ? hipEventRecord(ps.pool[ev0 + evn++], s) : hipSuccess; };
   hipError_t e;
-  if ((e = mark("start")) != hipSuccess) return fail_hip(e, "event");
+  if ((e = mark()) != hipSuccess) return fail_hip(e, "event");
   if ((e = launch_coarse_keys(ix->dev, queries, B, w, s)) != hipSuccess) return fail_hip(e, "launch coarse_keys");
-  if ((e = mark("coarse")) != hipSuccess) return fail_hip(e, "event");
+  if ((e = mark()) != hipSuccess) return fail_hip(e, "event");
   if ((e = launch_coarse_select(ix->dev, sh, w, s)) != hipSuccess) return fail_hip(e, "launch coarse_select");
-  if ((e = mark("select")) != hipSuccess) return fail_hip(e, "event");
+  if ((e = mark()) != hipSuccess) return fail_hip(e, "event");
   if ((e = launch_scan(ix->dev, queries, masks, sh, w, s)) != hipSuccess) return fail_hip(e, "launch scan");
-  if ((e = mark("scan")) != hipSuccess) return fail_hip(e, "event");
+  if ((e = mark()) != hipSuccess) return fail_hip(e, "event");
   if ((e = launch_merge(ix->dev, query_scales, sh, w, out_ids, out_scores, out_fscores, out_counts, s)) != hipSuccess)
     return fail_hip(e, "launch merge");
-  if ((e = mark("merge")) != hipSuccess) return fail_hip(e, "event");
+  if ((e = mark()) != hipSuccess) return fail_hip(e, "event");
+  if (prof) ++ps.searches;
   return SVT_OK;
 }
 
@@ -341,21 +342,30 @@ extern "C" int svt_profile_enable(int on) {
   return SVT_OK;
 }
 
-extern "C" int svt_profile_read(float *stage_ms, const char **stage_names, int32_t max_stages, int32_t *n_stages) {
+extern "C" int svt_profile_read(float *stage_ms, const char **stage_names, int32_t max_stages, int32_t *n_stages,
+                                int32_t *n_searches) {
   g_err.clear();
   ProfState &ps = g_prof;
-  const int n = ps.n > 1 ? ps.n - 1 : 0;
-  if (n_stages) *n_stages = n;
-  if (n == 0) return SVT_OK;
-  hipError_t e = hipEventSynchronize(ps.ev[ps.n - 1]);
-  if (e != hipSuccess) return fail_hip(e, "hipEventSynchronize");
-  for (int i = 0; i < n && i < max_stages; ++i) {
-    float ms = 0.f;
-    e = hipEventElapsedTime(&ms, ps.ev[i], ps.ev[i + 1]);
-    if (e != hipSuccess) return fail_hip(e, "hipEventElapsedTime");
-    if (stage_ms) stage_ms[i] = ms;
-    if (stage_names) stage_names[i] = ps.names[i + 1];
+  const int ns = ps.searches;
+  if (n_stages) *n_stages = kStages;
+  if (n_searches) *n_searches = ns;
+  double tot[kStages] = {0, 0, 0, 0};
+  if (ns > 0) {
+    hipError_t e = hipEventSynchronize(ps.pool[ns * (kStages + 1) - 1]);
+    if (e != hipSuccess) return fail_hip(e, "hipEventSynchronize");
+    for (int r = 0; r < ns; ++r)
+      for (int i = 0; i < kStages; ++i) {
+        float ms = 0.f;
+        e = hipEventElapsedTime(&ms, ps.pool[r * (kStages + 1) + i], ps.pool[r * (kStages + 1) + i + 1]);
+        if (e != hipSuccess) return fail_hip(e, "hipEventElapsedTime");
+        tot[i] += ms;
+      }
   }
+  for (int i = 0; i < kStages && i < max_stages; ++i) {
+    if (stage_ms) stage_ms[i] = (float)tot[i];
+    if (stage_names) stage_names[i] = kStageNames[i];
+  }
+  ps.searches = 0;
   return SVT_OK;
 }
 

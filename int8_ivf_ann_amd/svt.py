@@ -66,7 +66,7 @@ def lib():
     L.svt_bloom_mask.argtypes = [vp, i32, i32, i32, vp]
     L.svt_bloom_sign.argtypes = [vp, i64, i32, i32, i32, vp, i32]
     L.svt_profile_enable.argtypes = [ctypes.c_int]
-    L.svt_profile_read.argtypes = [vp, vp, i32, vp]
+    L.svt_profile_read.argtypes = [vp, vp, i32, vp, vp]
     for name in EXPORTED:
         if name not in ("svt_search_workspace_size", "svt_last_error"):
             getattr(L, name).restype = ctypes.c_int
@@ -184,12 +184,13 @@ def svt_profile_enable(on: bool) -> None:
     _check(lib().svt_profile_enable(1 if on else 0))
 
 
-def svt_profile_read(max_stages: int = 16):
+def svt_profile_read(max_stages: int = 8):
+    """Returns ({stage: total ms}, n_searches) over the searches recorded since the last read."""
     ms = (ctypes.c_float * max_stages)()
     names = (ctypes.c_char_p * max_stages)()
-    n = ctypes.c_int32()
-    _check(lib().svt_profile_read(ms, names, max_stages, ctypes.byref(n)))
-    return [(names[i].decode(), float(ms[i])) for i in range(min(n.value, max_stages))]
+    n, ns = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().svt_profile_read(ms, names, max_stages, ctypes.byref(n), ctypes.byref(ns)))
+    return {names[i].decode(): float(ms[i]) for i in range(min(n.value, max_stages))}, ns.value
 
 
 # ------------------------------------------------------------------------------------------------
