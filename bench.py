@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU-seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic", default=None, help="traffic summary json (profiles/); default by workload")
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="run one device copy of this many MiB after the timed region (counter calibration)")
     return ap.parse_args()
 
 
@@ -155,6 +157,17 @@ def main():
     value = steps_elig / elapsed
     log(f"[bench] {args.steps} steps in {elapsed * 1e3:.2f} ms; stages (ms/step): "
         + ", ".join(f"{kname} {v / max(n_prof, 1):.4f}" for kname, v in stage_ms.items()))
+
+    if args.copy_calibration_mb > 0:
+        # a plain copy of known size, for scaling hardware byte counters (read + write of n bytes each)
+        nb = args.copy_calibration_mb << 20
+        src = torch.ones(nb // 8, dtype=torch.int64, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy: {nb} bytes read, {nb} bytes written")
+        del src, dst
 
     # algorithmic bytes of the scan kernel (numpy bookkeeping, outside the timed region)
     order = np.argsort(cat.list_of, kind="stable")

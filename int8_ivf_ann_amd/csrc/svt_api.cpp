@@ -136,7 +136,11 @@ extern "C" int svt_index_upload(const svt_index_desc *d, void *hip_stream, svt_i
   hipDeviceProp_t prop;
   e = hipGetDeviceProperties(&prop, ix->device);
   if (e != hipSuccess) { delete ix; return fail_hip(e, "hipGetDeviceProperties"); }
-  ix->scan_wgs = std::min(kMaxScanWGs, std::max(64, prop.multiProcessorCount * 4));
+  {
+    // one resident wave of persistent scan workgroups
+    const int per_cu = std::max(1, scan_blocks_per_cu(dim, W));
+    ix->scan_wgs = std::min(kMaxScanWGs, std::max(64, prop.multiProcessorCount * per_cu));
+  }
 
   int32_t *d_pos_of = nullptr;
   int8_t *stage_rows = nullptr;
@@ -235,12 +239,15 @@ extern "C" int svt_index_info(const svt_index *ix, int64_t *n_items, int32_t *di
 namespace {
 
 struct Layout {
-  size_t coarse_keys, probes, seg, qlen, qstart, thr, counter, slot_cnt, slot_keys, stats, total;
+  size_t coarse_keys, probes, seg, qlen, qcost, cstart, chunks, thr, hlo, hshift, ghist, counter, slot_cnt, slot_min, slot_keys, stats, total;
+  int32_t max_chunks;
 };
 
 Layout layout(const svt_index *ix, int32_t B, int32_t nprobe, int32_t k) {
   Layout L{};
-  const size_t P = (size_t)ix->scan_wgs, nlist = (size_t)ix->dev.nlist;
+  const size_t nlist = (size_t)ix->dev.nlist;
+  L.max_chunks = max_chunks_for(B, ix->scan_wgs);
+  const size_t C = (size_t)L.max_chunks;
   size_t o = 0;
   auto take = [&](size_t bytes) {
     size_t at = o;
@@ -251,11 +258,17 @@ Layout layout(const svt_index *ix, int32_t B, int32_t nprobe, int32_t k) {
   L.probes = take((size_t)B * nprobe * sizeof(int32_t));
   L.seg = take((size_t)B * (nprobe + 1) * sizeof(int32_t));
   L.qlen = take((size_t)B * sizeof(int64_t));
-  L.qstart = take((size_t)(B + 1) * sizeof(int64_t));
+  L.qcost = take((size_t)B * sizeof(int64_t));
+  L.cstart = take((size_t)(B + 1) * sizeof(int32_t));
+  L.chunks = take(C * sizeof(Chunk));
   L.thr = take((size_t)B * sizeof(int32_t));
-  L.counter = take(sizeof(uint32_t));
-  L.slot_cnt = take((P + B) * sizeof(int32_t));
-  L.slot_keys = take((P + B) * (size_t)k * sizeof(uint64_t));
+  L.hlo = take((size_t)B * sizeof(int32_t));
+  L.hshift = take((size_t)B * sizeof(int32_t));
+  L.ghist = take((size_t)B * kQHistBins * sizeof(uint32_t));
+  L.counter = take(2 * sizeof(uint32_t));
+  L.slot_cnt = take(C * sizeof(int32_t));
+  L.slot_min = take(C * sizeof(uint64_t));
+  L.slot_keys = take(C * (size_t)k * sizeof(uint64_t));
   L.stats = take((size_t)B * 2 * sizeof(int64_t));
   L.total = o;
   return L;
@@ -301,13 +314,19 @@ extern "C" int svt_search(const svt_index *ix, int32_t B, const int8_t *queries,
   w.probes = (int32_t *)(base + L.probes);
   w.seg = (int32_t *)(base + L.seg);
   w.qlen = (int64_t *)(base + L.qlen);
-  w.qstart = (int64_t *)(base + L.qstart);
+  w.qcost = (int64_t *)(base + L.qcost);
+  w.cstart = (int32_t *)(base + L.cstart);
+  w.chunks = (Chunk *)(base + L.chunks);
   w.thr = (int32_t *)(base + L.thr);
+  w.hlo = (int32_t *)(base + L.hlo);
+  w.hshift = (int32_t *)(base + L.hshift);
+  w.ghist = (uint32_t *)(base + L.ghist);
   w.counter = (uint32_t *)(base + L.counter);
   w.slot_cnt = (int32_t *)(base + L.slot_cnt);
+  w.slot_min = (uint64_t *)(base + L.slot_min);
   w.slot_keys = (uint64_t *)(base + L.slot_keys);
   w.stats = out_stats ? out_stats : (int64_t *)(base + L.stats);
-  SearchShape sh{B, nprobe, k, ix->scan_wgs};
+  SearchShape sh{B, nprobe, k, ix->scan_wgs, L.max_chunks};
 
   const bool prof = g_prof_on.load(std::memory_order_relaxed) != 0 && g_prof.searches < kMaxProfiledSearches;
   ProfState &ps = g_prof;
@@ -326,7 +345,8 @@ extern "C" int svt_search(const svt_index *ix, int32_t B, const int8_t *queries,
   if ((e = mark()) != hipSuccess) return fail_hip(e, "event");
   if ((e = launch_coarse_keys(ix->dev, queries, B, w, s)) != hipSuccess) return fail_hip(e, "launch coarse_keys");
   if ((e = mark()) != hipSuccess) return fail_hip(e, "event");
-  if ((e = launch_coarse_select(ix->dev, sh, w, s)) != hipSuccess) return fail_hip(e, "launch coarse_select");
+  if ((e = launch_coarse_select(ix->dev, queries, masks, sh, w, s)) != hipSuccess)
+    return fail_hip(e, "launch coarse_select");
   if ((e = mark()) != hipSuccess) return fail_hip(e, "event");
   if ((e = launch_scan(ix->dev, queries, masks, sh, w, s)) != hipSuccess) return fail_hip(e, "launch scan");
   if ((e = mark()) != hipSuccess) return fail_hip(e, "event");

@@ -9,9 +9,21 @@ namespace svt {
 
 constexpr int kMaxK = 2048;          // largest top-k (SVT_MAX_K)
 constexpr int kScanThreads = 256;    // fused filter-score-select workgroup: 4 wave64
-constexpr int kScanGroups = 4;       // 64-item groups per wave per step
+#ifndef SVT_SCAN_GROUPS
+#define SVT_SCAN_GROUPS 4
+#endif
+#ifndef SVT_ROW_BATCH
+#define SVT_ROW_BATCH 32
+#endif
+constexpr int kScanGroups = SVT_SCAN_GROUPS;   // 64-item groups per wave per step
+constexpr int kRowBatch = SVT_ROW_BATCH;       // rows a wave requests together (d <= 128)
 constexpr int kScanStep = kScanThreads * kScanGroups;   // items per workgroup step (1024)
-constexpr int kListCap = kMaxK + kScanStep;             // LDS candidate list capacity (keys)
+constexpr int kListCap = 4096;                          // LDS candidate list capacity (keys)
+constexpr int kTrimAt = kListCap - kScanStep;           // a list longer than this is trimmed
+constexpr int kTrimBins = 1024;                         // score histogram bins of a trim
+constexpr int kSegWin = 64;                             // probed clusters staged in LDS at a time
+constexpr int kQHistBins = 256;                         // bins of a query's global score histogram
+constexpr int kHistFlushSteps = 4;                      // scan steps between histogram flushes
 constexpr int kSelThreads = 1024;    // coarse-select and merge workgroups
 constexpr int kCoarseQB = 8;         // queries per coarse-score workgroup
 constexpr int kMaxScanWGs = 4096;    // upper bound on persistent scan workgroups
@@ -29,33 +41,57 @@ struct DevIndex {
   float item_scale;
 };
 
+// One unit of scan work: items [lo, hi) of query q's stream (the concatenation, in cluster order, of
+// the items of its probed clusters).
+struct Chunk {
+  int32_t q, lo, hi, pad;
+};
+
+constexpr int kCostSamples = kSelThreads;   // items sampled per query to estimate its filter density
+constexpr int kMaxChunksPerQuery = 2048;    // a query's stream is cut into at most this many chunks
+constexpr int kMergeCap = 6144;             // merge candidates staged in LDS
+constexpr int kSelSegLds = 4096;            // probe lists up to this long are searched in LDS
+constexpr int64_t kMinChunkCost = 16 << 10; // smallest chunk, in estimated bytes moved
+
 // Per-search device workspace (carved by the host from the caller's buffer).
 struct Work {
   uint64_t *coarse_keys;    // [B][nlist]   coarse (score, cluster) keys
   int32_t *probes;          // [B][nprobe]  probed clusters, ascending cluster id
   int32_t *seg;             // [B][nprobe + 1] stream offset of each probed cluster within its query
   int64_t *qlen;            // [B]          items scanned per query
-  int64_t *qstart;          // [B + 1]      exclusive prefix of qlen (the batch stream)
+  int64_t *qcost;           // [B]          estimated bytes the scan moves for the query
+  int32_t *cstart;          // [B + 1]      first chunk of each query; cstart[B] = number of chunks
+  Chunk *chunks;            // [max_chunks] the work list, in query order
   int32_t *thr;             // [B]          per-query proven lower bound on the k-th best score
-  uint32_t *counter;        // [1]          completion counter of the select kernel
-  int32_t *slot_cnt;        // [P + B]      candidates held by each (workgroup, query) run
-  uint64_t *slot_keys;      // [P + B][k]   those candidates (score/id keys)
+  int32_t *hlo;             // [B]          score at the lower edge of bin 1 of the query's histogram
+  int32_t *hshift;          // [B]          bin width of that histogram is 2^hshift
+  uint32_t *ghist;          // [B][kQHistBins] scores of every candidate any chunk accepted
+  uint32_t *counter;        // [2]          select completion counter, scan work-queue head
+  int32_t *slot_cnt;        // [max_chunks] candidates each chunk left
+  uint64_t *slot_min;       // [max_chunks] smallest key of a slot holding k keys, else 0
+  uint64_t *slot_keys;      // [max_chunks][k] those candidates (score/id keys)
   int64_t *stats;           // [B][2] scanned / eligible (caller buffer or workspace)
 };
 
 struct SearchShape {
-  int32_t B, nprobe, k, P;
+  int32_t B, nprobe, k, P, max_chunks;
 };
+
+// most chunks a search can produce: cost-balanced chunks number at most 4 P + B
+inline int32_t max_chunks_for(int32_t B, int32_t P) { return 4 * P + B + 1; }
 
 // launch wrappers (svt_kernels.hip); each returns hipSuccess or the launch error
 hipError_t launch_coarse_keys(const DevIndex &ix, const int8_t *queries, int32_t B, const Work &w,
                               hipStream_t s);
-hipError_t launch_coarse_select(const DevIndex &ix, const SearchShape &sh, const Work &w, hipStream_t s);
+hipError_t launch_coarse_select(const DevIndex &ix, const int8_t *queries, const uint64_t *masks,
+                                const SearchShape &sh, const Work &w, hipStream_t s);
 hipError_t launch_scan(const DevIndex &ix, const int8_t *queries, const uint64_t *masks, const SearchShape &sh,
                        const Work &w, hipStream_t s);
 hipError_t launch_merge(const DevIndex &ix, const float *query_scales, const SearchShape &sh, const Work &w,
                         int64_t *out_ids, int32_t *out_scores, float *out_fscores, int32_t *out_counts,
                         hipStream_t s);
+// resident scan workgroups per compute unit for this shape (0 if unknown)
+int scan_blocks_per_cu(int32_t dim, int32_t sig_words);
 hipError_t launch_scatter_rows(const int8_t *src_rows, const uint64_t *src_sigs, const int32_t *pos_of,
                                int64_t i0, int64_t n, int32_t dim, int32_t sig_words, int8_t *dst_rows,
                                uint64_t *dst_sigs, hipStream_t s);

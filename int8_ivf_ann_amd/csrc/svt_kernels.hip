@@ -53,12 +53,6 @@ __device__ __forceinline__ int mbcnt(uint64_t mask) {
   return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
-// items per contiguous chunk of the batch stream, shared by k_scan and k_merge
-__device__ __forceinline__ int64_t stream_chunk(int64_t L, int32_t P) {
-  int64_t c = (L + P - 1) / P;
-  return ((c + 63) / 64) * 64;
-}
-
 template <typename T>
 __device__ __forceinline__ T wave_incl_scan(T v) {
   const int l = lane_id();
@@ -186,7 +180,7 @@ __global__ __launch_bounds__(256) void k_coarse_keys(const int8_t *__restrict__ 
   __shared__ int4 qs[kCoarseQB][LPR];
   const int tid = threadIdx.x;
   const int b0 = blockIdx.y * kCoarseQB;
-  if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) *counter = 0u;
+  if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) { counter[0] = 0u; counter[1] = 0u; }
   for (int i = tid; i < kCoarseQB * LPR; i += 256) {
     int qi = i / LPR, ch = i % LPR;
     int b = b0 + qi;
@@ -214,16 +208,31 @@ __global__ __launch_bounds__(256) void k_coarse_keys(const int8_t *__restrict__ 
 // k_coarse_select: one workgroup per query.
 //   probes[b][0..nprobe): the nprobe clusters with the largest keys, in ascending cluster id
 //   seg[b][j]: offset of probed cluster j in query b's item stream; seg[b][nprobe] = qlen[b]
-// The last workgroup to finish turns qlen into the batch stream prefix qstart[0..B].
+//   qcost[b]: estimated bytes the scan moves for the query: signatures of every probed item plus the
+//             rows of the fraction of kCostSamples evenly spaced probed items that pass the filter
+// The last workgroup to finish cuts every query's stream into chunks of about equal estimated cost
+// (the scan's work list), so that a dense filter does not leave one workgroup with far more bytes.
 
-__global__ __launch_bounds__(kSelThreads) void k_coarse_select(const int32_t *__restrict__ offsets, int32_t nlist,
-                                                                int32_t B, int32_t nprobe, Work w) {
+template <int W>
+__device__ __forceinline__ bool passes(const uint64_t *__restrict__ sig, const uint64_t *mk) {
+  bool ok = true;
+#pragma unroll
+  for (int u = 0; u < W; ++u) ok = ok && ((sig[u] & mk[u]) == mk[u]);
+  return ok;
+}
+
+__global__ __launch_bounds__(kSelThreads) void k_coarse_select(DevIndex ix, const int8_t *__restrict__ queries,
+                                                                const uint64_t *__restrict__ masks, int32_t B,
+                                                                int32_t nprobe, int32_t P, Work w) {
   __shared__ SelScratch sel;
   __shared__ int wave_tot[kSelThreads / 64 + 1];
   __shared__ int64_t wave_tot64[kSelThreads / 64 + 1];
+  __shared__ int32_t seg_lds[kSelSegLds + 1];
   __shared__ int last;
-  const int tid = threadIdx.x;
+  __shared__ int smax_s;
+  const int tid = threadIdx.x, l = lane_id();
   const int b = blockIdx.x;
+  const int nlist = ix.nlist;
   const uint64_t *row = w.coarse_keys + (size_t)b * nlist;
   uint64_t T = 0;
   if (nprobe < nlist) {
@@ -239,53 +248,152 @@ __global__ __launch_bounds__(kSelThreads) void k_coarse_select(const int32_t *__
   for (int c0 = 0; c0 < nlist; c0 += kSelThreads) {
     const int c = c0 + tid;
     const bool take = c < nlist && row[c] >= T;
-    const int sz = take ? offsets[c + 1] - offsets[c] : 0;
+    const int sz = take ? ix.offsets[c + 1] - ix.offsets[c] : 0;
     int cnt_tot, sz_tot;
     const int idx = block_excl_scan<kSelThreads>(take ? 1 : 0, wave_tot, &cnt_tot);
     const int pre = block_excl_scan<kSelThreads>(sz, wave_tot, &sz_tot);
     if (take && base + idx < nprobe) {
       probes[base + idx] = c;
       seg[base + idx] = run + pre;
+      if (nprobe <= kSelSegLds) seg_lds[base + idx] = run + pre;
     }
     base += cnt_tot;
     run += sz_tot;
   }
   if (tid == 0) {
     seg[nprobe] = run;
+    if (nprobe <= kSelSegLds) seg_lds[nprobe] = run;
     w.qlen[b] = run;
     w.thr[b] = INT32_MIN;
     if (w.stats) { w.stats[2 * (size_t)b] = 0; w.stats[2 * (size_t)b + 1] = 0; }
   }
-  // last workgroup: exclusive prefix of qlen over the batch
+  __syncthreads();
+  // evenly spaced samples of the query's probed items: their filter density sizes the query's share of
+  // the work list; their scores place the query's score histogram (the bins sit between the mean
+  // sample score and twice the largest margin above it)
+  int hit = 0, have = 0;
+  int32_t sc = 0;
+  if (run > 0) {
+    const int32_t t = (int32_t)((int64_t)tid * run / kCostSamples);
+    int32_t pos;
+    if (nprobe == nlist) {
+      pos = t;   // every cluster probed, in id order: the stream is the position order
+    } else {
+      int lo = 0, hi = nprobe - 1;   // largest j with seg[j] <= t
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        const int32_t sv = nprobe <= kSelSegLds ? seg_lds[mid] : seg[mid];
+        if (sv <= t) lo = mid; else hi = mid - 1;
+      }
+      const int32_t s0 = nprobe <= kSelSegLds ? seg_lds[lo] : seg[lo];
+      pos = ix.offsets[probes[lo]] + (t - s0);
+    }
+    uint64_t mk[2] = {0, 0};
+    for (int u = 0; u < ix.sig_words; ++u) mk[u] = masks[(size_t)b * ix.sig_words + u];
+    const uint64_t *sg = ix.sigs + (size_t)pos * ix.sig_words;
+    hit = ix.sig_words == 2 ? passes<2>(sg, mk) : passes<1>(sg, mk);
+    const int4 *xr = reinterpret_cast<const int4 *>(ix.items + (size_t)pos * ix.dim);
+    const int4 *qr = reinterpret_cast<const int4 *>(queries + (size_t)b * ix.dim);
+    for (int ch = 0; ch < ix.dim / 16; ++ch) sc = dot16(xr[ch], qr[ch], sc);
+    have = 1;
+  }
+  if (tid == 0) smax_s = INT32_MIN;
+  int hits;
+  block_excl_scan<kSelThreads>(hit, wave_tot, &hits);
+  int64_t ssum;
+  block_excl_scan<kSelThreads>(have ? (int64_t)sc : (int64_t)0, wave_tot64, &ssum);
+  int32_t mx = have ? sc : INT32_MIN;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const int32_t t2 = __shfl_xor(mx, o);
+    mx = t2 > mx ? t2 : mx;
+  }
+  if (l == 0) atomicMax(&smax_s, mx);
+  for (int i = tid; i < kQHistBins; i += kSelThreads) w.ghist[(size_t)b * kQHistBins + i] = 0u;
+  __syncthreads();
+  if (tid == 0) {
+    const double dens = (double)hits / kCostSamples;
+    w.qcost[b] = (int64_t)((double)run * (8.0 * ix.sig_words + dens * ix.dim)) + run / 8 + 1;
+    int32_t lo = 0, shift = 0;
+    if (run > 0) {
+      lo = (int32_t)(ssum / kCostSamples);
+      const int64_t hi = (int64_t)smax_s + ((int64_t)smax_s - lo) + 1;
+      const uint32_t range = (uint32_t)(hi - lo);
+      const int bits = range ? 32 - __clz((int)range) : 0;
+      shift = bits > 8 ? bits - 8 : 0;                        // (range >> shift) < kQHistBins
+    }
+    w.hlo[b] = lo;
+    w.hshift[b] = shift;
+  }
+  // last workgroup: the work list
   __threadfence();
   __syncthreads();
-  if (tid == 0) last = (atomicAdd(w.counter, 1u) == (uint32_t)(B - 1)) ? 1 : 0;
+  if (tid == 0) last = (atomicAdd(&w.counter[0], 1u) == (uint32_t)(B - 1)) ? 1 : 0;
   __syncthreads();
   if (!last) return;
   __threadfence();
-  int64_t carry = 0;
+  int64_t total = 0;
   for (int i0 = 0; i0 < B; i0 += kSelThreads) {
     const int i = i0 + tid;
-    const int64_t v = i < B ? __hip_atomic_load(&w.qlen[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
+    const int64_t v = i < B ? __hip_atomic_load(&w.qcost[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
     int64_t tot;
-    const int64_t ex = block_excl_scan<kSelThreads>(v, wave_tot64, &tot);
-    if (i < B) w.qstart[i] = carry + ex;
+    block_excl_scan<kSelThreads>(v, wave_tot64, &tot);
+    total += tot;
+  }
+  const int64_t tc_min = (total + 4 * (int64_t)P - 1) / (4 * (int64_t)P);
+  const int64_t Tc = tc_min > kMinChunkCost ? tc_min : kMinChunkCost;   // target cost of one chunk
+  int32_t carry = 0;
+  for (int i0 = 0; i0 < B; i0 += kSelThreads) {
+    const int i = i0 + tid;
+    int32_t nch = 0;
+    if (i < B) {
+      const int64_t len = __hip_atomic_load(&w.qlen[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int64_t cost = __hip_atomic_load(&w.qcost[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (len > 0) {
+        int64_t cl = (Tc * len + cost - 1) / cost;                          // items of one chunk
+        const int64_t cl_min = (len + kMaxChunksPerQuery - 1) / kMaxChunksPerQuery;
+        cl = cl > cl_min ? cl : cl_min;
+        cl = ((cl + 63) / 64) * 64;
+        cl = cl < len ? cl : len;
+        nch = (int32_t)((len + cl - 1) / cl);
+      }
+    }
+    int32_t tot;
+    const int32_t ex = block_excl_scan<kSelThreads>(nch, wave_tot, &tot);
+    if (i < B) w.cstart[i] = carry + ex;
     carry += tot;
   }
-  if (tid == 0) w.qstart[B] = carry;
+  if (tid == 0) w.cstart[B] = carry;
+  __syncthreads();
+  // chunk table: chunk c belongs to the query whose [cstart[q], cstart[q+1]) holds c
+  for (int c = tid; c < carry; c += kSelThreads) {
+    int lo = 0, hi = B - 1;   // largest q with cstart[q] <= c
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (w.cstart[mid] <= c) lo = mid; else hi = mid - 1;
+    }
+    // chunks of ceil(len / nch) items: none is empty, since that never exceeds the length chosen above
+    const int64_t len = __hip_atomic_load(&w.qlen[lo], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int32_t nch = w.cstart[lo + 1] - w.cstart[lo];
+    const int64_t cl = (len + nch - 1) / nch;
+    const int32_t i = c - w.cstart[lo];
+    const int64_t l0 = (int64_t)i * cl, l1 = l0 + cl < len ? l0 + cl : len;
+    w.chunks[c] = Chunk{lo, (int32_t)l0, (int32_t)l1, 0};
+  }
 }
 
 // ------------------------------------------------------------------------------------------------
 // k_scan: the fused filter -> score -> select hot loop.
 //
-// The batch stream is the concatenation over queries of the items of each query's probed clusters
-// (qstart, seg).  Workgroup g owns stream positions [g*chunk, (g+1)*chunk) and walks them in order.
+// A query's stream is the concatenation of the items of its probed clusters (seg).  The work list
+// cuts every stream into chunks of about equal estimated cost; persistent workgroups take chunks from
+// it with an atomic counter and walk each chunk in order.
 // For each 64-item group a wave loads the 64 signatures with one 128-bit (or 64-bit) load per lane,
 // tests (sig & mask) == mask, ballots the result and compacts the survivors into an LDS list; rows of
 // survivors only are then fetched, LPR lanes per row with 16-byte loads, and scored with v_dot4.
 // A candidate enters the workgroup's LDS list if it beats both the list's own k-th key and the
 // query's global bound thr[q]; whenever the list exceeds k keys it is cut back to exactly k by an
-// LDS radix select.  When the workgroup leaves a query it writes its <= k keys to slot (g + q).
+// LDS trim.  At the end of a chunk the workgroup writes the chunk's exact top k keys to slot c.
 // Nothing per item is ever written to HBM.
 
 struct ScanArgs {
@@ -298,46 +406,171 @@ struct ScanArgs {
 
 struct ScanLds {
   uint64_t list[kListCap];
-  uint16_t wl[kScanThreads / 64][64 * kScanGroups];
+  union {
+    uint16_t wl[kScanThreads / 64][64 * kScanGroups];   // per-wave survivor offsets of one step
+    uint32_t hist[kTrimBins];                           // score histogram of a trim
+  } u;
   SelScratch sel;
   int wave_tot[kScanThreads / 64 + 1];
   unsigned long long kmin;
-  int cnt;
+  uint32_t smin, smax;
+  int cnt, cut_bin, cut_above;
+  // window of the run's probed clusters: stream range [t0, t1) and position base (pos = pbase + t)
+  int32_t seg_t0[kSegWin], seg_t1[kSegWin], seg_pb[kSegWin];
+  int seg_n;
+  uint32_t qh[kQHistBins];   // scores of candidates accepted since the last flush to the query's histogram
+  int32_t gbound;            // the query's bound as read once for the whole block
 };
 
+// Keys held while a run is in progress: (biased score << 32) | position.  They are turned into
+// (score, id) ordering keys (make_key) only for the few that survive to the end of the run, so the hot
+// loop never waits on the position -> id table.
+__device__ __forceinline__ uint64_t pos_key(int32_t score, int32_t pos) {
+  return ((uint64_t)((uint32_t)score ^ 0x80000000u) << 32) | (uint64_t)(uint32_t)pos;
+}
+
+// Keep the keys >= T of list[0..cnt) (T from block_select), in place; returns the count kept and the
+// smallest kept key in *kmin_out.  Two rounds over halves of the list keep the register footprint at
+// half a list: a round reads its half into registers, then (after a barrier) writes the kept keys at
+// or below positions every thread has already read.
+__device__ __forceinline__ int keep_at_least(ScanLds &sm, int cnt, uint64_t T, uint64_t *kmin_out) {
+  constexpr int HALF = kListCap / 2, PER = HALF / kScanThreads;
+  const int tid = threadIdx.x, l = lane_id();
+  if (tid == 0) sm.kmin = ~0ull;
+  unsigned long long mn = ~0ull;
+  int base = 0;
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    uint64_t mine[PER];
+    int keep = 0;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int i = r * HALF + tid + u * kScanThreads;
+      mine[u] = i < cnt ? sm.list[i] : 0ull;
+      keep += (i < cnt && mine[u] >= T) ? 1 : 0;
+    }
+    int tot;
+    int off = base + block_excl_scan<kScanThreads>(keep, sm.wave_tot, &tot);   // barriers inside
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int i = r * HALF + tid + u * kScanThreads;
+      if (i < cnt && mine[u] >= T) {
+        sm.list[off++] = mine[u];
+        mn = mine[u] < mn ? mine[u] : mn;
+      }
+    }
+    base += tot;
+    __syncthreads();
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    unsigned long long t = __shfl_xor(mn, o);
+    mn = t < mn ? t : mn;
+  }
+  if (l == 0) atomicMin(&sm.kmin, mn);
+  __syncthreads();
+  *kmin_out = sm.kmin;
+  __syncthreads();
+  return base;
+}
+
+// Score-only trim of a list of pos_keys holding more than k keys: histogram the biased scores into
+// kTrimBins bins over [min, max], find the bin b* at which the count from the top reaches k and drop
+// every key below b*'s lower edge s*.  At least k keys have score >= s*, so no dropped key can be in
+// the top k; ties at the edge are all kept.  Returns the count kept; *edge receives s* (biased).
+__device__ __forceinline__ int trim_by_score(ScanLds &sm, int cnt, int k, uint32_t *edge) {
+  const int tid = threadIdx.x, l = lane_id();
+  if (tid == 0) { sm.smin = ~0u; sm.smax = 0u; }
+  __syncthreads();
+  uint32_t lmin = ~0u, lmax = 0u;
+  for (int i = tid; i < cnt; i += kScanThreads) {
+    const uint32_t s = (uint32_t)(sm.list[i] >> 32);
+    lmin = s < lmin ? s : lmin;
+    lmax = s > lmax ? s : lmax;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    uint32_t a = __shfl_xor(lmin, o), b = __shfl_xor(lmax, o);
+    lmin = a < lmin ? a : lmin;
+    lmax = b > lmax ? b : lmax;
+  }
+  if (l == 0) { atomicMin(&sm.smin, lmin); atomicMax(&sm.smax, lmax); }
+  for (int i = tid; i < kTrimBins; i += kScanThreads) sm.u.hist[i] = 0u;
+  __syncthreads();
+  const uint32_t smin = sm.smin, range = sm.smax - smin;
+  const int bits = range ? 32 - __clz(range) : 0;            // range < 2^bits
+  const int shift = bits > 10 ? bits - 10 : 0;               // (range >> shift) < kTrimBins
+  for (int i = tid; i < cnt; i += kScanThreads)
+    atomicAdd(&sm.u.hist[((uint32_t)(sm.list[i] >> 32) - smin) >> shift], 1u);
+  __syncthreads();
+  if (tid < 64) {
+    constexpr int PB = kTrimBins / 64;
+    uint32_t h[PB], sum = 0;
+#pragma unroll
+    for (int j = 0; j < PB; ++j) { h[j] = sm.u.hist[PB * l + j]; sum += h[j]; }
+    uint32_t suf = sum;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      uint32_t v = __shfl_down(suf, off);
+      if (l + off < 64) suf += v;
+    }
+    uint32_t above = suf - sum;
+#pragma unroll
+    for (int j = PB - 1; j >= 0; --j) {
+      if (above < (uint32_t)k && above + h[j] >= (uint32_t)k) { sm.cut_bin = PB * l + j; sm.cut_above = (int)above; }
+      above += h[j];
+    }
+  }
+  __syncthreads();
+  const uint32_t e = smin + ((uint32_t)sm.cut_bin << shift);
+  *edge = e;
+  uint64_t dummy;
+  return keep_at_least(sm, cnt, (uint64_t)e << 32, &dummy);
+}
+
+// Replace every pos_key of the list by its (score, id) ordering key.
+__device__ __forceinline__ void to_id_keys(ScanLds &sm, int cnt, const int32_t *__restrict__ perm) {
+  for (int i = threadIdx.x; i < cnt; i += kScanThreads) {
+    const uint64_t pk = sm.list[i];
+    sm.list[i] = make_key((int32_t)((uint32_t)(pk >> 32) ^ 0x80000000u), (uint32_t)perm[(uint32_t)pk]);
+  }
+  __syncthreads();
+}
+
 template <int LPR, int W>
-__global__ __launch_bounds__(kScanThreads) void k_scan(ScanArgs a) {
+__global__ __launch_bounds__(kScanThreads, 4) void k_scan(ScanArgs a) {
   constexpr int D = 16 * LPR;
   constexpr int RPI = 64 / LPR;                          // rows scored per wave iteration
-  constexpr int R = (32 / RPI) > 0 ? (32 / RPI) : 1;     // iterations issued together
+  constexpr int R = (kRowBatch / RPI) > 0 ? (kRowBatch / RPI) : 1;   // row loads issued together per lane
   __shared__ ScanLds sm;
   const int tid = threadIdx.x, l = lane_id(), wv = tid / 64, sub = l % LPR;
-  const int g = blockIdx.x;
-  const int64_t *qstart = a.w.qstart;
-  const int64_t L = qstart[a.B];
-  const int64_t chunk = stream_chunk(L, a.P);
-  const int64_t beg = (int64_t)g * chunk;
-  const int64_t end = beg + chunk < L ? beg + chunk : L;
-  if (beg >= end) return;
-  // first query whose stream range contains beg: largest q with qstart[q] <= beg
-  int lo = 0, hi = a.B - 1;
-  while (lo < hi) {
-    int mid = (lo + hi + 1) >> 1;
-    if (qstart[mid] <= beg) lo = mid; else hi = mid - 1;
-  }
-  for (int q = lo; q < a.B && qstart[q] < end; ++q) {
-    const int64_t q0 = qstart[q], q1 = qstart[q + 1];
-    const int32_t ra = (int32_t)((beg > q0 ? beg : q0) - q0);
-    const int32_t rb = (int32_t)((end < q1 ? end : q1) - q0);
-    if (ra >= rb) continue;
+  const int k = a.k;
+  __shared__ int s_chunk;
+  const int n_chunks = a.w.cstart[a.B];
+  // persistent workgroups take chunks from the work list until it is empty
+  for (;;) {
+    if (tid == 0) s_chunk = (int)atomicAdd(&a.w.counter[1], 1u);
+    __syncthreads();
+    const int c = s_chunk;
+    if (c >= n_chunks) break;
+    const Chunk ch = a.w.chunks[c];
+    const int q = ch.q;
+    const int32_t ra = ch.lo, rb = ch.hi;
+    const int32_t hlo = a.w.hlo[q];
+    const int hsh = a.w.hshift[q];
+    uint32_t *gh = a.w.ghist + (size_t)q * kQHistBins;
+    for (int i = tid; i < kQHistBins; i += kScanThreads) sm.qh[i] = 0u;
     // query vector slice held by this lane, request mask
     const int4 qv = reinterpret_cast<const int4 *>(a.queries + (size_t)q * D)[sub];
     uint64_t mk[W];
 #pragma unroll
     for (int i = 0; i < W; ++i) mk[i] = a.masks[(size_t)q * W + i];
     if (tid == 0) sm.cnt = 0;
-    uint64_t thr_key = 0;            // list's k-th key once the list has been cut (0: none)
-    int32_t thr_score = INT32_MIN;
+    // local bound: every candidate below thr_s is out of this run's top k.  In exact mode (entered only
+    // when score ties defeat the histogram trim) keys carry ids and thr_key is the run's k-th key.
+    int32_t thr_s = INT32_MIN;
+    bool exact = false;
+    uint64_t thr_key = 0;
     int64_t n_elig = 0;
     const int32_t *seg = a.w.seg + (size_t)q * (a.nprobe + 1);
     const int32_t *probes = a.w.probes + (size_t)q * a.nprobe;
@@ -348,130 +581,273 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(ScanArgs a) {
       if (seg[mid] <= ra) jl = mid; else jh = mid - 1;
     }
     __syncthreads();
-    for (int j = jl; j < a.nprobe; ++j) {
-      const int32_t s0 = seg[j], s1 = seg[j + 1];
-      if (s0 >= rb) break;
-      const int32_t t0 = ra > s0 ? ra : s0, t1 = rb < s1 ? rb : s1;
-      if (t0 >= t1) continue;
-      const int64_t pbase = (int64_t)a.ix.offsets[probes[j]] - s0;   // position = pbase + stream offset
-      for (int32_t st = t0; st < t1; st += kScanStep) {
-        const int32_t n = (t1 - st) < kScanStep ? (t1 - st) : kScanStep;
-        const int64_t p0 = pbase + st;
-        const int32_t gthr = __hip_atomic_load(&a.w.thr[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const int32_t thr_eff = gthr > thr_score ? gthr : thr_score;
-        // --- filter: signatures of kScanGroups x 64 items per wave
-        uint64_t sg[kScanGroups][W];
+    // Steps walk the run's probed clusters in order; the signatures of step s+1 are requested before
+    // the rows of step s are scored, so one memory round trip covers both.  The run's clusters are
+    // staged in LDS (kSegWin at a time) so that walking them never waits on vector memory.
+    struct Cursor {
+      int w;            // entry in the LDS window; w == sm.seg_n: run finished
+      int32_t st, t1;   // step start / cluster end, in stream offsets
+      int32_t pbase;    // position = pbase + stream offset (positions < 2^31)
+    };
+    int jwin = jl;      // first probed cluster of the current window
+    auto load_window = [&]() {   // all threads; entries jwin .. (first cluster at or past rb)
+      __syncthreads();
+      if (tid == 0) sm.seg_n = 0;
+      __syncthreads();
+      for (int i = tid; i < kSegWin && jwin + i < a.nprobe; i += kScanThreads) {
+        const int j = jwin + i;
+        const int32_t s0 = seg[j], s1 = seg[j + 1];
+        if (s0 < rb) {
+          sm.seg_t0[i] = ra > s0 ? ra : s0;
+          sm.seg_t1[i] = rb < s1 ? rb : s1;
+          sm.seg_pb[i] = a.ix.offsets[probes[j]] - s0;
+          atomicMax(&sm.seg_n, i + 1);
+        }
+      }
+      __syncthreads();
+    };
+    auto seek = [&](Cursor &c) {   // from entry c.w: first entry with items left in [ra, rb)
+      for (;;) {
+        for (; c.w < sm.seg_n; ++c.w) {
+          const int32_t t0 = sm.seg_t0[c.w], t1 = sm.seg_t1[c.w];
+          if (t0 < t1) {
+            c.st = t0; c.t1 = t1; c.pbase = sm.seg_pb[c.w];
+            return;
+          }
+        }
+        // window exhausted: another one if the run continues past it
+        if (sm.seg_n < kSegWin || jwin + kSegWin >= a.nprobe || seg[jwin + kSegWin] >= rb) { c.w = -1; return; }
+        jwin += kSegWin;
+        load_window();
+        c.w = 0;
+      }
+    };
+    auto advance = [&](Cursor &c) {
+      c.st += kScanStep;
+      if (c.st >= c.t1) { ++c.w; seek(c); }
+    };
+    // bin of a score in the query's histogram: bin 0 holds everything below hlo + 2^hsh, bin b >= 1
+    // holds [hlo + b 2^hsh, hlo + (b+1) 2^hsh), the last bin everything above
+    auto qbin = [&](int32_t score) -> int {
+      if (score < hlo) return 0;
+      const int32_t b = (score - hlo) >> hsh;
+      return b < kQHistBins - 1 ? b : kQHistBins - 1;
+    };
+    // Add this workgroup's counts to the query's histogram, then raise the query's bound to the lower
+    // edge of the highest bin at which at least k accepted candidates (of every chunk) lie at or above.
+    // Each candidate is counted once, when it is accepted, so the bound is proven.  All threads call it.
+    auto hist_flush = [&]() {
+      for (int i = tid; i < kQHistBins; i += kScanThreads) {
+        const uint32_t v = sm.qh[i];
+        if (v) { atomicAdd(&gh[i], v); sm.qh[i] = 0u; }
+      }
+      __syncthreads();
+      if (tid < 64) {
+        constexpr int PB = kQHistBins / 64;
+        uint32_t h[PB], sum = 0;
 #pragma unroll
-        for (int gi = 0; gi < kScanGroups; ++gi) {
-          const int i = gi * kScanThreads + wv * 64 + l;
-          if (i < n) {
-            if constexpr (W == 2) {
-              const ulonglong2 v = reinterpret_cast<const ulonglong2 *>(a.ix.sigs)[p0 + i];
-              sg[gi][0] = v.x; sg[gi][1] = v.y;
+        for (int j = 0; j < PB; ++j) {
+          h[j] = __hip_atomic_load(&gh[PB * l + j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          sum += h[j];
+        }
+        uint32_t suf = sum;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const uint32_t v = __shfl_down(suf, off);
+          if (l + off < 64) suf += v;
+        }
+        uint32_t above = suf - sum;
+#pragma unroll
+        for (int j = PB - 1; j >= 0; --j) {
+          const int bin = PB * l + j;
+          if (bin >= 1 && above < (uint32_t)k && above + h[j] >= (uint32_t)k)
+            atomicMax(&a.w.thr[q], hlo + (bin << hsh));
+          above += h[j];
+        }
+      }
+    };
+    // Loads are issued unconditionally (out-of-range lanes read an in-range clamped address and are
+    // masked afterwards), so the compiler can count outstanding loads exactly and wait only for the
+    // ones it needs: the rows of this step, not the signatures already requested for the next.
+    uint64_t sg[kScanGroups][W];
+    int32_t sg_n = 0;
+    auto load_sigs = [&](const Cursor &c) {
+      sg_n = c.w >= 0 ? ((c.t1 - c.st) < kScanStep ? (c.t1 - c.st) : kScanStep) : 0;
+      const int32_t p0 = c.w >= 0 ? c.pbase + c.st : 0;
+      const int32_t last = sg_n > 0 ? sg_n - 1 : 0;
+#pragma unroll
+      for (int gi = 0; gi < kScanGroups; ++gi) {
+        const int i = gi * kScanThreads + wv * 64 + l;
+        const int32_t p = p0 + (i < last ? i : last);
+        if constexpr (W == 2) {
+          const ulonglong2 v = reinterpret_cast<const ulonglong2 *>(a.ix.sigs)[p];
+          sg[gi][0] = v.x; sg[gi][1] = v.y;
+        } else {
+          sg[gi][0] = a.ix.sigs[p];
+        }
+      }
+    };
+    load_window();
+    int steps = 0;
+    Cursor cur{0, 0, 0, 0};
+    seek(cur);
+    load_sigs(cur);
+    while (cur.w >= 0) {
+      const int32_t n = sg_n;
+      const int32_t p0 = cur.pbase + cur.st;
+      // the query's global bound only ever rises, so a stale read merely prunes less
+      const int32_t gthr = *(volatile const int32_t *)&a.w.thr[q];
+      const int32_t thr_eff = gthr > thr_s ? gthr : thr_s;
+      // --- filter this step's signatures, compact the survivors per wave
+      int nw = 0;
+#pragma unroll
+      for (int gi = 0; gi < kScanGroups; ++gi) {
+        const int i = gi * kScanThreads + wv * 64 + l;
+        bool pass = i < n;
+#pragma unroll
+        for (int u = 0; u < W; ++u) pass = pass && ((sg[gi][u] & mk[u]) == mk[u]);
+        const uint64_t bal = __ballot(pass);
+        if (pass) sm.u.wl[wv][nw + mbcnt(bal)] = (uint16_t)i;
+        nw += __popcll(bal);
+      }
+      n_elig += nw;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // --- rows of the first R x RPI survivors, then the next step's signatures, all in flight
+      int4 x[R];
+      int32_t pos[R];
+      bool v[R];
+      auto load_rows = [&](int r0) {
+#pragma unroll
+        for (int u = 0; u < R; ++u) {
+          const int r = r0 + u * RPI + l / LPR;
+          v[u] = r < nw;
+          pos[u] = p0 + (v[u] ? (int)sm.u.wl[wv][r] : 0);
+          x[u] = reinterpret_cast<const int4 *>(a.ix.items + (size_t)pos[u] * D)[sub];
+        }
+      };
+      auto score_rows = [&]() {
+#pragma unroll
+        for (int u = 0; u < R; ++u) {
+          int32_t acc = dot16(x[u], qv, 0);
+#pragma unroll
+          for (int off = 1; off < LPR; off <<= 1) acc += __shfl_xor(acc, off);
+          if (sub == 0 && v[u] && acc >= thr_eff) {
+            if (!exact) {
+              sm.list[atomicAdd(&sm.cnt, 1)] = pos_key(acc, pos[u]);
+              atomicAdd(&sm.qh[qbin(acc)], 1u);
             } else {
-              sg[gi][0] = a.ix.sigs[p0 + i];
-            }
-          } else {
-#pragma unroll
-            for (int u = 0; u < W; ++u) sg[gi][u] = 0;
-          }
-        }
-        int nw = 0;
-#pragma unroll
-        for (int gi = 0; gi < kScanGroups; ++gi) {
-          const int i = gi * kScanThreads + wv * 64 + l;
-          bool pass = i < n;
-#pragma unroll
-          for (int u = 0; u < W; ++u) pass = pass && ((sg[gi][u] & mk[u]) == mk[u]);
-          const uint64_t bal = __ballot(pass);
-          if (pass) sm.wl[wv][nw + mbcnt(bal)] = (uint16_t)i;
-          nw += __popcll(bal);
-        }
-        n_elig += nw;
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        // --- score the survivors: LPR lanes per row, R x RPI rows in flight per wave
-        for (int r0 = 0; r0 < nw; r0 += RPI * R) {
-          int4 x[R];
-          int64_t pos[R];
-          bool v[R];
-#pragma unroll
-          for (int u = 0; u < R; ++u) {
-            const int r = r0 + u * RPI + l / LPR;
-            v[u] = r < nw;
-            const int i = v[u] ? (int)sm.wl[wv][r] : 0;
-            pos[u] = p0 + i;
-            x[u] = v[u] ? reinterpret_cast<const int4 *>(a.ix.items + (size_t)pos[u] * D)[sub] : make_int4(0, 0, 0, 0);
-          }
-#pragma unroll
-          for (int u = 0; u < R; ++u) {
-            int32_t acc = dot16(x[u], qv, 0);
-#pragma unroll
-            for (int off = 1; off < LPR; off <<= 1) acc += __shfl_xor(acc, off);
-            if (sub == 0 && v[u] && acc >= thr_eff) {
               const uint64_t key = make_key(acc, (uint32_t)a.ix.perm[pos[u]]);
               if (key > thr_key) {
-                const int slot = atomicAdd(&sm.cnt, 1);
-                sm.list[slot] = key;
+                sm.list[atomicAdd(&sm.cnt, 1)] = key;
+                atomicAdd(&sm.qh[qbin(acc)], 1u);
               }
             }
           }
         }
-        __syncthreads();
-        // --- keep the list at most k keys: cut to exactly k, raise the local and global bounds
-        if (sm.cnt > a.k) {
-          const int cnt = sm.cnt;
+      };
+      if (nw > 0) load_rows(0);
+      advance(cur);
+      load_sigs(cur);
+      if (nw > 0) score_rows();
+      // survivors beyond the first batch (dense filters)
+      for (int r0 = RPI * R; r0 < nw; r0 += RPI * R) {
+        load_rows(r0);
+        score_rows();
+      }
+      __syncthreads();
+      // --- trim the list when the next step could overflow it
+      if (sm.cnt > kTrimAt) {
+        const int cnt = sm.cnt;
+        int kept;
+        if (!exact) {
+          uint32_t edge;
+          kept = trim_by_score(sm, cnt, k, &edge);
+          thr_s = (int32_t)(edge ^ 0x80000000u);
+          if (kept > kTrimAt) {
+            // ties at the edge: switch this run to exact (score, id) keys and cut to exactly k
+            to_id_keys(sm, kept, a.ix.perm);
+            const uint64_t T = block_select<kScanThreads>(
+                [&](auto f) {
+                  for (int i = tid; i < kept; i += kScanThreads) f(sm.list[i]);
+                },
+                k, sm.sel);
+            kept = keep_at_least(sm, kept, T, &thr_key);
+            thr_s = key_score(thr_key);
+            exact = true;
+          }
+        } else {
           const uint64_t T = block_select<kScanThreads>(
               [&](auto f) {
                 for (int i = tid; i < cnt; i += kScanThreads) f(sm.list[i]);
               },
-              a.k, sm.sel);
-          constexpr int PER = kListCap / kScanThreads;
-          uint64_t mine[PER];
-          int keep = 0;
-#pragma unroll
-          for (int u = 0; u < PER; ++u) {
-            const int i = tid + u * kScanThreads;
-            mine[u] = i < cnt ? sm.list[i] : 0ull;
-            keep += (i < cnt && mine[u] >= T) ? 1 : 0;
-          }
-          if (tid == 0) sm.kmin = ~0ull;
-          int tot;
-          int off = block_excl_scan<kScanThreads>(keep, sm.wave_tot, &tot);
-          unsigned long long mn = ~0ull;
-#pragma unroll
-          for (int u = 0; u < PER; ++u) {
-            const int i = tid + u * kScanThreads;
-            if (i < cnt && mine[u] >= T) {
-              sm.list[off++] = mine[u];
-              mn = mine[u] < mn ? mine[u] : mn;
-            }
-          }
-#pragma unroll
-          for (int o = 32; o > 0; o >>= 1) {
-            unsigned long long t = __shfl_xor(mn, o);
-            mn = t < mn ? t : mn;
-          }
-          if (l == 0) atomicMin(&sm.kmin, mn);
-          __syncthreads();
-          thr_key = sm.kmin;
-          thr_score = key_score(thr_key);
-          if (tid == 0) {
-            sm.cnt = tot;
-            atomicMax(&a.w.thr[q], thr_score);
-          }
-          __syncthreads();
+              k, sm.sel);
+          kept = keep_at_least(sm, cnt, T, &thr_key);
+          thr_s = key_score(thr_key);
         }
+        if (tid == 0) {
+          sm.cnt = kept;
+          atomicMax(&a.w.thr[q], thr_s);   // at least k candidates score >= thr_s
+        }
+        __syncthreads();
+      }
+      // flush after steps 2, 4, 8, ...: the bound converges within a few flushes
+      ++steps;
+      if (steps >= 2 && (steps & (steps - 1)) == 0) {
+        hist_flush();
+        __syncthreads();
       }
     }
-    // --- leave the query: publish this run's keys in slot (g + q)
-    const int cnt = sm.cnt;
-    const size_t slot = (size_t)g + (size_t)q;
-    uint64_t *dst = a.w.slot_keys + slot * (size_t)a.k;
+    // --- end of the chunk: its exact top k above the query's bound, published in slot c
+    hist_flush();
+    __syncthreads();
+    int cnt = sm.cnt;
+    if (!exact) to_id_keys(sm, cnt, a.ix.perm);
+    uint64_t kth = 0;
+    if (cnt > k) {
+      const uint64_t T = block_select<kScanThreads>(
+          [&](auto f) {
+            for (int i = tid; i < cnt; i += kScanThreads) f(sm.list[i]);
+          },
+          k, sm.sel);
+      cnt = keep_at_least(sm, cnt, T, &kth);
+      if (tid == 0) atomicMax(&a.w.thr[q], key_score(kth));
+      __syncthreads();
+    }
+    {
+      // keys below the query's bound (as raised by every chunk so far) cannot be in its top k.  Other
+      // workgroups raise the bound concurrently, so one thread reads it and the block uses that value:
+      // the branch below contains barriers and must be taken by every thread alike.
+      if (tid == 0) sm.gbound = *(volatile const int32_t *)&a.w.thr[q];
+      __syncthreads();
+      const int32_t gb = sm.gbound;
+      __syncthreads();
+      if (gb != INT32_MIN) cnt = keep_at_least(sm, cnt, make_key(gb, 0xFFFFFFFFu), &kth);
+      else if (cnt == k) {
+        if (tid == 0) sm.kmin = ~0ull;
+        __syncthreads();
+        unsigned long long mn = ~0ull;
+        for (int i = tid; i < cnt; i += kScanThreads) mn = sm.list[i] < mn ? sm.list[i] : mn;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+          unsigned long long t = __shfl_xor(mn, o);
+          mn = t < mn ? t : mn;
+        }
+        if (l == 0) atomicMin(&sm.kmin, mn);
+        __syncthreads();
+        kth = sm.kmin;
+      }
+    }
+    const size_t slot = (size_t)c;
+    uint64_t *dst = a.w.slot_keys + slot * (size_t)k;
     for (int i = tid; i < cnt; i += kScanThreads) dst[i] = sm.list[i];
-    if (tid == 0) a.w.slot_cnt[slot] = cnt;
-    // per-query counters: items scanned by this run, items that passed the filter
+    if (tid == 0) {
+      a.w.slot_cnt[slot] = cnt;
+      // a full slot proves k keys >= its smallest one
+      a.w.slot_min[slot] = cnt == k ? kth : 0ull;
+    }
+    // per-query counters: items scanned by this chunk, items that passed the filter
     if (a.w.stats) {
       // n_elig is uniform across the wave: one add per wave
       if (l == 0) atomicAdd((unsigned long long *)&a.w.stats[2 * (size_t)q + 1], (unsigned long long)n_elig);
@@ -497,66 +873,200 @@ struct MergeArgs {
 };
 
 __global__ __launch_bounds__(kSelThreads) void k_merge(MergeArgs a) {
+  constexpr int kBins = 2048;
   __shared__ SelScratch sel;
-  __shared__ uint64_t buf[kMaxK];
-  __shared__ int scnt[kMaxScanWGs + 1];
+  __shared__ union {
+    uint64_t cand[kMergeCap];
+    uint32_t hist[kBins];
+  } mu;
+  __shared__ int sprefix[kMaxChunksPerQuery];
   __shared__ int wave_tot[kSelThreads / 64 + 1];
-  __shared__ int nbuf;
-  const int tid = threadIdx.x, l = lane_id(), wv = tid / 64;
-  constexpr int NW = kSelThreads / 64;
+  __shared__ int ncand, cut_bin;
+  __shared__ unsigned long long bound;
+  __shared__ uint32_t smin, smax;
+  uint64_t *cand = mu.cand;
+  const int tid = threadIdx.x, l = lane_id();
   const int q = blockIdx.x;
   const int k = a.k;
-  const int64_t q0 = a.w.qstart[q], q1 = a.w.qstart[q + 1];
-  int total = 0, ns = 0;
-  size_t s0 = 0;
-  if (q1 > q0) {
-    const int64_t chunk = stream_chunk(a.w.qstart[a.B], a.P);
-    const int64_t g0 = q0 / chunk, g1 = (q1 - 1) / chunk;
-    s0 = (size_t)g0 + (size_t)q;
-    ns = (int)(g1 - g0 + 1);
-    int part = 0;
-    for (int i = tid; i < ns; i += kSelThreads) {
-      const int c = a.w.slot_cnt[s0 + i];
-      scnt[i] = c;
-      part += c;
+  // the query's chunks, hence its slots, are cstart[q] .. cstart[q+1]-1 (contiguous in memory)
+  const size_t s0 = (size_t)a.w.cstart[q];
+  const int ns = a.w.cstart[q + 1] - a.w.cstart[q];
+  if (tid == 0) { ncand = 0; bound = 0ull; smin = ~0u; smax = 0u; }
+  __syncthreads();
+  // 1. counts and a proven lower bound on the k-th key: the largest smallest-key of a full slot
+  unsigned long long lb = 0ull;
+  int total = 0;
+  for (int i0 = 0; i0 < ns; i0 += kSelThreads) {
+    const int i = i0 + tid;
+    const int c = i < ns ? a.w.slot_cnt[s0 + i] : 0;
+    if (c == k) {
+      const uint64_t m = a.w.slot_min[s0 + i];
+      lb = m > lb ? m : lb;
     }
-    block_excl_scan<kSelThreads>(part, wave_tot, &total);
+    int tot;
+    const int ex = block_excl_scan<kSelThreads>(c, wave_tot, &tot);   // barriers inside
+    if (i < ns) sprefix[i] = total + ex;
+    total += tot;
   }
-  const uint64_t *keys = a.w.slot_keys;
-  auto visit = [&](auto f) {
-    for (int s = wv; s < ns; s += NW) {
-      const uint64_t *src = keys + (s0 + (size_t)s) * (size_t)k;
-      const int c = scnt[s];
-      for (int i = l; i < c; i += 64) f(src[i]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    unsigned long long t = __shfl_xor(lb, o);
+    lb = t > lb ? t : lb;
+  }
+  if (l == 0) atomicMax(&bound, lb);
+  __syncthreads();
+  uint64_t T = total > k ? (uint64_t)bound : 0ull;
+  if (total > k) {
+    // every chunk is done: the query's global score bound is final
+    const int32_t g = a.w.thr[q];
+    if (g != INT32_MIN) {
+      const uint64_t gk = make_key(g, 0xFFFFFFFFu);   // smallest key with score g
+      T = gk > T ? gk : T;
+    }
+  }
+  // keys >= lo of all slots, visited as one flat range over the valid keys (sprefix[s] = keys before
+  // slot s), eight loads in flight per thread
+  const uint64_t *keys = a.w.slot_keys + s0 * (size_t)k;
+  auto key_at = [&](int f) -> uint64_t {   // f-th valid key, 0 <= f < total
+    int lo = 0, hi = ns - 1;                 // largest slot with sprefix <= f
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (sprefix[mid] <= f) lo = mid; else hi = mid - 1;
+    }
+    return keys[(size_t)lo * k + (f - sprefix[lo])];
+  };
+  auto visit = [&](uint64_t lo, auto f) {
+    for (int i0 = tid; i0 < total; i0 += kSelThreads * 8) {
+      uint64_t v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = i0 + u * kSelThreads;
+        v[u] = i < total ? key_at(i) : 0ull;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (i0 + u * kSelThreads < total && v[u] >= lo) f(v[u]);
     }
   };
-  const int nout = total < k ? total : k;
-  uint64_t T = 0;
-  if (total > k) T = block_select<kSelThreads>(visit, k, sel);
-  if (tid == 0) nbuf = 0;
-  __syncthreads();
-  if (nout > 0) {
-    visit([&](uint64_t key) {
-      if (key >= T) {
-        const int o = atomicAdd(&nbuf, 1);
-        if (o < kMaxK) buf[o] = key;
-      }
+  if (total > k) {
+    // 2. pin the k-th key's score to one bin of a score histogram over [min, max]
+    uint32_t lmin = ~0u, lmax = 0u;
+    visit(T, [&](uint64_t key) {
+      const uint32_t sc = (uint32_t)(key >> 32);
+      lmin = sc < lmin ? sc : lmin;
+      lmax = sc > lmax ? sc : lmax;
     });
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      uint32_t x = __shfl_xor(lmin, o), y = __shfl_xor(lmax, o);
+      lmin = x < lmin ? x : lmin;
+      lmax = y > lmax ? y : lmax;
+    }
+    if (l == 0) { atomicMin(&smin, lmin); atomicMax(&smax, lmax); }
+    for (int i = tid; i < kBins; i += kSelThreads) mu.hist[i] = 0u;
+    __syncthreads();
+    const uint32_t bmin = smin, range = smax - smin;
+    const int bits = range ? 32 - __clz(range) : 0;
+    const int shift = bits > 11 ? bits - 11 : 0;          // (range >> shift) < kBins
+    visit(T, [&](uint64_t key) { atomicAdd(&mu.hist[((uint32_t)(key >> 32) - bmin) >> shift], 1u); });
+    __syncthreads();
+    if (tid < 64) {
+      constexpr int PB = kBins / 64;
+      uint32_t h[PB], sum = 0;
+#pragma unroll
+      for (int j = 0; j < PB; ++j) { h[j] = mu.hist[PB * l + j]; sum += h[j]; }
+      uint32_t suf = sum;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        uint32_t v = __shfl_down(suf, off);
+        if (l + off < 64) suf += v;
+      }
+      uint32_t above = suf - sum;
+#pragma unroll
+      for (int j = PB - 1; j >= 0; --j) {
+        if (above < (uint32_t)k && above + h[j] >= (uint32_t)k) cut_bin = PB * l + j;
+        above += h[j];
+      }
+    }
+    __syncthreads();
+    // at least k keys have a score >= the edge of the cut bin: smaller keys cannot be in the top k
+    const uint32_t edge = bmin + ((uint32_t)cut_bin << shift);
+    const uint64_t ek = (uint64_t)edge << 32;
+    T = ek > T ? ek : T;
+    __syncthreads();   // hist and cand share LDS
+  }
+  // 3. stage the surviving keys in LDS (one LDS atomic per wave)
+  for (int i0 = tid - l; i0 < total; i0 += kSelThreads * 8) {   // wave-uniform trip count
+    uint64_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + l + u * kSelThreads;
+      v[u] = i < total ? key_at(i) : 0ull;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const bool take = i0 + l + u * kSelThreads < total && v[u] >= T;
+      const uint64_t bal = __ballot(take);
+      int base = 0;
+      if (l == 0 && bal) base = atomicAdd(&ncand, __popcll(bal));
+      base = __shfl(base, 0);
+      const int o = base + mbcnt(bal);
+      if (take && o < kMergeCap) cand[o] = v[u];
+    }
   }
   __syncthreads();
-  // bitonic sort, descending, over the next power of two (padding keys 0 sort last)
+  int n = ncand;
+  const int nout = total < k ? total : k;
+  if (n > kMergeCap) {
+    // the cut bin alone overflows LDS (heavy ties): select over the slots in global memory
+    const uint64_t Tk = block_select<kSelThreads>([&](auto f) { visit(T, f); }, k, sel);
+    if (tid == 0) ncand = 0;
+    __syncthreads();
+    visit(Tk, [&](uint64_t key) {
+      const int o = atomicAdd(&ncand, 1);
+      if (o < kMergeCap) cand[o] = key;
+    });
+    __syncthreads();
+    n = nout;
+  } else if (n > k) {
+    // exact top k in LDS, compacted in place through registers
+    const uint64_t Tk = block_select<kSelThreads>(
+        [&](auto f) {
+          for (int i = tid; i < n; i += kSelThreads) f(cand[i]);
+        },
+        k, sel);
+    constexpr int PER = kMergeCap / kSelThreads;
+    uint64_t mine[PER];
+    int keep = 0;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int i = tid + u * kSelThreads;
+      mine[u] = i < n ? cand[i] : 0ull;
+      keep += (i < n && mine[u] >= Tk) ? 1 : 0;
+    }
+    int tot;
+    int off = block_excl_scan<kSelThreads>(keep, wave_tot, &tot);
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int i = tid + u * kSelThreads;
+      if (i < n && mine[u] >= Tk) cand[off++] = mine[u];
+    }
+    __syncthreads();
+    n = tot;
+  }
+  // 4. bitonic sort of the n (= nout) winners, descending, over the next power of two
   int np2 = 1;
-  while (np2 < nout) np2 <<= 1;
-  for (int i = nout + tid; i < np2; i += kSelThreads) buf[i] = 0ull;
+  while (np2 < n) np2 <<= 1;
+  for (int i = n + tid; i < np2; i += kSelThreads) cand[i] = 0ull;
   __syncthreads();
   for (int size = 2; size <= np2; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
       for (int i = tid; i < np2; i += kSelThreads) {
         const int j = i ^ stride;
         if (j > i) {
-          const uint64_t x = buf[i], y = buf[j];
+          const uint64_t x = cand[i], y = cand[j];
           const bool up = (i & size) == 0;   // this run sorts descending
-          if (up ? (x < y) : (x > y)) { buf[i] = y; buf[j] = x; }
+          if (up ? (x < y) : (x > y)) { cand[i] = y; cand[j] = x; }
         }
       }
       __syncthreads();
@@ -567,7 +1077,7 @@ __global__ __launch_bounds__(kSelThreads) void k_merge(MergeArgs a) {
   for (int i = tid; i < k; i += kSelThreads) {
     const size_t o = (size_t)q * k + i;
     if (i < nout) {
-      const uint64_t key = buf[i];
+      const uint64_t key = cand[i];
       const int32_t sc = key_score(key);
       a.out_ids[o] = (int64_t)key_id(key);
       a.out_scores[o] = sc;
@@ -615,8 +1125,9 @@ hipError_t launch_coarse_keys(const DevIndex &ix, const int8_t *queries, int32_t
   return hipGetLastError();
 }
 
-hipError_t launch_coarse_select(const DevIndex &ix, const SearchShape &sh, const Work &w, hipStream_t s) {
-  k_coarse_select<<<sh.B, kSelThreads, 0, s>>>(ix.offsets, ix.nlist, sh.B, sh.nprobe, w);
+hipError_t launch_coarse_select(const DevIndex &ix, const int8_t *queries, const uint64_t *masks,
+                                const SearchShape &sh, const Work &w, hipStream_t s) {
+  k_coarse_select<<<sh.B, kSelThreads, 0, s>>>(ix, queries, masks, sh.B, sh.nprobe, sh.P, w);
   return hipGetLastError();
 }
 
@@ -640,6 +1151,25 @@ hipError_t launch_scan(const DevIndex &ix, const int8_t *queries, const uint64_t
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <int LPR>
+static int scan_occ_w(int W) {
+  int n = 0;
+  hipError_t e = W == 2 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_scan<LPR, 2>, kScanThreads, 0)
+                        : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_scan<LPR, 1>, kScanThreads, 0);
+  return e == hipSuccess ? n : 0;
+}
+
+int scan_blocks_per_cu(int32_t dim, int32_t sig_words) {
+  switch (dim) {
+    case 16: return scan_occ_w<1>(sig_words);
+    case 32: return scan_occ_w<2>(sig_words);
+    case 64: return scan_occ_w<4>(sig_words);
+    case 128: return scan_occ_w<8>(sig_words);
+    case 256: return scan_occ_w<16>(sig_words);
+    default: return 0;
+  }
 }
 
 hipError_t launch_merge(const DevIndex &ix, const float *query_scales, const SearchShape &sh, const Work &w,
