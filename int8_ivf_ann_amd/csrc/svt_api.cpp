@@ -239,7 +239,7 @@ extern "C" int svt_index_info(const svt_index *ix, int64_t *n_items, int32_t *di
 namespace {
 
 struct Layout {
-  size_t coarse_keys, probes, seg, qlen, qcost, cstart, chunks, thr, hlo, hshift, ghist, counter, slot_cnt, slot_min, slot_keys, stats, total;
+  size_t coarse_keys, probes, seg, pb, qlen, qcost, cstart, chunks, thr, hlo, hshift, ghist, counter, slot_cnt, slot_min, slot_keys, stats, total;
   int32_t max_chunks;
 };
 
@@ -257,6 +257,7 @@ Layout layout(const svt_index *ix, int32_t B, int32_t nprobe, int32_t k) {
   L.coarse_keys = take((size_t)B * nlist * sizeof(uint64_t));
   L.probes = take((size_t)B * nprobe * sizeof(int32_t));
   L.seg = take((size_t)B * (nprobe + 1) * sizeof(int32_t));
+  L.pb = take((size_t)B * nprobe * sizeof(int32_t));
   L.qlen = take((size_t)B * sizeof(int64_t));
   L.qcost = take((size_t)B * sizeof(int64_t));
   L.cstart = take((size_t)(B + 1) * sizeof(int32_t));
@@ -313,6 +314,7 @@ extern "C" int svt_search(const svt_index *ix, int32_t B, const int8_t *queries,
   w.coarse_keys = (uint64_t *)(base + L.coarse_keys);
   w.probes = (int32_t *)(base + L.probes);
   w.seg = (int32_t *)(base + L.seg);
+  w.pb = (int32_t *)(base + L.pb);
   w.qlen = (int64_t *)(base + L.qlen);
   w.qcost = (int64_t *)(base + L.qcost);
   w.cstart = (int32_t *)(base + L.cstart);

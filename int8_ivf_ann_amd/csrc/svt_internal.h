@@ -23,7 +23,6 @@ constexpr int kTrimAt = kListCap - kScanStep;           // a list longer than th
 constexpr int kTrimBins = 1024;                         // score histogram bins of a trim
 constexpr int kSegWin = 64;                             // probed clusters staged in LDS at a time
 constexpr int kQHistBins = 256;                         // bins of a query's global score histogram
-constexpr int kHistFlushSteps = 4;                      // scan steps between histogram flushes
 constexpr int kSelThreads = 1024;    // coarse-select and merge workgroups
 constexpr int kCoarseQB = 8;         // queries per coarse-score workgroup
 constexpr int kMaxScanWGs = 4096;    // upper bound on persistent scan workgroups
@@ -42,9 +41,9 @@ struct DevIndex {
 };
 
 // One unit of scan work: items [lo, hi) of query q's stream (the concatenation, in cluster order, of
-// the items of its probed clusters).
+// the items of its probed clusters); j0 is the probed cluster that holds stream offset lo.
 struct Chunk {
-  int32_t q, lo, hi, pad;
+  int32_t q, lo, hi, j0;
 };
 
 constexpr int kCostSamples = kSelThreads;   // items sampled per query to estimate its filter density
@@ -58,6 +57,7 @@ struct Work {
   uint64_t *coarse_keys;    // [B][nlist]   coarse (score, cluster) keys
   int32_t *probes;          // [B][nprobe]  probed clusters, ascending cluster id
   int32_t *seg;             // [B][nprobe + 1] stream offset of each probed cluster within its query
+  int32_t *pb;              // [B][nprobe]  position of stream offset t in probed cluster j: pb[j] + t
   int64_t *qlen;            // [B]          items scanned per query
   int64_t *qcost;           // [B]          estimated bytes the scan moves for the query
   int32_t *cstart;          // [B + 1]      first chunk of each query; cstart[B] = number of chunks

@@ -255,6 +255,7 @@ __global__ __launch_bounds__(kSelThreads) void k_coarse_select(DevIndex ix, cons
     if (take && base + idx < nprobe) {
       probes[base + idx] = c;
       seg[base + idx] = run + pre;
+      w.pb[(size_t)b * nprobe + base + idx] = ix.offsets[c] - (run + pre);
       if (nprobe <= kSelSegLds) seg_lds[base + idx] = run + pre;
     }
     base += cnt_tot;
@@ -378,7 +379,14 @@ __global__ __launch_bounds__(kSelThreads) void k_coarse_select(DevIndex ix, cons
     const int64_t cl = (len + nch - 1) / nch;
     const int32_t i = c - w.cstart[lo];
     const int64_t l0 = (int64_t)i * cl, l1 = l0 + cl < len ? l0 + cl : len;
-    w.chunks[c] = Chunk{lo, (int32_t)l0, (int32_t)l1, 0};
+    // probed cluster holding offset l0: largest j with seg[j] <= l0 (written by this query's workgroup)
+    const int32_t *sq = w.seg + (size_t)lo * (nprobe + 1);
+    int jl = 0, jh = nprobe - 1;
+    while (jl < jh) {
+      const int mid = (jl + jh + 1) >> 1;
+      if (__hip_atomic_load(&sq[mid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <= l0) jl = mid; else jh = mid - 1;
+    }
+    w.chunks[c] = Chunk{lo, (int32_t)l0, (int32_t)l1, jl};
   }
 }
 
@@ -387,13 +395,17 @@ __global__ __launch_bounds__(kSelThreads) void k_coarse_select(DevIndex ix, cons
 //
 // A query's stream is the concatenation of the items of its probed clusters (seg).  The work list
 // cuts every stream into chunks of about equal estimated cost; persistent workgroups take chunks from
-// it with an atomic counter and walk each chunk in order.
-// For each 64-item group a wave loads the 64 signatures with one 128-bit (or 64-bit) load per lane,
-// tests (sig & mask) == mask, ballots the result and compacts the survivors into an LDS list; rows of
-// survivors only are then fetched, LPR lanes per row with 16-byte loads, and scored with v_dot4.
-// A candidate enters the workgroup's LDS list if it beats both the list's own k-th key and the
-// query's global bound thr[q]; whenever the list exceeds k keys it is cut back to exactly k by an
-// LDS trim.  At the end of a chunk the workgroup writes the chunk's exact top k keys to slot c.
+// it with an atomic counter (one chunk ahead) and walk each chunk in steps of kScanStep items.
+// In a step each wave loads 256 signatures (one 128- or 64-bit load per lane per 64-item group), tests
+// (sig & mask) == mask, ballots the result and compacts the survivors' offsets into LDS; it then
+// gathers the rows of its survivors (LPR lanes per row, 16-byte loads, up to 64 rows at once) and
+// scores them with v_dot4.  The next step's signatures and the query's current bound are requested
+// right after the rows, so a step costs one memory round trip.
+// A candidate enters the workgroup's LDS list if it scores at least the best proven bound known to the
+// wave; whenever the list could overflow it is cut back towards k by an LDS trim.  Accepted scores are
+// also counted in a per-query histogram in HBM shared by all chunks of the query: as soon as k counted
+// candidates lie at or above a bin's lower edge, that edge is a proven bound for the whole query.
+// At the end of a chunk the workgroup writes the chunk's exact top k keys above the bound to slot c.
 // Nothing per item is ever written to HBM.
 
 struct ScanArgs {
@@ -414,17 +426,21 @@ struct ScanLds {
   int wave_tot[kScanThreads / 64 + 1];
   unsigned long long kmin;
   uint32_t smin, smax;
-  int cnt, cut_bin, cut_above;
-  // window of the run's probed clusters: stream range [t0, t1) and position base (pos = pbase + t)
+  int cnt, cut_bin, cut_above;   // cnt: slot allocation counter of the list
+  // keys each wave appended in a step, by step parity: the list length after a step is computed from
+  // these by every thread, never read from cnt, which faster waves may already be advancing
+  int wadd[2][kScanThreads / 64];
+  // window of the chunk's probed clusters: stream range [t0, t1) and position base (pos = pb + t)
   int32_t seg_t0[kSegWin], seg_t1[kSegWin], seg_pb[kSegWin];
   int seg_n;
-  uint32_t qh[kQHistBins];   // scores of candidates accepted since the last flush to the query's histogram
+  uint32_t qh[kQHistBins];   // scores of candidates accepted since the last push to the query's histogram
   int32_t gbound;            // the query's bound as read once for the whole block
+  int next;                  // the next chunk of this workgroup
 };
 
-// Keys held while a run is in progress: (biased score << 32) | position.  They are turned into
-// (score, id) ordering keys (make_key) only for the few that survive to the end of the run, so the hot
-// loop never waits on the position -> id table.
+// Keys held while a chunk is in progress: (biased score << 32) | position.  They are turned into
+// (score, id) ordering keys (make_key) only for the few that survive to the end of the chunk, so the
+// hot loop never waits on the position -> id table.
 __device__ __forceinline__ uint64_t pos_key(int32_t score, int32_t pos) {
   return ((uint64_t)((uint32_t)score ^ 0x80000000u) << 32) | (uint64_t)(uint32_t)pos;
 }
@@ -528,68 +544,147 @@ __device__ __forceinline__ int trim_by_score(ScanLds &sm, int cnt, int k, uint32
   return keep_at_least(sm, cnt, (uint64_t)e << 32, &dummy);
 }
 
-// Replace every pos_key of the list by its (score, id) ordering key.
-__device__ __forceinline__ void to_id_keys(ScanLds &sm, int cnt, const int32_t *__restrict__ perm) {
-  for (int i = threadIdx.x; i < cnt; i += kScanThreads) {
-    const uint64_t pk = sm.list[i];
-    sm.list[i] = make_key((int32_t)((uint32_t)(pk >> 32) ^ 0x80000000u), (uint32_t)perm[(uint32_t)pk]);
+// Replace the pos_keys list[from..cnt) by their (score, id) ordering keys.  The position -> id loads
+// of a thread are issued in groups of 8 before any is used.
+__device__ __forceinline__ void to_id_keys(ScanLds &sm, int from, int cnt, const int32_t *__restrict__ perm) {
+  constexpr int PER = 8;
+  const int tid = threadIdx.x;
+  for (int i0 = from; i0 < cnt; i0 += PER * kScanThreads) {
+    uint32_t id[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int i = i0 + tid + u * kScanThreads;
+      id[u] = i < cnt ? (uint32_t)perm[(uint32_t)sm.list[i]] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int i = i0 + tid + u * kScanThreads;
+      if (i < cnt) sm.list[i] = make_key((int32_t)((uint32_t)(sm.list[i] >> 32) ^ 0x80000000u), id[u]);
+    }
   }
   __syncthreads();
+}
+
+// State of a chunk's candidate list that the cold paths below update.  Normally the list holds
+// pos_keys only (id_n == 0).  When score ties at the trim edge keep the list too long, the list is
+// switched to exact (score, id) keys and cut to exactly k: from then on list[0..id_n) are id keys and
+// the candidates appended after them are pos_keys, converted at the next trim.
+struct ListState {
+  int32_t thr_s;   // proven bound of the workgroup
+  int id_n;        // leading keys of the list that are (score, id) keys
+};
+
+// Cut an over-full list back towards k (rare: the bounds reject most candidates).  All threads call
+// it; returns the count kept.
+__device__ __forceinline__ int trim_list(ScanLds &sm, int cnt, int k, const int32_t *__restrict__ perm,
+                                         ListState &st) {
+  const int tid = threadIdx.x;
+  int kept = cnt;
+  if (st.id_n == 0) {
+    uint32_t edge;
+    kept = trim_by_score(sm, cnt, k, &edge);
+    const int32_t es = (int32_t)(edge ^ 0x80000000u);
+    st.thr_s = es > st.thr_s ? es : st.thr_s;
+    if (kept <= kTrimAt) return kept;
+  }
+  // exact: (score, id) keys throughout, then exactly the k best
+  to_id_keys(sm, st.id_n, kept, perm);
+  const uint64_t T = block_select<kScanThreads>(
+      [&](auto f) {
+        for (int i = tid; i < kept; i += kScanThreads) f(sm.list[i]);
+      },
+      k, sm.sel);
+  uint64_t tk;
+  kept = keep_at_least(sm, kept, T, &tk);
+  const int32_t ks = key_score(tk);
+  st.thr_s = ks > st.thr_s ? ks : st.thr_s;
+  st.id_n = kept;
+  return kept;
+}
+
+// End of a chunk: turn the list into (score, id) keys, drop keys below the bound gb and cut to the
+// exact top k; *kth receives the smallest kept key when exactly k remain (0 otherwise).  All threads
+// call it; returns the count kept.
+__device__ __forceinline__ int finish_list(ScanLds &sm, int cnt, int k, int id_n, int32_t gb,
+                                           const int32_t *__restrict__ perm, int32_t *thr_q, uint64_t *kth_out) {
+  const int tid = threadIdx.x, l = lane_id();
+  to_id_keys(sm, id_n, cnt, perm);   // ends with a barrier
+  uint64_t kth = 0;
+  if (gb != INT32_MIN) cnt = keep_at_least(sm, cnt, make_key(gb, 0xFFFFFFFFu), &kth);
+  if (cnt > k) {
+    const uint64_t T = block_select<kScanThreads>(
+        [&](auto f) {
+          for (int i = tid; i < cnt; i += kScanThreads) f(sm.list[i]);
+        },
+        k, sm.sel);
+    cnt = keep_at_least(sm, cnt, T, &kth);
+    if (tid == 0) atomicMax(thr_q, key_score(kth));
+  } else if (cnt == k && gb == INT32_MIN) {
+    if (tid == 0) sm.kmin = ~0ull;
+    __syncthreads();
+    unsigned long long mn = ~0ull;
+    for (int i = tid; i < cnt; i += kScanThreads) mn = sm.list[i] < mn ? sm.list[i] : mn;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      unsigned long long t = __shfl_xor(mn, o);
+      mn = t < mn ? t : mn;
+    }
+    if (l == 0) atomicMin(&sm.kmin, mn);
+    __syncthreads();
+    kth = sm.kmin;
+  }
+  *kth_out = cnt == k ? kth : 0ull;
+  return cnt;
 }
 
 template <int LPR, int W>
 __global__ __launch_bounds__(kScanThreads, 4) void k_scan(ScanArgs a) {
   constexpr int D = 16 * LPR;
-  constexpr int RPI = 64 / LPR;                          // rows scored per wave iteration
-  constexpr int R = (kRowBatch / RPI) > 0 ? (kRowBatch / RPI) : 1;   // row loads issued together per lane
+  constexpr int RPI = 64 / LPR;                   // rows covered by one 16-byte load per lane
+  constexpr int RB = D <= 128 ? 64 : 32;          // rows a wave requests together
+  constexpr int R = RB / RPI;                     // row loads per lane in one batch (<= 8)
   __shared__ ScanLds sm;
   const int tid = threadIdx.x, l = lane_id(), wv = tid / 64, sub = l % LPR;
   const int k = a.k;
-  __shared__ int s_chunk;
   const int n_chunks = a.w.cstart[a.B];
+  if (tid == 0) sm.next = (int)atomicAdd(&a.w.counter[1], 1u);
+  __syncthreads();
   // persistent workgroups take chunks from the work list until it is empty
   for (;;) {
-    if (tid == 0) s_chunk = (int)atomicAdd(&a.w.counter[1], 1u);
-    __syncthreads();
-    const int c = s_chunk;
+    const int c = __builtin_amdgcn_readfirstlane(sm.next);
     if (c >= n_chunks) break;
+    // the chunk after this one, requested now so the request is answered by the time it is needed
+    int next_c = 0;
+    if (tid == 0) next_c = (int)atomicAdd(&a.w.counter[1], 1u);
     const Chunk ch = a.w.chunks[c];
     const int q = ch.q;
     const int32_t ra = ch.lo, rb = ch.hi;
     const int32_t hlo = a.w.hlo[q];
     const int hsh = a.w.hshift[q];
     uint32_t *gh = a.w.ghist + (size_t)q * kQHistBins;
-    for (int i = tid; i < kQHistBins; i += kScanThreads) sm.qh[i] = 0u;
+    int32_t *thr_q = a.w.thr + q;
     // query vector slice held by this lane, request mask
     const int4 qv = reinterpret_cast<const int4 *>(a.queries + (size_t)q * D)[sub];
     uint64_t mk[W];
 #pragma unroll
     for (int i = 0; i < W; ++i) mk[i] = a.masks[(size_t)q * W + i];
+    for (int i = tid; i < kQHistBins; i += kScanThreads) sm.qh[i] = 0u;
     if (tid == 0) sm.cnt = 0;
-    // local bound: every candidate below thr_s is out of this run's top k.  In exact mode (entered only
-    // when score ties defeat the histogram trim) keys carry ids and thr_key is the run's k-th key.
-    int32_t thr_s = INT32_MIN;
-    bool exact = false;
-    uint64_t thr_key = 0;
+    // thr_s: proven bound of this workgroup (trims, histogram pulls); gthr: the query's global bound
+    // as last read
+    int32_t thr_s = INT32_MIN, gthr = __hip_atomic_load(thr_q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    int id_n = 0;
     int64_t n_elig = 0;
     const int32_t *seg = a.w.seg + (size_t)q * (a.nprobe + 1);
-    const int32_t *probes = a.w.probes + (size_t)q * a.nprobe;
-    // first probed cluster overlapping [ra, rb): largest j with seg[j] <= ra
-    int jl = 0, jh = a.nprobe - 1;
-    while (jl < jh) {
-      int mid = (jl + jh + 1) >> 1;
-      if (seg[mid] <= ra) jl = mid; else jh = mid - 1;
-    }
-    __syncthreads();
-    // Steps walk the run's probed clusters in order; the signatures of step s+1 are requested before
-    // the rows of step s are scored, so one memory round trip covers both.  The run's clusters are
-    // staged in LDS (kSegWin at a time) so that walking them never waits on vector memory.
+    const int32_t *pbq = a.w.pb + (size_t)q * a.nprobe;
+    // Steps walk the chunk's probed clusters in order.  The clusters are staged in LDS (kSegWin at a
+    // time) so that walking them never waits on vector memory.
     struct Cursor {
-      int w;            // entry in the LDS window; w == sm.seg_n: run finished
+      int w;            // entry in the LDS window; -1: chunk finished
       int32_t st, t1;   // step start / cluster end, in stream offsets
       int32_t pbase;    // position = pbase + stream offset (positions < 2^31)
     };
-    int jwin = jl;      // first probed cluster of the current window
+    int jwin = ch.j0;   // first probed cluster of the current window
     auto load_window = [&]() {   // all threads; entries jwin .. (first cluster at or past rb)
       __syncthreads();
       if (tid == 0) sm.seg_n = 0;
@@ -600,31 +695,31 @@ __global__ __launch_bounds__(kScanThreads, 4) void k_scan(ScanArgs a) {
         if (s0 < rb) {
           sm.seg_t0[i] = ra > s0 ? ra : s0;
           sm.seg_t1[i] = rb < s1 ? rb : s1;
-          sm.seg_pb[i] = a.ix.offsets[probes[j]] - s0;
+          sm.seg_pb[i] = pbq[j];
           atomicMax(&sm.seg_n, i + 1);
         }
       }
       __syncthreads();
     };
-    auto seek = [&](Cursor &c) {   // from entry c.w: first entry with items left in [ra, rb)
+    auto seek = [&](Cursor &cu) {   // from entry cu.w: first entry with items left in [ra, rb)
       for (;;) {
-        for (; c.w < sm.seg_n; ++c.w) {
-          const int32_t t0 = sm.seg_t0[c.w], t1 = sm.seg_t1[c.w];
+        for (; cu.w < sm.seg_n; ++cu.w) {
+          const int32_t t0 = sm.seg_t0[cu.w], t1 = sm.seg_t1[cu.w];
           if (t0 < t1) {
-            c.st = t0; c.t1 = t1; c.pbase = sm.seg_pb[c.w];
+            cu.st = t0; cu.t1 = t1; cu.pbase = sm.seg_pb[cu.w];
             return;
           }
         }
-        // window exhausted: another one if the run continues past it
-        if (sm.seg_n < kSegWin || jwin + kSegWin >= a.nprobe || seg[jwin + kSegWin] >= rb) { c.w = -1; return; }
+        // window exhausted: another one if the chunk continues past it
+        if (sm.seg_n < kSegWin || jwin + kSegWin >= a.nprobe || seg[jwin + kSegWin] >= rb) { cu.w = -1; return; }
         jwin += kSegWin;
         load_window();
-        c.w = 0;
+        cu.w = 0;
       }
     };
-    auto advance = [&](Cursor &c) {
-      c.st += kScanStep;
-      if (c.st >= c.t1) { ++c.w; seek(c); }
+    auto advance = [&](Cursor &cu) {
+      cu.st += kScanStep;
+      if (cu.st >= cu.t1) { ++cu.w; seek(cu); }
     };
     // bin of a score in the query's histogram: bin 0 holds everything below hlo + 2^hsh, bin b >= 1
     // holds [hlo + b 2^hsh, hlo + (b+1) 2^hsh), the last bin everything above
@@ -633,47 +728,59 @@ __global__ __launch_bounds__(kScanThreads, 4) void k_scan(ScanArgs a) {
       const int32_t b = (score - hlo) >> hsh;
       return b < kQHistBins - 1 ? b : kQHistBins - 1;
     };
-    // Add this workgroup's counts to the query's histogram, then raise the query's bound to the lower
-    // edge of the highest bin at which at least k accepted candidates (of every chunk) lie at or above.
-    // Each candidate is counted once, when it is accepted, so the bound is proven.  All threads call it.
-    auto hist_flush = [&]() {
+    // Histogram exchange in two halves so that neither waits on memory.  push (all threads, after the
+    // step's barrier) adds the counts accepted since the last push to the query's histogram; pull
+    // (wave 0) requests the histogram with the next step's loads and, once they have arrived, raises the
+    // bound to the lower edge of the highest bin at which at least k counted candidates lie at or above.
+    // Every accepted candidate is counted exactly once, so the bound is proven whatever the
+    // interleaving; a stale read only yields a lower bound.
+    auto hist_push = [&]() {
       for (int i = tid; i < kQHistBins; i += kScanThreads) {
-        const uint32_t v = sm.qh[i];
-        if (v) { atomicAdd(&gh[i], v); sm.qh[i] = 0u; }
+        const uint32_t v = atomicExch(&sm.qh[i], 0u);
+        if (v) atomicAdd(&gh[i], v);
       }
-      __syncthreads();
-      if (tid < 64) {
-        constexpr int PB = kQHistBins / 64;
-        uint32_t h[PB], sum = 0;
+    };
+    constexpr int HPB = kQHistBins / 64;   // histogram bins per lane of wave 0
+    uint32_t hq[HPB];
+    auto hist_pull_issue = [&]() {
 #pragma unroll
-        for (int j = 0; j < PB; ++j) {
-          h[j] = __hip_atomic_load(&gh[PB * l + j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          sum += h[j];
-        }
-        uint32_t suf = sum;
+      for (int j = 0; j < HPB; ++j)
+        hq[j] = __hip_atomic_load(&gh[HPB * l + j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    auto hist_pull_use = [&]() {   // wave 0 only
+      uint32_t sum = 0;
 #pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-          const uint32_t v = __shfl_down(suf, off);
-          if (l + off < 64) suf += v;
-        }
-        uint32_t above = suf - sum;
+      for (int j = 0; j < HPB; ++j) sum += hq[j];
+      uint32_t suf = sum;
 #pragma unroll
-        for (int j = PB - 1; j >= 0; --j) {
-          const int bin = PB * l + j;
-          if (bin >= 1 && above < (uint32_t)k && above + h[j] >= (uint32_t)k)
-            atomicMax(&a.w.thr[q], hlo + (bin << hsh));
-          above += h[j];
-        }
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t v = __shfl_down(suf, off);
+        if (l + off < 64) suf += v;
       }
+      uint32_t above = suf - sum;
+      int32_t bound = INT32_MIN;
+#pragma unroll
+      for (int j = HPB - 1; j >= 0; --j) {
+        const int bin = HPB * l + j;
+        if (bin >= 1 && above < (uint32_t)k && above + hq[j] >= (uint32_t)k) bound = hlo + (bin << hsh);
+        above += hq[j];
+      }
+      if (bound != INT32_MIN) atomicMax(thr_q, bound);
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        const int32_t t = __shfl_xor(bound, o);
+        bound = t > bound ? t : bound;
+      }
+      thr_s = bound > thr_s ? bound : thr_s;
     };
     // Loads are issued unconditionally (out-of-range lanes read an in-range clamped address and are
     // masked afterwards), so the compiler can count outstanding loads exactly and wait only for the
     // ones it needs: the rows of this step, not the signatures already requested for the next.
     uint64_t sg[kScanGroups][W];
     int32_t sg_n = 0;
-    auto load_sigs = [&](const Cursor &c) {
-      sg_n = c.w >= 0 ? ((c.t1 - c.st) < kScanStep ? (c.t1 - c.st) : kScanStep) : 0;
-      const int32_t p0 = c.w >= 0 ? c.pbase + c.st : 0;
+    auto load_sigs = [&](const Cursor &cu) {
+      sg_n = cu.w >= 0 ? ((cu.t1 - cu.st) < kScanStep ? (cu.t1 - cu.st) : kScanStep) : 0;
+      const int32_t p0 = cu.w >= 0 ? cu.pbase + cu.st : 0;
       const int32_t last = sg_n > 0 ? sg_n - 1 : 0;
 #pragma unroll
       for (int gi = 0; gi < kScanGroups; ++gi) {
@@ -688,15 +795,14 @@ __global__ __launch_bounds__(kScanThreads, 4) void k_scan(ScanArgs a) {
       }
     };
     load_window();
-    int steps = 0;
+    int steps = 0, par = 0, cnt_base = 0;   // cnt_base: list length at the start of the step
+    bool pull = false;
     Cursor cur{0, 0, 0, 0};
     seek(cur);
     load_sigs(cur);
     while (cur.w >= 0) {
       const int32_t n = sg_n;
       const int32_t p0 = cur.pbase + cur.st;
-      // the query's global bound only ever rises, so a stale read merely prunes less
-      const int32_t gthr = *(volatile const int32_t *)&a.w.thr[q];
       const int32_t thr_eff = gthr > thr_s ? gthr : thr_s;
       // --- filter this step's signatures, compact the survivors per wave
       int nw = 0;
@@ -714,138 +820,111 @@ __global__ __launch_bounds__(kScanThreads, 4) void k_scan(ScanArgs a) {
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      // --- rows of the first R x RPI survivors, then the next step's signatures, all in flight
+      // --- rows of the first RB survivors, then the next step's signatures and bound, all in flight
       int4 x[R];
-      int32_t pos[R];
-      bool v[R];
       auto load_rows = [&](int r0) {
 #pragma unroll
         for (int u = 0; u < R; ++u) {
           const int r = r0 + u * RPI + l / LPR;
-          v[u] = r < nw;
-          pos[u] = p0 + (v[u] ? (int)sm.u.wl[wv][r] : 0);
-          x[u] = reinterpret_cast<const int4 *>(a.ix.items + (size_t)pos[u] * D)[sub];
+          const int32_t p = p0 + (r < nw ? (int)sm.u.wl[wv][r] : 0);
+          x[u] = reinterpret_cast<const int4 *>(a.ix.items + (size_t)p * D)[sub];
         }
       };
-      auto score_rows = [&]() {
+      // score the batch at r0.  Each row's lane 0 counts the rows it accepts; one wave prefix sum and
+      // one LDS atomic give every accepted candidate its list slot.
+      auto score_rows = [&](int r0) -> int {
+        uint32_t okm = 0;
+        int myc = 0;
+        int32_t sc[R];
 #pragma unroll
         for (int u = 0; u < R; ++u) {
           int32_t acc = dot16(x[u], qv, 0);
 #pragma unroll
           for (int off = 1; off < LPR; off <<= 1) acc += __shfl_xor(acc, off);
-          if (sub == 0 && v[u] && acc >= thr_eff) {
-            if (!exact) {
-              sm.list[atomicAdd(&sm.cnt, 1)] = pos_key(acc, pos[u]);
-              atomicAdd(&sm.qh[qbin(acc)], 1u);
-            } else {
-              const uint64_t key = make_key(acc, (uint32_t)a.ix.perm[pos[u]]);
-              if (key > thr_key) {
-                sm.list[atomicAdd(&sm.cnt, 1)] = key;
-                atomicAdd(&sm.qh[qbin(acc)], 1u);
-              }
-            }
+          const int r = r0 + u * RPI + l / LPR;
+          sc[u] = acc;
+          if (sub == 0 && r < nw && acc >= thr_eff) {
+            okm |= 1u << u;
+            ++myc;
           }
         }
+        const int incl = wave_incl_scan(myc);
+        const int tot = __builtin_amdgcn_readlane(incl, 63);
+        if (tot == 0) return 0;
+        int at = 0;
+        if (l == 63) at = atomicAdd(&sm.cnt, tot);
+        at = __builtin_amdgcn_readlane(at, 63) + incl - myc;
+#pragma unroll
+        for (int u = 0; u < R; ++u) {
+          if (okm & (1u << u)) {
+            const int r = r0 + u * RPI + l / LPR;
+            sm.list[at++] = pos_key(sc[u], p0 + (int)sm.u.wl[wv][r]);
+            atomicAdd(&sm.qh[qbin(sc[u])], 1u);
+          }
+        }
+        return tot;
       };
       if (nw > 0) load_rows(0);
       advance(cur);
       load_sigs(cur);
-      if (nw > 0) score_rows();
+      const int32_t gthr_next = __hip_atomic_load(thr_q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (pull && wv == 0) hist_pull_issue();
+      int wtot = nw > 0 ? score_rows(0) : 0;
       // survivors beyond the first batch (dense filters)
-      for (int r0 = RPI * R; r0 < nw; r0 += RPI * R) {
+      for (int r0 = RB; r0 < nw; r0 += RB) {
         load_rows(r0);
-        score_rows();
+        wtot += score_rows(r0);
       }
+      if (l == 0) sm.wadd[par][wv] = wtot;
       __syncthreads();
+      int cnt_now = cnt_base;
+#pragma unroll
+      for (int i = 0; i < kScanThreads / 64; ++i) cnt_now += sm.wadd[par][i];
+      par ^= 1;
+      gthr = gthr_next;
+      if (pull) {
+        if (wv == 0) hist_pull_use();
+        pull = false;
+      }
       // --- trim the list when the next step could overflow it
-      if (sm.cnt > kTrimAt) {
-        const int cnt = sm.cnt;
-        int kept;
-        if (!exact) {
-          uint32_t edge;
-          kept = trim_by_score(sm, cnt, k, &edge);
-          thr_s = (int32_t)(edge ^ 0x80000000u);
-          if (kept > kTrimAt) {
-            // ties at the edge: switch this run to exact (score, id) keys and cut to exactly k
-            to_id_keys(sm, kept, a.ix.perm);
-            const uint64_t T = block_select<kScanThreads>(
-                [&](auto f) {
-                  for (int i = tid; i < kept; i += kScanThreads) f(sm.list[i]);
-                },
-                k, sm.sel);
-            kept = keep_at_least(sm, kept, T, &thr_key);
-            thr_s = key_score(thr_key);
-            exact = true;
-          }
-        } else {
-          const uint64_t T = block_select<kScanThreads>(
-              [&](auto f) {
-                for (int i = tid; i < cnt; i += kScanThreads) f(sm.list[i]);
-              },
-              k, sm.sel);
-          kept = keep_at_least(sm, cnt, T, &thr_key);
-          thr_s = key_score(thr_key);
-        }
+      cnt_base = cnt_now;
+      if (cnt_now > kTrimAt) {
+        ListState st{thr_s, id_n};
+        const int kept = trim_list(sm, cnt_now, k, a.ix.perm, st);
+        cnt_base = kept;
+        thr_s = st.thr_s;
+        id_n = st.id_n;
         if (tid == 0) {
           sm.cnt = kept;
-          atomicMax(&a.w.thr[q], thr_s);   // at least k candidates score >= thr_s
+          atomicMax(thr_q, thr_s);   // at least k candidates score >= thr_s
         }
         __syncthreads();
+        // the next step's signatures are requested again rather than held in registers across the trim
+        load_sigs(cur);
       }
-      // flush after steps 2, 4, 8, ...: the bound converges within a few flushes
+      // histogram exchange after steps 2, 4, 8, ...: the bound converges within a few exchanges
       ++steps;
       if (steps >= 2 && (steps & (steps - 1)) == 0) {
-        hist_flush();
-        __syncthreads();
+        hist_push();
+        pull = true;
       }
     }
     // --- end of the chunk: its exact top k above the query's bound, published in slot c
-    hist_flush();
+    hist_push();
+    // keys below the query's bound cannot be in its top k.  The branches below contain barriers, so
+    // the block uses one value of the bound, read by one thread.
+    if (tid == 0) sm.gbound = gthr > thr_s ? gthr : thr_s;
     __syncthreads();
-    int cnt = sm.cnt;
-    if (!exact) to_id_keys(sm, cnt, a.ix.perm);
-    uint64_t kth = 0;
-    if (cnt > k) {
-      const uint64_t T = block_select<kScanThreads>(
-          [&](auto f) {
-            for (int i = tid; i < cnt; i += kScanThreads) f(sm.list[i]);
-          },
-          k, sm.sel);
-      cnt = keep_at_least(sm, cnt, T, &kth);
-      if (tid == 0) atomicMax(&a.w.thr[q], key_score(kth));
-      __syncthreads();
-    }
-    {
-      // keys below the query's bound (as raised by every chunk so far) cannot be in its top k.  Other
-      // workgroups raise the bound concurrently, so one thread reads it and the block uses that value:
-      // the branch below contains barriers and must be taken by every thread alike.
-      if (tid == 0) sm.gbound = *(volatile const int32_t *)&a.w.thr[q];
-      __syncthreads();
-      const int32_t gb = sm.gbound;
-      __syncthreads();
-      if (gb != INT32_MIN) cnt = keep_at_least(sm, cnt, make_key(gb, 0xFFFFFFFFu), &kth);
-      else if (cnt == k) {
-        if (tid == 0) sm.kmin = ~0ull;
-        __syncthreads();
-        unsigned long long mn = ~0ull;
-        for (int i = tid; i < cnt; i += kScanThreads) mn = sm.list[i] < mn ? sm.list[i] : mn;
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-          unsigned long long t = __shfl_xor(mn, o);
-          mn = t < mn ? t : mn;
-        }
-        if (l == 0) atomicMin(&sm.kmin, mn);
-        __syncthreads();
-        kth = sm.kmin;
-      }
-    }
-    const size_t slot = (size_t)c;
-    uint64_t *dst = a.w.slot_keys + slot * (size_t)k;
+    const int32_t gb = sm.gbound;
+    uint64_t kth;
+    const int cnt = finish_list(sm, cnt_base, k, id_n, gb, a.ix.perm, thr_q, &kth);
+    uint64_t *dst = a.w.slot_keys + (size_t)c * (size_t)k;
     for (int i = tid; i < cnt; i += kScanThreads) dst[i] = sm.list[i];
     if (tid == 0) {
-      a.w.slot_cnt[slot] = cnt;
+      a.w.slot_cnt[c] = cnt;
       // a full slot proves k keys >= its smallest one
-      a.w.slot_min[slot] = cnt == k ? kth : 0ull;
+      a.w.slot_min[c] = kth;
+      sm.next = next_c;
     }
     // per-query counters: items scanned by this chunk, items that passed the filter
     if (a.w.stats) {
