@@ -239,7 +239,7 @@ extern "C" int svt_index_info(const svt_index *ix, int64_t *n_items, int32_t *di
 namespace {
 
 struct Layout {
-  size_t coarse_keys, probes, seg, pb, qlen, qcost, cstart, chunks, thr, hlo, hshift, ghist, counter, slot_cnt, slot_min, slot_keys, stats, total;
+  size_t coarse_keys, probes, seg, pb, qlen, qcost, cstart, chunks, order, thr, hlo, hshift, ghist, counter, slot_cnt, slot_min, slot_keys, stats, total;
   int32_t max_chunks;
 };
 
@@ -262,6 +262,7 @@ Layout layout(const svt_index *ix, int32_t B, int32_t nprobe, int32_t k) {
   L.qcost = take((size_t)B * sizeof(int64_t));
   L.cstart = take((size_t)(B + 1) * sizeof(int32_t));
   L.chunks = take(C * sizeof(Chunk));
+  L.order = take(C * sizeof(int32_t));
   L.thr = take((size_t)B * sizeof(int32_t));
   L.hlo = take((size_t)B * sizeof(int32_t));
   L.hshift = take((size_t)B * sizeof(int32_t));
@@ -319,6 +320,7 @@ extern "C" int svt_search(const svt_index *ix, int32_t B, const int8_t *queries,
   w.qcost = (int64_t *)(base + L.qcost);
   w.cstart = (int32_t *)(base + L.cstart);
   w.chunks = (Chunk *)(base + L.chunks);
+  w.order = (int32_t *)(base + L.order);
   w.thr = (int32_t *)(base + L.thr);
   w.hlo = (int32_t *)(base + L.hlo);
   w.hshift = (int32_t *)(base + L.hshift);

@@ -62,6 +62,7 @@ struct Work {
   int64_t *qcost;           // [B]          estimated bytes the scan moves for the query
   int32_t *cstart;          // [B + 1]      first chunk of each query; cstart[B] = number of chunks
   Chunk *chunks;            // [max_chunks] the work list, in query order
+  int32_t *order;           // [max_chunks] the order in which the scan takes the chunks
   int32_t *thr;             // [B]          per-query proven lower bound on the k-th best score
   int32_t *hlo;             // [B]          score at the lower edge of bin 1 of the query's histogram
   int32_t *hshift;          // [B]          bin width of that histogram is 2^hshift

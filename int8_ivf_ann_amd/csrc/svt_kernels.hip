@@ -46,6 +46,18 @@ __device__ __forceinline__ int32_t dot16(const int4 x, const int4 y, int32_t acc
   return acc;
 }
 
+// Sum of v over each group of LPR consecutive lanes (LPR = 1, 2, 4, 8 or 16), valid in the group's first
+// lane.  DPP lane moves: quad permutations for lane ^ 1 and lane ^ 2, then row shifts that bring lane
+// + 4 and lane + 8 (within a 16-lane row) to the group's first lane.
+template <int LPR>
+__device__ __forceinline__ int32_t group_sum(int32_t v) {
+  if constexpr (LPR >= 2) v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, true);    // quad_perm 1,0,3,2
+  if constexpr (LPR >= 4) v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, true);    // quad_perm 2,3,0,1
+  if constexpr (LPR >= 8) v += __builtin_amdgcn_update_dpp(0, v, 0x104, 0xF, 0xF, true);   // row_shl:4
+  if constexpr (LPR >= 16) v += __builtin_amdgcn_update_dpp(0, v, 0x108, 0xF, 0xF, true);  // row_shl:8
+  return v;
+}
+
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
 
 // number of set bits of `mask` below this lane
@@ -388,14 +400,43 @@ __global__ __launch_bounds__(kSelThreads) void k_coarse_select(DevIndex ix, cons
     }
     w.chunks[c] = Chunk{lo, (int32_t)l0, (int32_t)l1, jl};
   }
+  // Queue order: chunks grouped by the band (1/256 of the cluster ids) of their first probed cluster, so
+  // that chunks of different queries that read the same clusters run at about the same time and the
+  // second reader finds the data in cache.  Counting sort; the order inside a band is arbitrary.
+  auto band_of = [&](int c) -> int {
+    int lo = 0, hi = B - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (w.cstart[mid] <= c) lo = mid; else hi = mid - 1;
+    }
+    const int j0 = w.chunks[c].j0;
+    const int32_t cl = __hip_atomic_load(&w.probes[(size_t)lo * nprobe + j0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return (int)(((int64_t)cl * 256) / nlist);
+  };
+  __syncthreads();
+  for (int i = tid; i < 256; i += kSelThreads) sel.hist[i] = 0u;
+  __syncthreads();
+  for (int c = tid; c < carry; c += kSelThreads) atomicAdd(&sel.hist[band_of(c)], 1u);
+  __syncthreads();
+  if (tid < 64) {
+    uint32_t h[4], sum = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { h[j] = sel.hist[4 * l + j]; sum += h[j]; }
+    uint32_t run = wave_incl_scan(sum) - sum;   // exclusive prefix of this lane's four bins
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { sel.hist[4 * l + j] = run; run += h[j]; }
+  }
+  __syncthreads();
+  for (int c = tid; c < carry; c += kSelThreads) w.order[atomicAdd(&sel.hist[band_of(c)], 1u)] = c;
 }
 
 // ------------------------------------------------------------------------------------------------
 // k_scan: the fused filter -> score -> select hot loop.
 //
 // A query's stream is the concatenation of the items of its probed clusters (seg).  The work list
-// cuts every stream into chunks of about equal estimated cost; persistent workgroups take chunks from
-// it with an atomic counter (one chunk ahead) and walk each chunk in steps of kScanStep items.
+// cuts every stream into chunks of about equal estimated cost and orders them by the clusters they start
+// in; persistent workgroups take chunks in that order with an atomic counter (one chunk ahead) and walk
+// each chunk in steps of kScanStep items.
 // In a step each wave loads 256 signatures (one 128- or 64-bit load per lane per 64-item group), tests
 // (sig & mask) == mask, ballots the result and compacts the survivors' offsets into LDS; it then
 // gathers the rows of its survivors (LPR lanes per row, 16-byte loads, up to 64 rows at once) and
@@ -419,8 +460,8 @@ struct ScanArgs {
 struct ScanLds {
   uint64_t list[kListCap];
   union {
-    uint16_t wl[kScanThreads / 64][64 * kScanGroups];   // per-wave survivor offsets of one step
-    uint32_t hist[kTrimBins];                           // score histogram of a trim
+    uint16_t wl[kScanThreads * kScanGroups];   // survivor offsets of one step, wave w's at [w * 256, ...)
+    uint32_t hist[kTrimBins];                  // score histogram of a trim
   } u;
   SelScratch sel;
   int wave_tot[kScanThreads / 64 + 1];
@@ -430,12 +471,13 @@ struct ScanLds {
   // keys each wave appended in a step, by step parity: the list length after a step is computed from
   // these by every thread, never read from cnt, which faster waves may already be advancing
   int wadd[2][kScanThreads / 64];
+  int wcnt[kScanThreads / 64];   // survivors each wave found in the current step
   // window of the chunk's probed clusters: stream range [t0, t1) and position base (pos = pb + t)
   int32_t seg_t0[kSegWin], seg_t1[kSegWin], seg_pb[kSegWin];
   int seg_n;
   uint32_t qh[kQHistBins];   // scores of candidates accepted since the last push to the query's histogram
   int32_t gbound;            // the query's bound as read once for the whole block
-  int next;                  // the next chunk of this workgroup
+  int next;                  // queue position of this workgroup's next chunk
 };
 
 // Keys held while a chunk is in progress: (biased score << 32) | position.  They are turned into
@@ -651,8 +693,9 @@ __global__ __launch_bounds__(kScanThreads, 4) void k_scan(ScanArgs a) {
   __syncthreads();
   // persistent workgroups take chunks from the work list until it is empty
   for (;;) {
-    const int c = __builtin_amdgcn_readfirstlane(sm.next);
-    if (c >= n_chunks) break;
+    const int qpos = __builtin_amdgcn_readfirstlane(sm.next);
+    if (qpos >= n_chunks) break;
+    const int c = a.w.order[qpos];
     // the chunk after this one, requested now so the request is answered by the time it is needed
     int next_c = 0;
     if (tid == 0) next_c = (int)atomicAdd(&a.w.counter[1], 1u);
@@ -813,65 +856,82 @@ __global__ __launch_bounds__(kScanThreads, 4) void k_scan(ScanArgs a) {
 #pragma unroll
         for (int u = 0; u < W; ++u) pass = pass && ((sg[gi][u] & mk[u]) == mk[u]);
         const uint64_t bal = __ballot(pass);
-        if (pass) sm.u.wl[wv][nw + mbcnt(bal)] = (uint16_t)i;
+        if (pass) sm.u.wl[wv * 64 * kScanGroups + nw + mbcnt(bal)] = (uint16_t)i;
         nw += __popcll(bal);
       }
       n_elig += nw;
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      // --- rows of the first RB survivors, then the next step's signatures and bound, all in flight
+      if (l == 0) sm.wcnt[wv] = nw;
+      __syncthreads();
+      // --- the step's survivors are shared out evenly: wave wv scores survivors [rbeg, rend) of the
+      // concatenation of the waves' lists
+      constexpr int NWV = kScanThreads / 64;
+      int pre[NWV + 1];
+      pre[0] = 0;
+#pragma unroll
+      for (int i = 0; i < NWV; ++i) pre[i + 1] = pre[i] + sm.wcnt[i];
+      const int total = pre[NWV];
+      const int per = (total + NWV - 1) / NWV;
+      const int rbeg = wv * per, rend = rbeg + per < total ? rbeg + per : total;
+      auto surv_at = [&](int r) -> int {   // LDS index of survivor r (pre is nondecreasing)
+        int adj = 0;
+#pragma unroll
+        for (int i = 1; i < NWV; ++i) adj = r >= pre[i] ? i * 64 * kScanGroups - pre[i] : adj;
+        return r + adj;
+      };
+      // --- rows of the first RB survivors, then the next step's signatures, all in flight
       int4 x[R];
       auto load_rows = [&](int r0) {
 #pragma unroll
         for (int u = 0; u < R; ++u) {
           const int r = r0 + u * RPI + l / LPR;
-          const int32_t p = p0 + (r < nw ? (int)sm.u.wl[wv][r] : 0);
+          const int32_t p = p0 + (r < rend ? (int)sm.u.wl[surv_at(r)] : 0);
           x[u] = reinterpret_cast<const int4 *>(a.ix.items + (size_t)p * D)[sub];
         }
       };
-      // score the batch at r0.  Each row's lane 0 counts the rows it accepts; one wave prefix sum and
-      // one LDS atomic give every accepted candidate its list slot.
+      // score the batch at r0.  The wave's accepted candidates take their list slots with one LDS atomic;
+      // a candidate's slot is its rank among them (ballots over the rows of the batch in turn).
       auto score_rows = [&](int r0) -> int {
         uint32_t okm = 0;
-        int myc = 0;
         int32_t sc[R];
+        int tot = 0;
 #pragma unroll
         for (int u = 0; u < R; ++u) {
-          int32_t acc = dot16(x[u], qv, 0);
-#pragma unroll
-          for (int off = 1; off < LPR; off <<= 1) acc += __shfl_xor(acc, off);
+          const int32_t acc = group_sum<LPR>(dot16(x[u], qv, 0));
           const int r = r0 + u * RPI + l / LPR;
           sc[u] = acc;
-          if (sub == 0 && r < nw && acc >= thr_eff) {
-            okm |= 1u << u;
-            ++myc;
-          }
+          const bool ok = sub == 0 && r < rend && acc >= thr_eff;
+          okm |= ok ? 1u << u : 0u;
+          tot += __popcll(__ballot(ok));
         }
-        const int incl = wave_incl_scan(myc);
-        const int tot = __builtin_amdgcn_readlane(incl, 63);
         if (tot == 0) return 0;
         int at = 0;
-        if (l == 63) at = atomicAdd(&sm.cnt, tot);
-        at = __builtin_amdgcn_readlane(at, 63) + incl - myc;
+        if (l == 0) at = atomicAdd(&sm.cnt, tot);
+        at = __builtin_amdgcn_readfirstlane(at);
 #pragma unroll
         for (int u = 0; u < R; ++u) {
-          if (okm & (1u << u)) {
+          const bool ok = (okm >> u) & 1u;
+          const uint64_t b = __ballot(ok);
+          if (ok) {
             const int r = r0 + u * RPI + l / LPR;
-            sm.list[at++] = pos_key(sc[u], p0 + (int)sm.u.wl[wv][r]);
+            sm.list[at + mbcnt(b)] = pos_key(sc[u], p0 + (int)sm.u.wl[surv_at(r)]);
             atomicAdd(&sm.qh[qbin(sc[u])], 1u);
           }
+          at += __popcll(b);
         }
         return tot;
       };
-      if (nw > 0) load_rows(0);
+      if (rbeg < rend) load_rows(rbeg);
       advance(cur);
       load_sigs(cur);
-      const int32_t gthr_next = __hip_atomic_load(thr_q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (pull && wv == 0) hist_pull_issue();
-      int wtot = nw > 0 ? score_rows(0) : 0;
+      // the query's global bound and histogram are read only on exchange steps
+      int32_t gthr_next = gthr;
+      if (pull) {
+        gthr_next = __hip_atomic_load(thr_q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (wv == 0) hist_pull_issue();
+      }
+      int wtot = rbeg < rend ? score_rows(rbeg) : 0;
       // survivors beyond the first batch (dense filters)
-      for (int r0 = RB; r0 < nw; r0 += RB) {
+      for (int r0 = rbeg + RB; r0 < rend; r0 += RB) {
         load_rows(r0);
         wtot += score_rows(r0);
       }
