@@ -45,7 +45,8 @@ def parse():
     ap.add_argument("--batches", type=int, default=4, help="distinct query batches cycled over the steps")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU-seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--traffic", default=None, help="traffic summary json (profiles/); default by workload")
+    ap.add_argument("--traffic", default=None, help="traffic summary (profiles/); default by workload")
+    ap.add_argument("--print-sha", action="store_true", help="print the hash of the kernel sources and exit")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="run one device copy of this many MiB after the timed region (counter calibration)")
     return ap.parse_args()
@@ -92,6 +93,9 @@ def algorithmic_bytes(cat, sigs_sorted, offsets, queries, masks, nprobe, W, d):
 
 def main():
     args = parse()
+    if args.print_sha:
+        print(kernel_source_hash())
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}); "
               "the sharding design is described in DESIGN.md", file=sys.stderr)
@@ -188,12 +192,12 @@ def main():
         f"{np.mean([a[4] for a in alg]):.0f} distinct clusters) in {scan_ms:.4f} ms -> {achieved:.1f} GB/s")
 
     traffic = None
-    tpath = args.traffic or os.path.join(ROOT, "profiles", f"traffic_scan_{name}_b{B}.json")
+    tpath = args.traffic or os.path.join(ROOT, "profiles", f"traffic_k_scan_{name}_b{B}.md")
     if os.path.exists(tpath):
-        with open(tpath) as f:
-            tj = json.load(f)
+        from int8_ivf_ann_amd.rocprof_summary import read_traffic
+        tj = read_traffic(tpath)
         if tj.get("kernel_source_sha") == kernel_source_hash():
-            traffic = tj.get("bytes_per_launch")
+            traffic = float(tj["hbm_bytes_per_launch"])
         else:
             log(f"[bench] {tpath} was taken on other kernel sources: traffic reported as null")
 
