@@ -8,6 +8,7 @@
 #include <atomic>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <new>
@@ -55,8 +56,9 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // stage timing: per-process switch; per-thread record of the searches since the last read
 std::atomic<int> g_prof_on{0};
-constexpr int kStages = 4;
-const char *const kStageNames[kStages] = {"coarse", "select", "scan", "merge"};
+constexpr int kStages = 6;
+// "plan" and "fallback" are empty when a search runs query by query
+const char *const kStageNames[kStages] = {"coarse", "select", "plan", "scan", "fallback", "merge"};
 struct ProfState {
   std::vector<hipEvent_t> pool;   // kStages + 1 events per recorded search
   int searches = 0;
@@ -79,6 +81,8 @@ struct svt_index {
   int32_t *d_offsets = nullptr;
   int8_t *d_centroids = nullptr;
   int32_t scan_wgs;                 // persistent workgroups of the fused kernel
+  int64_t n_tiles;                  // sum over clusters of ceil(size / kGTile)
+  int64_t max_cluster_tiles;        // tiles of the largest cluster
 };
 
 // ------------------------------------------------------------------------------------------------
@@ -131,6 +135,13 @@ extern "C" int svt_index_upload(const svt_index_desc *d, void *hip_stream, svt_i
   svt_index *ix = new (std::nothrow) svt_index();
   if (!ix) return fail(SVT_ENOMEM, "svt_index_upload: host allocation");
   ix->magic = kMagic;
+  ix->n_tiles = 0;
+  ix->max_cluster_tiles = 0;
+  for (int32_t c = 0; c < nlist; ++c) {
+    const int64_t t = (offsets[c + 1] - offsets[c] + kGTile - 1) / kGTile;
+    ix->n_tiles += t;
+    ix->max_cluster_tiles = std::max(ix->max_cluster_tiles, t);
+  }
   hipError_t e = hipGetDevice(&ix->device);
   if (e != hipSuccess) { delete ix; return fail_hip(e, "hipGetDevice"); }
   hipDeviceProp_t prop;
@@ -239,9 +250,23 @@ extern "C" int svt_index_info(const svt_index *ix, int64_t *n_items, int32_t *di
 namespace {
 
 struct Layout {
-  size_t coarse_keys, probes, seg, pb, qlen, qcost, cstart, chunks, order, thr, hlo, hshift, ghist, counter, slot_cnt, slot_min, slot_keys, stats, total;
+  size_t coarse_keys, probes, seg, pb, qlen, qcost, cstart, chunks, order, thr, hlo, hshift, ghist, counter, slot_cnt,
+      slot_min, slot_keys, stats;
+  size_t gcnt, gfill, gstart, ustart, gq, units, pool_cnt, pool;   // grouped path (0 bytes when impossible)
+  size_t total;
   int32_t max_chunks;
+  int32_t max_units;    // 0: the grouped path does not fit this shape
+  int32_t pool_cap;
 };
+
+// Grouped searches: candidate pools take at most kPoolBudget bytes in all, at least 16 k and at most
+// kPoolMaxKeys keys per query.  Shapes whose work list would not fit an int32 run query by query.
+constexpr size_t kPoolBudget = size_t(256) << 20;
+constexpr int64_t kPoolMaxKeys = int64_t(1) << 22;
+// The grouped path is selected explicitly (SVT_PATH=grouped); by default every batch runs query by
+// query, which is faster on every workload measured so far (it keeps an exact top-k per workgroup in LDS,
+// the grouped path sends every candidate above the query's bound to HBM).
+constexpr int32_t kGroupedMinBatch = 1 << 30;
 
 Layout layout(const svt_index *ix, int32_t B, int32_t nprobe, int32_t k) {
   Layout L{};
@@ -267,11 +292,29 @@ Layout layout(const svt_index *ix, int32_t B, int32_t nprobe, int32_t k) {
   L.hlo = take((size_t)B * sizeof(int32_t));
   L.hshift = take((size_t)B * sizeof(int32_t));
   L.ghist = take((size_t)B * kQHistBins * sizeof(uint32_t));
-  L.counter = take(2 * sizeof(uint32_t));
+  L.counter = take(3 * sizeof(uint32_t));
   L.slot_cnt = take(C * sizeof(int32_t));
   L.slot_min = take(C * sizeof(uint64_t));
   L.slot_keys = take(C * (size_t)k * sizeof(uint64_t));
   L.stats = take((size_t)B * 2 * sizeof(int64_t));
+  // grouped path: units <= sum_c tiles_c * ceil(queries_c / kGMax), bounded two ways
+  const int64_t gpc = ((int64_t)B + kGMax - 1) / kGMax;
+  const int64_t u1 = ix->n_tiles * gpc;
+  const int64_t u2 = ix->n_tiles + ix->max_cluster_tiles * (((int64_t)B * nprobe + kGMax - 1) / kGMax);
+  const int64_t mu = std::max<int64_t>(1, std::min(u1, u2));
+  if (mu < (int64_t(1) << 31) - 256) {
+    L.max_units = (int32_t)mu;
+    const int64_t per_q = (int64_t)(kPoolBudget / 8 / (size_t)std::max(B, 1));
+    L.pool_cap = (int32_t)std::min(kPoolMaxKeys, std::max<int64_t>(16 * (int64_t)k, per_q));
+    L.gcnt = take(nlist * sizeof(int32_t));
+    L.gfill = take(nlist * sizeof(int32_t));
+    L.gstart = take((nlist + 1) * sizeof(int32_t));
+    L.ustart = take((nlist + 1) * sizeof(int32_t));
+    L.gq = take((size_t)B * nprobe * sizeof(int32_t));
+    L.units = take((size_t)L.max_units * sizeof(GUnit));
+    L.pool_cnt = take((size_t)B * sizeof(uint32_t));
+    L.pool = take((size_t)B * (size_t)L.pool_cap * sizeof(uint64_t));
+  }
   L.total = o;
   return L;
 }
@@ -330,7 +373,34 @@ extern "C" int svt_search(const svt_index *ix, int32_t B, const int8_t *queries,
   w.slot_min = (uint64_t *)(base + L.slot_min);
   w.slot_keys = (uint64_t *)(base + L.slot_keys);
   w.stats = out_stats ? out_stats : (int64_t *)(base + L.stats);
-  SearchShape sh{B, nprobe, k, ix->scan_wgs, L.max_chunks};
+  // path: SVT_PATH=query|grouped forces one; otherwise batches of kGroupedMinBatch or more queries are
+  // grouped
+  int grouped = B >= kGroupedMinBatch ? 1 : 0;
+  if (const char *pe = getenv("SVT_PATH")) {
+    if (!strcmp(pe, "query")) grouped = 0;
+    else if (!strcmp(pe, "grouped")) grouped = 1;
+  }
+  if (L.max_units == 0) grouped = 0;
+  int32_t pool_cap = L.pool_cap;
+  if (const char *pc = getenv("SVT_POOL_CAP")) {   // smaller pools, to exercise the overflow fallback
+    const long v = strtol(pc, nullptr, 10);
+    if (v >= 1 && v < pool_cap) pool_cap = (int32_t)v;
+  }
+  w.gcnt = w.gfill = w.gstart = w.ustart = w.gq = nullptr;
+  w.units = nullptr;
+  w.pool_cnt = nullptr;
+  w.pool = nullptr;
+  if (grouped) {
+    w.gcnt = (int32_t *)(base + L.gcnt);
+    w.gfill = (int32_t *)(base + L.gfill);
+    w.gstart = (int32_t *)(base + L.gstart);
+    w.ustart = (int32_t *)(base + L.ustart);
+    w.gq = (int32_t *)(base + L.gq);
+    w.units = (GUnit *)(base + L.units);
+    w.pool_cnt = (uint32_t *)(base + L.pool_cnt);
+    w.pool = (uint64_t *)(base + L.pool);
+  }
+  SearchShape sh{B, nprobe, k, ix->scan_wgs, L.max_chunks, grouped, pool_cap, L.max_units};
 
   const bool prof = g_prof_on.load(std::memory_order_relaxed) != 0 && g_prof.searches < kMaxProfiledSearches;
   ProfState &ps = g_prof;
@@ -352,10 +422,28 @@ extern "C" int svt_search(const svt_index *ix, int32_t B, const int8_t *queries,
   if ((e = launch_coarse_select(ix->dev, queries, masks, sh, w, s)) != hipSuccess)
     return fail_hip(e, "launch coarse_select");
   if ((e = mark()) != hipSuccess) return fail_hip(e, "event");
-  if ((e = launch_scan(ix->dev, queries, masks, sh, w, s)) != hipSuccess) return fail_hip(e, "launch scan");
+  if (grouped && (e = launch_group_plan(ix->dev, sh, w, s)) != hipSuccess) return fail_hip(e, "launch group plan");
   if ((e = mark()) != hipSuccess) return fail_hip(e, "event");
-  if ((e = launch_merge(ix->dev, query_scales, sh, w, out_ids, out_scores, out_fscores, out_counts, s)) != hipSuccess)
-    return fail_hip(e, "launch merge");
+  if (grouped) {
+    if ((e = launch_gscan(ix->dev, queries, masks, sh, w, s)) != hipSuccess) return fail_hip(e, "launch gscan");
+    if ((e = mark()) != hipSuccess) return fail_hip(e, "event");
+    // queries whose pools overflowed, query by query (every other chunk and query returns at once)
+    if ((e = launch_scan(ix->dev, queries, masks, sh, w, s)) != hipSuccess) return fail_hip(e, "launch scan");
+    if ((e = launch_merge(ix->dev, query_scales, sh, w, out_ids, out_scores, out_fscores, out_counts, s)) !=
+        hipSuccess)
+      return fail_hip(e, "launch merge");
+    if ((e = mark()) != hipSuccess) return fail_hip(e, "event");
+    if ((e = launch_pool_merge(ix->dev, query_scales, sh, w, out_ids, out_scores, out_fscores, out_counts, s)) !=
+        hipSuccess)
+      return fail_hip(e, "launch pool merge");
+  } else {
+    if ((e = launch_scan(ix->dev, queries, masks, sh, w, s)) != hipSuccess) return fail_hip(e, "launch scan");
+    if ((e = mark()) != hipSuccess) return fail_hip(e, "event");
+    if ((e = mark()) != hipSuccess) return fail_hip(e, "event");
+    if ((e = launch_merge(ix->dev, query_scales, sh, w, out_ids, out_scores, out_fscores, out_counts, s)) !=
+        hipSuccess)
+      return fail_hip(e, "launch merge");
+  }
   if ((e = mark()) != hipSuccess) return fail_hip(e, "event");
   if (prof) ++ps.searches;
   return SVT_OK;
@@ -373,7 +461,7 @@ extern "C" int svt_profile_read(float *stage_ms, const char **stage_names, int32
   const int ns = ps.searches;
   if (n_stages) *n_stages = kStages;
   if (n_searches) *n_searches = ns;
-  double tot[kStages] = {0, 0, 0, 0};
+  double tot[kStages] = {0, 0, 0, 0, 0, 0};
   if (ns > 0) {
     hipError_t e = hipEventSynchronize(ps.pool[ns * (kStages + 1) - 1]);
     if (e != hipSuccess) return fail_hip(e, "hipEventSynchronize");

@@ -52,6 +52,14 @@ constexpr int kMergeCap = 6144;             // merge candidates staged in LDS
 constexpr int kSelSegLds = 4096;            // probe lists up to this long are searched in LDS
 constexpr int64_t kMinChunkCost = 16 << 10; // smallest chunk, in estimated bytes moved
 
+// Grouped path: one unit of work is a tile of at most kGTile items of one probed cluster together
+// with a group of at most kGMax of the queries that probe that cluster (gq[q0..q1)).
+constexpr int kGTile = 4096;
+constexpr int kGMax = 32;
+struct GUnit {
+  int32_t c, lo, hi, q0, q1, pad0, pad1, pad2;   // items at positions [lo, hi) of cluster c
+};
+
 // Per-search device workspace (carved by the host from the caller's buffer).
 struct Work {
   uint64_t *coarse_keys;    // [B][nlist]   coarse (score, cluster) keys
@@ -67,15 +75,27 @@ struct Work {
   int32_t *hlo;             // [B]          score at the lower edge of bin 1 of the query's histogram
   int32_t *hshift;          // [B]          bin width of that histogram is 2^hshift
   uint32_t *ghist;          // [B][kQHistBins] scores of every candidate any chunk accepted
-  uint32_t *counter;        // [2]          select completion counter, scan work-queue head
+  uint32_t *counter;        // [3]          select completion counter, scan and grouped-scan queue heads
   int32_t *slot_cnt;        // [max_chunks] candidates each chunk left
   uint64_t *slot_min;       // [max_chunks] smallest key of a slot holding k keys, else 0
   uint64_t *slot_keys;      // [max_chunks][k] those candidates (score/id keys)
   int64_t *stats;           // [B][2] scanned / eligible (caller buffer or workspace)
+  // grouped path (null when the search runs query by query)
+  int32_t *gcnt;            // [nlist]      queries probing each cluster
+  int32_t *gfill;           // [nlist]      fill cursor of each cluster's query list
+  int32_t *gstart;          // [nlist + 1]  each cluster's query list in gq
+  int32_t *ustart;          // [nlist + 1]  first unit of each cluster; ustart[nlist] = number of units
+  int32_t *gq;              // [B * nprobe] queries of every probed cluster, grouped by cluster
+  GUnit *units;             // [max_units]
+  uint32_t *pool_cnt;       // [B]          candidates offered to each query's pool (> pool_cap: overflow)
+  uint64_t *pool;           // [B][pool_cap] (score, position) keys of the candidates
 };
 
 struct SearchShape {
   int32_t B, nprobe, k, P, max_chunks;
+  int32_t grouped;     // 1: grouped path with the query-by-query scan as fallback for overflowing pools
+  int32_t pool_cap;    // keys per query pool
+  int32_t max_units;
 };
 
 // most chunks a search can produce: cost-balanced chunks number at most 4 P + B
@@ -91,6 +111,13 @@ hipError_t launch_scan(const DevIndex &ix, const int8_t *queries, const uint64_t
 hipError_t launch_merge(const DevIndex &ix, const float *query_scales, const SearchShape &sh, const Work &w,
                         int64_t *out_ids, int32_t *out_scores, float *out_fscores, int32_t *out_counts,
                         hipStream_t s);
+// grouped path (svt_group.hip)
+hipError_t launch_group_plan(const DevIndex &ix, const SearchShape &sh, const Work &w, hipStream_t s);
+hipError_t launch_gscan(const DevIndex &ix, const int8_t *queries, const uint64_t *masks, const SearchShape &sh,
+                        const Work &w, hipStream_t s);
+hipError_t launch_pool_merge(const DevIndex &ix, const float *query_scales, const SearchShape &sh, const Work &w,
+                             int64_t *out_ids, int32_t *out_scores, float *out_fscores, int32_t *out_counts,
+                             hipStream_t s);
 // resident scan workgroups per compute unit for this shape (0 if unknown)
 int scan_blocks_per_cu(int32_t dim, int32_t sig_words);
 hipError_t launch_scatter_rows(const int8_t *src_rows, const uint64_t *src_sigs, const int32_t *pos_of,

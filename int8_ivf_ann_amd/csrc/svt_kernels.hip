@@ -22,163 +22,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "svt_device.h"
 #include "svt_internal.h"
 
 namespace svt {
-
-// ------------------------------------------------------------------------------------------------
-// small device helpers
-
-__device__ __forceinline__ uint64_t make_key(int32_t score, uint32_t id) {
-  return ((uint64_t)((uint32_t)score ^ 0x80000000u) << 32) | (uint64_t)(0xFFFFFFFFu - id);
-}
-__device__ __forceinline__ int32_t key_score(uint64_t key) {
-  return (int32_t)((uint32_t)(key >> 32) ^ 0x80000000u);
-}
-__device__ __forceinline__ uint32_t key_id(uint64_t key) { return 0xFFFFFFFFu - (uint32_t)key; }
-
-// 16 int8 products accumulated in int32 with four v_dot4 instructions
-__device__ __forceinline__ int32_t dot16(const int4 x, const int4 y, int32_t acc) {
-  acc = __builtin_amdgcn_sdot4(x.x, y.x, acc, false);
-  acc = __builtin_amdgcn_sdot4(x.y, y.y, acc, false);
-  acc = __builtin_amdgcn_sdot4(x.z, y.z, acc, false);
-  acc = __builtin_amdgcn_sdot4(x.w, y.w, acc, false);
-  return acc;
-}
-
-// Sum of v over each group of LPR consecutive lanes (LPR = 1, 2, 4, 8 or 16), valid in the group's first
-// lane.  DPP lane moves: quad permutations for lane ^ 1 and lane ^ 2, then row shifts that bring lane
-// + 4 and lane + 8 (within a 16-lane row) to the group's first lane.
-template <int LPR>
-__device__ __forceinline__ int32_t group_sum(int32_t v) {
-  if constexpr (LPR >= 2) v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, true);    // quad_perm 1,0,3,2
-  if constexpr (LPR >= 4) v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, true);    // quad_perm 2,3,0,1
-  if constexpr (LPR >= 8) v += __builtin_amdgcn_update_dpp(0, v, 0x104, 0xF, 0xF, true);   // row_shl:4
-  if constexpr (LPR >= 16) v += __builtin_amdgcn_update_dpp(0, v, 0x108, 0xF, 0xF, true);  // row_shl:8
-  return v;
-}
-
-__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
-
-// number of set bits of `mask` below this lane
-__device__ __forceinline__ int mbcnt(uint64_t mask) {
-  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-}
-
-template <typename T>
-__device__ __forceinline__ T wave_incl_scan(T v) {
-  const int l = lane_id();
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    T u = __shfl_up(v, off);
-    if (l >= off) v += u;
-  }
-  return v;
-}
-
-// exclusive block scan of one value per thread; returns the block total in *total.
-// wave_tot: LDS scratch of NT/64 + 1 values.
-template <int NT, typename T>
-__device__ __forceinline__ T block_excl_scan(T v, T *wave_tot, T *total) {
-  constexpr int NW = NT / 64;
-  const int l = lane_id(), wv = threadIdx.x / 64;
-  T inc = wave_incl_scan(v);
-  if (l == 63) wave_tot[wv] = inc;
-  __syncthreads();
-  if (wv == 0) {
-    T t = l < NW ? wave_tot[l] : T(0);
-    T ti = wave_incl_scan(t);
-    if (l < NW) wave_tot[l] = ti - t;           // exclusive wave offsets
-    if (l == NW - 1) wave_tot[NW] = ti;         // total
-  }
-  __syncthreads();
-  T r = wave_tot[wv] + inc - v;
-  *total = wave_tot[NW];
-  __syncthreads();
-  return r;
-}
-
-// ------------------------------------------------------------------------------------------------
-// Block radix select over distinct 64-bit keys.
-//
-// Returns T such that the keys >= T are exactly the `need` largest keys visited by `for_each`
-// (1 <= need <= number of keys).  Passes of 8-bit digits start at the highest bit in which the keys
-// differ and stop as soon as the boundary bucket is taken whole.  Every thread of the block calls it.
-
-struct SelScratch {
-  uint32_t hist[256];
-  unsigned long long kmin, kmax;
-  int digit, above;
-};
-
-template <int NT, class ForEach>
-__device__ uint64_t block_select(ForEach for_each, int need, SelScratch &sh) {
-  const int tid = threadIdx.x, l = lane_id();
-  if (tid == 0) { sh.kmin = ~0ull; sh.kmax = 0ull; }
-  __syncthreads();
-  unsigned long long lmin = ~0ull, lmax = 0ull;
-  for_each([&](uint64_t key) {
-    lmin = key < lmin ? key : lmin;
-    lmax = key > lmax ? key : lmax;
-  });
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    unsigned long long a = __shfl_xor(lmin, off), b = __shfl_xor(lmax, off);
-    lmin = a < lmin ? a : lmin;
-    lmax = b > lmax ? b : lmax;
-  }
-  if (l == 0) { atomicMin(&sh.kmin, lmin); atomicMax(&sh.kmax, lmax); }
-  __syncthreads();
-  const uint64_t kmin = sh.kmin, kmax = sh.kmax;
-  if (kmin == kmax) return kmin;
-  const int hb = 63 - __clzll((long long)(kmin ^ kmax));   // highest bit in which keys differ
-  int fixed = hb + 1;                                        // bits >= fixed are common to all keys
-  int shift = fixed >= 8 ? fixed - 8 : 0;
-  uint64_t hi_mask = fixed >= 64 ? 0ull : ~((1ull << fixed) - 1);
-  uint64_t prefix = kmin & hi_mask;
-  int need_rem = need;
-  for (;;) {
-    for (int i = tid; i < 256; i += NT) sh.hist[i] = 0u;
-    if (tid == 0) { sh.digit = 0; sh.above = 0; }
-    __syncthreads();
-    const uint64_t m = hi_mask, p = prefix;
-    const int s = shift;
-    for_each([&](uint64_t key) {
-      if ((key & m) == p) atomicAdd(&sh.hist[(key >> s) & 255u], 1u);
-    });
-    __syncthreads();
-    if (tid < 64) {
-      uint32_t h0 = sh.hist[4 * l], h1 = sh.hist[4 * l + 1], h2 = sh.hist[4 * l + 2], h3 = sh.hist[4 * l + 3];
-      uint32_t sum = h0 + h1 + h2 + h3, suf = sum;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        uint32_t u = __shfl_down(suf, off);
-        if (l + off < 64) suf += u;
-      }
-      uint32_t above = suf - sum;   // keys in buckets above 4l+3
-      const uint32_t nr = (uint32_t)need_rem;
-      uint32_t hh[4] = {h0, h1, h2, h3};
-#pragma unroll
-      for (int j = 3; j >= 0; --j) {
-        if (above < nr && above + hh[j] >= nr) { sh.digit = 4 * l + j; sh.above = (int)above; }
-        above += hh[j];
-      }
-    }
-    __syncthreads();
-    const int d = sh.digit;
-    const int hd = (int)sh.hist[d];
-    need_rem -= sh.above;
-    prefix |= (uint64_t)d << shift;
-    if (hd == need_rem || shift == 0) break;
-    fixed = shift;
-    hi_mask = ~((1ull << fixed) - 1);
-    prefix &= hi_mask;
-    shift = fixed >= 8 ? fixed - 8 : 0;
-    __syncthreads();
-  }
-  __syncthreads();
-  return prefix;
-}
 
 // ------------------------------------------------------------------------------------------------
 // k_coarse_keys: key (s, c) for every query b and cluster c, s = <q_b, centroid_c> (int32).
@@ -187,12 +34,17 @@ __device__ uint64_t block_select(ForEach for_each, int need, SelScratch &sh) {
 template <int LPR>
 __global__ __launch_bounds__(256) void k_coarse_keys(const int8_t *__restrict__ centroids, int32_t nlist,
                                                      const int8_t *__restrict__ queries, int32_t B,
-                                                     uint64_t *__restrict__ keys, uint32_t *counter) {
+                                                     uint64_t *__restrict__ keys, uint32_t *counter,
+                                                     int32_t *__restrict__ gcnt, int32_t *__restrict__ gfill) {
   constexpr int D = 16 * LPR;
   __shared__ int4 qs[kCoarseQB][LPR];
   const int tid = threadIdx.x;
   const int b0 = blockIdx.y * kCoarseQB;
-  if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) { counter[0] = 0u; counter[1] = 0u; }
+  if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) { counter[0] = 0u; counter[1] = 0u; counter[2] = 0u; }
+  if (gcnt && blockIdx.y == 0 && blockIdx.x * 256 + tid < nlist) {   // grouped path: per-cluster counters
+    gcnt[blockIdx.x * 256 + tid] = 0;
+    gfill[blockIdx.x * 256 + tid] = 0;
+  }
   for (int i = tid; i < kCoarseQB * LPR; i += 256) {
     int qi = i / LPR, ch = i % LPR;
     int b = b0 + qi;
@@ -278,6 +130,7 @@ __global__ __launch_bounds__(kSelThreads) void k_coarse_select(DevIndex ix, cons
     if (nprobe <= kSelSegLds) seg_lds[nprobe] = run;
     w.qlen[b] = run;
     w.thr[b] = INT32_MIN;
+    if (w.pool_cnt) w.pool_cnt[b] = 0u;
     if (w.stats) { w.stats[2 * (size_t)b] = 0; w.stats[2 * (size_t)b + 1] = 0; }
   }
   __syncthreads();
@@ -455,6 +308,10 @@ struct ScanArgs {
   const uint64_t *masks;
   Work w;
   int32_t B, nprobe, k, P;
+  // fallback mode (grouped search): only queries whose candidate pool overflowed are scanned, without
+  // the histogram exchange (the grouped scan already counted their candidates) and without statistics
+  int32_t fallback;
+  uint32_t pool_cap;
 };
 
 struct ScanLds {
@@ -479,13 +336,6 @@ struct ScanLds {
   int32_t gbound;            // the query's bound as read once for the whole block
   int next;                  // queue position of this workgroup's next chunk
 };
-
-// Keys held while a chunk is in progress: (biased score << 32) | position.  They are turned into
-// (score, id) ordering keys (make_key) only for the few that survive to the end of the chunk, so the
-// hot loop never waits on the position -> id table.
-__device__ __forceinline__ uint64_t pos_key(int32_t score, int32_t pos) {
-  return ((uint64_t)((uint32_t)score ^ 0x80000000u) << 32) | (uint64_t)(uint32_t)pos;
-}
 
 // Keep the keys >= T of list[0..cnt) (T from block_select), in place; returns the count kept and the
 // smallest kept key in *kmin_out.  Two rounds over halves of the list keep the register footprint at
@@ -644,15 +494,21 @@ __device__ __forceinline__ int trim_list(ScanLds &sm, int cnt, int k, const int3
   return kept;
 }
 
-// End of a chunk: turn the list into (score, id) keys, drop keys below the bound gb and cut to the
-// exact top k; *kth receives the smallest kept key when exactly k remain (0 otherwise).  All threads
-// call it; returns the count kept.
+// End of a chunk: drop keys below the bound gb, turn the rest into (score, id) keys and cut them to the
+// exact top k; *kth receives the smallest kept key when exactly k remain (0 otherwise).  Keys below the
+// bound go before the position -> id lookups, so that only survivors pay for them; both key kinds hold
+// the biased score in their upper half, so one threshold serves either.  All threads call it; returns
+// the count kept.
 __device__ __forceinline__ int finish_list(ScanLds &sm, int cnt, int k, int id_n, int32_t gb,
                                            const int32_t *__restrict__ perm, int32_t *thr_q, uint64_t *kth_out) {
   const int tid = threadIdx.x, l = lane_id();
-  to_id_keys(sm, id_n, cnt, perm);   // ends with a barrier
   uint64_t kth = 0;
-  if (gb != INT32_MIN) cnt = keep_at_least(sm, cnt, make_key(gb, 0xFFFFFFFFu), &kth);
+  if (id_n > 0) {   // rare (score ties at a trim): the list already starts with id keys; convert the rest
+    to_id_keys(sm, id_n, cnt, perm);
+    id_n = cnt;
+  }
+  if (gb != INT32_MIN) cnt = keep_at_least(sm, cnt, (uint64_t)((uint32_t)gb ^ 0x80000000u) << 32, &kth);
+  if (id_n == 0) to_id_keys(sm, 0, cnt, perm);   // ends with a barrier
   if (cnt > k) {
     const uint64_t T = block_select<kScanThreads>(
         [&](auto f) {
@@ -661,7 +517,7 @@ __device__ __forceinline__ int finish_list(ScanLds &sm, int cnt, int k, int id_n
         k, sm.sel);
     cnt = keep_at_least(sm, cnt, T, &kth);
     if (tid == 0) atomicMax(thr_q, key_score(kth));
-  } else if (cnt == k && gb == INT32_MIN) {
+  } else if (cnt == k) {
     if (tid == 0) sm.kmin = ~0ull;
     __syncthreads();
     unsigned long long mn = ~0ull;
@@ -701,6 +557,16 @@ __global__ __launch_bounds__(kScanThreads, 4) void k_scan(ScanArgs a) {
     if (tid == 0) next_c = (int)atomicAdd(&a.w.counter[1], 1u);
     const Chunk ch = a.w.chunks[c];
     const int q = ch.q;
+    if (a.fallback && a.w.pool_cnt[q] <= a.pool_cap) {   // this query's pool holds all its candidates
+      __syncthreads();   // every thread has read sm.next before it is replaced
+      if (tid == 0) {
+        a.w.slot_cnt[c] = 0;
+        a.w.slot_min[c] = 0ull;
+        sm.next = next_c;
+      }
+      __syncthreads();
+      continue;
+    }
     const int32_t ra = ch.lo, rb = ch.hi;
     const int32_t hlo = a.w.hlo[q];
     const int hsh = a.w.hshift[q];
@@ -964,13 +830,13 @@ __global__ __launch_bounds__(kScanThreads, 4) void k_scan(ScanArgs a) {
       }
       // histogram exchange after steps 2, 4, 8, ...: the bound converges within a few exchanges
       ++steps;
-      if (steps >= 2 && (steps & (steps - 1)) == 0) {
+      if (!a.fallback && steps >= 2 && (steps & (steps - 1)) == 0) {
         hist_push();
         pull = true;
       }
     }
     // --- end of the chunk: its exact top k above the query's bound, published in slot c
-    hist_push();
+    if (!a.fallback) hist_push();
     // keys below the query's bound cannot be in its top k.  The branches below contain barriers, so
     // the block uses one value of the bound, read by one thread.
     if (tid == 0) sm.gbound = gthr > thr_s ? gthr : thr_s;
@@ -987,7 +853,7 @@ __global__ __launch_bounds__(kScanThreads, 4) void k_scan(ScanArgs a) {
       sm.next = next_c;
     }
     // per-query counters: items scanned by this chunk, items that passed the filter
-    if (a.w.stats) {
+    if (a.w.stats && !a.fallback) {
       // n_elig is uniform across the wave: one add per wave
       if (l == 0) atomicAdd((unsigned long long *)&a.w.stats[2 * (size_t)q + 1], (unsigned long long)n_elig);
       if (tid == 0) atomicAdd((unsigned long long *)&a.w.stats[2 * (size_t)q], (unsigned long long)(rb - ra));
@@ -1005,6 +871,8 @@ struct MergeArgs {
   const float *query_scales;
   float item_scale;
   int32_t B, k, P;
+  int32_t fallback;     // grouped search: only queries whose pool overflowed are merged here
+  uint32_t pool_cap;
   int64_t *out_ids;
   int32_t *out_scores;
   float *out_fscores;
@@ -1027,6 +895,7 @@ __global__ __launch_bounds__(kSelThreads) void k_merge(MergeArgs a) {
   const int tid = threadIdx.x, l = lane_id();
   const int q = blockIdx.x;
   const int k = a.k;
+  if (a.fallback && a.w.pool_cnt[q] <= a.pool_cap) return;   // merged from its pool
   // the query's chunks, hence its slots, are cstart[q] .. cstart[q+1]-1 (contiguous in memory)
   const size_t s0 = (size_t)a.w.cstart[q];
   const int ns = a.w.cstart[q + 1] - a.w.cstart[q];
@@ -1193,40 +1062,8 @@ __global__ __launch_bounds__(kSelThreads) void k_merge(MergeArgs a) {
     __syncthreads();
     n = tot;
   }
-  // 4. bitonic sort of the n (= nout) winners, descending, over the next power of two
-  int np2 = 1;
-  while (np2 < n) np2 <<= 1;
-  for (int i = n + tid; i < np2; i += kSelThreads) cand[i] = 0ull;
-  __syncthreads();
-  for (int size = 2; size <= np2; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = tid; i < np2; i += kSelThreads) {
-        const int j = i ^ stride;
-        if (j > i) {
-          const uint64_t x = cand[i], y = cand[j];
-          const bool up = (i & size) == 0;   // this run sorts descending
-          if (up ? (x < y) : (x > y)) { cand[i] = y; cand[j] = x; }
-        }
-      }
-      __syncthreads();
-    }
-  }
-  const float qs = a.query_scales ? a.query_scales[q] : a.item_scale;
-  const double denom = (double)a.item_scale * (double)qs;
-  for (int i = tid; i < k; i += kSelThreads) {
-    const size_t o = (size_t)q * k + i;
-    if (i < nout) {
-      const uint64_t key = cand[i];
-      const int32_t sc = key_score(key);
-      a.out_ids[o] = (int64_t)key_id(key);
-      a.out_scores[o] = sc;
-      if (a.out_fscores) a.out_fscores[o] = (float)((double)sc / denom);
-    } else {
-      a.out_ids[o] = -1;
-      a.out_scores[o] = INT32_MIN;
-      if (a.out_fscores) a.out_fscores[o] = -__builtin_huge_valf();
-    }
-  }
+  // 4. sort the n (= nout) winners and write the query's row
+  emit_sorted<kSelThreads>(cand, n, nout, q, k, a.query_scales, a.item_scale, a.out_ids, a.out_scores, a.out_fscores);
   if (tid == 0 && a.out_counts) a.out_counts[q] = nout;
 }
 
@@ -1254,11 +1091,11 @@ __global__ __launch_bounds__(256) void k_scatter_rows(const int8_t *__restrict__
 hipError_t launch_coarse_keys(const DevIndex &ix, const int8_t *queries, int32_t B, const Work &w, hipStream_t s) {
   dim3 grid((ix.nlist + 255) / 256, (B + kCoarseQB - 1) / kCoarseQB);
   switch (ix.dim) {
-    case 16: k_coarse_keys<1><<<grid, 256, 0, s>>>(ix.centroids, ix.nlist, queries, B, w.coarse_keys, w.counter); break;
-    case 32: k_coarse_keys<2><<<grid, 256, 0, s>>>(ix.centroids, ix.nlist, queries, B, w.coarse_keys, w.counter); break;
-    case 64: k_coarse_keys<4><<<grid, 256, 0, s>>>(ix.centroids, ix.nlist, queries, B, w.coarse_keys, w.counter); break;
-    case 128: k_coarse_keys<8><<<grid, 256, 0, s>>>(ix.centroids, ix.nlist, queries, B, w.coarse_keys, w.counter); break;
-    case 256: k_coarse_keys<16><<<grid, 256, 0, s>>>(ix.centroids, ix.nlist, queries, B, w.coarse_keys, w.counter); break;
+    case 16: k_coarse_keys<1><<<grid, 256, 0, s>>>(ix.centroids, ix.nlist, queries, B, w.coarse_keys, w.counter, w.gcnt, w.gfill); break;
+    case 32: k_coarse_keys<2><<<grid, 256, 0, s>>>(ix.centroids, ix.nlist, queries, B, w.coarse_keys, w.counter, w.gcnt, w.gfill); break;
+    case 64: k_coarse_keys<4><<<grid, 256, 0, s>>>(ix.centroids, ix.nlist, queries, B, w.coarse_keys, w.counter, w.gcnt, w.gfill); break;
+    case 128: k_coarse_keys<8><<<grid, 256, 0, s>>>(ix.centroids, ix.nlist, queries, B, w.coarse_keys, w.counter, w.gcnt, w.gfill); break;
+    case 256: k_coarse_keys<16><<<grid, 256, 0, s>>>(ix.centroids, ix.nlist, queries, B, w.coarse_keys, w.counter, w.gcnt, w.gfill); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -1280,7 +1117,7 @@ static void scan_w(const ScanArgs &a, int W, hipStream_t s) {
 
 hipError_t launch_scan(const DevIndex &ix, const int8_t *queries, const uint64_t *masks, const SearchShape &sh,
                        const Work &w, hipStream_t s) {
-  ScanArgs a{ix, queries, masks, w, sh.B, sh.nprobe, sh.k, sh.P};
+  ScanArgs a{ix, queries, masks, w, sh.B, sh.nprobe, sh.k, sh.P, sh.grouped, (uint32_t)sh.pool_cap};
   switch (ix.dim) {
     case 16: scan_w<1>(a, ix.sig_words, s); break;
     case 32: scan_w<2>(a, ix.sig_words, s); break;
@@ -1314,7 +1151,8 @@ int scan_blocks_per_cu(int32_t dim, int32_t sig_words) {
 hipError_t launch_merge(const DevIndex &ix, const float *query_scales, const SearchShape &sh, const Work &w,
                         int64_t *out_ids, int32_t *out_scores, float *out_fscores, int32_t *out_counts,
                         hipStream_t s) {
-  MergeArgs a{w, query_scales, ix.item_scale, sh.B, sh.k, sh.P, out_ids, out_scores, out_fscores, out_counts};
+  MergeArgs a{w, query_scales, ix.item_scale, sh.B, sh.k, sh.P, sh.grouped, (uint32_t)sh.pool_cap,
+              out_ids, out_scores, out_fscores, out_counts};
   k_merge<<<sh.B, kSelThreads, 0, s>>>(a);
   return hipGetLastError();
 }

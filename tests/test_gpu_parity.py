@@ -21,6 +21,21 @@ def svt():
     return m
 
 
+# Every case runs on both search paths: query by query, and grouped (each probed cluster read once for
+# all the queries probing it), the latter also with candidate pools so small that most queries overflow
+# and are redone query by query.  The library reads SVT_PATH / SVT_POOL_CAP at each search.
+@pytest.fixture(params=["query", "grouped", "grouped-overflow"], autouse=True)
+def search_path(request, monkeypatch):
+    path = request.param
+    monkeypatch.setenv("SVT_PATH", "query" if path == "query" else "grouped")
+    if path == "grouped-overflow":
+        monkeypatch.setenv("SVT_POOL_CAP", "64")
+    else:
+        monkeypatch.delenv("SVT_POOL_CAP", raising=False)
+    print(f"path {path}", flush=True)
+    return path
+
+
 def _run(svt, items, sigs, list_of, cent, scale, q, masks, nprobe, k, label, query_scales=None, invariants=True):
     say(f"case {label}: n={items.shape[0]} d={items.shape[1]} W={sigs.shape[1]} nlist={cent.shape[0]} "
         f"B={q.shape[0]} nprobe={nprobe} k={k}")

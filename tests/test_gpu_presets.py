@@ -99,3 +99,9 @@ def test_10m_batch64(p10m):
 
 def test_10m_batch64_other(p10m):
     p10m.check(64, 5000, label="10m-b64-2")
+
+
+def test_10m_batch64_query_path(p10m, monkeypatch):
+    """Batches of this size are grouped by default; the query-by-query path at full size too."""
+    monkeypatch.setenv("SVT_PATH", "query")
+    p10m.check(64, 10_000, label="10m-b64-query-path")
