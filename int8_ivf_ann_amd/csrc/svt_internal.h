@@ -12,15 +12,25 @@ constexpr int kScanThreads = 256;    // fused filter-score-select workgroup: 4 w
 #ifndef SVT_SCAN_GROUPS
 #define SVT_SCAN_GROUPS 4
 #endif
-#ifndef SVT_ROW_BATCH
-#define SVT_ROW_BATCH 32
-#endif
 constexpr int kScanGroups = SVT_SCAN_GROUPS;   // 64-item groups per wave per step
-constexpr int kRowBatch = SVT_ROW_BATCH;       // rows a wave requests together (d <= 128)
 constexpr int kScanStep = kScanThreads * kScanGroups;   // items per workgroup step (1024)
-constexpr int kListCap = 4096;                          // LDS candidate list capacity (keys)
+#ifndef SVT_SCAN_OCC
+#define SVT_SCAN_OCC 3
+#endif
+#ifndef SVT_SCAN_ROW_BATCH
+#define SVT_SCAN_ROW_BATCH 32
+#endif
+constexpr int kScanOcc = SVT_SCAN_OCC;              // query-by-query scan: waves per SIMD (workgroups per CU)
+constexpr int kScanRowBatch = SVT_SCAN_ROW_BATCH;   // rows a wave gathers together (at least one load per lane)
+#ifndef SVT_LIST_CAP
+#define SVT_LIST_CAP 4096
+#endif
+constexpr int kListCap = SVT_LIST_CAP;                  // LDS candidate list capacity (keys)
 constexpr int kTrimAt = kListCap - kScanStep;           // a list longer than this is trimmed
-constexpr int kTrimBins = 1024;                         // score histogram bins of a trim
+// a trim cuts the list to at least k keys and must leave room for a step's appends
+static_assert(kTrimAt >= kMaxK, "the candidate list must hold k keys plus one step");
+constexpr int kTrimBinsLog2 = 9;
+constexpr int kTrimBins = 1 << kTrimBinsLog2;           // score histogram bins of a trim
 constexpr int kSegWin = 64;                             // probed clusters staged in LDS at a time
 constexpr int kQHistBins = 256;                         // bins of a query's global score histogram
 constexpr int kSelThreads = 1024;    // coarse-select and merge workgroups

@@ -316,11 +316,9 @@ struct ScanArgs {
 
 struct ScanLds {
   uint64_t list[kListCap];
-  union {
-    uint16_t wl[kScanThreads * kScanGroups];   // survivor offsets of one step, wave w's at [w * 256, ...)
-    uint32_t hist[kTrimBins];                  // score histogram of a trim
-  } u;
-  SelScratch sel;
+  // survivor offsets of three consecutive steps (step i in wl[i % 3], wave w's at [w * 256, ...)); the
+  // buffer of step i - 1 is free while step i is scored and serves as scratch of trims and selects
+  uint16_t wl[3][kScanThreads * kScanGroups];
   int wave_tot[kScanThreads / 64 + 1];
   unsigned long long kmin;
   uint32_t smin, smax;
@@ -328,7 +326,7 @@ struct ScanLds {
   // keys each wave appended in a step, by step parity: the list length after a step is computed from
   // these by every thread, never read from cnt, which faster waves may already be advancing
   int wadd[2][kScanThreads / 64];
-  int wcnt[kScanThreads / 64];   // survivors each wave found in the current step
+  int wcnt[2][kScanThreads / 64];   // survivors each wave found in a step, by step parity
   // window of the chunk's probed clusters: stream range [t0, t1) and position base (pos = pb + t)
   int32_t seg_t0[kSegWin], seg_t1[kSegWin], seg_pb[kSegWin];
   int seg_n;
@@ -386,7 +384,7 @@ __device__ __forceinline__ int keep_at_least(ScanLds &sm, int cnt, uint64_t T, u
 // kTrimBins bins over [min, max], find the bin b* at which the count from the top reaches k and drop
 // every key below b*'s lower edge s*.  At least k keys have score >= s*, so no dropped key can be in
 // the top k; ties at the edge are all kept.  Returns the count kept; *edge receives s* (biased).
-__device__ __forceinline__ int trim_by_score(ScanLds &sm, int cnt, int k, uint32_t *edge) {
+__device__ __forceinline__ int trim_by_score(ScanLds &sm, int cnt, int k, uint32_t *edge, uint32_t *hist) {
   const int tid = threadIdx.x, l = lane_id();
   if (tid == 0) { sm.smin = ~0u; sm.smax = 0u; }
   __syncthreads();
@@ -403,19 +401,19 @@ __device__ __forceinline__ int trim_by_score(ScanLds &sm, int cnt, int k, uint32
     lmax = b > lmax ? b : lmax;
   }
   if (l == 0) { atomicMin(&sm.smin, lmin); atomicMax(&sm.smax, lmax); }
-  for (int i = tid; i < kTrimBins; i += kScanThreads) sm.u.hist[i] = 0u;
+  for (int i = tid; i < kTrimBins; i += kScanThreads) hist[i] = 0u;
   __syncthreads();
   const uint32_t smin = sm.smin, range = sm.smax - smin;
   const int bits = range ? 32 - __clz(range) : 0;            // range < 2^bits
-  const int shift = bits > 10 ? bits - 10 : 0;               // (range >> shift) < kTrimBins
+  const int shift = bits > kTrimBinsLog2 ? bits - kTrimBinsLog2 : 0;   // (range >> shift) < kTrimBins
   for (int i = tid; i < cnt; i += kScanThreads)
-    atomicAdd(&sm.u.hist[((uint32_t)(sm.list[i] >> 32) - smin) >> shift], 1u);
+    atomicAdd(&hist[((uint32_t)(sm.list[i] >> 32) - smin) >> shift], 1u);
   __syncthreads();
   if (tid < 64) {
     constexpr int PB = kTrimBins / 64;
     uint32_t h[PB], sum = 0;
 #pragma unroll
-    for (int j = 0; j < PB; ++j) { h[j] = sm.u.hist[PB * l + j]; sum += h[j]; }
+    for (int j = 0; j < PB; ++j) { h[j] = hist[PB * l + j]; sum += h[j]; }
     uint32_t suf = sum;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -469,12 +467,12 @@ struct ListState {
 // Cut an over-full list back towards k (rare: the bounds reject most candidates).  All threads call
 // it; returns the count kept.
 __device__ __forceinline__ int trim_list(ScanLds &sm, int cnt, int k, const int32_t *__restrict__ perm,
-                                         ListState &st) {
+                                         ListState &st, uint32_t *scratch) {
   const int tid = threadIdx.x;
   int kept = cnt;
   if (st.id_n == 0) {
     uint32_t edge;
-    kept = trim_by_score(sm, cnt, k, &edge);
+    kept = trim_by_score(sm, cnt, k, &edge, scratch);
     const int32_t es = (int32_t)(edge ^ 0x80000000u);
     st.thr_s = es > st.thr_s ? es : st.thr_s;
     if (kept <= kTrimAt) return kept;
@@ -485,7 +483,7 @@ __device__ __forceinline__ int trim_list(ScanLds &sm, int cnt, int k, const int3
       [&](auto f) {
         for (int i = tid; i < kept; i += kScanThreads) f(sm.list[i]);
       },
-      k, sm.sel);
+      k, *reinterpret_cast<SelScratch *>(scratch));
   uint64_t tk;
   kept = keep_at_least(sm, kept, T, &tk);
   const int32_t ks = key_score(tk);
@@ -500,7 +498,8 @@ __device__ __forceinline__ int trim_list(ScanLds &sm, int cnt, int k, const int3
 // the biased score in their upper half, so one threshold serves either.  All threads call it; returns
 // the count kept.
 __device__ __forceinline__ int finish_list(ScanLds &sm, int cnt, int k, int id_n, int32_t gb,
-                                           const int32_t *__restrict__ perm, int32_t *thr_q, uint64_t *kth_out) {
+                                           const int32_t *__restrict__ perm, int32_t *thr_q, uint64_t *kth_out,
+                                           uint32_t *scratch) {
   const int tid = threadIdx.x, l = lane_id();
   uint64_t kth = 0;
   if (id_n > 0) {   // rare (score ties at a trim): the list already starts with id keys; convert the rest
@@ -514,7 +513,7 @@ __device__ __forceinline__ int finish_list(ScanLds &sm, int cnt, int k, int id_n
         [&](auto f) {
           for (int i = tid; i < cnt; i += kScanThreads) f(sm.list[i]);
         },
-        k, sm.sel);
+        k, *reinterpret_cast<SelScratch *>(scratch));
     cnt = keep_at_least(sm, cnt, T, &kth);
     if (tid == 0) atomicMax(thr_q, key_score(kth));
   } else if (cnt == k) {
@@ -535,11 +534,13 @@ __device__ __forceinline__ int finish_list(ScanLds &sm, int cnt, int k, int id_n
   return cnt;
 }
 
+// Three workgroups per CU (168 VGPRs a wave): the pipeline holds a step's rows and the next step's
+// signatures in registers across the filter, and spills at four per CU would add waits on every load.
 template <int LPR, int W>
-__global__ __launch_bounds__(kScanThreads, 4) void k_scan(ScanArgs a) {
+__global__ __launch_bounds__(kScanThreads, kScanOcc) void k_scan(ScanArgs a) {
   constexpr int D = 16 * LPR;
   constexpr int RPI = 64 / LPR;                   // rows covered by one 16-byte load per lane
-  constexpr int RB = D <= 128 ? 64 : 32;          // rows a wave requests together
+  constexpr int RB = RPI > kScanRowBatch ? RPI : kScanRowBatch;   // rows a wave requests together
   constexpr int R = RB / RPI;                     // row loads per lane in one batch (<= 8)
   __shared__ ScanLds sm;
   const int tid = threadIdx.x, l = lane_id(), wv = tid / 64, sub = l % LPR;
@@ -686,10 +687,11 @@ __global__ __launch_bounds__(kScanThreads, 4) void k_scan(ScanArgs a) {
     // masked afterwards), so the compiler can count outstanding loads exactly and wait only for the
     // ones it needs: the rows of this step, not the signatures already requested for the next.
     uint64_t sg[kScanGroups][W];
-    int32_t sg_n = 0;
+    int32_t sg_n = 0, sg_p0 = 0;
     auto load_sigs = [&](const Cursor &cu) {
       sg_n = cu.w >= 0 ? ((cu.t1 - cu.st) < kScanStep ? (cu.t1 - cu.st) : kScanStep) : 0;
       const int32_t p0 = cu.w >= 0 ? cu.pbase + cu.st : 0;
+      sg_p0 = p0;
       const int32_t last = sg_n > 0 ? sg_n - 1 : 0;
 #pragma unroll
       for (int gi = 0; gi < kScanGroups; ++gi) {
@@ -703,120 +705,138 @@ __global__ __launch_bounds__(kScanThreads, 4) void k_scan(ScanArgs a) {
         }
       }
     };
-    load_window();
-    int steps = 0, par = 0, cnt_base = 0;   // cnt_base: list length at the start of the step
-    bool pull = false;
-    Cursor cur{0, 0, 0, 0};
-    seek(cur);
-    load_sigs(cur);
-    while (cur.w >= 0) {
-      const int32_t n = sg_n;
-      const int32_t p0 = cur.pbase + cur.st;
-      const int32_t thr_eff = gthr > thr_s ? gthr : thr_s;
-      // --- filter this step's signatures, compact the survivors per wave
+    // --- The steps of the chunk run as a pipeline.  Iteration i filters step i + 1 (its signatures were
+    // requested an iteration earlier), requests the signatures of step i + 2, passes the step barrier,
+    // then scores step i, whose rows were requested at the end of iteration i - 1, and requests the rows
+    // of step i + 1.  A row gather thus overlaps the next filter and barrier instead of stalling the
+    // step.  Survivor lists rotate through three LDS buffers (step i in wl[i % 3]); after the barrier of
+    // iteration i every wave has finished scoring step i - 1, so the list length through step i - 1 is
+    // known to every thread (per-wave append counts) and the buffer of step i - 1 is free scratch.
+    constexpr int NWV = kScanThreads / 64;
+    struct Share {           // wave wv scores survivors [rbeg, rend) of a step's concatenated lists
+      int pre[NWV + 1];
+      int rbeg, rend;
+    };
+    auto share = [&](int par) -> Share {
+      Share s;
+      s.pre[0] = 0;
+#pragma unroll
+      for (int i = 0; i < NWV; ++i) s.pre[i + 1] = s.pre[i] + sm.wcnt[par][i];
+      const int total = s.pre[NWV];
+      const int per = (total + NWV - 1) / NWV;
+      s.rbeg = wv * per;
+      s.rend = s.rbeg + per < total ? s.rbeg + per : total;
+      return s;
+    };
+    auto surv_at = [&](const Share &s, int r) -> int {   // index of survivor r in its buffer
+      int adj = 0;
+#pragma unroll
+      for (int i = 1; i < NWV; ++i) adj = r >= s.pre[i] ? i * 64 * kScanGroups - s.pre[i] : adj;
+      return r + adj;
+    };
+    auto filter = [&](int buf) -> int {   // the step in sg into wl[buf]; returns this wave's survivors
       int nw = 0;
 #pragma unroll
       for (int gi = 0; gi < kScanGroups; ++gi) {
         const int i = gi * kScanThreads + wv * 64 + l;
-        bool pass = i < n;
+        bool pass = i < sg_n;
 #pragma unroll
         for (int u = 0; u < W; ++u) pass = pass && ((sg[gi][u] & mk[u]) == mk[u]);
         const uint64_t bal = __ballot(pass);
-        if (pass) sm.u.wl[wv * 64 * kScanGroups + nw + mbcnt(bal)] = (uint16_t)i;
+        if (pass) sm.wl[buf][wv * 64 * kScanGroups + nw + mbcnt(bal)] = (uint16_t)i;
         nw += __popcll(bal);
       }
+      return nw;
+    };
+    int4 x[R];
+    auto load_rows = [&](int32_t p0, int buf, const Share &s, int r0) {
+#pragma unroll
+      for (int u = 0; u < R; ++u) {
+        const int r = r0 + u * RPI + l / LPR;
+        const int32_t p = p0 + (r < s.rend ? (int)sm.wl[buf][surv_at(s, r)] : 0);
+        x[u] = reinterpret_cast<const int4 *>(a.ix.items + (size_t)p * D)[sub];
+      }
+    };
+    // score the batch at r0.  The wave's accepted candidates take their list slots with one LDS atomic;
+    // a candidate's slot is its rank among them (ballots over the rows of the batch in turn).
+    auto score_rows = [&](int32_t p0, int buf, const Share &s, int r0, int32_t thr_eff) -> int {
+      uint32_t okm = 0;
+      int32_t sc[R];
+      int tot = 0;
+#pragma unroll
+      for (int u = 0; u < R; ++u) {
+        const int32_t acc = group_sum<LPR>(dot16(x[u], qv, 0));
+        const int r = r0 + u * RPI + l / LPR;
+        sc[u] = acc;
+        const bool ok = sub == 0 && r < s.rend && acc >= thr_eff;
+        okm |= ok ? 1u << u : 0u;
+        tot += __popcll(__ballot(ok));
+      }
+      if (tot == 0) return 0;
+      int at = 0;
+      if (l == 0) at = atomicAdd(&sm.cnt, tot);
+      at = __builtin_amdgcn_readfirstlane(at);
+#pragma unroll
+      for (int u = 0; u < R; ++u) {
+        const bool ok = (okm >> u) & 1u;
+        const uint64_t b = __ballot(ok);
+        if (ok) {
+          const int r = r0 + u * RPI + l / LPR;
+          sm.list[at + mbcnt(b)] = pos_key(sc[u], p0 + (int)sm.wl[buf][surv_at(s, r)]);
+          atomicAdd(&sm.qh[qbin(sc[u])], 1u);
+        }
+        at += __popcll(b);
+      }
+      return tot;
+    };
+    load_window();
+    int steps = 0, cnt_base = 0;   // cnt_base: list length through the last step counted
+    bool pull = false;
+    Cursor cur{0, 0, 0, 0};
+    seek(cur);
+    // prologue: step 0 filtered, step 1's signatures requested, step 0's first rows requested
+    load_sigs(cur);
+    Cursor cur_sg = cur;   // the step whose signatures are in sg
+    if (cur.w >= 0) advance(cur);
+    int32_t p0_i = sg_p0;
+    {
+      const int nw = filter(0);
       n_elig += nw;
-      if (l == 0) sm.wcnt[wv] = nw;
+      if (l == 0) sm.wcnt[0][wv] = nw;
+    }
+    load_sigs(cur);
+    cur_sg = cur;
+    if (cur.w >= 0) advance(cur);
+    __syncthreads();
+    Share sh_i = share(0);
+    if (sh_i.rbeg < sh_i.rend) load_rows(p0_i, 0, sh_i, sh_i.rbeg);
+    int32_t gthr_next = gthr;
+    for (int i = 0;; ++i) {
+      const bool more = sg_n > 0;   // step i + 1 exists (the same for every thread)
+      const int32_t p0_n = sg_p0;
+      const int bi = i % 3, bn = (i + 1) % 3, bf = (i + 2) % 3;
+      if (more) {
+        const int nw = filter(bn);   // waits for step i + 1's signatures; step i's rows keep flying
+        n_elig += nw;
+        if (l == 0) sm.wcnt[(i + 1) & 1][wv] = nw;
+        // the query's global bound and histogram, on exchange steps only
+        if (pull) {
+          gthr_next = __hip_atomic_load(thr_q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (wv == 0) hist_pull_issue();
+        }
+        load_sigs(cur);
+        cur_sg = cur;
+        if (cur.w >= 0) advance(cur);
+      }
       __syncthreads();
-      // --- the step's survivors are shared out evenly: wave wv scores survivors [rbeg, rend) of the
-      // concatenation of the waves' lists
-      constexpr int NWV = kScanThreads / 64;
-      int pre[NWV + 1];
-      pre[0] = 0;
+      // list length through step i - 1; trim when step i's appends could overflow the list
+      if (i >= 1) {
 #pragma unroll
-      for (int i = 0; i < NWV; ++i) pre[i + 1] = pre[i] + sm.wcnt[i];
-      const int total = pre[NWV];
-      const int per = (total + NWV - 1) / NWV;
-      const int rbeg = wv * per, rend = rbeg + per < total ? rbeg + per : total;
-      auto surv_at = [&](int r) -> int {   // LDS index of survivor r (pre is nondecreasing)
-        int adj = 0;
-#pragma unroll
-        for (int i = 1; i < NWV; ++i) adj = r >= pre[i] ? i * 64 * kScanGroups - pre[i] : adj;
-        return r + adj;
-      };
-      // --- rows of the first RB survivors, then the next step's signatures, all in flight
-      int4 x[R];
-      auto load_rows = [&](int r0) {
-#pragma unroll
-        for (int u = 0; u < R; ++u) {
-          const int r = r0 + u * RPI + l / LPR;
-          const int32_t p = p0 + (r < rend ? (int)sm.u.wl[surv_at(r)] : 0);
-          x[u] = reinterpret_cast<const int4 *>(a.ix.items + (size_t)p * D)[sub];
-        }
-      };
-      // score the batch at r0.  The wave's accepted candidates take their list slots with one LDS atomic;
-      // a candidate's slot is its rank among them (ballots over the rows of the batch in turn).
-      auto score_rows = [&](int r0) -> int {
-        uint32_t okm = 0;
-        int32_t sc[R];
-        int tot = 0;
-#pragma unroll
-        for (int u = 0; u < R; ++u) {
-          const int32_t acc = group_sum<LPR>(dot16(x[u], qv, 0));
-          const int r = r0 + u * RPI + l / LPR;
-          sc[u] = acc;
-          const bool ok = sub == 0 && r < rend && acc >= thr_eff;
-          okm |= ok ? 1u << u : 0u;
-          tot += __popcll(__ballot(ok));
-        }
-        if (tot == 0) return 0;
-        int at = 0;
-        if (l == 0) at = atomicAdd(&sm.cnt, tot);
-        at = __builtin_amdgcn_readfirstlane(at);
-#pragma unroll
-        for (int u = 0; u < R; ++u) {
-          const bool ok = (okm >> u) & 1u;
-          const uint64_t b = __ballot(ok);
-          if (ok) {
-            const int r = r0 + u * RPI + l / LPR;
-            sm.list[at + mbcnt(b)] = pos_key(sc[u], p0 + (int)sm.u.wl[surv_at(r)]);
-            atomicAdd(&sm.qh[qbin(sc[u])], 1u);
-          }
-          at += __popcll(b);
-        }
-        return tot;
-      };
-      if (rbeg < rend) load_rows(rbeg);
-      advance(cur);
-      load_sigs(cur);
-      // the query's global bound and histogram are read only on exchange steps
-      int32_t gthr_next = gthr;
-      if (pull) {
-        gthr_next = __hip_atomic_load(thr_q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (wv == 0) hist_pull_issue();
+        for (int w2 = 0; w2 < NWV; ++w2) cnt_base += sm.wadd[(i - 1) & 1][w2];
       }
-      int wtot = rbeg < rend ? score_rows(rbeg) : 0;
-      // survivors beyond the first batch (dense filters)
-      for (int r0 = rbeg + RB; r0 < rend; r0 += RB) {
-        load_rows(r0);
-        wtot += score_rows(r0);
-      }
-      if (l == 0) sm.wadd[par][wv] = wtot;
-      __syncthreads();
-      int cnt_now = cnt_base;
-#pragma unroll
-      for (int i = 0; i < kScanThreads / 64; ++i) cnt_now += sm.wadd[par][i];
-      par ^= 1;
-      gthr = gthr_next;
-      if (pull) {
-        if (wv == 0) hist_pull_use();
-        pull = false;
-      }
-      // --- trim the list when the next step could overflow it
-      cnt_base = cnt_now;
-      if (cnt_now > kTrimAt) {
+      if (cnt_base > kTrimAt) {
         ListState st{thr_s, id_n};
-        const int kept = trim_list(sm, cnt_now, k, a.ix.perm, st);
+        const int kept = trim_list(sm, cnt_base, k, a.ix.perm, st, reinterpret_cast<uint32_t *>(sm.wl[bf]));
         cnt_base = kept;
         thr_s = st.thr_s;
         id_n = st.id_n;
@@ -825,8 +845,24 @@ __global__ __launch_bounds__(kScanThreads, 4) void k_scan(ScanArgs a) {
           atomicMax(thr_q, thr_s);   // at least k candidates score >= thr_s
         }
         __syncthreads();
-        // the next step's signatures are requested again rather than held in registers across the trim
-        load_sigs(cur);
+        // rows and signatures in flight are requested again rather than held in registers across the trim
+        if (sh_i.rbeg < sh_i.rend) load_rows(p0_i, bi, sh_i, sh_i.rbeg);
+        load_sigs(cur_sg);
+      }
+      Share sh_n;
+      if (more) sh_n = share((i + 1) & 1);
+      // --- score step i
+      const int32_t thr_eff = gthr > thr_s ? gthr : thr_s;
+      int wtot = sh_i.rbeg < sh_i.rend ? score_rows(p0_i, bi, sh_i, sh_i.rbeg, thr_eff) : 0;
+      for (int r0 = sh_i.rbeg + RB; r0 < sh_i.rend; r0 += RB) {   // dense filters: further batches
+        load_rows(p0_i, bi, sh_i, r0);
+        wtot += score_rows(p0_i, bi, sh_i, r0, thr_eff);
+      }
+      if (l == 0) sm.wadd[i & 1][wv] = wtot;
+      if (pull && more) {
+        gthr = gthr_next;
+        if (wv == 0) hist_pull_use();
+        pull = false;
       }
       // histogram exchange after steps 2, 4, 8, ...: the bound converges within a few exchanges
       ++steps;
@@ -834,6 +870,18 @@ __global__ __launch_bounds__(kScanThreads, 4) void k_scan(ScanArgs a) {
         hist_push();
         pull = true;
       }
+      if (!more) break;
+      if (sh_n.rbeg < sh_n.rend) load_rows(p0_n, bn, sh_n, sh_n.rbeg);   // step i + 1's first rows
+      sh_i = sh_n;
+      p0_i = p0_n;
+    }
+    __syncthreads();
+    {
+      // the last step's appends (counted at no later barrier)
+      int last = 0;
+#pragma unroll
+      for (int w2 = 0; w2 < NWV; ++w2) last += sm.wadd[steps & 1 ? 0 : 1][w2];
+      cnt_base += last;
     }
     // --- end of the chunk: its exact top k above the query's bound, published in slot c
     if (!a.fallback) hist_push();
@@ -843,7 +891,7 @@ __global__ __launch_bounds__(kScanThreads, 4) void k_scan(ScanArgs a) {
     __syncthreads();
     const int32_t gb = sm.gbound;
     uint64_t kth;
-    const int cnt = finish_list(sm, cnt_base, k, id_n, gb, a.ix.perm, thr_q, &kth);
+    const int cnt = finish_list(sm, cnt_base, k, id_n, gb, a.ix.perm, thr_q, &kth, reinterpret_cast<uint32_t *>(sm.wl[0]));
     uint64_t *dst = a.w.slot_keys + (size_t)c * (size_t)k;
     for (int i = tid; i < cnt; i += kScanThreads) dst[i] = sm.list[i];
     if (tid == 0) {
