@@ -3,6 +3,9 @@
     python -m int8_ivf_ann_amd.rocprof_summary kernels RESULTS.db [--match k_scan] [--command "..."]
         per-kernel dispatch count and duration statistics (microseconds)
 
+    python -m int8_ivf_ann_amd.rocprof_summary counters RESULTS.db [RESULTS.db ...] --match k_scan [--command "..."]
+        mean value per dispatch of every counter collected for the matching kernels (one line per counter)
+
     python -m int8_ivf_ann_amd.rocprof_summary traffic --fetch FETCH.db --write WRITE.db --kernel k_scan \
         --calib copyBuffer --calib-bytes 1073741824 --sha SHA [--command-fetch ...] [--command-write ...]
         HBM bytes per dispatch of a kernel from FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each scaled by
@@ -52,6 +55,24 @@ def kernels_md(db: str, match: Optional[List[str]], command: Optional[str]) -> s
             continue
         lines.append(f"| `{name[:90]}` | {len(d)} | {statistics.mean(d):.2f} | {min(d):.2f} | {max(d):.2f} | "
                      f"{sum(d):.1f} |")
+    return "\n".join(lines) + "\n"
+
+
+def counters_md(dbs: List[str], match: str, commands: Optional[List[str]]) -> str:
+    lines = []
+    for c in commands or []:
+        lines += ["    " + c, ""]
+    lines += ["| kernel | counter | dispatches | mean per dispatch |", "|---|---|---|---|"]
+    for db in dbs:
+        con = sqlite3.connect(db)
+        rows = con.execute("select kernel_name, counter_name, value from counters_collection").fetchall()
+        con.close()
+        acc: Dict[tuple, List[float]] = {}
+        for name, cn, v in rows:
+            if match in name:
+                acc.setdefault((name, cn), []).append(float(v))
+        for (name, cn), v in sorted(acc.items()):
+            lines.append(f"| `{name[:40]}` | {cn} | {len(v)} | {statistics.mean(v):.6g} |")
     return "\n".join(lines) + "\n"
 
 
@@ -113,6 +134,10 @@ def main(argv=None) -> None:
     k.add_argument("db")
     k.add_argument("--match", action="append")
     k.add_argument("--command")
+    c = sub.add_parser("counters")
+    c.add_argument("dbs", nargs="+")
+    c.add_argument("--match", required=True)
+    c.add_argument("--command", action="append")
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
@@ -125,6 +150,8 @@ def main(argv=None) -> None:
     a = ap.parse_args(argv)
     if a.cmd == "kernels":
         sys.stdout.write(kernels_md(a.db, a.match, a.command))
+    elif a.cmd == "counters":
+        sys.stdout.write(counters_md(a.dbs, a.match, a.command))
     else:
         sys.stdout.write(traffic_md(a.fetch, a.write, a.kernel, a.calib, a.calib_bytes, a.sha, a.command_fetch,
                                     a.command_write))
