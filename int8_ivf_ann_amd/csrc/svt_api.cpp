@@ -81,6 +81,7 @@ struct svt_index {
   int32_t *d_offsets = nullptr;
   int8_t *d_centroids = nullptr;
   int32_t scan_wgs;                 // persistent workgroups of the fused kernel
+  int32_t gscan_wgs;                // persistent workgroups of the grouped scan
   int64_t n_tiles;                  // sum over clusters of ceil(size / kGTile)
   int64_t max_cluster_tiles;        // tiles of the largest cluster
 };
@@ -151,6 +152,8 @@ extern "C" int svt_index_upload(const svt_index_desc *d, void *hip_stream, svt_i
     // one resident wave of persistent scan workgroups
     const int per_cu = std::max(1, scan_blocks_per_cu(dim, W));
     ix->scan_wgs = std::min(kMaxScanWGs, std::max(64, prop.multiProcessorCount * per_cu));
+    const int g_per_cu = std::max(1, gscan_blocks_per_cu(dim, W));
+    ix->gscan_wgs = std::min(kMaxScanWGs, std::max(64, prop.multiProcessorCount * g_per_cu));
   }
 
   int32_t *d_pos_of = nullptr;
@@ -261,7 +264,7 @@ struct Layout {
 
 // Grouped searches: candidate pools take at most kPoolBudget bytes in all, at least 16 k and at most
 // kPoolMaxKeys keys per query.  Shapes whose work list would not fit an int32 run query by query.
-constexpr size_t kPoolBudget = size_t(256) << 20;
+constexpr size_t kPoolBudget = size_t(1) << 30;
 constexpr int64_t kPoolMaxKeys = int64_t(1) << 22;
 // The grouped path is selected explicitly (SVT_PATH=grouped); by default every batch runs query by
 // query, which is faster on every workload measured so far (it keeps an exact top-k per workgroup in LDS,
@@ -400,7 +403,7 @@ extern "C" int svt_search(const svt_index *ix, int32_t B, const int8_t *queries,
     w.pool_cnt = (uint32_t *)(base + L.pool_cnt);
     w.pool = (uint64_t *)(base + L.pool);
   }
-  SearchShape sh{B, nprobe, k, ix->scan_wgs, L.max_chunks, grouped, pool_cap, L.max_units};
+  SearchShape sh{B, nprobe, k, ix->scan_wgs, L.max_chunks, grouped, pool_cap, L.max_units, ix->gscan_wgs};
 
   const bool prof = g_prof_on.load(std::memory_order_relaxed) != 0 && g_prof.searches < kMaxProfiledSearches;
   ProfState &ps = g_prof;

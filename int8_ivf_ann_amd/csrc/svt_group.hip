@@ -5,12 +5,11 @@
 //             work list: the queries of every probed cluster (gq, grouped by cluster), and units of
 //             work = tiles of at most kGTile items of one cluster x groups of at most kGMax of the
 //             queries probing it
-//   k_gscan   persistent workgroups take units from an atomic queue.  A step of 1024 items loads the
-//             signatures once and tests them against every request mask of the group; the rows of the
-//             items that at least one query accepts are gathered once and scored (v_dot4) for each
-//             query that accepted them.  A candidate that reaches the query's proven bound goes to the
-//             query's pool in HBM and is counted in the query's score histogram; as soon as k counted
-//             candidates lie at or above a bin's lower edge, that edge is the query's new bound.
+//   k_gscan   every wave of the persistent workgroups takes units from an atomic queue on its own.
+//             A step of 256 items loads the signatures once and tests them against every request mask
+//             of the unit's group; the rows of the items that at least one member accepts are gathered
+//             once and scored (v_dot4) for each member that accepted them.  A candidate at or above
+//             its query's bound goes to the query's pool in HBM.
 //   k_pmerge  per query: the exact top k of its pool
 // A query whose pool overflows is scanned again query by query (k_scan and k_merge in fallback mode),
 // so the result is exact whatever the data.
@@ -98,7 +97,17 @@ __global__ __launch_bounds__(256) void k_gunits(DevIndex ix, Work w) {
 }
 
 // ------------------------------------------------------------------------------------------------
-// k_gscan
+// k_gscan: every wave of a persistent workgroup works on its own, with no block barrier.  A wave
+// takes units from the queue and walks a unit in steps of kGStep items: it loads the step's
+// signatures once, tests them against every request mask of the unit's query group, compacts the
+// items that at least one member accepts (with the set of members that accept each) into its LDS,
+// gathers those rows once and scores each of them (v_dot4) for every member that accepted it.  The
+// steps of a unit run as a two-stage pipeline: while the rows of step i are in flight the wave filters
+// step i + 1 and requests the signatures of step i + 2.  The next unit is set up (queue position,
+// unit, member queries, their masks, bounds and query vectors) one stage per step while the current
+// unit runs, and the signatures of its first step are requested with the last step of the current one.
+// A candidate at or above its query's bound is staged in LDS; staged candidates go to the queries'
+// pools with one pool reservation per member (at the end of a unit, or when the stage is full).
 
 struct GScanArgs {
   DevIndex ix;
@@ -109,32 +118,44 @@ struct GScanArgs {
   uint32_t pool_cap;
 };
 
-constexpr int kStage = 1024;      // candidates staged in LDS before they go to the pools
-constexpr int kStageFlush = 512;  // a step that ends with at least this many staged flushes them
-constexpr int kGLH = 4;           // queries of a group whose histogram counts are gathered in LDS
+constexpr int kGStep = 256;      // items of one wave step: four 64-item groups
+constexpr int kGStage = 256;     // candidates a wave stages in LDS
+constexpr int kGRowBatch = 32;   // rows a wave gathers together
+constexpr int kGPullMin = 32;    // a flush that gives a member this many candidates pulls its histogram
 
-struct GScanLds {
-  uint16_t wl[kScanThreads * kScanGroups];   // items some query accepts, wave w's at [w * 256, ...)
-  uint32_t wq[kScanThreads * kScanGroups];   // for each of them, the group's queries that accept it
-  int wcnt[kScanThreads / 64];
-  uint64_t gmask[kGMax][2];                  // the group's request masks
-  int4 gqv[kGMax][16];                       // the group's query vectors (d <= 256)
-  int32_t gq[kGMax], gthr[kGMax], ghlo[kGMax], ghsh[kGMax];
-  uint32_t gelig[kGMax];                     // items of the unit each query accepts
-  uint32_t gadd[kGMax];                      // candidates the unit gave each query
-  uint64_t stage_key[kStage];                // staged candidates: (score, position) key
-  uint8_t stage_q[kStage];                   //   and the group index of their query
-  uint32_t scnt[kGMax], sbase[kGMax], scur[kGMax];
-  int scnt_total;                            // candidates offered to the stage (may exceed kStage)
-  uint32_t lh[kGLH][kQHistBins];             // histogram counts of the group's first queries
-  int next;                                  // queue position of this workgroup's next unit
+template <int LPR>
+struct GGroup {                  // a unit's query group as the wave uses it
+  uint64_t mask[kGMax][2];       // request masks
+  int4 qv[kGMax][LPR];           // query vectors
+  int32_t q[kGMax];              // query index in the batch
+  int32_t thr[kGMax];            // proven bounds (read at set-up, raised by the wave's pulls)
+  int32_t hlo[kGMax], hsh[kGMax];  // the queries' histogram bins (lower edge of bin 1, log2 width)
+  uint32_t scnt[kGMax];          // staged candidates of each member
+  uint32_t sbase[kGMax];         // pool cursor of each member during a flush
 };
 
+template <int LPR>
+struct GWave {
+  uint16_t wl[2][kGStep];        // accepted items of a step (offset in the step); two steps in flight
+  uint16_t wq[2][kGStep];        // the members that accept each (bit j: member j)
+  uint64_t key[kGStage];         // staged candidates: (score, position) keys
+  uint8_t kj[kGStage];           //   and their member
+  GGroup<LPR> grp[2];            // the current unit's group and the next unit's
+};
+
+// Order of LDS accesses between lanes of one wave (the wave's LDS operations complete in order; this
+// keeps the compiler from moving them across each other).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Queue position -> unit: a bijection of [0, n) that scatters the units of a cluster (which are numbered
-// consecutively) over the whole run.  Otherwise the tiles of a large cluster would all be scanned at
-// once, before any of them could raise the bound of the queries probing it.  A permutation of
-// [0, 2^m) (odd multiplications and an xor-shift, each invertible modulo 2^m), walked until it lands
-// below n; the walk ends because every cycle of the permutation holds a position below n (the start).
+// consecutively) over the whole run, so that the queries' units are spread over the run rather than
+// clustered.  A permutation of [0, 2^m) (odd multiplications and an xor-shift, each invertible modulo
+// 2^m), walked until it lands below n; the walk ends because every cycle of the permutation holds a
+// position below n (the start).
 __device__ __forceinline__ int scatter_unit(int pos, int n) {
   const int m = n > 1 ? 32 - __clz(n - 1) : 1;   // 2^m >= n
   const uint32_t mask = m >= 32 ? 0xFFFFFFFFu : ((1u << m) - 1u);
@@ -148,233 +169,185 @@ __device__ __forceinline__ int scatter_unit(int pos, int n) {
 }
 
 template <int LPR, int W>
-__global__ __launch_bounds__(kScanThreads, 4) void k_gscan(GScanArgs a) {
+__global__ __launch_bounds__(kScanThreads, kGScanOcc) void k_gscan(GScanArgs a) {
   constexpr int D = 16 * LPR;
-  constexpr int RPI = 64 / LPR;            // rows covered by one 16-byte load per lane
-  constexpr int RB = D <= 128 ? 64 : 32;   // rows a wave requests together
-  constexpr int R = RB / RPI;              // row loads per lane in one batch (<= 8)
-  constexpr int NWV = kScanThreads / 64;
-  __shared__ GScanLds sm;
-  const int tid = threadIdx.x, l = lane_id(), wv = tid / 64, sub = l % LPR;
+  constexpr int RPI = 64 / LPR;                                  // rows covered by one 16-byte load per lane
+  constexpr int RB = RPI > kGRowBatch ? RPI : kGRowBatch;        // rows a wave requests together
+  constexpr int R = RB / RPI;                                    // row loads per lane in one batch
+  constexpr int QVL = (kGMax * LPR + 63) / 64;                   // query-vector loads per lane in a set-up
+  constexpr int NG = kGStep / 64;
+  __shared__ GWave<LPR> gws[kScanThreads / 64];
+  const int l = lane_id(), sub = l % LPR;
+  GWave<LPR> &s = gws[threadIdx.x / 64];
   const uint32_t cap = a.pool_cap;
   const int n_units = a.w.ustart[a.ix.nlist];
-  if (tid == 0) sm.next = (int)atomicAdd(&a.w.counter[2], 1u);
-  __syncthreads();
-  for (;;) {
-    const int upos = __builtin_amdgcn_readfirstlane(sm.next);
-    if (upos >= n_units) break;
-    int next_u = 0;
-    if (tid == 0) next_u = (int)atomicAdd(&a.w.counter[2], 1u);
-    const GUnit un = a.w.units[scatter_unit(upos, n_units)];
-    const int g = un.q1 - un.q0;   // 1 .. kGMax
-    for (int j = tid; j < g; j += kScanThreads) {
-      const int q = a.w.gq[un.q0 + j];
-      sm.gq[j] = q;
+  const bool want_stats = a.w.stats != nullptr;
+
+  // --- set-up of the next unit, one stage per call (all values wave-uniform but the per-lane loads)
+  int pf = 0;          // 1..4: stage whose loads are in flight; 5: ready in grp[nslot]; 6: queue empty
+  int nslot = 0;
+  int32_t pf_v = 0, pf_q = 0, pf_thr = INT32_MIN, pf_hlo = 0, pf_hsh = 0;
+  uint64_t pf_m[W];
+  int4 pf_qa = {}, pf_qb = {}, pf_qc = {}, pf_qd = {};   // query-vector parts in flight (QVL <= 4)
+  int32_t n_lo = 0, n_hi = 0, n_g = 0;
+  auto pf_start = [&]() {
+    pf_v = 0;
+    if (l == 0) pf_v = (int)atomicAdd(&a.w.counter[2], 1u);
+    pf = 1;
+  };
+  auto pf_step = [&]() {
+    if (pf == 1) {
+      const int upos = __builtin_amdgcn_readfirstlane(pf_v);
+      if (upos >= n_units) {
+        pf = 6;
+        return;
+      }
+      const int u = scatter_unit(upos, n_units);
+      pf_v = reinterpret_cast<const int32_t *>(a.w.units + u)[l & 7];
+      pf = 2;
+    } else if (pf == 2) {
+      n_lo = __builtin_amdgcn_readlane(pf_v, 1);
+      n_hi = __builtin_amdgcn_readlane(pf_v, 2);
+      const int q0 = __builtin_amdgcn_readlane(pf_v, 3);
+      n_g = __builtin_amdgcn_readlane(pf_v, 4) - q0;
+      pf_v = a.w.gq[q0 + (l < n_g ? l : 0)];
+      pf = 3;
+    } else if (pf == 3) {
+      pf_q = pf_v;
 #pragma unroll
-      for (int t = 0; t < W; ++t) sm.gmask[j][t] = a.masks[(size_t)q * W + t];
-      sm.gthr[j] = __hip_atomic_load(&a.w.thr[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      sm.ghlo[j] = a.w.hlo[q];
-      sm.ghsh[j] = a.w.hshift[q];
-      sm.gelig[j] = 0u;
-      sm.gadd[j] = 0u;
-      sm.scnt[j] = 0u;
-    }
-    for (int i = tid; i < kGLH * kQHistBins; i += kScanThreads) sm.lh[i / kQHistBins][i % kQHistBins] = 0u;
-    if (tid == 0) sm.scnt_total = 0;
-    for (int i = tid; i < g * LPR; i += kScanThreads) {
-      const int j = i / LPR, ch = i % LPR;
-      sm.gqv[j][ch] = reinterpret_cast<const int4 *>(a.queries + (size_t)a.w.gq[un.q0 + j] * D)[ch];
-    }
-    __syncthreads();
-    // Signatures of a step are requested with the previous step's rows.  Loads are issued
-    // unconditionally (lanes past the end read an in-range clamped position and are masked).
-    uint64_t sg[kScanGroups][W];
-    int32_t sg_n = 0;
-    auto load_sigs = [&](int32_t st) {
-      const int32_t rem = un.hi - st;
-      sg_n = rem <= 0 ? 0 : (rem < kScanStep ? rem : kScanStep);
-      const int32_t p0 = rem <= 0 ? un.lo : st;
-      const int32_t last = sg_n > 0 ? sg_n - 1 : 0;
+      for (int t = 0; t < W; ++t) pf_m[t] = a.masks[(size_t)pf_q * W + t];
+      pf_thr = __hip_atomic_load(&a.w.thr[pf_q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      pf_hlo = a.w.hlo[pf_q];
+      pf_hsh = a.w.hshift[pf_q];
+      auto qv_load = [&](int t) -> int4 {
+        const int idx = t * 64 + l, j = (idx / LPR) % kGMax;
+        const int qj = __shfl(pf_q, j < n_g ? j : 0);
+        return reinterpret_cast<const int4 *>(a.queries + (size_t)qj * D)[idx % LPR];
+      };
+      pf_qa = qv_load(0);
+      if constexpr (QVL > 1) pf_qb = qv_load(1);
+      if constexpr (QVL > 2) pf_qc = qv_load(2);
+      if constexpr (QVL > 3) pf_qd = qv_load(3);
+      pf = 4;
+    } else if (pf == 4) {
+      GGroup<LPR> &G = s.grp[nslot];
+      if (l < n_g) {
+        G.q[l] = pf_q;
+        G.thr[l] = pf_thr;
+        G.hlo[l] = pf_hlo;
+        G.hsh[l] = pf_hsh;
 #pragma unroll
-      for (int gi = 0; gi < kScanGroups; ++gi) {
-        const int i = gi * kScanThreads + wv * 64 + l;
-        const int32_t p = p0 + (i < last ? i : last);
-        if constexpr (W == 2) {
-          const ulonglong2 v = reinterpret_cast<const ulonglong2 *>(a.ix.sigs)[p];
-          sg[gi][0] = v.x;
-          sg[gi][1] = v.y;
-        } else {
-          sg[gi][0] = a.ix.sigs[p];
-        }
+        for (int t = 0; t < W; ++t) G.mask[l][t] = pf_m[t];
+        G.scnt[l] = 0u;
       }
-    };
-    // Move the staged candidates to their pools: one pool reservation per query, then every thread
-    // copies entries.  All threads call it, after a barrier that ends the step's appends.
-    auto flush_stage = [&]() {
-      const int tot = sm.scnt_total < kStage ? sm.scnt_total : kStage;
-      if (tid < g) {
-        const uint32_t nj = sm.scnt[tid];
-        sm.sbase[tid] = nj ? atomicAdd(&a.w.pool_cnt[sm.gq[tid]], nj) : 0u;
-        sm.scur[tid] = 0u;
+      auto qv_store = [&](int t, const int4 v) {
+        const int idx = t * 64 + l;
+        if (idx < n_g * LPR) G.qv[idx / LPR][idx % LPR] = v;
+      };
+      qv_store(0, pf_qa);
+      if constexpr (QVL > 1) qv_store(1, pf_qb);
+      if constexpr (QVL > 2) qv_store(2, pf_qc);
+      if constexpr (QVL > 3) qv_store(3, pf_qd);
+      pf = 5;
+    }
+  };
+
+  uint64_t sg[NG][W];
+  int32_t sg_n = 0;
+  bool sg_pre = false;   // the signatures of the prepared unit's first step are in sg
+  // Loads are issued unconditionally (a step that does not exist reads an in-range position and counts
+  // no items), so the compiler can count outstanding loads exactly and wait only for the ones it needs.
+  auto load_sigs = [&](int32_t st, int32_t end) {   // st: a valid position; no items unless st < end
+    const int32_t rem = end - st;
+    sg_n = rem <= 0 ? 0 : (rem < kGStep ? rem : kGStep);
+    const int32_t last = sg_n > 0 ? sg_n - 1 : 0;
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+      const int i = gi * 64 + l;
+      const int32_t p = st + (i < last ? i : last);
+      if constexpr (W == 2) {
+        const ulonglong2 v = reinterpret_cast<const ulonglong2 *>(a.ix.sigs)[p];
+        sg[gi][0] = v.x;
+        sg[gi][1] = v.y;
+      } else {
+        sg[gi][0] = a.ix.sigs[p];
       }
-      __syncthreads();
-      for (int e = tid; e < tot; e += kScanThreads) {
-        const int j = sm.stage_q[e];
-        const uint32_t slot = sm.sbase[j] + atomicAdd(&sm.scur[j], 1u);
-        if (slot < cap) a.w.pool[(size_t)sm.gq[j] * cap + slot] = sm.stage_key[e];
-      }
-      __syncthreads();
-      if (tid < g) sm.scnt[tid] = 0u;
-      if (tid == 0) sm.scnt_total = 0;
-    };
-    load_sigs(un.lo);
-    for (int32_t st = un.lo; st < un.hi; st += kScanStep) {
-      const int32_t n = sg_n;
-      // --- every request mask of the group against this step's signatures; compact the items at least
-      // one query accepts, with the set of queries that accept each
+    }
+  };
+
+  pf_start();
+  while (pf < 5) pf_step();
+  while (pf == 5) {
+    // --- take the prepared unit; the unit after it is set up in the other group slot
+    const int slot = nslot;
+    nslot ^= 1;
+    const int32_t lo = n_lo, hi = n_hi, g = n_g;
+    GGroup<LPR> &G = s.grp[slot];
+    pf_start();
+    uint32_t elig = 0;   // lane j: items of the unit member j accepts
+    int stage_n = 0;     // staged candidates (wave-uniform)
+    wave_lds_sync();
+
+    // The step in sg into wl/wq[buf]; returns the accepted count.  Member 0 is tested for every group
+    // before the loop over the other members, so that the wait for the signatures sits in straight-line
+    // code (and leaves the rows requested after them in flight).
+    auto filter = [&](int buf) -> int {
       int nw = 0;
+      uint32_t qms[NG];
+      uint64_t m0[W];
 #pragma unroll
-      for (int gi = 0; gi < kScanGroups; ++gi) {
-        const int i = gi * kScanThreads + wv * 64 + l;
-        uint32_t qm = 0u;
-        if (i < n) {
-          for (int j = 0; j < g; ++j) {
-            bool pass = true;
+      for (int t = 0; t < W; ++t) m0[t] = G.mask[0][t];
 #pragma unroll
-            for (int t = 0; t < W; ++t) pass = pass && ((sg[gi][t] & sm.gmask[j][t]) == sm.gmask[j][t]);
-            qm |= pass ? (1u << j) : 0u;
-          }
+      for (int gi = 0; gi < NG; ++gi) {
+        bool pass = gi * 64 + l < sg_n;
+#pragma unroll
+        for (int t = 0; t < W; ++t) pass = pass && ((sg[gi][t] & m0[t]) == m0[t]);
+        qms[gi] = pass ? 1u : 0u;
+      }
+      for (int j = 1; j < g; ++j) {
+        uint64_t mj[W];
+#pragma unroll
+        for (int t = 0; t < W; ++t) mj[t] = G.mask[j][t];
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) {
+          bool pass = gi * 64 + l < sg_n;
+#pragma unroll
+          for (int t = 0; t < W; ++t) pass = pass && ((sg[gi][t] & mj[t]) == mj[t]);
+          qms[gi] |= pass ? (1u << j) : 0u;
         }
+      }
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi) {
+        const int i = gi * 64 + l;
+        const uint32_t qm = qms[gi];
         const uint64_t bal = __ballot(qm != 0u);
         if (qm != 0u) {
-          const int o = wv * 64 * kScanGroups + nw + mbcnt(bal);
-          sm.wl[o] = (uint16_t)i;
-          sm.wq[o] = qm;
+          const int o = nw + mbcnt(bal);
+          s.wl[buf][o] = (uint16_t)i;
+          s.wq[buf][o] = (uint16_t)qm;
         }
         nw += __popcll(bal);
-        for (int j = 0; j < g; ++j) {
-          const uint64_t b = __ballot((qm >> j) & 1u);
-          if (l == 0 && b) atomicAdd(&sm.gelig[j], (uint32_t)__popcll(b));
-        }
-      }
-      if (l == 0) sm.wcnt[wv] = nw;
-      __syncthreads();
-      // --- the step's accepted items are shared out evenly: wave wv takes [rbeg, rend) of the
-      // concatenation of the waves' lists
-      int pre[NWV + 1];
-      pre[0] = 0;
-#pragma unroll
-      for (int i = 0; i < NWV; ++i) pre[i + 1] = pre[i] + sm.wcnt[i];
-      const int total = pre[NWV];
-      const int per = (total + NWV - 1) / NWV;
-      const int rbeg = wv * per, rend = rbeg + per < total ? rbeg + per : total;
-      auto surv_at = [&](int r) -> int {   // LDS index of accepted item r (pre is nondecreasing)
-        int adj = 0;
-#pragma unroll
-        for (int i = 1; i < NWV; ++i) adj = r >= pre[i] ? i * 64 * kScanGroups - pre[i] : adj;
-        return r + adj;
-      };
-      int4 x[R];
-      auto load_rows = [&](int r0) {
-#pragma unroll
-        for (int uu = 0; uu < R; ++uu) {
-          const int r = r0 + uu * RPI + l / LPR;
-          const int32_t p = st + (r < rend ? (int)sm.wl[surv_at(r)] : 0);
-          x[uu] = reinterpret_cast<const int4 *>(a.ix.items + (size_t)p * D)[sub];
-        }
-      };
-      // score each loaded row for every query of the group that accepts it; a candidate reaching the
-      // query's bound takes a pool slot (one atomic per wave and query) and is counted in the query's
-      // histogram
-      auto score_rows = [&](int r0) {
-#pragma unroll
-        for (int uu = 0; uu < R; ++uu) {
-          const int r = r0 + uu * RPI + l / LPR;
-          const bool valid = r < rend;
-          const int si = valid ? surv_at(r) : 0;
-          const uint32_t qm = valid ? sm.wq[si] : 0u;
+        if (want_stats) {
           for (int j = 0; j < g; ++j) {
-            const bool want = (qm >> j) & 1u;
-            if (__ballot(want) == 0ull) continue;
-            const int32_t acc = group_sum<LPR>(dot16(x[uu], sm.gqv[j][sub], 0));
-            const bool ok = sub == 0 && want && acc >= sm.gthr[j];
-            const uint64_t b = __ballot(ok);
-            if (b == 0ull) continue;
-            // the wave's candidates take consecutive stage entries; past the stage's end they go
-            // straight to the pool
-            int at = 0;
-            if (l == 0) at = atomicAdd(&sm.scnt_total, __popcll(b));
-            at = __builtin_amdgcn_readfirstlane(at);
-            if (ok) {
-              const uint64_t key = pos_key(acc, st + (int)sm.wl[si]);
-              const int e = at + mbcnt(b);
-              const int q = sm.gq[j];
-              if (e < kStage) {
-                sm.stage_key[e] = key;
-                sm.stage_q[e] = (uint8_t)j;
-                atomicAdd(&sm.scnt[j], 1u);
-              } else {
-                const uint32_t slot = atomicAdd(&a.w.pool_cnt[q], 1u);
-                if (slot < cap) a.w.pool[(size_t)q * cap + slot] = key;
-              }
-              const int32_t hlo = sm.ghlo[j];
-              int bin = 0;
-              if (acc >= hlo) {
-                const int32_t bb = (acc - hlo) >> sm.ghsh[j];
-                bin = bb < kQHistBins - 1 ? bb : kQHistBins - 1;
-              }
-              if (j < kGLH) atomicAdd(&sm.lh[j][bin], 1u);
-              else atomicAdd(&a.w.ghist[(size_t)q * kQHistBins + bin], 1u);
-            }
-            if (l == 0) atomicAdd(&sm.gadd[j], (uint32_t)__popcll(b));
+            const uint64_t b = __ballot((qm >> j) & 1u);
+            elig += l == j ? (uint32_t)__popcll(b) : 0u;
           }
         }
-      };
-      if (rbeg < rend) load_rows(rbeg);
-      load_sigs(st + kScanStep);
-      // the group's current bounds, requested with the loads and installed after the step
-      int32_t thr_pref = INT32_MIN;
-      if (wv == 0 && l < g)
-        thr_pref = __hip_atomic_load(&a.w.thr[sm.gq[l]], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (rbeg < rend) score_rows(rbeg);
-      for (int r0 = rbeg + RB; r0 < rend; r0 += RB) {   // dense filters: further batches
-        load_rows(r0);
-        score_rows(r0);
       }
-      __syncthreads();
-      // bounds are read in the scoring phase only, which the next step enters after its barrier
-      if (wv == 0 && l < g && thr_pref > sm.gthr[l]) sm.gthr[l] = thr_pref;
-      // staged candidates go out when the stage is half full or the unit ends (the decision reads a
-      // value no thread changes before the next step's second barrier)
-      if (sm.scnt_total >= kStageFlush || st + kScanStep >= un.hi) flush_stage();
-    }
-    __syncthreads();
-    // histogram counts gathered in LDS go to the queries' histograms before the bounds are computed
-    for (int i = tid; i < kGLH * kQHistBins; i += kScanThreads) {
-      const int j = i / kQHistBins, bin = i % kQHistBins;
-      if (j < g) {
-        const uint32_t v = sm.lh[j][bin];
-        if (v) atomicAdd(&a.w.ghist[(size_t)sm.gq[j] * kQHistBins + bin], v);
-      }
-    }
-    __syncthreads();
-    // --- end of the unit: statistics, and new bounds for the queries that received candidates
-    for (int j = tid; j < g; j += kScanThreads) {
-      const int q = sm.gq[j];
-      if (a.w.stats) {
-        atomicAdd((unsigned long long *)&a.w.stats[2 * (size_t)q + 1], (unsigned long long)sm.gelig[j]);
-        atomicAdd((unsigned long long *)&a.w.stats[2 * (size_t)q], (unsigned long long)(un.hi - un.lo));
-      }
-    }
-    for (int j = wv; j < g; j += NWV) {   // wave-uniform
-      if (sm.gadd[j] == 0u) continue;
-      const int q = sm.gq[j];
-      const uint32_t *gh = a.w.ghist + (size_t)q * kQHistBins;
+      return nw;
+    };
+    // Raise member j's bound from its query's histogram: the lower edge of the highest bin at which at
+    // least k counted candidates lie at or above (bin 0, everything below the histogram, never
+    // counts).  Every candidate is counted once, so a stale read only gives a lower bound.
+    auto pull = [&](int j) {
+      const int q = G.q[j];
+      const int32_t hlo = G.hlo[j], hsh = G.hsh[j];
       constexpr int HPB = kQHistBins / 64;
       uint32_t h[HPB], sum = 0u;
 #pragma unroll
       for (int t = 0; t < HPB; ++t) {
-        h[t] = __hip_atomic_load(&gh[HPB * l + t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        h[t] = __hip_atomic_load(&a.w.ghist[(size_t)q * kQHistBins + HPB * l + t], __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
         sum += h[t];
       }
       uint32_t suf = sum;
@@ -384,19 +357,163 @@ __global__ __launch_bounds__(kScanThreads, 4) void k_gscan(GScanArgs a) {
         if (l + off < 64) suf += v;
       }
       uint32_t above = suf - sum;
+      int32_t bound = INT32_MIN;
 #pragma unroll
       for (int t = HPB - 1; t >= 0; --t) {
         const int bin = HPB * l + t;
-        if (bin >= 1 && above < (uint32_t)a.k && above + h[t] >= (uint32_t)a.k)
-          atomicMax(&a.w.thr[q], sm.ghlo[j] + (bin << sm.ghsh[j]));
+        if (bin >= 1 && above < (uint32_t)a.k && above + h[t] >= (uint32_t)a.k) bound = hlo + (bin << hsh);
         above += h[t];
       }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        const int32_t v = __shfl_xor(bound, o);
+        bound = v > bound ? v : bound;
+      }
+      if (l == 0 && bound > G.thr[j]) {
+        G.thr[j] = bound;
+        atomicMax(&a.w.thr[q], bound);
+      }
+    };
+    // Staged candidates to the pools (one reservation per member, then one slot per candidate) and
+    // to their queries' histograms; members that received many pull their bound.
+    auto flush = [&]() {
+      wave_lds_sync();
+      uint32_t c = 0u;
+      if (l < g) {
+        c = G.scnt[l];
+        const uint32_t base = c ? atomicAdd(&a.w.pool_cnt[G.q[l]], c) : 0u;
+        G.sbase[l] = base;
+        G.scnt[l] = 0u;
+      }
+      wave_lds_sync();
+      for (int e = l; e < stage_n; e += 64) {
+        const int j = s.kj[e];
+        const uint64_t key = s.key[e];
+        const int q = G.q[j];
+        const uint32_t at = atomicAdd(&G.sbase[j], 1u);
+        if (at < cap) a.w.pool[(size_t)q * cap + at] = key;
+        const int32_t sc = (int32_t)((uint32_t)(key >> 32) ^ 0x80000000u), hlo = G.hlo[j];
+        int bin = 0;
+        if (sc >= hlo) {
+          const int32_t bb = (sc - hlo) >> G.hsh[j];
+          bin = bb < kQHistBins - 1 ? bb : kQHistBins - 1;
+        }
+        atomicAdd(&a.w.ghist[(size_t)q * kQHistBins + bin], 1u);
+      }
+      wave_lds_sync();
+      stage_n = 0;
+      uint64_t pm = __ballot(c >= (uint32_t)kGPullMin);
+      while (pm) {
+        const int j = __builtin_ctzll(pm);
+        pm &= pm - 1ull;
+        pull(j);
+      }
+      wave_lds_sync();
+    };
+    int4 x[R];
+    auto load_rows = [&](int32_t p0, int buf, int r0, int nrows) {
+#pragma unroll
+      for (int u = 0; u < R; ++u) {
+        const int r = r0 + u * RPI + l / LPR;
+        const int32_t p = p0 + (r < nrows ? (int)s.wl[buf][r] : 0);
+        x[u] = reinterpret_cast<const int4 *>(a.ix.items + (size_t)p * D)[sub];
+      }
+    };
+    // Score the batch at r0 for every member that accepts each row.  Each row's first member is scored
+    // for the whole batch in straight-line code first, so that the wait for the rows sits there (and
+    // leaves the signatures requested after them in flight); the loops for further members and the
+    // candidate staging follow.
+    auto score_rows = [&](int32_t p0, int buf, int r0, int nrows) {
+      uint32_t qmv[R];
+      int32_t posv[R], acc0[R];
+#pragma unroll
+      for (int u = 0; u < R; ++u) {
+        const int r = r0 + u * RPI + l / LPR;
+        const bool valid = r < nrows;
+        qmv[u] = valid ? (uint32_t)s.wq[buf][r] : 0u;
+        posv[u] = p0 + (valid ? (int)s.wl[buf][r] : 0);
+        const int j = qmv[u] ? __builtin_ctz(qmv[u]) : 0;
+        acc0[u] = group_sum<LPR>(dot16(x[u], G.qv[j][sub], 0));
+      }
+#pragma unroll
+      for (int u = 0; u < R; ++u) {
+        uint32_t qm = qmv[u];
+        int32_t acc = acc0[u];
+        for (;;) {
+          if (stage_n > kGStage - RPI) flush();
+          const int j = qm ? __builtin_ctz(qm) : 0;
+          const bool ok = qm != 0u && sub == 0 && acc >= G.thr[j];
+          const uint64_t b = __ballot(ok);
+          if (ok) {
+            const int e = stage_n + mbcnt(b);
+            s.key[e] = pos_key(acc, posv[u]);
+            s.kj[e] = (uint8_t)j;
+            atomicAdd(&G.scnt[j], 1u);
+          }
+          stage_n += __popcll(b);
+          qm &= qm - 1u;
+          if (__ballot(qm != 0u) == 0ull) break;
+          const int j2 = qm ? __builtin_ctz(qm) : 0;
+          acc = group_sum<LPR>(dot16(x[u], G.qv[j2][sub], 0));
+        }
+      }
+    };
+
+    // After the signatures of the unit's last step: those of the prepared unit's first step when it is
+    // ready, else a dummy request.
+    int32_t rq_st = lo, rq_end = hi;   // the last request
+    auto request_after = [&](int32_t st_next) -> bool {   // returns whether it requested a step of this unit
+      const bool own = st_next < hi, pre = !own && pf == 5;
+      rq_st = own ? st_next : (pre ? n_lo : lo);
+      rq_end = own ? hi : (pre ? n_hi : lo);
+      load_sigs(rq_st, rq_end);
+      sg_pre = pre;
+      return own;
+    };
+    // --- the unit's steps: iteration i scores step i while step i + 1 is filtered
+    if (!sg_pre) load_sigs(lo, hi);
+    sg_pre = false;
+    int32_t st_sg = lo;   // start of the step whose signatures are in sg
+    int n_i = filter(0);
+    int32_t p0_i = st_sg;
+    bool has_next = request_after(st_sg + kGStep);
+    if (has_next) st_sg += kGStep;
+    wave_lds_sync();
+    load_rows(p0_i, 0, 0, n_i);
+    for (int i = 0;; ++i) {
+      const int bi = i & 1, bn = bi ^ 1;
+      const bool cont = has_next;
+      int n_n = 0;
+      const int32_t p0_n = st_sg;
+      if (cont) {
+        n_n = filter(bn);   // waits for step i + 1's signatures; step i's rows keep flying
+        has_next = request_after(st_sg + kGStep);
+        if (has_next) st_sg += kGStep;
+      } else {
+        load_sigs(rq_st, rq_end);   // the same request again, so that every iteration issues the same loads
+      }
+      score_rows(p0_i, bi, 0, n_i);
+      for (int r0 = RB; r0 < n_i; r0 += RB) {   // dense filters: further batches
+        load_rows(p0_i, bi, r0, n_i);
+        score_rows(p0_i, bi, r0, n_i);
+      }
+      pf_step();
+      if (!cont) break;
+      wave_lds_sync();
+      load_rows(p0_n, bn, 0, n_n);
+      n_i = n_n;
+      p0_i = p0_n;
     }
-    if (tid == 0) sm.next = next_u;
-    __syncthreads();
+    // --- end of the unit
+    flush();
+    if (want_stats && l < g) {
+      const int q = G.q[l];
+      atomicAdd((unsigned long long *)&a.w.stats[2 * (size_t)q + 1], (unsigned long long)elig);
+      atomicAdd((unsigned long long *)&a.w.stats[2 * (size_t)q], (unsigned long long)(hi - lo));
+    }
+    while (pf >= 1 && pf <= 4) pf_step();
   }
 }
-
 // ------------------------------------------------------------------------------------------------
 // k_pmerge: one workgroup per query whose pool held all its candidates.  The k-th best (score,
 // position) key fixes the k-th best score; every key at that score or above becomes a (score, id) key,
@@ -518,9 +635,28 @@ static void gscan_w(const GScanArgs &a, int W, hipStream_t s) {
     k_gscan<LPR, 1><<<a.P, kScanThreads, 0, s>>>(a);
 }
 
+template <int LPR>
+static int gscan_occ_w(int W) {
+  int n = 0;
+  hipError_t e = W == 2 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_gscan<LPR, 2>, kScanThreads, 0)
+                        : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_gscan<LPR, 1>, kScanThreads, 0);
+  return e == hipSuccess ? n : 0;
+}
+
+int gscan_blocks_per_cu(int32_t dim, int32_t sig_words) {
+  switch (dim) {
+    case 16: return gscan_occ_w<1>(sig_words);
+    case 32: return gscan_occ_w<2>(sig_words);
+    case 64: return gscan_occ_w<4>(sig_words);
+    case 128: return gscan_occ_w<8>(sig_words);
+    case 256: return gscan_occ_w<16>(sig_words);
+    default: return 0;
+  }
+}
+
 hipError_t launch_gscan(const DevIndex &ix, const int8_t *queries, const uint64_t *masks, const SearchShape &sh,
                         const Work &w, hipStream_t s) {
-  GScanArgs a{ix, queries, masks, w, sh.B, sh.nprobe, sh.k, sh.P, (uint32_t)sh.pool_cap};
+  GScanArgs a{ix, queries, masks, w, sh.B, sh.nprobe, sh.k, sh.GP, (uint32_t)sh.pool_cap};
   switch (ix.dim) {
     case 16: gscan_w<1>(a, ix.sig_words, s); break;
     case 32: gscan_w<2>(a, ix.sig_words, s); break;

@@ -65,7 +65,8 @@ constexpr int64_t kMinChunkCost = 16 << 10; // smallest chunk, in estimated byte
 // Grouped path: one unit of work is a tile of at most kGTile items of one probed cluster together
 // with a group of at most kGMax of the queries that probe that cluster (gq[q0..q1)).
 constexpr int kGTile = 4096;
-constexpr int kGMax = 32;
+constexpr int kGMax = 16;
+constexpr int kGScanOcc = 4;         // grouped scan: workgroups per CU (4 independent waves each)
 struct GUnit {
   int32_t c, lo, hi, q0, q1, pad0, pad1, pad2;   // items at positions [lo, hi) of cluster c
 };
@@ -106,6 +107,7 @@ struct SearchShape {
   int32_t grouped;     // 1: grouped path with the query-by-query scan as fallback for overflowing pools
   int32_t pool_cap;    // keys per query pool
   int32_t max_units;
+  int32_t GP;          // persistent workgroups of the grouped scan
 };
 
 // most chunks a search can produce: cost-balanced chunks number at most 4 P + B
@@ -130,6 +132,7 @@ hipError_t launch_pool_merge(const DevIndex &ix, const float *query_scales, cons
                              hipStream_t s);
 // resident scan workgroups per compute unit for this shape (0 if unknown)
 int scan_blocks_per_cu(int32_t dim, int32_t sig_words);
+int gscan_blocks_per_cu(int32_t dim, int32_t sig_words);
 hipError_t launch_scatter_rows(const int8_t *src_rows, const uint64_t *src_sigs, const int32_t *pos_of,
                                int64_t i0, int64_t n, int32_t dim, int32_t sig_words, int8_t *dst_rows,
                                uint64_t *dst_sigs, hipStream_t s);
