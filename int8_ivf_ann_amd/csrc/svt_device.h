@@ -168,45 +168,69 @@ __device__ __forceinline__ uint64_t pos_key(int32_t score, int32_t pos) {
   return ((uint64_t)((uint32_t)score ^ 0x80000000u) << 32) | (uint64_t)(uint32_t)pos;
 }
 
-// The n best ordering keys of a query, cand[0..n) in LDS (room for the next power of two), sorted best
-// first by a bitonic sort and written as row q: ids, int32 scores and scores dequantised as
-// S / (item_scale * query_scale) in double, rounded once to float.  Entries nout..k-1 are padding.
-// All NT threads of the block call it; nout <= n <= k.
+// The n best ordering keys of a query, cand[0..n) in LDS (room for 2 NT keys), sorted best first and
+// written as row q: ids, int32 scores and scores dequantised as S / (item_scale * query_scale) in double,
+// rounded once to float.  Entries nout..k-1 are padding.  All NT threads of the block call it;
+// nout <= n <= k <= 2 NT.
+// The sort is a bitonic network over 2 NT keys (missing keys are 0, below every real key), two per
+// thread (elements 2t and 2t + 1): strides up to 64 pair lanes of one wave and run on shuffles, larger
+// strides exchange through LDS.
 template <int NT>
 __device__ void emit_sorted(uint64_t *cand, int n, int nout, int q, int k, const float *query_scales,
                             float item_scale, int64_t *out_ids, int32_t *out_scores, float *out_fscores) {
+  constexpr int N = 2 * NT;
   const int tid = threadIdx.x;
-  int np2 = 1;
-  while (np2 < n) np2 <<= 1;
-  for (int i = n + tid; i < np2; i += NT) cand[i] = 0ull;
+  uint64_t v[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) v[e] = 2 * tid + e < n ? cand[2 * tid + e] : 0ull;
   __syncthreads();
-  for (int size = 2; size <= np2; size <<= 1) {
+  for (int size = 2; size <= N; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = tid; i < np2; i += NT) {
-        const int j = i ^ stride;
-        if (j > i) {
-          const uint64_t x = cand[i], y = cand[j];
-          const bool up = (i & size) == 0;   // this run sorts descending
-          if (up ? (x < y) : (x > y)) { cand[i] = y; cand[j] = x; }
-        }
+      const bool desc = ((2 * tid) & size) == 0;   // the run holding this thread's elements sorts descending
+      if (stride == 1) {
+        const bool sw = desc ? v[0] < v[1] : v[0] > v[1];
+        if (sw) { const uint64_t x = v[0]; v[0] = v[1]; v[1] = x; }
+        continue;
       }
-      __syncthreads();
+      uint64_t p[2];
+      const int h = stride >> 1;   // partner thread: tid ^ h
+      if (stride <= 64) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e) p[e] = __shfl_xor(v[e], h);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 2; ++e) cand[2 * tid + e] = v[e];
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < 2; ++e) p[e] = cand[2 * (tid ^ h) + e];
+        __syncthreads();
+      }
+      const bool lower = (tid & h) == 0;   // this thread holds the lower index of each pair
+      const bool keep_max = lower == desc;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const uint64_t a = v[e], b = p[e];
+        v[e] = keep_max ? (a > b ? a : b) : (a < b ? a : b);
+      }
     }
   }
   const float qs = query_scales ? query_scales[q] : item_scale;
   const double denom = (double)item_scale * (double)qs;
-  for (int i = tid; i < k; i += NT) {
-    const size_t o = (size_t)q * k + i;
-    if (i < nout) {
-      const uint64_t key = cand[i];
-      const int32_t sc = key_score(key);
-      out_ids[o] = (int64_t)key_id(key);
-      out_scores[o] = sc;
-      if (out_fscores) out_fscores[o] = (float)((double)sc / denom);
-    } else {
-      out_ids[o] = -1;
-      out_scores[o] = INT32_MIN;
-      if (out_fscores) out_fscores[o] = -__builtin_huge_valf();
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int i = 2 * tid + e;
+    if (i < k) {
+      const size_t o = (size_t)q * k + i;
+      if (i < nout) {
+        const int32_t sc = key_score(v[e]);
+        out_ids[o] = (int64_t)key_id(v[e]);
+        out_scores[o] = sc;
+        if (out_fscores) out_fscores[o] = (float)((double)sc / denom);
+      } else {
+        out_ids[o] = -1;
+        out_scores[o] = INT32_MIN;
+        if (out_fscores) out_fscores[o] = -__builtin_huge_valf();
+      }
     }
   }
 }

@@ -34,6 +34,7 @@ constexpr int kTrimBins = 1 << kTrimBinsLog2;           // score histogram bins 
 constexpr int kSegWin = 64;                             // probed clusters staged in LDS at a time
 constexpr int kQHistBins = 256;                         // bins of a query's global score histogram
 constexpr int kSelThreads = 1024;    // coarse-select and merge workgroups
+static_assert(2 * kSelThreads >= kMaxK, "the final sort holds two keys per merge thread");
 constexpr int kCoarseQB = 8;         // queries per coarse-score workgroup
 constexpr int kMaxScanWGs = 4096;    // upper bound on persistent scan workgroups
 
@@ -58,9 +59,15 @@ struct Chunk {
 
 constexpr int kCostSamples = kSelThreads;   // items sampled per query to estimate its filter density
 constexpr int kMaxChunksPerQuery = 2048;    // a query's stream is cut into at most this many chunks
-constexpr int kMergeCap = 6144;             // merge candidates staged in LDS
+#ifndef SVT_MERGE_CAP
+#define SVT_MERGE_CAP 6144
+#endif
+constexpr int kMergeCap = SVT_MERGE_CAP;      // merge candidates staged in LDS
+static_assert(kMergeCap >= kMaxK && kMergeCap % kSelThreads == 0,
+              "the merge stages at least k keys, a whole number per thread");
 constexpr int kSelSegLds = 4096;            // probe lists up to this long are searched in LDS
 constexpr int64_t kMinChunkCost = 16 << 10; // smallest chunk, in estimated bytes moved
+constexpr int kPlanBands = 256;             // cluster-id bands of the scan's queue order
 
 // Grouped path: one unit of work is a tile of at most kGTile items of one probed cluster together
 // with a group of at most kGMax of the queries that probe that cluster (gq[q0..q1)).
@@ -82,6 +89,8 @@ struct Work {
   int32_t *cstart;          // [B + 1]      first chunk of each query; cstart[B] = number of chunks
   Chunk *chunks;            // [max_chunks] the work list, in query order
   int32_t *order;           // [max_chunks] the order in which the scan takes the chunks
+  int32_t *cband;           // [max_chunks] band of the probed cluster each chunk starts in
+  uint32_t *band;           // [2][kPlanBands] chunks per band, then each band's next queue position
   int32_t *thr;             // [B]          per-query proven lower bound on the k-th best score
   int32_t *hlo;             // [B]          score at the lower edge of bin 1 of the query's histogram
   int32_t *hshift;          // [B]          bin width of that histogram is 2^hshift

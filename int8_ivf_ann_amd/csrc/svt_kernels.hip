@@ -74,8 +74,8 @@ __global__ __launch_bounds__(256) void k_coarse_keys(const int8_t *__restrict__ 
 //   seg[b][j]: offset of probed cluster j in query b's item stream; seg[b][nprobe] = qlen[b]
 //   qcost[b]: estimated bytes the scan moves for the query: signatures of every probed item plus the
 //             rows of the fraction of kCostSamples evenly spaced probed items that pass the filter
-// The last workgroup to finish cuts every query's stream into chunks of about equal estimated cost
-// (the scan's work list), so that a dense filter does not leave one workgroup with far more bytes.
+// The work list follows in four small kernels (k_plan_*): every query's stream is cut into chunks of
+// about equal estimated cost, so that a dense filter does not leave one workgroup with far more bytes.
 
 template <int W>
 __device__ __forceinline__ bool passes(const uint64_t *__restrict__ sig, const uint64_t *mk) {
@@ -85,49 +85,121 @@ __device__ __forceinline__ bool passes(const uint64_t *__restrict__ sig, const u
   return ok;
 }
 
+constexpr int kSelKR = 16;   // coarse keys a select thread keeps in registers (nlist <= kSelThreads * kSelKR)
+
 __global__ __launch_bounds__(kSelThreads) void k_coarse_select(DevIndex ix, const int8_t *__restrict__ queries,
                                                                 const uint64_t *__restrict__ masks, int32_t B,
-                                                                int32_t nprobe, int32_t P, Work w) {
+                                                                int32_t nprobe, Work w) {
+  constexpr int NWV = kSelThreads / 64;
   __shared__ SelScratch sel;
-  __shared__ int wave_tot[kSelThreads / 64 + 1];
-  __shared__ int64_t wave_tot64[kSelThreads / 64 + 1];
-  __shared__ int32_t seg_lds[kSelSegLds + 1];
-  __shared__ int last;
+  __shared__ int wave_tot[NWV + 1];
+  __shared__ int64_t wave_tot64[NWV + 1];
+  __shared__ int32_t seg_lds[kSelSegLds + 1];   // the probed clusters, then their stream offsets
+  __shared__ int32_t pb_lds[kSelSegLds];
+  __shared__ int32_t tcnt[kSelKR * NWV];         // probed clusters per (register slot, wave)
   __shared__ int smax_s;
-  const int tid = threadIdx.x, l = lane_id();
+  const int tid = threadIdx.x, l = lane_id(), wv = tid / 64;
   const int b = blockIdx.x;
   const int nlist = ix.nlist;
   const uint64_t *row = w.coarse_keys + (size_t)b * nlist;
-  uint64_t T = 0;
-  if (nprobe < nlist) {
-    T = block_select<kSelThreads>(
-        [&](auto f) {
-          for (int c = tid; c < nlist; c += kSelThreads) f(row[c]);
-        },
-        nprobe, sel);
-  }
   int32_t *probes = w.probes + (size_t)b * nprobe;
   int32_t *seg = w.seg + (size_t)b * (nprobe + 1);
-  int base = 0, run = 0;
-  for (int c0 = 0; c0 < nlist; c0 += kSelThreads) {
-    const int c = c0 + tid;
-    const bool take = c < nlist && row[c] >= T;
-    const int sz = take ? ix.offsets[c + 1] - ix.offsets[c] : 0;
-    int cnt_tot, sz_tot;
-    const int idx = block_excl_scan<kSelThreads>(take ? 1 : 0, wave_tot, &cnt_tot);
-    const int pre = block_excl_scan<kSelThreads>(sz, wave_tot, &sz_tot);
-    if (take && base + idx < nprobe) {
-      probes[base + idx] = c;
-      seg[base + idx] = run + pre;
-      w.pb[(size_t)b * nprobe + base + idx] = ix.offsets[c] - (run + pre);
-      if (nprobe <= kSelSegLds) seg_lds[base + idx] = run + pre;
+  int32_t *pb = w.pb + (size_t)b * nprobe;
+  const bool in_lds = nprobe <= kSelSegLds;
+  // --- the nprobe largest keys (keys are distinct: the cluster id is part of them)
+  uint64_t T = 0;
+  if (nlist <= kSelThreads * kSelKR) {
+    // keys of clusters tid + i * kSelThreads held in registers; 0 marks a missing cluster (no key is 0)
+    uint64_t kr[kSelKR];
+#pragma unroll
+    for (int i = 0; i < kSelKR; ++i) {
+      const int c = i * kSelThreads + tid;
+      kr[i] = c < nlist ? row[c] : 0ull;
     }
-    base += cnt_tot;
-    run += sz_tot;
+    if (nprobe < nlist) {
+      T = block_select<kSelThreads>(
+          [&](auto f) {
+#pragma unroll
+            for (int i = 0; i < kSelKR; ++i)
+              if (i * kSelThreads + tid < nlist) f(kr[i]);
+          },
+          nprobe, sel);
+    }
+    // probe list in one pass: a probed cluster's rank is its order by id (register slot, wave, lane)
+    uint64_t bal[kSelKR];
+#pragma unroll
+    for (int i = 0; i < kSelKR; ++i) {
+      bal[i] = __ballot(kr[i] != 0ull && kr[i] >= T);
+      if (l == 0) tcnt[i * NWV + wv] = __popcll(bal[i]);
+    }
+    __syncthreads();
+    if (wv == 0) {   // exclusive prefix of the kSelKR * NWV counts (in slot-major order)
+      constexpr int PL = kSelKR * NWV / 64;
+      int v[PL], sum = 0;
+#pragma unroll
+      for (int u = 0; u < PL; ++u) { v[u] = tcnt[PL * l + u]; sum += v[u]; }
+      int run = wave_incl_scan(sum) - sum;
+#pragma unroll
+      for (int u = 0; u < PL; ++u) { tcnt[PL * l + u] = run; run += v[u]; }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kSelKR; ++i) {
+      if ((bal[i] >> l) & 1ull) {
+        const int r = tcnt[i * NWV + wv] + mbcnt(bal[i]);
+        if (r < nprobe) {
+          probes[r] = i * kSelThreads + tid;
+          if (in_lds) seg_lds[r] = i * kSelThreads + tid;   // the cluster, until its offset replaces it
+        }
+      }
+    }
+  } else {
+    if (nprobe < nlist) {
+      T = block_select<kSelThreads>(
+          [&](auto f) {
+            for (int c = tid; c < nlist; c += kSelThreads) f(row[c]);
+          },
+          nprobe, sel);
+    }
+    int base = 0;
+    for (int c0 = 0; c0 < nlist; c0 += kSelThreads) {
+      const int c = c0 + tid;
+      const bool take = c < nlist && row[c] >= T;
+      int cnt_tot;
+      const int idx = block_excl_scan<kSelThreads>(take ? 1 : 0, wave_tot, &cnt_tot);
+      if (take && base + idx < nprobe) {
+        probes[base + idx] = c;
+        if (in_lds) seg_lds[base + idx] = c;
+      }
+      base += cnt_tot;
+    }
+  }
+  __syncthreads();
+  // --- stream offsets: prefix of the probed clusters' sizes in probe order
+  int run = 0;
+  for (int r0 = 0; r0 < nprobe; r0 += kSelThreads) {
+    const int r = r0 + tid;
+    int32_t c = 0, o0 = 0, sz = 0;
+    if (r < nprobe) {
+      c = in_lds ? seg_lds[r] : probes[r];
+      o0 = ix.offsets[c];
+      sz = ix.offsets[c + 1] - o0;
+    }
+    int tot;
+    const int pre = block_excl_scan<kSelThreads>(sz, wave_tot, &tot);
+    if (r < nprobe) {
+      seg[r] = run + pre;
+      pb[r] = o0 - (run + pre);
+      if (in_lds) {
+        seg_lds[r] = run + pre;
+        pb_lds[r] = o0 - (run + pre);
+      }
+    }
+    run += tot;
   }
   if (tid == 0) {
     seg[nprobe] = run;
-    if (nprobe <= kSelSegLds) seg_lds[nprobe] = run;
+    if (in_lds) seg_lds[nprobe] = run;
     w.qlen[b] = run;
     w.thr[b] = INT32_MIN;
     if (w.pool_cnt) w.pool_cnt[b] = 0u;
@@ -148,11 +220,10 @@ __global__ __launch_bounds__(kSelThreads) void k_coarse_select(DevIndex ix, cons
       int lo = 0, hi = nprobe - 1;   // largest j with seg[j] <= t
       while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        const int32_t sv = nprobe <= kSelSegLds ? seg_lds[mid] : seg[mid];
+        const int32_t sv = in_lds ? seg_lds[mid] : seg[mid];
         if (sv <= t) lo = mid; else hi = mid - 1;
       }
-      const int32_t s0 = nprobe <= kSelSegLds ? seg_lds[lo] : seg[lo];
-      pos = ix.offsets[probes[lo]] + (t - s0);
+      pos = (in_lds ? pb_lds[lo] : pb[lo]) + t;
     }
     uint64_t mk[2] = {0, 0};
     for (int u = 0; u < ix.sig_words; ++u) mk[u] = masks[(size_t)b * ix.sig_words + u];
@@ -191,19 +262,27 @@ __global__ __launch_bounds__(kSelThreads) void k_coarse_select(DevIndex ix, cons
     w.hlo[b] = lo;
     w.hshift[b] = shift;
   }
-  // last workgroup: the work list
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) last = (atomicAdd(&w.counter[0], 1u) == (uint32_t)(B - 1)) ? 1 : 0;
-  __syncthreads();
-  if (!last) return;
-  __threadfence();
+}
+
+// ------------------------------------------------------------------------------------------------
+// The work list.  k_plan_count (one workgroup): the target cost of a chunk from the batch's total
+// estimated cost, every query's chunk count and length, and where its chunks start (cstart).
+// k_plan_chunks (one thread per query and probed cluster): the chunks that start inside that cluster,
+// and the band (1/256 of the cluster ids) of the cluster, counted per band.  k_plan_bands: where each
+// band starts in the queue.  k_plan_order: the queue, chunks grouped by band, so that chunks of
+// different queries that read the same clusters run at about the same time and the second reader finds
+// the data in cache (the order inside a band is arbitrary).
+
+__global__ __launch_bounds__(kSelThreads) void k_plan_count(int32_t B, int32_t P, Work w) {
+  __shared__ int wave_tot[kSelThreads / 64 + 1];
+  __shared__ int64_t wave_tot64[kSelThreads / 64 + 1];
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kPlanBands; i += kSelThreads) w.band[i] = 0u;
   int64_t total = 0;
   for (int i0 = 0; i0 < B; i0 += kSelThreads) {
     const int i = i0 + tid;
-    const int64_t v = i < B ? __hip_atomic_load(&w.qcost[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
     int64_t tot;
-    block_excl_scan<kSelThreads>(v, wave_tot64, &tot);
+    block_excl_scan<kSelThreads>(i < B ? w.qcost[i] : (int64_t)0, wave_tot64, &tot);
     total += tot;
   }
   const int64_t tc_min = (total + 4 * (int64_t)P - 1) / (4 * (int64_t)P);
@@ -213,8 +292,7 @@ __global__ __launch_bounds__(kSelThreads) void k_coarse_select(DevIndex ix, cons
     const int i = i0 + tid;
     int32_t nch = 0;
     if (i < B) {
-      const int64_t len = __hip_atomic_load(&w.qlen[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const int64_t cost = __hip_atomic_load(&w.qcost[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int64_t len = w.qlen[i], cost = w.qcost[i];
       if (len > 0) {
         int64_t cl = (Tc * len + cost - 1) / cost;                          // items of one chunk
         const int64_t cl_min = (len + kMaxChunksPerQuery - 1) / kMaxChunksPerQuery;
@@ -230,57 +308,47 @@ __global__ __launch_bounds__(kSelThreads) void k_coarse_select(DevIndex ix, cons
     carry += tot;
   }
   if (tid == 0) w.cstart[B] = carry;
-  __syncthreads();
-  // chunk table: chunk c belongs to the query whose [cstart[q], cstart[q+1]) holds c
-  for (int c = tid; c < carry; c += kSelThreads) {
-    int lo = 0, hi = B - 1;   // largest q with cstart[q] <= c
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (w.cstart[mid] <= c) lo = mid; else hi = mid - 1;
-    }
-    // chunks of ceil(len / nch) items: none is empty, since that never exceeds the length chosen above
-    const int64_t len = __hip_atomic_load(&w.qlen[lo], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int32_t nch = w.cstart[lo + 1] - w.cstart[lo];
-    const int64_t cl = (len + nch - 1) / nch;
-    const int32_t i = c - w.cstart[lo];
-    const int64_t l0 = (int64_t)i * cl, l1 = l0 + cl < len ? l0 + cl : len;
-    // probed cluster holding offset l0: largest j with seg[j] <= l0 (written by this query's workgroup)
-    const int32_t *sq = w.seg + (size_t)lo * (nprobe + 1);
-    int jl = 0, jh = nprobe - 1;
-    while (jl < jh) {
-      const int mid = (jl + jh + 1) >> 1;
-      if (__hip_atomic_load(&sq[mid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <= l0) jl = mid; else jh = mid - 1;
-    }
-    w.chunks[c] = Chunk{lo, (int32_t)l0, (int32_t)l1, jl};
+}
+
+__global__ __launch_bounds__(256) void k_plan_chunks(int32_t B, int32_t nprobe, int32_t nlist, Work w) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= (int64_t)B * nprobe) return;
+  const int q = (int)(t / nprobe), j = (int)(t % nprobe);
+  const int32_t c0 = w.cstart[q], nch = w.cstart[q + 1] - c0;
+  if (nch == 0) return;
+  // chunks of ceil(len / nch) items: none is empty, since that never exceeds the length chosen above
+  const int64_t len = w.qlen[q];
+  const int64_t cl = (len + nch - 1) / nch;
+  const int32_t *sq = w.seg + (size_t)q * (nprobe + 1);
+  const int64_t s0 = sq[j], s1 = sq[j + 1];
+  // chunk i starts in this cluster when s0 <= i * cl < s1
+  int64_t i = (s0 + cl - 1) / cl;
+  if (i * cl >= s1) return;
+  const int band = (int)(((int64_t)w.probes[(size_t)q * nprobe + j] * kPlanBands) / nlist);
+  int n = 0;
+  for (; i < nch && i * cl < s1; ++i, ++n) {
+    const int64_t l0 = i * cl, l1 = l0 + cl < len ? l0 + cl : len;
+    w.chunks[c0 + i] = Chunk{q, (int32_t)l0, (int32_t)l1, j};
+    w.cband[c0 + i] = band;
   }
-  // Queue order: chunks grouped by the band (1/256 of the cluster ids) of their first probed cluster, so
-  // that chunks of different queries that read the same clusters run at about the same time and the
-  // second reader finds the data in cache.  Counting sort; the order inside a band is arbitrary.
-  auto band_of = [&](int c) -> int {
-    int lo = 0, hi = B - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (w.cstart[mid] <= c) lo = mid; else hi = mid - 1;
-    }
-    const int j0 = w.chunks[c].j0;
-    const int32_t cl = __hip_atomic_load(&w.probes[(size_t)lo * nprobe + j0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return (int)(((int64_t)cl * 256) / nlist);
-  };
-  __syncthreads();
-  for (int i = tid; i < 256; i += kSelThreads) sel.hist[i] = 0u;
-  __syncthreads();
-  for (int c = tid; c < carry; c += kSelThreads) atomicAdd(&sel.hist[band_of(c)], 1u);
-  __syncthreads();
-  if (tid < 64) {
-    uint32_t h[4], sum = 0;
+  atomicAdd(&w.band[band], (uint32_t)n);
+}
+
+__global__ __launch_bounds__(64) void k_plan_bands(Work w) {
+  const int l = threadIdx.x;
+  constexpr int PB = kPlanBands / 64;
+  uint32_t h[PB], sum = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) { h[j] = sel.hist[4 * l + j]; sum += h[j]; }
-    uint32_t run = wave_incl_scan(sum) - sum;   // exclusive prefix of this lane's four bins
+  for (int u = 0; u < PB; ++u) { h[u] = w.band[PB * l + u]; sum += h[u]; }
+  uint32_t run = wave_incl_scan(sum) - sum;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) { sel.hist[4 * l + j] = run; run += h[j]; }
-  }
-  __syncthreads();
-  for (int c = tid; c < carry; c += kSelThreads) w.order[atomicAdd(&sel.hist[band_of(c)], 1u)] = c;
+  for (int u = 0; u < PB; ++u) { w.band[kPlanBands + PB * l + u] = run; run += h[u]; }
+}
+
+__global__ __launch_bounds__(256) void k_plan_order(int32_t B, Work w) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= w.cstart[B]) return;
+  w.order[atomicAdd(&w.band[kPlanBands + w.cband[c]], 1u)] = c;
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -1004,8 +1072,32 @@ __global__ __launch_bounds__(kSelThreads) void k_merge(MergeArgs a) {
         if (i0 + u * kSelThreads < total && v[u] >= lo) f(v[u]);
     }
   };
-  if (total > k) {
-    // 2. pin the k-th key's score to one bin of a score histogram over [min, max]
+  // 2. stage the keys >= T in LDS (one LDS atomic per wave); ncand counts them all
+  auto stage = [&]() {
+    for (int i0 = tid - l; i0 < total; i0 += kSelThreads * 8) {   // wave-uniform trip count
+      uint64_t v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = i0 + l + u * kSelThreads;
+        v[u] = i < total ? key_at(i) : 0ull;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const bool take = i0 + l + u * kSelThreads < total && v[u] >= T;
+        const uint64_t bal = __ballot(take);
+        int base = 0;
+        if (l == 0 && bal) base = atomicAdd(&ncand, __popcll(bal));
+        base = __shfl(base, 0);
+        const int o = base + mbcnt(bal);
+        if (take && o < kMergeCap) cand[o] = v[u];
+      }
+    }
+  };
+  stage();
+  __syncthreads();
+  if (ncand > kMergeCap) {
+    // 3. too many for LDS: pin the k-th key's score to one bin of a score histogram over [min, max]
+    // and stage again above its lower edge
     uint32_t lmin = ~0u, lmax = 0u;
     visit(T, [&](uint64_t key) {
       const uint32_t sc = (uint32_t)(key >> 32);
@@ -1050,25 +1142,9 @@ __global__ __launch_bounds__(kSelThreads) void k_merge(MergeArgs a) {
     const uint64_t ek = (uint64_t)edge << 32;
     T = ek > T ? ek : T;
     __syncthreads();   // hist and cand share LDS
-  }
-  // 3. stage the surviving keys in LDS (one LDS atomic per wave)
-  for (int i0 = tid - l; i0 < total; i0 += kSelThreads * 8) {   // wave-uniform trip count
-    uint64_t v[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int i = i0 + l + u * kSelThreads;
-      v[u] = i < total ? key_at(i) : 0ull;
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const bool take = i0 + l + u * kSelThreads < total && v[u] >= T;
-      const uint64_t bal = __ballot(take);
-      int base = 0;
-      if (l == 0 && bal) base = atomicAdd(&ncand, __popcll(bal));
-      base = __shfl(base, 0);
-      const int o = base + mbcnt(bal);
-      if (take && o < kMergeCap) cand[o] = v[u];
-    }
+    if (tid == 0) ncand = 0;
+    __syncthreads();
+    stage();
   }
   __syncthreads();
   int n = ncand;
@@ -1151,7 +1227,12 @@ hipError_t launch_coarse_keys(const DevIndex &ix, const int8_t *queries, int32_t
 
 hipError_t launch_coarse_select(const DevIndex &ix, const int8_t *queries, const uint64_t *masks,
                                 const SearchShape &sh, const Work &w, hipStream_t s) {
-  k_coarse_select<<<sh.B, kSelThreads, 0, s>>>(ix, queries, masks, sh.B, sh.nprobe, sh.P, w);
+  k_coarse_select<<<sh.B, kSelThreads, 0, s>>>(ix, queries, masks, sh.B, sh.nprobe, w);
+  k_plan_count<<<1, kSelThreads, 0, s>>>(sh.B, sh.P, w);
+  const int64_t pairs = (int64_t)sh.B * sh.nprobe;
+  if (pairs > 0) k_plan_chunks<<<(unsigned)((pairs + 255) / 256), 256, 0, s>>>(sh.B, sh.nprobe, ix.nlist, w);
+  k_plan_bands<<<1, 64, 0, s>>>(w);
+  k_plan_order<<<(unsigned)((sh.max_chunks + 255) / 256), 256, 0, s>>>(sh.B, w);
   return hipGetLastError();
 }
 
