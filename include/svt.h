@@ -147,14 +147,17 @@ int svt_bloom_sign(const uint64_t *token_keys, int64_t n_items, int32_t tokens_p
                    int32_t sig_words, uint64_t *out, int32_t n_threads);
 
 /*
- * Stage timing.  While enabled (per process), svt_search records a HIP event on hip_stream before its
- * first kernel and after each kernel it launches (the calling thread keeps up to 100000 searches).
- * svt_profile_read synchronises on the last recorded event and returns, for each stage in launch
- * order ("coarse", "select", "scan", "merge"), the elapsed milliseconds summed over every search this
- * thread recorded since the previous read, then forgets them.
+ * Stage timing.  While enabled (per process), svt_search records HIP events on hip_stream around its
+ * stages (the calling thread keeps up to 100000 searches).  svt_profile_read synchronises on the last
+ * recorded event and returns, for each stage in launch order ("coarse", "select", "plan", "scan",
+ * "fallback", "merge"), the elapsed milliseconds summed over every search this thread recorded since
+ * the previous read, then forgets them.  "plan" and "fallback" hold work only on the grouped path (set
+ * by the environment variable SVT_PATH=grouped; SVT_PATH=query forces the query-by-query path); on the
+ * query-by-query path they measure only the gap between two event records.
+ *   on      0 off (default), 1 every stage (seven event records per search), 2 the scan stage only
+ *           (two event records per search; the other stages read 0); any other value: SVT_EINVAL
  *   stage_ms, stage_names  host arrays of max_stages entries (either may be NULL)
- *   n_stages               receives the number of stages (4); n_searches the number of searches summed
- * Disabled by default; enabling adds one event record per kernel.
+ *   n_stages               receives the number of stages (6); n_searches the number of searches summed
  */
 int svt_profile_enable(int on);
 int svt_profile_read(float *stage_ms, const char **stage_names, int32_t max_stages, int32_t *n_stages,

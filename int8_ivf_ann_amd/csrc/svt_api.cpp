@@ -54,13 +54,15 @@ bool supported_dim(int32_t d) { return d == 16 || d == 32 || d == 64 || d == 128
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// stage timing: per-process switch; per-thread record of the searches since the last read
+// stage timing: per-process switch (0 off, 1 every stage, 2 the scan stage only); per-thread record of
+// the searches since the last read
 std::atomic<int> g_prof_on{0};
 constexpr int kStages = 6;
 // "plan" and "fallback" are empty when a search runs query by query
 const char *const kStageNames[kStages] = {"coarse", "select", "plan", "scan", "fallback", "merge"};
 struct ProfState {
   std::vector<hipEvent_t> pool;   // kStages + 1 events per recorded search
+  std::vector<int> mode;          // the switch's value when each search was recorded
   int searches = 0;
   ~ProfState() {
     for (auto e : pool) (void)hipEventDestroy(e);
@@ -409,10 +411,13 @@ extern "C" int svt_search(const svt_index *ix, int32_t B, const int8_t *queries,
   }
   SearchShape sh{B, nprobe, k, ix->scan_wgs, L.max_chunks, grouped, pool_cap, L.max_units, ix->gscan_wgs};
 
-  const bool prof = g_prof_on.load(std::memory_order_relaxed) != 0 && g_prof.searches < kMaxProfiledSearches;
+  const int prof_mode = g_prof_on.load(std::memory_order_relaxed);
+  const bool prof = prof_mode != 0 && g_prof.searches < kMaxProfiledSearches;
   ProfState &ps = g_prof;
   int ev0 = 0, evn = 0;
   if (prof) {
+    if ((int)ps.mode.size() <= ps.searches) ps.mode.resize(ps.searches + 1);
+    ps.mode[ps.searches] = prof_mode;
     ev0 = ps.searches * (kStages + 1);
     while ((int)ps.pool.size() < ev0 + kStages + 1) {
       hipEvent_t ev;
@@ -421,7 +426,12 @@ extern "C" int svt_search(const svt_index *ix, int32_t B, const int8_t *queries,
       ps.pool.push_back(ev);
     }
   }
-  auto mark = [&]() -> hipError_t { return prof ? hipEventRecord(ps.pool[ev0 + evn++], s) : hipSuccess; };
+  // mark i ends stage i - 1; the scan stage lies between marks 3 and 4
+  auto mark = [&]() -> hipError_t {
+    const int i = evn++;
+    if (!prof || (prof_mode == 2 && i != 3 && i != 4)) return hipSuccess;
+    return hipEventRecord(ps.pool[ev0 + i], s);
+  };
   hipError_t e;
   if ((e = mark()) != hipSuccess) return fail_hip(e, "event");
   if ((e = launch_coarse_keys(ix->dev, queries, B, w, s)) != hipSuccess) return fail_hip(e, "launch coarse_keys");
@@ -457,7 +467,9 @@ extern "C" int svt_search(const svt_index *ix, int32_t B, const int8_t *queries,
 }
 
 extern "C" int svt_profile_enable(int on) {
-  g_prof_on.store(on ? 1 : 0);
+  g_err.clear();
+  if (on < 0 || on > 2) return fail(SVT_EINVAL, "svt_profile_enable: mode %d out of [0, 2]", on);
+  g_prof_on.store(on);
   return SVT_OK;
 }
 
@@ -474,6 +486,7 @@ extern "C" int svt_profile_read(float *stage_ms, const char **stage_names, int32
     if (e != hipSuccess) return fail_hip(e, "hipEventSynchronize");
     for (int r = 0; r < ns; ++r)
       for (int i = 0; i < kStages; ++i) {
+        if (ps.mode[r] == 2 && i != 3) continue;   // scan-only record
         float ms = 0.f;
         e = hipEventElapsedTime(&ms, ps.pool[r * (kStages + 1) + i], ps.pool[r * (kStages + 1) + i + 1]);
         if (e != hipSuccess) return fail_hip(e, "hipEventElapsedTime");

@@ -180,8 +180,9 @@ def svt_search(handle, queries, masks, nprobe: int, k: int, query_scales=None, o
     return out_ids, out_scores, out_fscores, out_counts, out_stats
 
 
-def svt_profile_enable(on: bool) -> None:
-    _check(lib().svt_profile_enable(1 if on else 0))
+def svt_profile_enable(on) -> None:
+    """False/0: off; True/1: every stage; 2: the scan stage only (two event records per search)."""
+    _check(lib().svt_profile_enable(int(on)))
 
 
 def svt_profile_read(max_stages: int = 8):

@@ -82,3 +82,14 @@ def test_search_rejects_dead_index(L):
     assert L.svt_search_workspace_size(bogus, 1, 1, 1) == 0
     assert L.svt_index_free(bogus) == svt.SVT_ESTATE
     assert L.svt_index_free(None) == svt.SVT_OK
+
+
+def test_profile_modes(L):
+    # 0 off, 1 every stage, 2 the scan stage only; anything else is rejected
+    for mode in (0, 1, 2, 0):
+        assert L.svt_profile_enable(mode) == svt.SVT_OK
+    assert L.svt_profile_enable(3) == svt.SVT_EINVAL
+    assert L.svt_profile_enable(-1) == svt.SVT_EINVAL
+    assert L.svt_profile_enable(0) == svt.SVT_OK
+    stages, n = svt.svt_profile_read()
+    assert n == 0 and list(stages) == ["coarse", "select", "plan", "scan", "fallback", "merge"]
