@@ -16,6 +16,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -53,10 +54,15 @@ def parse():
 
 
 def kernel_source_hash() -> str:
+    """Hash of the code the scan kernel is built from (its source, the shared device helpers and the
+    constants), with comments removed and whitespace collapsed, so that a comment edit keeps it."""
     h = hashlib.sha256()
-    for f in ("svt_kernels.hip", "svt_internal.h"):
-        with open(os.path.join(ROOT, "int8_ivf_ann_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    for f in ("svt_kernels.hip", "svt_device.h", "svt_internal.h"):
+        with open(os.path.join(ROOT, "int8_ivf_ann_amd", "csrc", f)) as fh:
+            src = fh.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()[:16]
 
 

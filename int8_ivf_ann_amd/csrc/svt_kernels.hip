@@ -3,11 +3,12 @@
 // Pipeline per svt_search (all on the caller's stream, no host synchronisation):
 //   k_coarse_keys   int8 centroid scores for every (query, cluster), packed as (score, cluster) keys
 //   k_coarse_select per query: exact top-nprobe clusters (radix select), probe list in cluster order,
-//                   per-query item stream layout; the last workgroup lays out the batch stream
+//                   per-query item stream layout, filter density and score samples
+//   k_plan_*        the work list: every query's stream cut into chunks of about equal estimated cost,
+//                   queued by the cluster band they start in
 //   k_scan          the fused hot loop: Bloom filter -> int8 dot4 score -> per-workgroup top-k in LDS;
-//                   a fixed grid of workgroups splits the concatenated (query, probed item) stream
-//                   into equal contiguous chunks; each (workgroup, query) run leaves at most k keys
-//   k_merge         per query: exact top-k over its runs' keys (radix select), sorted, written out
+//                   persistent workgroups take chunks from the queue; each chunk leaves at most k keys
+//   k_merge         per query: exact top-k over its chunks' keys (radix select), sorted, written out
 //
 // Method: "SilverTorch - Index as Model" (Meta engineering post): probe the most promising clusters
 // first, filter only inside them with Bloom signatures and bit operations, score only survivors
