@@ -251,7 +251,7 @@ __global__ __launch_bounds__(kSelThreads) void k_coarse_select(DevIndex ix, cons
   __syncthreads();
   if (tid == 0) {
     const double dens = (double)hits / kCostSamples;
-    w.qcost[b] = (int64_t)((double)run * (8.0 * ix.sig_words + dens * ix.dim)) + run / 8 + 1;
+    w.qcost[b] = (int64_t)((double)run * (8.0 * ix.sig_words + dens * ix.dim + kItemCost)) + 1;
     int32_t lo = 0, shift = 0;
     if (run > 0) {
       lo = (int32_t)(ssum / kCostSamples);
