@@ -255,7 +255,7 @@ extern "C" int svt_index_info(const svt_index *ix, int64_t *n_items, int32_t *di
 namespace {
 
 struct Layout {
-  size_t coarse_keys, probes, seg, pb, qlen, qcost, cstart, chunks, order, cband, band, thr, hlo, hshift, ghist, counter, slot_cnt,
+  size_t coarse_keys, probes, seg, pb, qlen, qcost, cstart, chunks, order, cband, thr, hlo, hshift, ghist, counter, slot_cnt,
       slot_min, slot_keys, stats;
   size_t gcnt, gfill, gstart, ustart, gq, units, pool_cnt, pool;   // grouped path (0 bytes when impossible)
   size_t total;
@@ -294,7 +294,6 @@ Layout layout(const svt_index *ix, int32_t B, int32_t nprobe, int32_t k) {
   L.chunks = take(C * sizeof(Chunk));
   L.order = take(C * sizeof(int32_t));
   L.cband = take(C * sizeof(int32_t));
-  L.band = take(2 * kPlanBands * sizeof(uint32_t));
   L.thr = take((size_t)B * sizeof(int32_t));
   L.hlo = take((size_t)B * sizeof(int32_t));
   L.hshift = take((size_t)B * sizeof(int32_t));
@@ -372,7 +371,6 @@ extern "C" int svt_search(const svt_index *ix, int32_t B, const int8_t *queries,
   w.chunks = (Chunk *)(base + L.chunks);
   w.order = (int32_t *)(base + L.order);
   w.cband = (int32_t *)(base + L.cband);
-  w.band = (uint32_t *)(base + L.band);
   w.thr = (int32_t *)(base + L.thr);
   w.hlo = (int32_t *)(base + L.hlo);
   w.hshift = (int32_t *)(base + L.hshift);

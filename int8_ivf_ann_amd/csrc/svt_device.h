@@ -161,6 +161,21 @@ __device__ uint64_t block_select(ForEach for_each, int need, SelScratch &sh) {
   return prefix;
 }
 
+// A bijection of [0, n) that scatters consecutive positions over the whole range: a permutation of
+// [0, 2^m) (odd multiplications and an xor-shift, each invertible modulo 2^m), walked until it lands
+// below n; the walk ends because every cycle of the permutation holds a position below n (the start).
+__device__ __forceinline__ int scatter_index(int pos, int n) {
+  const int m = n > 1 ? 32 - __clz(n - 1) : 1;   // 2^m >= n
+  const uint32_t mask = m >= 32 ? 0xFFFFFFFFu : ((1u << m) - 1u);
+  uint32_t x = (uint32_t)pos;
+  do {
+    x = (x * 0x9E3779B1u) & mask;
+    x ^= x >> ((m >> 1) + 1);
+    x = (x * 0x85EBCA77u) & mask;
+  } while (x >= (uint32_t)n);
+  return (int)x;
+}
+
 // Keys held while items are being scanned: (biased score << 32) | position.  They order candidates by
 // score like the ordering keys; they are turned into (score, id) keys (make_key) only for the few
 // candidates that can still reach a final top k, so the scan never waits on the position -> id table.

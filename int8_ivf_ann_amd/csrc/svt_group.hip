@@ -151,22 +151,6 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Queue position -> unit: a bijection of [0, n) that scatters the units of a cluster (which are numbered
-// consecutively) over the whole run, so that the queries' units are spread over the run rather than
-// clustered.  A permutation of [0, 2^m) (odd multiplications and an xor-shift, each invertible modulo
-// 2^m), walked until it lands below n; the walk ends because every cycle of the permutation holds a
-// position below n (the start).
-__device__ __forceinline__ int scatter_unit(int pos, int n) {
-  const int m = n > 1 ? 32 - __clz(n - 1) : 1;   // 2^m >= n
-  const uint32_t mask = m >= 32 ? 0xFFFFFFFFu : ((1u << m) - 1u);
-  uint32_t x = (uint32_t)pos;
-  do {
-    x = (x * 0x9E3779B1u) & mask;
-    x ^= x >> ((m >> 1) + 1);
-    x = (x * 0x85EBCA77u) & mask;
-  } while (x >= (uint32_t)n);
-  return (int)x;
-}
 
 template <int LPR, int W>
 __global__ __launch_bounds__(kScanThreads, kGScanOcc) void k_gscan(GScanArgs a) {
@@ -202,7 +186,7 @@ __global__ __launch_bounds__(kScanThreads, kGScanOcc) void k_gscan(GScanArgs a) 
         pf = 6;
         return;
       }
-      const int u = scatter_unit(upos, n_units);
+      const int u = scatter_index(upos, n_units);
       pf_v = reinterpret_cast<const int32_t *>(a.w.units + u)[l & 7];
       pf = 2;
     } else if (pf == 2) {

@@ -98,7 +98,6 @@ struct Work {
   Chunk *chunks;            // [max_chunks] the work list, in query order
   int32_t *order;           // [max_chunks] the order in which the scan takes the chunks
   int32_t *cband;           // [max_chunks] band of the probed cluster each chunk starts in
-  uint32_t *band;           // [2][kPlanBands] chunks per band, then each band's next queue position
   int32_t *thr;             // [B]          per-query proven lower bound on the k-th best score
   int32_t *hlo;             // [B]          score at the lower edge of bin 1 of the query's histogram
   int32_t *hshift;          // [B]          bin width of that histogram is 2^hshift

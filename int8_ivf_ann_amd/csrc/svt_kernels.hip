@@ -269,16 +269,15 @@ __global__ __launch_bounds__(kSelThreads) void k_coarse_select(DevIndex ix, cons
 // The work list.  k_plan_count (one workgroup): the target cost of a chunk from the batch's total
 // estimated cost, every query's chunk count and length, and where its chunks start (cstart).
 // k_plan_chunks (one thread per query and probed cluster): the chunks that start inside that cluster,
-// and the band (1/256 of the cluster ids) of the cluster, counted per band.  k_plan_bands: where each
-// band starts in the queue.  k_plan_order: the queue, chunks grouped by band, so that chunks of
-// different queries that read the same clusters run at about the same time and the second reader finds
-// the data in cache (the order inside a band is arbitrary).
+// with the band (1/256 of the cluster ids) of the cluster.  k_plan_order (one workgroup): the queue,
+// chunks grouped by band, so that chunks of different queries that read the same clusters run at about
+// the same time and the second reader finds the data in cache (Infinity Cache: every XCD works through
+// the same bands at the same time).
 
 __global__ __launch_bounds__(kSelThreads) void k_plan_count(int32_t B, int32_t P, Work w) {
   __shared__ int wave_tot[kSelThreads / 64 + 1];
   __shared__ int64_t wave_tot64[kSelThreads / 64 + 1];
   const int tid = threadIdx.x;
-  for (int i = tid; i < kPlanBands; i += kSelThreads) w.band[i] = 0u;
   int64_t total = 0;
   for (int i0 = 0; i0 < B; i0 += kSelThreads) {
     const int i = i0 + tid;
@@ -326,30 +325,71 @@ __global__ __launch_bounds__(256) void k_plan_chunks(int32_t B, int32_t nprobe, 
   int64_t i = (s0 + cl - 1) / cl;
   if (i * cl >= s1) return;
   const int band = (int)(((int64_t)w.probes[(size_t)q * nprobe + j] * kPlanBands) / nlist);
-  int n = 0;
-  for (; i < nch && i * cl < s1; ++i, ++n) {
+  for (; i < nch && i * cl < s1; ++i) {
     const int64_t l0 = i * cl, l1 = l0 + cl < len ? l0 + cl : len;
     w.chunks[c0 + i] = Chunk{q, (int32_t)l0, (int32_t)l1, j};
     w.cband[c0 + i] = band;
   }
-  atomicAdd(&w.band[band], (uint32_t)n);
 }
 
-__global__ __launch_bounds__(64) void k_plan_bands(Work w) {
-  const int l = threadIdx.x;
-  constexpr int PB = kPlanBands / 64;
-  uint32_t h[PB], sum = 0;
+// The queue: a counting sort of the chunks by band.  Inside a band the chunks follow a scattered order
+// (scatter_index), which interleaves the queries: consecutive queue entries then belong to different
+// queries, so the workgroups running at the same time read the same clusters for different queries
+// (measured: both one query's chunks together and chunk order make the scan slower).  The sort is stable
+// over that order: wave w of the one workgroup owns scattered positions [w * per, (w + 1) * per); it
+// counts their chunks per band, every (wave, band) gets its start from the band totals and the counts of
+// the waves before it, and the wave places its chunks, ranking the lanes of a 64-position group that
+// share a band with ballots on the band's bits.
+__global__ __launch_bounds__(kSelThreads) void k_plan_order(int32_t B, Work w) {
+  constexpr int NWV = kSelThreads / 64;
+  constexpr int BB = 8;                              // bits of a band
+  static_assert(kPlanBands == 1 << BB, "bands are ranked with one ballot per band bit");
+  __shared__ uint32_t cnt[NWV][kPlanBands];          // per wave: chunks per band, then next position
+  __shared__ uint32_t wave_tot[NWV + 1];
+  const int tid = threadIdx.x, l = lane_id(), wv = tid / 64;
+  const int n = w.cstart[B];
+  const int per = ((n + NWV - 1) / NWV + 63) / 64 * 64;
+  const int c_lo = wv * per, c_hi = c_lo + per < n ? c_lo + per : n;
+  for (int i = tid; i < NWV * kPlanBands; i += kSelThreads) cnt[i / kPlanBands][i % kPlanBands] = 0u;
+  __syncthreads();
+  for (int p = c_lo + l; p < c_hi; p += 64) atomicAdd(&cnt[wv][w.cband[scatter_index(p, n)]], 1u);
+  __syncthreads();
+  // band totals -> band starts (threads of the first kPlanBands), then each wave's start per band
+  uint32_t tot = 0u;
+  if (tid < kPlanBands)
+    for (int v = 0; v < NWV; ++v) tot += cnt[v][tid];
+  uint32_t all;
+  uint32_t run = block_excl_scan<kSelThreads>(tot, wave_tot, &all);
+  if (tid < kPlanBands)
+    for (int v = 0; v < NWV; ++v) {
+      const uint32_t x = cnt[v][tid];
+      cnt[v][tid] = run;
+      run += x;
+    }
+  __syncthreads();
+  // each wave places its chunks in order
+  for (int c0 = c_lo; c0 < c_hi; c0 += 64) {
+    const bool have = c0 + l < c_hi;
+    const int c = have ? scatter_index(c0 + l, n) : 0;
+    const int b = have ? w.cband[c] : 0;
+    uint64_t eq = __ballot(have);
 #pragma unroll
-  for (int u = 0; u < PB; ++u) { h[u] = w.band[PB * l + u]; sum += h[u]; }
-  uint32_t run = wave_incl_scan(sum) - sum;
-#pragma unroll
-  for (int u = 0; u < PB; ++u) { w.band[kPlanBands + PB * l + u] = run; run += h[u]; }
-}
-
-__global__ __launch_bounds__(256) void k_plan_order(int32_t B, Work w) {
-  const int c = blockIdx.x * 256 + threadIdx.x;
-  if (c >= w.cstart[B]) return;
-  w.order[atomicAdd(&w.band[kPlanBands + w.cband[c]], 1u)] = c;
+    for (int k = 0; k < BB; ++k) {
+      const uint64_t m = __ballot((b >> k) & 1);
+      eq &= ((b >> k) & 1) ? m : ~m;
+    }
+    const int rank = mbcnt(eq);
+    uint32_t pos = 0u;
+    if (have) pos = cnt[wv][b] + (uint32_t)rank;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (have) w.order[pos] = c;
+    if (have && rank == 0) cnt[wv][b] += (uint32_t)__popcll(eq);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -1232,8 +1272,7 @@ hipError_t launch_coarse_select(const DevIndex &ix, const int8_t *queries, const
   k_plan_count<<<1, kSelThreads, 0, s>>>(sh.B, sh.P, w);
   const int64_t pairs = (int64_t)sh.B * sh.nprobe;
   if (pairs > 0) k_plan_chunks<<<(unsigned)((pairs + 255) / 256), 256, 0, s>>>(sh.B, sh.nprobe, ix.nlist, w);
-  k_plan_bands<<<1, 64, 0, s>>>(w);
-  k_plan_order<<<(unsigned)((sh.max_chunks + 255) / 256), 256, 0, s>>>(sh.B, w);
+  k_plan_order<<<1, kSelThreads, 0, s>>>(sh.B, w);
   return hipGetLastError();
 }
 
