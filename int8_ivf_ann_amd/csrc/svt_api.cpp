@@ -255,7 +255,7 @@ extern "C" int svt_index_info(const svt_index *ix, int64_t *n_items, int32_t *di
 namespace {
 
 struct Layout {
-  size_t coarse_keys, probes, seg, pb, qlen, qcost, cstart, chunks, order, cband, thr, hlo, hshift, ghist, counter, slot_cnt,
+  size_t coarse_scores, probes, seg, pb, qlen, qcost, cstart, chunks, order, cband, thr, hlo, hshift, ghist, counter, slot_cnt,
       slot_min, slot_keys, stats;
   size_t gcnt, gfill, gstart, ustart, gq, units, pool_cnt, pool;   // grouped path (0 bytes when impossible)
   size_t total;
@@ -284,7 +284,7 @@ Layout layout(const svt_index *ix, int32_t B, int32_t nprobe, int32_t k) {
     o += align256(bytes);
     return at;
   };
-  L.coarse_keys = take((size_t)B * nlist * sizeof(uint64_t));
+  L.coarse_scores = take((size_t)B * nlist * sizeof(int32_t));
   L.probes = take((size_t)B * nprobe * sizeof(int32_t));
   L.seg = take((size_t)B * (nprobe + 1) * sizeof(int32_t));
   L.pb = take((size_t)B * nprobe * sizeof(int32_t));
@@ -361,7 +361,7 @@ extern "C" int svt_search(const svt_index *ix, int32_t B, const int8_t *queries,
   hipStream_t s = (hipStream_t)hip_stream;
   char *base = (char *)workspace;
   Work w;
-  w.coarse_keys = (uint64_t *)(base + L.coarse_keys);
+  w.coarse_scores = (int32_t *)(base + L.coarse_scores);
   w.probes = (int32_t *)(base + L.probes);
   w.seg = (int32_t *)(base + L.seg);
   w.pb = (int32_t *)(base + L.pb);

@@ -35,7 +35,10 @@ constexpr int kSegWin = 64;                             // probed clusters stage
 constexpr int kQHistBins = 256;                         // bins of a query's global score histogram
 constexpr int kSelThreads = 1024;    // coarse-select and merge workgroups
 static_assert(2 * kSelThreads >= kMaxK, "the final sort holds two keys per merge thread");
-constexpr int kCoarseQB = 8;         // queries per coarse-score workgroup
+#ifndef SVT_COARSE_QB
+#define SVT_COARSE_QB 16
+#endif
+constexpr int kCoarseQB = SVT_COARSE_QB;   // queries per coarse-score workgroup
 constexpr int kMaxScanWGs = 4096;    // upper bound on persistent scan workgroups
 
 // Device-resident index.  Items of cluster c occupy positions [offsets[c], offsets[c+1]); within a
@@ -88,7 +91,7 @@ struct GUnit {
 
 // Per-search device workspace (carved by the host from the caller's buffer).
 struct Work {
-  uint64_t *coarse_keys;    // [B][nlist]   coarse (score, cluster) keys
+  int32_t *coarse_scores;   // [B][nlist]   coarse scores <query, centroid>
   int32_t *probes;          // [B][nprobe]  probed clusters, ascending cluster id
   int32_t *seg;             // [B][nprobe + 1] stream offset of each probed cluster within its query
   int32_t *pb;              // [B][nprobe]  position of stream offset t in probed cluster j: pb[j] + t

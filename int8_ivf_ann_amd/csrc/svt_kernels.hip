@@ -1,7 +1,7 @@
 // svt_kernels.hip - gfx950 kernels of the fused int8 IVF + Bloom-signature top-k search.
 //
 // Pipeline per svt_search (all on the caller's stream, no host synchronisation):
-//   k_coarse_keys   int8 centroid scores for every (query, cluster), packed as (score, cluster) keys
+//   k_coarse_keys   int8 centroid scores for every (query, cluster)
 //   k_coarse_select per query: exact top-nprobe clusters (radix select), probe list in cluster order,
 //                   per-query item stream layout, filter density and score samples
 //   k_plan_*        the work list: every query's stream cut into chunks of about equal estimated cost,
@@ -29,13 +29,13 @@
 namespace svt {
 
 // ------------------------------------------------------------------------------------------------
-// k_coarse_keys: key (s, c) for every query b and cluster c, s = <q_b, centroid_c> (int32).
-// One thread per cluster, kCoarseQB queries per workgroup staged in LDS.
+// k_coarse_keys: s = <q_b, centroid_c> (int32) for every query b and cluster c; the select forms the
+// ordering key (s, c) from it.  One thread per cluster, kCoarseQB queries per workgroup staged in LDS.
 
 template <int LPR>
 __global__ __launch_bounds__(256) void k_coarse_keys(const int8_t *__restrict__ centroids, int32_t nlist,
                                                      const int8_t *__restrict__ queries, int32_t B,
-                                                     uint64_t *__restrict__ keys, uint32_t *counter,
+                                                     int32_t *__restrict__ scores, uint32_t *counter,
                                                      int32_t *__restrict__ gcnt, int32_t *__restrict__ gfill) {
   constexpr int D = 16 * LPR;
   __shared__ int4 qs[kCoarseQB][LPR];
@@ -65,7 +65,7 @@ __global__ __launch_bounds__(256) void k_coarse_keys(const int8_t *__restrict__ 
     int32_t acc = 0;
 #pragma unroll
     for (int ch = 0; ch < LPR; ++ch) acc = dot16(row[ch], qs[qi][ch], acc);
-    keys[(size_t)b * nlist + c] = make_key(acc, (uint32_t)c);
+    scores[(size_t)b * nlist + c] = acc;
   }
 }
 
@@ -102,7 +102,7 @@ __global__ __launch_bounds__(kSelThreads) void k_coarse_select(DevIndex ix, cons
   const int tid = threadIdx.x, l = lane_id(), wv = tid / 64;
   const int b = blockIdx.x;
   const int nlist = ix.nlist;
-  const uint64_t *row = w.coarse_keys + (size_t)b * nlist;
+  const int32_t *row = w.coarse_scores + (size_t)b * nlist;
   int32_t *probes = w.probes + (size_t)b * nprobe;
   int32_t *seg = w.seg + (size_t)b * (nprobe + 1);
   int32_t *pb = w.pb + (size_t)b * nprobe;
@@ -115,7 +115,7 @@ __global__ __launch_bounds__(kSelThreads) void k_coarse_select(DevIndex ix, cons
 #pragma unroll
     for (int i = 0; i < kSelKR; ++i) {
       const int c = i * kSelThreads + tid;
-      kr[i] = c < nlist ? row[c] : 0ull;
+      kr[i] = c < nlist ? make_key(row[c], (uint32_t)c) : 0ull;
     }
     if (nprobe < nlist) {
       T = block_select<kSelThreads>(
@@ -158,14 +158,14 @@ __global__ __launch_bounds__(kSelThreads) void k_coarse_select(DevIndex ix, cons
     if (nprobe < nlist) {
       T = block_select<kSelThreads>(
           [&](auto f) {
-            for (int c = tid; c < nlist; c += kSelThreads) f(row[c]);
+            for (int c = tid; c < nlist; c += kSelThreads) f(make_key(row[c], (uint32_t)c));
           },
           nprobe, sel);
     }
     int base = 0;
     for (int c0 = 0; c0 < nlist; c0 += kSelThreads) {
       const int c = c0 + tid;
-      const bool take = c < nlist && row[c] >= T;
+      const bool take = c < nlist && make_key(row[c], (uint32_t)c) >= T;
       int cnt_tot;
       const int idx = block_excl_scan<kSelThreads>(take ? 1 : 0, wave_tot, &cnt_tot);
       if (take && base + idx < nprobe) {
@@ -1256,11 +1256,11 @@ __global__ __launch_bounds__(256) void k_scatter_rows(const int8_t *__restrict__
 hipError_t launch_coarse_keys(const DevIndex &ix, const int8_t *queries, int32_t B, const Work &w, hipStream_t s) {
   dim3 grid((ix.nlist + 255) / 256, (B + kCoarseQB - 1) / kCoarseQB);
   switch (ix.dim) {
-    case 16: k_coarse_keys<1><<<grid, 256, 0, s>>>(ix.centroids, ix.nlist, queries, B, w.coarse_keys, w.counter, w.gcnt, w.gfill); break;
-    case 32: k_coarse_keys<2><<<grid, 256, 0, s>>>(ix.centroids, ix.nlist, queries, B, w.coarse_keys, w.counter, w.gcnt, w.gfill); break;
-    case 64: k_coarse_keys<4><<<grid, 256, 0, s>>>(ix.centroids, ix.nlist, queries, B, w.coarse_keys, w.counter, w.gcnt, w.gfill); break;
-    case 128: k_coarse_keys<8><<<grid, 256, 0, s>>>(ix.centroids, ix.nlist, queries, B, w.coarse_keys, w.counter, w.gcnt, w.gfill); break;
-    case 256: k_coarse_keys<16><<<grid, 256, 0, s>>>(ix.centroids, ix.nlist, queries, B, w.coarse_keys, w.counter, w.gcnt, w.gfill); break;
+    case 16: k_coarse_keys<1><<<grid, 256, 0, s>>>(ix.centroids, ix.nlist, queries, B, w.coarse_scores, w.counter, w.gcnt, w.gfill); break;
+    case 32: k_coarse_keys<2><<<grid, 256, 0, s>>>(ix.centroids, ix.nlist, queries, B, w.coarse_scores, w.counter, w.gcnt, w.gfill); break;
+    case 64: k_coarse_keys<4><<<grid, 256, 0, s>>>(ix.centroids, ix.nlist, queries, B, w.coarse_scores, w.counter, w.gcnt, w.gfill); break;
+    case 128: k_coarse_keys<8><<<grid, 256, 0, s>>>(ix.centroids, ix.nlist, queries, B, w.coarse_scores, w.counter, w.gcnt, w.gfill); break;
+    case 256: k_coarse_keys<16><<<grid, 256, 0, s>>>(ix.centroids, ix.nlist, queries, B, w.coarse_scores, w.counter, w.gcnt, w.gfill); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -210,3 +210,21 @@ def test_zipf_skewed_cluster(svt):
     q[:6] = cent[0]      # half the queries probe the giant cluster first
     masks = P.random_masks(rng, 12, 2, nbits_max=2)
     _run(svt, items, sigs, cl, cent, 1.0, q, masks, 4, 2048, "zipf")
+
+
+def test_many_clusters(svt):
+    # more clusters than the coarse select keeps in registers: its keys are read from memory instead
+    rng = np.random.default_rng(15)
+    items, sigs, cl, cent = P.small_catalogue(rng, n=60_000, d=32, nlist=20_000, W=1, empty_clusters=50)
+    q = rng.integers(-127, 128, (8, 32)).astype(np.int8)
+    masks = P.random_masks(rng, 8, 1, nbits_max=2)
+    _run(svt, items, sigs, cl, cent, 0.5, q, masks, 200, 100, "many-clusters")
+
+
+def test_nprobe_beyond_lds_probe_list(svt):
+    # more probes than the select's LDS probe list holds: stream offsets are read from memory instead
+    rng = np.random.default_rng(16)
+    items, sigs, cl, cent = P.small_catalogue(rng, n=60_000, d=16, nlist=9_000, W=2, empty_clusters=20)
+    q = rng.integers(-127, 128, (6, 16)).astype(np.int8)
+    masks = P.random_masks(rng, 6, 2, nbits_max=3)
+    _run(svt, items, sigs, cl, cent, 1.0, q, masks, 5_000, 300, "many-probes")
