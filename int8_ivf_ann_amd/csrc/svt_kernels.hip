@@ -86,7 +86,23 @@ __device__ __forceinline__ bool passes(const uint64_t *__restrict__ sig, const u
   return ok;
 }
 
+// <x, q> over NCH 16-byte parts, every part requested before any is used
+template <int NCH>
+__device__ __forceinline__ int32_t row_dot(const int4 *__restrict__ x, const int4 *__restrict__ q) {
+  int4 xv[NCH], qv[NCH];
+#pragma unroll
+  for (int ch = 0; ch < NCH; ++ch) {
+    xv[ch] = x[ch];
+    qv[ch] = q[ch];
+  }
+  int32_t s = 0;
+#pragma unroll
+  for (int ch = 0; ch < NCH; ++ch) s = dot16(xv[ch], qv[ch], s);
+  return s;
+}
+
 constexpr int kSelKR = 16;   // coarse keys a select thread keeps in registers (nlist <= kSelThreads * kSelKR)
+constexpr int kSelTwoLevel = kSelSegLds / 2 / kSelKR;   // largest nprobe the two-level selection stages
 
 __global__ __launch_bounds__(kSelThreads) void k_coarse_select(DevIndex ix, const int8_t *__restrict__ queries,
                                                                 const uint64_t *__restrict__ masks, int32_t B,
@@ -96,7 +112,11 @@ __global__ __launch_bounds__(kSelThreads) void k_coarse_select(DevIndex ix, cons
   __shared__ int wave_tot[NWV + 1];
   __shared__ int64_t wave_tot64[NWV + 1];
   __shared__ int32_t seg_lds[kSelSegLds + 1];   // the probed clusters, then their stream offsets
-  __shared__ int32_t pb_lds[kSelSegLds];
+  __shared__ union {
+    int32_t pb[kSelSegLds];                        // position base of each probed cluster
+    uint64_t cand[kSelSegLds / 2];                 // candidates of the two-level selection
+  } su;
+  __shared__ int ncand_s;
   __shared__ int32_t tcnt[kSelKR * NWV];         // probed clusters per (register slot, wave)
   __shared__ int smax_s;
   const int tid = threadIdx.x, l = lane_id(), wv = tid / 64;
@@ -117,7 +137,42 @@ __global__ __launch_bounds__(kSelThreads) void k_coarse_select(DevIndex ix, cons
       const int c = i * kSelThreads + tid;
       kr[i] = c < nlist ? make_key(row[c], (uint32_t)c) : 0ull;
     }
-    if (nprobe < nlist) {
+    const int nthr = nlist < kSelThreads ? nlist : kSelThreads;   // threads holding at least one key
+    if (nprobe < nlist && nprobe <= kSelTwoLevel && nprobe <= nthr) {
+      // Two levels.  The nprobe largest of the threads' largest keys are nprobe distinct keys, so the
+      // smallest of them, T1, is at or below the nprobe-th largest key: only the nprobe threads whose
+      // largest key reaches T1 hold keys >= T1.  Those (at most nprobe * kSelKR) are staged in LDS and
+      // the exact selection runs over them.
+      uint64_t tmax = 0ull;
+#pragma unroll
+      for (int i = 0; i < kSelKR; ++i) tmax = kr[i] > tmax ? kr[i] : tmax;
+      const uint64_t T1 = block_select<kSelThreads>(
+          [&](auto f) {
+            if (tmax != 0ull) f(tmax);
+          },
+          nprobe, sel);
+      if (tid == 0) ncand_s = 0;
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < kSelKR; ++i) {
+        const bool take = kr[i] != 0ull && kr[i] >= T1;
+        const uint64_t bal = __ballot(take);
+        int base = 0;
+        if (l == 0 && bal) base = atomicAdd(&ncand_s, __popcll(bal));
+        base = __shfl(base, 0);
+        if (take) su.cand[base + mbcnt(bal)] = kr[i];
+      }
+      __syncthreads();
+      const int nc = ncand_s;
+      T = block_select<kSelThreads>(
+          [&](auto f) {
+            for (int j = tid; j < nc; j += kSelThreads) f(su.cand[j]);
+          },
+          nprobe, sel);
+      // the threshold separates the candidates only; every other key lies below T1
+      T = T > T1 ? T : T1;
+      __syncthreads();   // su.cand is reused for the position bases below
+    } else if (nprobe < nlist) {
       T = block_select<kSelThreads>(
           [&](auto f) {
 #pragma unroll
@@ -193,7 +248,7 @@ __global__ __launch_bounds__(kSelThreads) void k_coarse_select(DevIndex ix, cons
       pb[r] = o0 - (run + pre);
       if (in_lds) {
         seg_lds[r] = run + pre;
-        pb_lds[r] = o0 - (run + pre);
+        su.pb[r] = o0 - (run + pre);
       }
     }
     run += tot;
@@ -224,7 +279,7 @@ __global__ __launch_bounds__(kSelThreads) void k_coarse_select(DevIndex ix, cons
         const int32_t sv = in_lds ? seg_lds[mid] : seg[mid];
         if (sv <= t) lo = mid; else hi = mid - 1;
       }
-      pos = (in_lds ? pb_lds[lo] : pb[lo]) + t;
+      pos = (in_lds ? su.pb[lo] : pb[lo]) + t;
     }
     uint64_t mk[2] = {0, 0};
     for (int u = 0; u < ix.sig_words; ++u) mk[u] = masks[(size_t)b * ix.sig_words + u];
@@ -232,7 +287,13 @@ __global__ __launch_bounds__(kSelThreads) void k_coarse_select(DevIndex ix, cons
     hit = ix.sig_words == 2 ? passes<2>(sg, mk) : passes<1>(sg, mk);
     const int4 *xr = reinterpret_cast<const int4 *>(ix.items + (size_t)pos * ix.dim);
     const int4 *qr = reinterpret_cast<const int4 *>(queries + (size_t)b * ix.dim);
-    for (int ch = 0; ch < ix.dim / 16; ++ch) sc = dot16(xr[ch], qr[ch], sc);
+    switch (ix.dim) {
+      case 16: sc = row_dot<1>(xr, qr); break;
+      case 32: sc = row_dot<2>(xr, qr); break;
+      case 64: sc = row_dot<4>(xr, qr); break;
+      case 128: sc = row_dot<8>(xr, qr); break;
+      default: sc = row_dot<16>(xr, qr); break;
+    }
     have = 1;
   }
   if (tid == 0) smax_s = INT32_MIN;
