@@ -255,7 +255,7 @@ extern "C" int svt_index_info(const svt_index *ix, int64_t *n_items, int32_t *di
 namespace {
 
 struct Layout {
-  size_t coarse_scores, probes, seg, pb, qlen, qcost, cstart, chunks, order, cband, thr, hlo, hshift, ghist, counter, slot_cnt,
+  size_t coarse_scores, probes, seg, pb, qlen, qcost, qtail, cstart, chunks, order, cband, thr, hlo, hshift, ghist, counter, slot_cnt,
       slot_min, slot_keys, stats;
   size_t gcnt, gfill, gstart, ustart, gq, units, pool_cnt, pool;   // grouped path (0 bytes when impossible)
   size_t total;
@@ -290,6 +290,7 @@ Layout layout(const svt_index *ix, int32_t B, int32_t nprobe, int32_t k) {
   L.pb = take((size_t)B * nprobe * sizeof(int32_t));
   L.qlen = take((size_t)B * sizeof(int64_t));
   L.qcost = take((size_t)B * sizeof(int64_t));
+  L.qtail = take((size_t)B * 2 * sizeof(int32_t));
   L.cstart = take((size_t)(B + 1) * sizeof(int32_t));
   L.chunks = take(C * sizeof(Chunk));
   L.order = take(C * sizeof(int32_t));
@@ -367,6 +368,7 @@ extern "C" int svt_search(const svt_index *ix, int32_t B, const int8_t *queries,
   w.pb = (int32_t *)(base + L.pb);
   w.qlen = (int64_t *)(base + L.qlen);
   w.qcost = (int64_t *)(base + L.qcost);
+  w.qtail = (int32_t *)(base + L.qtail);
   w.cstart = (int32_t *)(base + L.cstart);
   w.chunks = (Chunk *)(base + L.chunks);
   w.order = (int32_t *)(base + L.order);

@@ -79,6 +79,18 @@ static_assert(kMergeCap >= kMaxK && kMergeCap % kSelThreads == 0,
 constexpr int kSelSegLds = 4096;            // probe lists up to this long are searched in LDS
 constexpr int64_t kMinChunkCost = 16 << 10; // smallest chunk, in estimated bytes moved
 constexpr int kPlanBands = 256;             // cluster-id bands of the scan's queue order
+// The queue ends with the chunks of the highest bands.  Items of a query's probed clusters in bands
+// kTailBand and above are cut into chunks kTailDiv times shorter, so that the workgroups taking the last
+// chunks finish closer together.  kTailBand == kPlanBands: no shorter chunks.
+#ifndef SVT_TAIL_BAND
+#define SVT_TAIL_BAND 160
+#endif
+#ifndef SVT_TAIL_DIV
+#define SVT_TAIL_DIV 2
+#endif
+constexpr int kTailBand = SVT_TAIL_BAND;
+constexpr int kTailDiv = SVT_TAIL_DIV;
+static_assert(kTailBand >= 0 && kTailBand <= kPlanBands && kTailDiv >= 1, "tail region");
 
 // Grouped path: one unit of work is a tile of at most kGTile items of one probed cluster together
 // with a group of at most kGMax of the queries that probe that cluster (gq[q0..q1)).
@@ -97,6 +109,7 @@ struct Work {
   int32_t *pb;              // [B][nprobe]  position of stream offset t in probed cluster j: pb[j] + t
   int64_t *qlen;            // [B]          items scanned per query
   int64_t *qcost;           // [B]          estimated bytes the scan moves for the query
+  int32_t *qtail;           // [B][2]       stream offset where the query's tail region starts; its first chunk
   int32_t *cstart;          // [B + 1]      first chunk of each query; cstart[B] = number of chunks
   Chunk *chunks;            // [max_chunks] the work list, in query order
   int32_t *order;           // [max_chunks] the order in which the scan takes the chunks
@@ -129,8 +142,12 @@ struct SearchShape {
   int32_t GP;          // persistent workgroups of the grouped scan
 };
 
-// most chunks a search can produce: cost-balanced chunks number at most 4 P + B
-inline int32_t max_chunks_for(int32_t B, int32_t P) { return 4 * P + B + 1; }
+// most chunks a search can produce.  The costs of the queries add up to at most 4 P Tc.  Without a tail
+// region a query of estimated cost c gets at most c / Tc + 1 chunks; with one, at most kTailDiv c / Tc + 2
+// (two regions), or kTailDiv + 1 when it is shorter than one chunk.
+inline int32_t max_chunks_for(int32_t B, int32_t P) {
+  return kTailBand < kPlanBands ? 4 * kTailDiv * P + (kTailDiv + 1) * B + 1 : 4 * P + B + 1;
+}
 
 // launch wrappers (svt_kernels.hip); each returns hipSuccess or the launch error
 hipError_t launch_coarse_keys(const DevIndex &ix, const int8_t *queries, int32_t B, const Work &w,

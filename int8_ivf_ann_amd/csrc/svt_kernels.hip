@@ -119,6 +119,7 @@ __global__ __launch_bounds__(kSelThreads) void k_coarse_select(DevIndex ix, cons
   __shared__ int ncand_s;
   __shared__ int32_t tcnt[kSelKR * NWV];         // probed clusters per (register slot, wave)
   __shared__ int smax_s;
+  __shared__ int32_t tail_s;                     // stream offset of the first probed cluster in the tail bands
   const int tid = threadIdx.x, l = lane_id(), wv = tid / 64;
   const int b = blockIdx.x;
   const int nlist = ix.nlist;
@@ -232,6 +233,8 @@ __global__ __launch_bounds__(kSelThreads) void k_coarse_select(DevIndex ix, cons
   }
   __syncthreads();
   // --- stream offsets: prefix of the probed clusters' sizes in probe order
+  const int32_t c_tail = (int32_t)(((int64_t)kTailBand * nlist + kPlanBands - 1) / kPlanBands);
+  if (tid == 0) tail_s = INT32_MAX;
   int run = 0;
   for (int r0 = 0; r0 < nprobe; r0 += kSelThreads) {
     const int r = r0 + tid;
@@ -244,6 +247,7 @@ __global__ __launch_bounds__(kSelThreads) void k_coarse_select(DevIndex ix, cons
     int tot;
     const int pre = block_excl_scan<kSelThreads>(sz, wave_tot, &tot);
     if (r < nprobe) {
+      if (c >= c_tail) atomicMin(&tail_s, run + pre);   // probes ascend, so the first such cluster
       seg[r] = run + pre;
       pb[r] = o0 - (run + pre);
       if (in_lds) {
@@ -313,6 +317,7 @@ __global__ __launch_bounds__(kSelThreads) void k_coarse_select(DevIndex ix, cons
   if (tid == 0) {
     const double dens = (double)hits / kCostSamples;
     w.qcost[b] = (int64_t)((double)run * (8.0 * ix.sig_words + dens * ix.dim + kItemCost)) + 1;
+    w.qtail[2 * (size_t)b] = tail_s < run ? tail_s : run;
     int32_t lo = 0, shift = 0;
     if (run > 0) {
       lo = (int32_t)(ssum / kCostSamples);
@@ -354,14 +359,26 @@ __global__ __launch_bounds__(kSelThreads) void k_plan_count(int32_t B, int32_t P
     int32_t nch = 0;
     if (i < B) {
       const int64_t len = w.qlen[i], cost = w.qcost[i];
+      const int64_t ta = w.qtail[2 * (size_t)i];   // [0, ta): regular chunks; [ta, len): shorter ones
+      int32_t na = 0;
       if (len > 0) {
         int64_t cl = (Tc * len + cost - 1) / cost;                          // items of one chunk
-        const int64_t cl_min = (len + kMaxChunksPerQuery - 1) / kMaxChunksPerQuery;
+        // each region is cut into at most half the chunks a query may have when there are two
+        const int64_t per = ta < len ? kMaxChunksPerQuery / 2 : kMaxChunksPerQuery;
+        const int64_t cl_min = (len + per - 1) / per;
         cl = cl > cl_min ? cl : cl_min;
         cl = ((cl + 63) / 64) * 64;
         cl = cl < len ? cl : len;
-        nch = (int32_t)((len + cl - 1) / cl);
+        na = ta > 0 ? (int32_t)((ta + cl - 1) / cl) : 0;
+        int32_t nb = 0;
+        if (ta < len) {
+          int64_t clb = ((cl + kTailDiv - 1) / kTailDiv + 63) / 64 * 64;
+          clb = clb > cl_min ? clb : cl_min;
+          nb = (int32_t)((len - ta + clb - 1) / clb);
+        }
+        nch = na + nb;
       }
+      w.qtail[2 * (size_t)i + 1] = na;
     }
     int32_t tot;
     const int32_t ex = block_excl_scan<kSelThreads>(nch, wave_tot, &tot);
@@ -377,20 +394,25 @@ __global__ __launch_bounds__(256) void k_plan_chunks(int32_t B, int32_t nprobe, 
   const int q = (int)(t / nprobe), j = (int)(t % nprobe);
   const int32_t c0 = w.cstart[q], nch = w.cstart[q + 1] - c0;
   if (nch == 0) return;
-  // chunks of ceil(len / nch) items: none is empty, since that never exceeds the length chosen above
-  const int64_t len = w.qlen[q];
-  const int64_t cl = (len + nch - 1) / nch;
+  const int64_t len = w.qlen[q], ta = w.qtail[2 * (size_t)q];
+  const int32_t na = w.qtail[2 * (size_t)q + 1], nb = nch - na;
   const int32_t *sq = w.seg + (size_t)q * (nprobe + 1);
   const int64_t s0 = sq[j], s1 = sq[j + 1];
-  // chunk i starts in this cluster when s0 <= i * cl < s1
-  int64_t i = (s0 + cl - 1) / cl;
-  if (i * cl >= s1) return;
   const int band = (int)(((int64_t)w.probes[(size_t)q * nprobe + j] * kPlanBands) / nlist);
-  for (; i < nch && i * cl < s1; ++i) {
-    const int64_t l0 = i * cl, l1 = l0 + cl < len ? l0 + cl : len;
-    w.chunks[c0 + i] = Chunk{q, (int32_t)l0, (int32_t)l1, j};
-    w.cband[c0 + i] = band;
-  }
+  // Each region [r0, r1) holds n chunks of ceil((r1 - r0) / n) items: none is empty, since that never
+  // exceeds the length chosen for the region.  Chunk i starts in this cluster when s0 <= r0 + i cl < s1.
+  auto cut = [&](int64_t r0, int64_t r1, int32_t n, int32_t first) {
+    if (n <= 0 || s1 <= r0 || s0 >= r1) return;
+    const int64_t cl = (r1 - r0 + n - 1) / n;
+    const int64_t from = s0 > r0 ? s0 - r0 : 0;
+    for (int64_t i = (from + cl - 1) / cl; i < n && r0 + i * cl < s1; ++i) {
+      const int64_t l0 = r0 + i * cl, l1 = l0 + cl < r1 ? l0 + cl : r1;
+      w.chunks[c0 + first + i] = Chunk{q, (int32_t)l0, (int32_t)l1, j};
+      w.cband[c0 + first + i] = band;
+    }
+  };
+  cut(0, ta, na, 0);
+  cut(ta, len, nb, na);
 }
 
 // The queue: a counting sort of the chunks by band.  Inside a band the chunks follow a scattered order
