@@ -256,7 +256,7 @@ namespace {
 
 struct Layout {
   size_t coarse_scores, probes, seg, pb, qlen, qcost, qtail, cstart, chunks, order, cband, thr, hlo, hshift, ghist, counter, slot_cnt,
-      slot_min, slot_keys, stats;
+      slot_min, slot_keys, mbound, mcnt, mkeys, stats;
   size_t gcnt, gfill, gstart, ustart, gq, units, pool_cnt, pool;   // grouped path (0 bytes when impossible)
   size_t total;
   int32_t max_chunks;
@@ -303,6 +303,9 @@ Layout layout(const svt_index *ix, int32_t B, int32_t nprobe, int32_t k) {
   L.slot_cnt = take(C * sizeof(int32_t));
   L.slot_min = take(C * sizeof(uint64_t));
   L.slot_keys = take(C * (size_t)k * sizeof(uint64_t));
+  L.mbound = take((size_t)B * sizeof(uint64_t));
+  L.mcnt = take((size_t)B * sizeof(uint32_t));
+  L.mkeys = take((size_t)B * kGatherCap * sizeof(uint64_t));
   L.stats = take((size_t)B * 2 * sizeof(int64_t));
   // grouped path: units <= sum_c tiles_c * ceil(queries_c / kGMax), bounded two ways
   const int64_t gpc = ((int64_t)B + kGMax - 1) / kGMax;
@@ -381,6 +384,9 @@ extern "C" int svt_search(const svt_index *ix, int32_t B, const int8_t *queries,
   w.slot_cnt = (int32_t *)(base + L.slot_cnt);
   w.slot_min = (uint64_t *)(base + L.slot_min);
   w.slot_keys = (uint64_t *)(base + L.slot_keys);
+  w.mbound = (uint64_t *)(base + L.mbound);
+  w.mcnt = (uint32_t *)(base + L.mcnt);
+  w.mkeys = (uint64_t *)(base + L.mkeys);
   w.stats = out_stats ? out_stats : (int64_t *)(base + L.stats);
   // path: SVT_PATH=query|grouped forces one; otherwise batches of kGroupedMinBatch or more queries are
   // grouped

@@ -74,6 +74,8 @@ constexpr int kMaxChunksPerQuery = 2048;    // a query's stream is cut into at m
 #define SVT_MERGE_CAP 6144
 #endif
 constexpr int kMergeCap = SVT_MERGE_CAP;      // merge candidates staged in LDS
+constexpr int kMergeGatherWGs = 2048;       // persistent workgroups gathering slot keys for the merge
+constexpr int kGatherCap = 3 * kMergeCap;   // keys gathered per query above its final bound
 static_assert(kMergeCap >= kMaxK && kMergeCap % kSelThreads == 0,
               "the merge stages at least k keys, a whole number per thread");
 constexpr int kSelSegLds = 4096;            // probe lists up to this long are searched in LDS
@@ -122,6 +124,9 @@ struct Work {
   int32_t *slot_cnt;        // [max_chunks] candidates each chunk left
   uint64_t *slot_min;       // [max_chunks] smallest key of a slot holding k keys, else 0
   uint64_t *slot_keys;      // [max_chunks][k] those candidates (score/id keys)
+  uint64_t *mbound;         // [B]          the query's final proven bound, as the smallest key it admits
+  uint32_t *mcnt;           // [B]          slot keys at or above it (more than kGatherCap: not all kept)
+  uint64_t *mkeys;          // [B][kGatherCap] those keys, gathered from the query's slots
   int64_t *stats;           // [B][2] scanned / eligible (caller buffer or workspace)
   // grouped path (null when the search runs query by query)
   int32_t *gcnt;            // [nlist]      queries probing each cluster
@@ -156,6 +161,7 @@ hipError_t launch_coarse_select(const DevIndex &ix, const int8_t *queries, const
                                 const SearchShape &sh, const Work &w, hipStream_t s);
 hipError_t launch_scan(const DevIndex &ix, const int8_t *queries, const uint64_t *masks, const SearchShape &sh,
                        const Work &w, hipStream_t s);
+// launch_merge: k_merge_bound, k_merge_gather (query-by-query search only), then k_merge
 hipError_t launch_merge(const DevIndex &ix, const float *query_scales, const SearchShape &sh, const Work &w,
                         int64_t *out_ids, int32_t *out_scores, float *out_fscores, int32_t *out_counts,
                         hipStream_t s);

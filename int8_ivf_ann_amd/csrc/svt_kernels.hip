@@ -1103,6 +1103,86 @@ __global__ __launch_bounds__(kScanThreads, kScanOcc) void k_scan(ScanArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------------
+// Before the merge.  k_merge_bound (one wave per query): every chunk has pushed the candidates it
+// accepted to its query's score histogram, so the histogram is final; the lower edge of the highest bin at
+// which at least k counted candidates lie at or above is a proven bound on the k-th score (at least k items
+// score that much), as is the query's running bound.  k_merge_gather (persistent workgroups, one slot at a
+// time): the keys of every slot at or above its query's bound, compacted per query with one atomic per slot.
+// A query's top k is among them: its true top k all score at least the bound.
+
+__global__ __launch_bounds__(64) void k_merge_bound(Work w, int32_t k) {
+  constexpr int HPB = kQHistBins / 64;
+  const int q = blockIdx.x, l = threadIdx.x;
+  const uint32_t *gh = w.ghist + (size_t)q * kQHistBins;
+  uint32_t h[HPB], sum = 0;
+#pragma unroll
+  for (int j = 0; j < HPB; ++j) { h[j] = gh[HPB * l + j]; sum += h[j]; }
+  uint32_t suf = sum;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t v = __shfl_down(suf, off);
+    if (l + off < 64) suf += v;
+  }
+  uint32_t above = suf - sum;   // counted candidates in the bins above this lane's
+  const int32_t hlo = w.hlo[q];
+  const int hsh = w.hshift[q];
+  int32_t bound = INT32_MIN;
+#pragma unroll
+  for (int j = HPB - 1; j >= 0; --j) {
+    const int bin = HPB * l + j;
+    if (bin >= 1 && above < (uint32_t)k && above + h[j] >= (uint32_t)k) bound = hlo + (bin << hsh);
+    above += h[j];
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const int32_t t = __shfl_xor(bound, o);
+    bound = t > bound ? t : bound;
+  }
+  const int32_t g = w.thr[q];
+  bound = g > bound ? g : bound;
+  if (l == 0) {
+    w.mbound[q] = bound == INT32_MIN ? 0ull : make_key(bound, 0xFFFFFFFFu);   // smallest key of that score
+    w.mcnt[q] = 0u;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_merge_gather(Work w, int32_t B, int32_t k) {
+  constexpr int PER = kMaxK / 256;   // a slot holds at most k <= kMaxK keys: one pass of PER per thread
+  __shared__ int wave_tot[256 / 64 + 1];
+  __shared__ uint32_t sbase;
+  const int tid = threadIdx.x;
+  const int n = w.cstart[B];
+  for (int c = blockIdx.x; c < n; c += gridDim.x) {
+    const int q = w.chunks[c].q;
+    const int cnt = w.slot_cnt[c];
+    const uint64_t T = w.mbound[q];
+    const uint64_t *keys = w.slot_keys + (size_t)c * k;
+    uint64_t v[PER];
+    int take = 0;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int i = u * 256 + tid;
+      v[u] = i < cnt ? keys[i] : 0ull;   // valid keys are never 0
+      take += v[u] >= T && v[u] != 0ull ? 1 : 0;
+    }
+    int tot;
+    int off = block_excl_scan<256>(take, wave_tot, &tot);   // barriers inside
+    if (tid == 0) sbase = tot > 0 ? atomicAdd(&w.mcnt[q], (uint32_t)tot) : 0u;
+    __syncthreads();
+    const uint32_t base = sbase;
+    uint64_t *dst = w.mkeys + (size_t)q * kGatherCap;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      if (v[u] >= T && v[u] != 0ull) {
+        const uint32_t o = base + (uint32_t)off++;
+        if (o < (uint32_t)kGatherCap) dst[o] = v[u];
+      }
+    }
+    __syncthreads();   // sbase and wave_tot are reused for the next slot
+  }
+}
+
+// ------------------------------------------------------------------------------------------------
 // k_merge: one workgroup per query.  Exact top-k over the keys its (workgroup, query) runs left,
 // bitonic sort in LDS, decode, dequantise, write.
 
@@ -1141,10 +1221,15 @@ __global__ __launch_bounds__(kSelThreads) void k_merge(MergeArgs a) {
   const int ns = a.w.cstart[q + 1] - a.w.cstart[q];
   if (tid == 0) { ncand = 0; bound = 0ull; smin = ~0u; smax = 0u; }
   __syncthreads();
+  // The keys gathered above the query's final bound hold its top k.  When all of them were kept
+  // (flat), they are the candidates, read as one array; otherwise the slots are read.
+  const uint32_t gathered = a.fallback ? ~0u : a.w.mcnt[q];
+  const bool flat = gathered <= (uint32_t)kGatherCap;
+  const uint64_t *gk = a.w.mkeys + (size_t)q * kGatherCap;
   // 1. counts and a proven lower bound on the k-th key: the largest smallest-key of a full slot
   unsigned long long lb = 0ull;
-  int total = 0;
-  for (int i0 = 0; i0 < ns; i0 += kSelThreads) {
+  int total = flat ? (int)gathered : 0;
+  for (int i0 = 0; i0 < (flat ? 0 : ns); i0 += kSelThreads) {
     const int i = i0 + tid;
     const int c = i < ns ? a.w.slot_cnt[s0 + i] : 0;
     if (c == k) {
@@ -1164,7 +1249,7 @@ __global__ __launch_bounds__(kSelThreads) void k_merge(MergeArgs a) {
   if (l == 0) atomicMax(&bound, lb);
   __syncthreads();
   uint64_t T = total > k ? (uint64_t)bound : 0ull;
-  if (total > k) {
+  if (!flat && total > k) {
     // every chunk is done: the query's global score bound is final
     const int32_t g = a.w.thr[q];
     if (g != INT32_MIN) {
@@ -1176,6 +1261,7 @@ __global__ __launch_bounds__(kSelThreads) void k_merge(MergeArgs a) {
   // slot s), eight loads in flight per thread
   const uint64_t *keys = a.w.slot_keys + s0 * (size_t)k;
   auto key_at = [&](int f) -> uint64_t {   // f-th valid key, 0 <= f < total
+    if (flat) return gk[f];
     int lo = 0, hi = ns - 1;                 // largest slot with sprefix <= f
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
@@ -1272,6 +1358,8 @@ __global__ __launch_bounds__(kSelThreads) void k_merge(MergeArgs a) {
   }
   __syncthreads();
   int n = ncand;
+  // gathered keys: the slots' keys at or above the final bound, which include the query's top k (or all of
+  // its candidates, when it has fewer than k)
   const int nout = total < k ? total : k;
   if (n > kMergeCap) {
     // the cut bin alone overflows LDS (heavy ties): select over the slots in global memory
@@ -1405,6 +1493,11 @@ hipError_t launch_merge(const DevIndex &ix, const float *query_scales, const Sea
                         hipStream_t s) {
   MergeArgs a{w, query_scales, ix.item_scale, sh.B, sh.k, sh.P, sh.grouped, (uint32_t)sh.pool_cap,
               out_ids, out_scores, out_fscores, out_counts};
+  if (!sh.grouped) {
+    k_merge_bound<<<sh.B, 64, 0, s>>>(w, sh.k);
+    const int g = sh.max_chunks < kMergeGatherWGs ? sh.max_chunks : kMergeGatherWGs;
+    k_merge_gather<<<g, 256, 0, s>>>(w, sh.B, sh.k);
+  }
   k_merge<<<sh.B, kSelThreads, 0, s>>>(a);
   return hipGetLastError();
 }
