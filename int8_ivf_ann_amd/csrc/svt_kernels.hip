@@ -334,8 +334,8 @@ __global__ __launch_bounds__(kSelThreads) void k_coarse_select(DevIndex ix, cons
 // ------------------------------------------------------------------------------------------------
 // The work list.  k_plan_count (one workgroup): the target cost of a chunk from the batch's total
 // estimated cost, every query's chunk count and length, and where its chunks start (cstart).
-// k_plan_chunks (one thread per query and probed cluster): the chunks that start inside that cluster,
-// with the band (1/256 of the cluster ids) of the cluster.  k_plan_order (one workgroup): the queue,
+// k_plan_chunks (one workgroup per query, one thread per chunk): each chunk's stream range, the probed
+// cluster it starts in and that cluster's band (1/256 of the cluster ids).  k_plan_order (one workgroup): the queue,
 // chunks grouped by band, so that chunks of different queries that read the same clusters run at about
 // the same time and the second reader finds the data in cache (Infinity Cache: every XCD works through
 // the same bands at the same time).
@@ -389,30 +389,42 @@ __global__ __launch_bounds__(kSelThreads) void k_plan_count(int32_t B, int32_t P
 }
 
 __global__ __launch_bounds__(256) void k_plan_chunks(int32_t B, int32_t nprobe, int32_t nlist, Work w) {
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (t >= (int64_t)B * nprobe) return;
-  const int q = (int)(t / nprobe), j = (int)(t % nprobe);
+  __shared__ int32_t sseg[kSelSegLds + 1];   // the query's stream offsets, when they fit
+  const int q = blockIdx.x, tid = threadIdx.x;
   const int32_t c0 = w.cstart[q], nch = w.cstart[q + 1] - c0;
   if (nch == 0) return;
   const int64_t len = w.qlen[q], ta = w.qtail[2 * (size_t)q];
   const int32_t na = w.qtail[2 * (size_t)q + 1], nb = nch - na;
   const int32_t *sq = w.seg + (size_t)q * (nprobe + 1);
-  const int64_t s0 = sq[j], s1 = sq[j + 1];
-  const int band = (int)(((int64_t)w.probes[(size_t)q * nprobe + j] * kPlanBands) / nlist);
-  // Each region [r0, r1) holds n chunks of ceil((r1 - r0) / n) items: none is empty, since that never
-  // exceeds the length chosen for the region.  Chunk i starts in this cluster when s0 <= r0 + i cl < s1.
-  auto cut = [&](int64_t r0, int64_t r1, int32_t n, int32_t first) {
-    if (n <= 0 || s1 <= r0 || s0 >= r1) return;
-    const int64_t cl = (r1 - r0 + n - 1) / n;
-    const int64_t from = s0 > r0 ? s0 - r0 : 0;
-    for (int64_t i = (from + cl - 1) / cl; i < n && r0 + i * cl < s1; ++i) {
-      const int64_t l0 = r0 + i * cl, l1 = l0 + cl < r1 ? l0 + cl : r1;
-      w.chunks[c0 + first + i] = Chunk{q, (int32_t)l0, (int32_t)l1, j};
-      w.cband[c0 + first + i] = band;
+  const int32_t *pq = w.probes + (size_t)q * nprobe;
+  const bool in_lds = nprobe <= kSelSegLds;
+  if (in_lds)
+    for (int i = tid; i <= nprobe; i += 256) sseg[i] = sq[i];
+  __syncthreads();
+  // Each region holds its chunks of ceil(region length / chunks) items: none is empty, since that never
+  // exceeds the length chosen for the region.
+  const int64_t cla = na > 0 ? (ta + na - 1) / na : 0;
+  const int64_t clb = nb > 0 ? (len - ta + nb - 1) / nb : 0;
+  for (int i = tid; i < nch; i += 256) {
+    int64_t l0, l1;
+    if (i < na) {
+      l0 = (int64_t)i * cla;
+      l1 = l0 + cla < ta ? l0 + cla : ta;
+    } else {
+      l0 = ta + (int64_t)(i - na) * clb;
+      l1 = l0 + clb < len ? l0 + clb : len;
     }
-  };
-  cut(0, ta, na, 0);
-  cut(ta, len, nb, na);
+    // the probed cluster holding stream offset l0: the largest j with seg[j] <= l0 (empty clusters
+    // before it share its offset and are skipped)
+    int lo = 0, hi = nprobe - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      const int32_t sv = in_lds ? sseg[mid] : sq[mid];
+      if (sv <= l0) lo = mid; else hi = mid - 1;
+    }
+    w.chunks[c0 + i] = Chunk{q, (int32_t)l0, (int32_t)l1, lo};
+    w.cband[c0 + i] = (int)(((int64_t)pq[lo] * kPlanBands) / nlist);
+  }
 }
 
 // The queue: a counting sort of the chunks by band.  Inside a band the chunks follow a scattered order
@@ -1441,8 +1453,7 @@ hipError_t launch_coarse_select(const DevIndex &ix, const int8_t *queries, const
                                 const SearchShape &sh, const Work &w, hipStream_t s) {
   k_coarse_select<<<sh.B, kSelThreads, 0, s>>>(ix, queries, masks, sh.B, sh.nprobe, w);
   k_plan_count<<<1, kSelThreads, 0, s>>>(sh.B, sh.P, w);
-  const int64_t pairs = (int64_t)sh.B * sh.nprobe;
-  if (pairs > 0) k_plan_chunks<<<(unsigned)((pairs + 255) / 256), 256, 0, s>>>(sh.B, sh.nprobe, ix.nlist, w);
+  k_plan_chunks<<<sh.B, 256, 0, s>>>(sh.B, sh.nprobe, ix.nlist, w);
   k_plan_order<<<1, kSelThreads, 0, s>>>(sh.B, w);
   return hipGetLastError();
 }
