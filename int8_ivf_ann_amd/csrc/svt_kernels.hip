@@ -351,8 +351,14 @@ __global__ __launch_bounds__(kSelThreads) void k_plan_count(int32_t B, int32_t P
     block_excl_scan<kSelThreads>(i < B ? w.qcost[i] : (int64_t)0, wave_tot64, &tot);
     total += tot;
   }
-  const int64_t tc_min = (total + 4 * (int64_t)P - 1) / (4 * (int64_t)P);
-  const int64_t Tc = tc_min > kMinChunkCost ? tc_min : kMinChunkCost;   // target cost of one chunk
+  // target cost of one chunk: four chunks per workgroup; when that is small, one chunk per workgroup
+  // (up to four minimum chunks), since a chunk's set-up and end then outweigh its items; never less than
+  // the minimum chunk
+  const int64_t tc_four = (total + 4 * (int64_t)P - 1) / (4 * (int64_t)P);
+  const int64_t tc_one = (total + P - 1) / P;
+  const int64_t tc_small = tc_one < 4 * kMinChunkCost ? tc_one : 4 * kMinChunkCost;
+  int64_t Tc = tc_four > tc_small ? tc_four : tc_small;
+  Tc = Tc > kMinChunkCost ? Tc : kMinChunkCost;
   int32_t carry = 0;
   for (int i0 = 0; i0 < B; i0 += kSelThreads) {
     const int i = i0 + tid;
