@@ -160,6 +160,13 @@ int svt_bloom_sign(const uint64_t *token_keys, int64_t n_items, int32_t tokens_p
  *   n_stages               receives the number of stages (6); n_searches the number of searches summed
  */
 int svt_profile_enable(int on);
+/*
+ * Environment variables read by svt_search on every call (tests use them to force rare paths):
+ *   SVT_PATH=query|grouped   the search path (default query)
+ *   SVT_POOL_CAP=n           grouped path: at most n candidate keys per query pool (overflow -> rescan)
+ *   SVT_GATHER_CAP=n         query path: at most n keys gathered per query for the merge (more -> the
+ *                            merge reads the chunks' slots)
+ */
 int svt_profile_read(float *stage_ms, const char **stage_names, int32_t max_stages, int32_t *n_stages,
                      int32_t *n_searches);
 

@@ -415,7 +415,12 @@ extern "C" int svt_search(const svt_index *ix, int32_t B, const int8_t *queries,
     w.pool_cnt = (uint32_t *)(base + L.pool_cnt);
     w.pool = (uint64_t *)(base + L.pool);
   }
-  SearchShape sh{B, nprobe, k, ix->scan_wgs, L.max_chunks, grouped, pool_cap, L.max_units, ix->gscan_wgs};
+  int32_t gather_cap = kGatherCap;
+  if (const char *gc = getenv("SVT_GATHER_CAP")) {   // fewer gathered keys, to exercise the merge from the slots
+    const long v = strtol(gc, nullptr, 10);
+    if (v >= 0 && v < gather_cap) gather_cap = (int32_t)v;
+  }
+  SearchShape sh{B, nprobe, k, ix->scan_wgs, L.max_chunks, grouped, pool_cap, L.max_units, ix->gscan_wgs, gather_cap};
 
   const int prof_mode = g_prof_on.load(std::memory_order_relaxed);
   const bool prof = prof_mode != 0 && g_prof.searches < kMaxProfiledSearches;

@@ -145,6 +145,7 @@ struct SearchShape {
   int32_t pool_cap;    // keys per query pool
   int32_t max_units;
   int32_t GP;          // persistent workgroups of the grouped scan
+  int32_t gather_cap;  // keys the merge gathers per query (at most kGatherCap)
 };
 
 // most chunks a search can produce.  The costs of the queries add up to at most 4 P Tc.  Without a tail

@@ -1164,7 +1164,7 @@ __global__ __launch_bounds__(64) void k_merge_bound(Work w, int32_t k) {
   }
 }
 
-__global__ __launch_bounds__(256) void k_merge_gather(Work w, int32_t B, int32_t k) {
+__global__ __launch_bounds__(256) void k_merge_gather(Work w, int32_t B, int32_t k, uint32_t cap) {
   constexpr int PER = kMaxK / 256;   // a slot holds at most k <= kMaxK keys: one pass of PER per thread
   __shared__ int wave_tot[256 / 64 + 1];
   __shared__ uint32_t sbase;
@@ -1193,7 +1193,7 @@ __global__ __launch_bounds__(256) void k_merge_gather(Work w, int32_t B, int32_t
     for (int u = 0; u < PER; ++u) {
       if (v[u] >= T && v[u] != 0ull) {
         const uint32_t o = base + (uint32_t)off++;
-        if (o < (uint32_t)kGatherCap) dst[o] = v[u];
+        if (o < cap) dst[o] = v[u];
       }
     }
     __syncthreads();   // sbase and wave_tot are reused for the next slot
@@ -1211,6 +1211,7 @@ struct MergeArgs {
   int32_t B, k, P;
   int32_t fallback;     // grouped search: only queries whose pool overflowed are merged here
   uint32_t pool_cap;
+  uint32_t gather_cap;  // keys gathered per query; a query with more is merged from its slots
   int64_t *out_ids;
   int32_t *out_scores;
   float *out_fscores;
@@ -1242,7 +1243,7 @@ __global__ __launch_bounds__(kSelThreads) void k_merge(MergeArgs a) {
   // The keys gathered above the query's final bound hold its top k.  When all of them were kept
   // (flat), they are the candidates, read as one array; otherwise the slots are read.
   const uint32_t gathered = a.fallback ? ~0u : a.w.mcnt[q];
-  const bool flat = gathered <= (uint32_t)kGatherCap;
+  const bool flat = gathered <= a.gather_cap;
   const uint64_t *gk = a.w.mkeys + (size_t)q * kGatherCap;
   // 1. counts and a proven lower bound on the k-th key: the largest smallest-key of a full slot
   unsigned long long lb = 0ull;
@@ -1509,11 +1510,11 @@ hipError_t launch_merge(const DevIndex &ix, const float *query_scales, const Sea
                         int64_t *out_ids, int32_t *out_scores, float *out_fscores, int32_t *out_counts,
                         hipStream_t s) {
   MergeArgs a{w, query_scales, ix.item_scale, sh.B, sh.k, sh.P, sh.grouped, (uint32_t)sh.pool_cap,
-              out_ids, out_scores, out_fscores, out_counts};
+              (uint32_t)sh.gather_cap, out_ids, out_scores, out_fscores, out_counts};
   if (!sh.grouped) {
     k_merge_bound<<<sh.B, 64, 0, s>>>(w, sh.k);
     const int g = sh.max_chunks < kMergeGatherWGs ? sh.max_chunks : kMergeGatherWGs;
-    k_merge_gather<<<g, 256, 0, s>>>(w, sh.B, sh.k);
+    k_merge_gather<<<g, 256, 0, s>>>(w, sh.B, sh.k, (uint32_t)sh.gather_cap);
   }
   k_merge<<<sh.B, kSelThreads, 0, s>>>(a);
   return hipGetLastError();

@@ -23,15 +23,21 @@ def svt():
 
 # Every case runs on both search paths: query by query, and grouped (each probed cluster read once for
 # all the queries probing it), the latter also with candidate pools so small that most queries overflow
-# and are redone query by query.  The library reads SVT_PATH / SVT_POOL_CAP at each search.
-@pytest.fixture(params=["query", "grouped", "grouped-overflow"], autouse=True)
+# and are redone query by query.  The query-by-query path also runs with no room for the keys its merge
+# gathers above each query's final bound, so that every query is merged from its chunks' slots.  The
+# library reads SVT_PATH / SVT_POOL_CAP / SVT_GATHER_CAP at each search.
+@pytest.fixture(params=["query", "query-slots", "grouped", "grouped-overflow"], autouse=True)
 def search_path(request, monkeypatch):
     path = request.param
-    monkeypatch.setenv("SVT_PATH", "query" if path == "query" else "grouped")
+    monkeypatch.setenv("SVT_PATH", "query" if path.startswith("query") else "grouped")
     if path == "grouped-overflow":
         monkeypatch.setenv("SVT_POOL_CAP", "64")
     else:
         monkeypatch.delenv("SVT_POOL_CAP", raising=False)
+    if path == "query-slots":
+        monkeypatch.setenv("SVT_GATHER_CAP", "0")
+    else:
+        monkeypatch.delenv("SVT_GATHER_CAP", raising=False)
     print(f"path {path}", flush=True)
     return path
 
