@@ -10,18 +10,18 @@ namespace svt {
 constexpr int kMaxK = 2048;          // largest top-k (SVT_MAX_K)
 constexpr int kScanThreads = 256;    // fused filter-score-select workgroup: 4 wave64
 #ifndef SVT_SCAN_GROUPS
-#define SVT_SCAN_GROUPS 4
+#define SVT_SCAN_GROUPS 5
 #endif
 constexpr int kScanGroups = SVT_SCAN_GROUPS;   // 64-item groups per wave per step
-constexpr int kScanStep = kScanThreads * kScanGroups;   // items per workgroup step (1024)
+constexpr int kScanStep = kScanThreads * kScanGroups;   // items per workgroup step (1280)
 #ifndef SVT_SCAN_OCC
 #define SVT_SCAN_OCC 3
 #endif
 #ifndef SVT_SCAN_ROW_BATCH
-#define SVT_SCAN_ROW_BATCH 32
+#define SVT_SCAN_ROW_BATCH 40
 #endif
 constexpr int kScanOcc = SVT_SCAN_OCC;              // query-by-query scan: waves per SIMD (workgroups per CU)
-constexpr int kScanRowBatch = SVT_SCAN_ROW_BATCH;   // rows a wave gathers together (at least one load per lane)
+constexpr int kScanRowBatch = SVT_SCAN_ROW_BATCH;   // rows a wave gathers together, rounded down to whole loads
 #ifndef SVT_LIST_CAP
 #define SVT_LIST_CAP 4096
 #endif

@@ -750,8 +750,9 @@ template <int LPR, int W>
 __global__ __launch_bounds__(kScanThreads, kScanOcc) void k_scan(ScanArgs a) {
   constexpr int D = 16 * LPR;
   constexpr int RPI = 64 / LPR;                   // rows covered by one 16-byte load per lane
-  constexpr int RB = RPI > kScanRowBatch ? RPI : kScanRowBatch;   // rows a wave requests together
-  constexpr int R = RB / RPI;                     // row loads per lane in one batch (<= 8)
+  constexpr int R0 = kScanRowBatch / RPI;
+  constexpr int R = R0 < 1 ? 1 : (R0 > 8 ? 8 : R0);   // row loads per lane in one batch (1 to 8)
+  constexpr int RB = R * RPI;                     // rows a wave requests together
   __shared__ ScanLds sm;
   const int tid = threadIdx.x, l = lane_id(), wv = tid / 64, sub = l % LPR;
   const int k = a.k;
