@@ -500,9 +500,9 @@ __global__ __launch_bounds__(kSelThreads) void k_plan_order(int32_t B, Work w) {
 // cuts every stream into chunks of about equal estimated cost and orders them by the clusters they start
 // in; persistent workgroups take chunks in that order with an atomic counter (one chunk ahead) and walk
 // each chunk in steps of kScanStep items.
-// In a step each wave loads 256 signatures (one 128- or 64-bit load per lane per 64-item group), tests
+// In a step each wave loads 64 kScanGroups signatures (one 128- or 64-bit load per lane per 64-item group), tests
 // (sig & mask) == mask, ballots the result and compacts the survivors' offsets into LDS; it then
-// gathers the rows of its survivors (LPR lanes per row, 16-byte loads, up to 64 rows at once) and
+// gathers the rows of its survivors (LPR lanes per row, 16-byte loads, about kScanRowBatch rows at once) and
 // scores them with v_dot4.  The next step's signatures and the query's current bound are requested
 // right after the rows, so a step costs one memory round trip.
 // A candidate enters the workgroup's LDS list if it scores at least the best proven bound known to the
