@@ -44,6 +44,7 @@ def parse():
     ap.add_argument("--workload", default="80m", help="preset: tiny, 1m, 10m, 80m, exh")
     ap.add_argument("--batch", type=int, default=None, help="queries per step (default: preset's largest)")
     ap.add_argument("--batches", type=int, default=4, help="distinct query batches cycled over the steps")
+    ap.add_argument("--path", default="auto", choices=["auto", "query", "tile"], help="search path")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU-seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic", default=None, help="traffic summary (profiles/); default by workload")
@@ -70,9 +71,24 @@ def algorithmic_bytes(cat, sigs_sorted, offsets, queries, masks, nprobe, W, d):
     """Bytes the scan must move for one batch when every probed cluster is read once per batch:
     signatures of every item of the union of probed clusters, plus the row of every item eligible for
     at least one query probing its cluster.  Also returns the number of eligible (query, item) pairs."""
+    nlist = cat.centroids.shape[0]
+    if nprobe == nlist:
+        # every query probes every cluster: one pass over the catalogue per query
+        need = np.zeros(sigs_sorted.shape[0], bool)
+        pairs = 0
+        for b in range(queries.shape[0]):
+            ok = np.ones(sigs_sorted.shape[0], bool)
+            for w in range(W):
+                ok &= (sigs_sorted[:, w] & masks[b, w]) == masks[b, w]
+            pairs += int(ok.sum())
+            need |= ok
+            if b % 8 == 7:
+                log(f"[bench] bookkeeping: {b + 1} of {queries.shape[0]} queries")
+        sig_bytes = sigs_sorted.shape[0] * 8 * W
+        rows = int(need.sum())
+        return sig_bytes + rows * d, sig_bytes, rows * d, pairs, nlist
     C = cat.centroids.astype(np.float64)
     S = queries.astype(np.float64) @ C.T            # exact: |score| < 2^21
-    nlist = C.shape[0]
     cl_q = {}
     for b in range(queries.shape[0]):
         s = S[b]
@@ -103,8 +119,9 @@ def main():
         print(kernel_source_hash())
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}); "
-              "the sharding design is described in DESIGN.md", file=sys.stderr)
+        print(f"bench.py runs on one GPU only: the library has no multi-GPU path (asked for --gpus {args.gpus}); "
+              "an index would shard by cluster ranges, each GPU scanning its own clusters for every query "
+              "and the per-GPU top-k lists merged afterwards", file=sys.stderr)
         sys.exit(2)
     import torch
     import synth
@@ -132,7 +149,9 @@ def main():
         masks = np.stack([svt.svt_bloom_mask(qs.required(b), h, W) for b in range(B)])
         batches.append(dict(q=qs.queries, m=masks, q_d=torch.from_numpy(qs.queries).cuda(),
                             m_d=torch.from_numpy(masks.view(np.int64)).cuda()))
-    ws = ix.workspace(B, nprobe, k)
+    opts = svt.make_options(args.path)
+    ws = ix.workspace(B, nprobe, k, opts)
+    log(f"[bench] workspace {ws.numel() / 2**20:.1f} MiB (path {args.path})")
     outs = dict(out_ids=torch.empty((B, k), dtype=torch.int64, device="cuda"),
                 out_scores=torch.empty((B, k), dtype=torch.int32, device="cuda"),
                 out_fscores=torch.empty((B, k), dtype=torch.float32, device="cuda"),
@@ -142,7 +161,7 @@ def main():
     def step(i):
         bt = batches[i % len(batches)]
         svt.svt_search(ix.handle, bt["q_d"], bt["m_d"], nprobe, k, workspace=ws, out_stats=stats[i % len(batches)],
-                       **outs)
+                       opts=opts, **outs)
 
     for i in range(max(args.warmup, len(batches))):
         step(i)

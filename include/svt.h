@@ -81,23 +81,73 @@ typedef struct {
  */
 int svt_index_upload(const svt_index_desc *desc, void *hip_stream, svt_index **out);
 
-/* svt_index_free - release an index and its device memory (synchronises the device first).
- * NULL is accepted (no-op).  SVT_ESTATE if ix is not a live index from svt_index_upload. */
-int svt_index_free(svt_index *ix);
+/* svt_index_free - release an index and its device memory.
+ * hip_stream: the stream the caller's searches on this index ran on (NULL = the default stream); the
+ * call synchronises that stream before freeing.  Searches enqueued on other streams must have
+ * completed (the caller synchronises them); the device as a whole is not synchronised.
+ * NULL ix is accepted (no-op).  SVT_ESTATE if ix is not a live index from svt_index_upload;
+ * SVT_EDEVICE if the stream synchronisation fails (the index is then still freed). */
+int svt_index_free(svt_index *ix, void *hip_stream);
 
 /* svt_index_info - shape of an uploaded index; any output pointer may be NULL. */
 int svt_index_info(const svt_index *ix, int64_t *n_items, int32_t *dim, int32_t *sig_words, int32_t *nlist);
 
 /*
- * svt_search_workspace_size - bytes of device workspace svt_search needs for these sizes.
- * Returns 0 if the arguments are invalid (see svt_search).  The size never depends on query values.
+ * Search paths.  Every path returns the same, exact result (tested element by element); they differ in
+ * how the probed clusters are read.
+ *   SVT_PATH_AUTO   chosen from the batch shape alone (never from query values): the tile path for
+ *                   batches whose queries share probed clusters, the query path otherwise
+ *   SVT_PATH_QUERY  query by query: each query's probed clusters are read for that query, an exact
+ *                   top-k is kept per workgroup in LDS and merged ("SilverTorch - Index as Model":
+ *                   probe the most promising clusters first, filter only inside them, score only the
+ *                   survivors)
+ *   SVT_PATH_TILE   each probed cluster is read once per batch for every query that probes it
+ *                   (the union of the batch's probed clusters is streamed once); with nprobe == nlist
+ *                   the catalogue is streamed once and scored for the whole batch with int8 MFMA.
+ *                   Candidates at or above a per-query threshold estimated from a sample of the
+ *                   query's items are kept in per-query pools; a query whose pool holds fewer than k
+ *                   candidates (with a threshold above the minimum) or overflows is redone on the query
+ *                   path, so the result stays exact whatever the data.
  */
-size_t svt_search_workspace_size(const svt_index *ix, int32_t n_queries, int32_t nprobe, int32_t k);
+enum { SVT_PATH_AUTO = 0, SVT_PATH_QUERY = 1, SVT_PATH_TILE = 2 };
+
+/* svt_search_options.flags */
+#define SVT_OPT_MERGE_FROM_SLOTS 1u  /* query path: the merge reads every chunk's slot instead of the keys
+                                        gathered above each query's final bound (a test of that branch)  */
+#define SVT_OPT_FORCE_REDO 2u        /* tile path: every query's threshold is set above any score, so
+                                        every query with an eligible item is redone on the query path
+                                        (a test of that branch)                                         */
+
+/*
+ * Options of one search.  A NULL pointer, or a zero-initialised struct, selects the defaults.  The
+ * workspace size depends on the options: pass the same options to svt_search_workspace_size and
+ * svt_search.
+ *   path       SVT_PATH_AUTO (default), SVT_PATH_QUERY or SVT_PATH_TILE
+ *   pool_keys  tile path: candidate keys kept per query (0 = default, 16 k rounded up to 4096); a
+ *              smaller value makes more pools overflow (their queries are redone)
+ *   flags      OR of SVT_OPT_* above
+ * Errors (returned by the calls that take the options): SVT_EINVAL for an unknown path, a negative
+ * pool_keys, unknown flag bits or non-zero reserved words.
+ */
+typedef struct {
+  int32_t path;
+  int32_t pool_keys;
+  uint32_t flags;
+  int32_t reserved[5];   /* must be 0 */
+} svt_search_options;
+
+/*
+ * svt_search_workspace_size - bytes of device workspace svt_search needs for these sizes and options.
+ * Returns 0 if the arguments are invalid (see svt_search; svt_last_error() then says why).  The size
+ * never depends on query values.
+ */
+size_t svt_search_workspace_size(const svt_index *ix, int32_t n_queries, int32_t nprobe, int32_t k,
+                                 const svt_search_options *opts);
 
 /*
  * svt_search - batched fused search (steps 1-4 above), asynchronous on hip_stream.
- *   queries       device, [n_queries][dim] int8, row-major
- *   masks         device, [n_queries][sig_words] uint64 request masks (see svt_bloom_mask)
+ *   queries       device, [n_queries][dim] int8, row-major, 16-byte aligned
+ *   masks         device, [n_queries][sig_words] uint64 request masks (see svt_bloom_mask), 8-byte aligned
  *   query_scales  device, [n_queries] float > 0, or NULL to use the index's item_scale
  *   nprobe        1 <= nprobe <= nlist
  *   k             1 <= k <= SVT_MAX_K
@@ -108,19 +158,21 @@ size_t svt_search_workspace_size(const svt_index *ix, int32_t n_queries, int32_t
  *                 clusters)
  *   out_stats     device, [n_queries][2] int64 or NULL: items scanned in the probed clusters, items
  *                 that passed the filter and were scored
- *   workspace     device, at least svt_search_workspace_size(ix, n_queries, nprobe, k) bytes, 256-byte
- *                 aligned; contents on entry are ignored, contents on exit are unspecified
- * Result rows are sorted by (score desc, id asc) and identical for any batch composition.
+ *   opts          search options or NULL (defaults)
+ *   workspace     device, at least svt_search_workspace_size(ix, n_queries, nprobe, k, opts) bytes,
+ *                 256-byte aligned; contents on entry are ignored, contents on exit are unspecified
+ * Result rows are sorted by (score desc, id asc) and identical for any batch composition and path.
  * n_queries == 0 returns SVT_OK without enqueuing anything.
  * Errors: SVT_EINVAL (NULL required pointer, n_queries < 0 or > 65535, nprobe or k out of range,
- * workspace too small or misaligned), SVT_ESTATE (freed index), SVT_EDEVICE (launch failure).
+ * misaligned queries, masks or workspace, workspace too small, invalid options), SVT_ESTATE (freed
+ * index), SVT_EDEVICE (launch failure).  On any error nothing is enqueued and no output is written.
  * Concurrency: the index is read-only; concurrent calls are safe if each uses its own workspace and
  * outputs.  Outputs are valid once hip_stream has been synchronised.
  */
 int svt_search(const svt_index *ix, int32_t n_queries, const int8_t *queries, const uint64_t *masks,
                const float *query_scales, int32_t nprobe, int32_t k, int64_t *out_ids, int32_t *out_scores,
-               float *out_fscores, int32_t *out_counts, int64_t *out_stats, void *workspace,
-               size_t workspace_bytes, void *hip_stream);
+               float *out_fscores, int32_t *out_counts, int64_t *out_stats, const svt_search_options *opts,
+               void *workspace, size_t workspace_bytes, void *hip_stream);
 
 /* svt_last_error - message of the last failed call on this thread ("" if none). */
 const char *svt_last_error(void);
@@ -149,24 +201,22 @@ int svt_bloom_sign(const uint64_t *token_keys, int64_t n_items, int32_t tokens_p
 /*
  * Stage timing.  While enabled (per process), svt_search records HIP events on hip_stream around its
  * stages (the calling thread keeps up to 100000 searches).  svt_profile_read synchronises on the last
- * recorded event and returns, for each stage in launch order ("coarse", "select", "plan", "scan",
- * "fallback", "merge"), the elapsed milliseconds summed over every search this thread recorded since
- * the previous read, then forgets them.  "plan" and "fallback" hold work only on the grouped path (set
- * by the environment variable SVT_PATH=grouped; SVT_PATH=query forces the query-by-query path); on the
- * query-by-query path they measure only the gap between two event records.
+ * recorded event and returns, for each stage in launch order, the elapsed milliseconds summed over every
+ * search this thread recorded since the previous read, then forgets them.  Stages:
+ *   "coarse"   centroid scores
+ *   "select"   top-nprobe per query, stream layout, samples and thresholds, query-path work list
+ *   "plan"     tile path: the batch's probed clusters and the queries of each
+ *   "scan"     the fused filter -> score -> select kernel of the path taken (k_scan, k_tscan or k_xscan
+ *              with its sample pass)
+ *   "fallback" tile path: redo of the queries whose pools missed (work list, k_scan, merge)
+ *   "merge"    the final top-k per query
+ * Stages a path does not run measure only the gap between two event records.
  *   on      0 off (default), 1 every stage (seven event records per search), 2 the scan stage only
  *           (two event records per search; the other stages read 0); any other value: SVT_EINVAL
  *   stage_ms, stage_names  host arrays of max_stages entries (either may be NULL)
  *   n_stages               receives the number of stages (6); n_searches the number of searches summed
  */
 int svt_profile_enable(int on);
-/*
- * Environment variables read by svt_search on every call (tests use them to force rare paths):
- *   SVT_PATH=query|grouped   the search path (default query)
- *   SVT_POOL_CAP=n           grouped path: at most n candidate keys per query pool (overflow -> rescan)
- *   SVT_GATHER_CAP=n         query path: at most n keys gathered per query for the merge (more -> the
- *                            merge reads the chunks' slots)
- */
 int svt_profile_read(float *stage_ms, const char **stage_names, int32_t max_stages, int32_t *n_stages,
                      int32_t *n_searches);
 

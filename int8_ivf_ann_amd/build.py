@@ -18,7 +18,7 @@ def build(verbose: bool = False) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     with tempfile.TemporaryDirectory(prefix="svt_build_") as td:
         objs = []
-        for src, dev in (("svt_kernels.hip", True), ("svt_group.hip", True), ("svt_api.cpp", False)):
+        for src, dev in (("svt_kernels.hip", True), ("svt_tile.hip", True), ("svt_api.cpp", False)):
             obj = os.path.join(td, src + ".o")
             cmd = [hipcc] + COMMON + ["-c", os.path.join(CSRC, src), "-o", obj]
             if dev:

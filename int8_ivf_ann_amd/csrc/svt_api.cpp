@@ -82,10 +82,9 @@ struct svt_index {
   int32_t *d_perm = nullptr;
   int32_t *d_offsets = nullptr;
   int8_t *d_centroids = nullptr;
-  int32_t scan_wgs;                 // persistent workgroups of the fused kernel
-  int32_t gscan_wgs;                // persistent workgroups of the grouped scan
-  int64_t n_tiles;                  // sum over clusters of ceil(size / kGTile)
-  int64_t max_cluster_tiles;        // tiles of the largest cluster
+  int32_t scan_wgs;                 // persistent workgroups of the query-by-query scan
+  int32_t tscan_wgs;                // persistent workgroups of the tile scan
+  int32_t xscan_wgs;                // workgroups of the exhaustive MFMA scan
 };
 
 // ------------------------------------------------------------------------------------------------
@@ -138,13 +137,6 @@ extern "C" int svt_index_upload(const svt_index_desc *d, void *hip_stream, svt_i
   svt_index *ix = new (std::nothrow) svt_index();
   if (!ix) return fail(SVT_ENOMEM, "svt_index_upload: host allocation");
   ix->magic = kMagic;
-  ix->n_tiles = 0;
-  ix->max_cluster_tiles = 0;
-  for (int32_t c = 0; c < nlist; ++c) {
-    const int64_t t = (offsets[c + 1] - offsets[c] + kGTile - 1) / kGTile;
-    ix->n_tiles += t;
-    ix->max_cluster_tiles = std::max(ix->max_cluster_tiles, t);
-  }
   hipError_t e = hipGetDevice(&ix->device);
   if (e != hipSuccess) { delete ix; return fail_hip(e, "hipGetDevice"); }
   hipDeviceProp_t prop;
@@ -154,8 +146,10 @@ extern "C" int svt_index_upload(const svt_index_desc *d, void *hip_stream, svt_i
     // one resident wave of persistent scan workgroups
     const int per_cu = std::max(1, scan_blocks_per_cu(dim, W));
     ix->scan_wgs = std::min(kMaxScanWGs, std::max(64, prop.multiProcessorCount * per_cu));
-    const int g_per_cu = std::max(1, gscan_blocks_per_cu(dim, W));
-    ix->gscan_wgs = std::min(kMaxScanWGs, std::max(64, prop.multiProcessorCount * g_per_cu));
+    const int t_per_cu = std::max(1, tscan_blocks_per_cu(dim, W));
+    ix->tscan_wgs = std::min(kMaxScanWGs, std::max(64, prop.multiProcessorCount * t_per_cu));
+    const int x_per_cu = std::max(1, xscan_blocks_per_cu(dim, W));
+    ix->xscan_wgs = std::min(kMaxScanWGs, std::max(64, prop.multiProcessorCount * x_per_cu));
   }
 
   int32_t *d_pos_of = nullptr;
@@ -224,7 +218,7 @@ extern "C" int svt_index_upload(const svt_index_desc *d, void *hip_stream, svt_i
   return SVT_OK;
 }
 
-extern "C" int svt_index_free(svt_index *ix) {
+extern "C" int svt_index_free(svt_index *ix, void *hip_stream) {
   g_err.clear();
   if (!ix) return SVT_OK;
   {
@@ -232,10 +226,12 @@ extern "C" int svt_index_free(svt_index *ix) {
     if (!g_live.count(ix) || ix->magic != kMagic) return fail(SVT_ESTATE, "svt_index_free: not a live index");
     g_live.erase(ix);
   }
-  (void)hipDeviceSynchronize();
+  // the caller's searches on this index ran on hip_stream: they end before the memory is released
+  const hipError_t e = hipStreamSynchronize((hipStream_t)hip_stream);
   free_index_memory(ix);
   ix->magic = 0;
   delete ix;
+  if (e != hipSuccess) return fail_hip(e, "svt_index_free: hipStreamSynchronize");
   return SVT_OK;
 }
 
@@ -255,33 +251,71 @@ extern "C" int svt_index_info(const svt_index *ix, int64_t *n_items, int32_t *di
 namespace {
 
 struct Layout {
-  size_t coarse_scores, probes, seg, pb, qlen, qcost, qtail, cstart, chunks, order, cband, thr, hlo, hshift, ghist, counter, slot_cnt,
-      slot_min, slot_keys, mbound, mcnt, mkeys, stats;
-  size_t gcnt, gfill, gstart, ustart, gq, units, pool_cnt, pool;   // grouped path (0 bytes when impossible)
+  size_t coarse_scores, probes, seg, pb, qlen, qcost, qtail, cstart, chunks, order, cband, thr, hlo, hshift, ghist, counter,
+      slot_cnt, slot_min, slot_keys, mbound, mcnt, mkeys, stats;
+  // tile and exhaustive paths (absent on the query path)
+  size_t sthr, redo, pool_cnt, pool, gcnt, gfill, gstart, estart, uoff, mrec, entries, ctab, thdr, tblk, sbuf;
+  size_t qdens, clog, ccost, cstart_u;
   size_t total;
-  int32_t max_chunks;
-  int32_t max_units;    // 0: the grouped path does not fit this shape
-  int32_t pool_cap;
+  SearchShape sh;
 };
 
-// Grouped searches: candidate pools take at most kPoolBudget bytes in all, at least 16 k and at most
-// kPoolMaxKeys keys per query.  Shapes whose work list would not fit an int32 run query by query.
-constexpr size_t kPoolBudget = size_t(1) << 30;
-constexpr int64_t kPoolMaxKeys = int64_t(1) << 22;
-// The grouped path is selected explicitly (SVT_PATH=grouped); by default every batch runs query by
-// query, which is faster on every workload measured so far (it keeps an exact top-k per workgroup in LDS,
-// the grouped path sends every candidate above the query's bound to HBM).
-constexpr int32_t kGroupedMinBatch = 1 << 30;
+// Batches of at least this many queries take the tile path by default (their queries share enough
+// probed clusters for one read per batch to pay for the work list and the pools).
+constexpr int32_t kTileMinBatch = 32;
+// The union stream is indexed with 32-bit offsets.
+constexpr int64_t kMaxUnion = (int64_t(1) << 31) - (int64_t(1) << 20);
 
-Layout layout(const svt_index *ix, int32_t B, int32_t nprobe, int32_t k) {
+bool tile_fits(const svt_index *ix, int32_t B, int32_t nprobe) {
+  const int64_t blocks = ((int64_t)B + kTMembers - 1) / kTMembers;
+  return ix->dev.n_items * blocks < kMaxUnion && (int64_t)B * nprobe < kMaxUnion;
+}
+
+int resolve_path(const svt_index *ix, int32_t B, int32_t nprobe, const svt_search_options *o) {
+  const int want = o ? o->path : SVT_PATH_AUTO;
+  if (want == SVT_PATH_QUERY || ix->dev.n_items == 0) return kPathQuery;
+  const bool exh = nprobe == ix->dev.nlist;
+  if (want == SVT_PATH_TILE) {
+    if (exh) return kPathExh;
+    return tile_fits(ix, B, nprobe) ? kPathTile : kPathQuery;
+  }
+  if (exh && B >= 2) return kPathExh;
+  if (B >= kTileMinBatch && tile_fits(ix, B, nprobe)) return kPathTile;
+  return kPathQuery;
+}
+
+// SVT_OK or SVT_EINVAL (message set)
+int check_options(const svt_search_options *o, const char *who) {
+  if (!o) return SVT_OK;
+  if (o->path != SVT_PATH_AUTO && o->path != SVT_PATH_QUERY && o->path != SVT_PATH_TILE)
+    return fail(SVT_EINVAL, "%s: unknown path %d", who, o->path);
+  if (o->pool_keys < 0) return fail(SVT_EINVAL, "%s: pool_keys %d < 0", who, o->pool_keys);
+  if (o->flags & ~(SVT_OPT_MERGE_FROM_SLOTS | SVT_OPT_FORCE_REDO))
+    return fail(SVT_EINVAL, "%s: unknown flag bits 0x%x", who, o->flags);
+  for (int i = 0; i < 5; ++i)
+    if (o->reserved[i] != 0) return fail(SVT_EINVAL, "%s: reserved word %d is not 0", who, i);
+  return SVT_OK;
+}
+
+Layout layout(const svt_index *ix, int32_t B, int32_t nprobe, int32_t k, const svt_search_options *o) {
   Layout L{};
   const size_t nlist = (size_t)ix->dev.nlist;
-  L.max_chunks = max_chunks_for(B, ix->scan_wgs);
-  const size_t C = (size_t)L.max_chunks;
-  size_t o = 0;
+  SearchShape &sh = L.sh;
+  sh.B = B;
+  sh.nprobe = nprobe;
+  sh.k = k;
+  sh.P = ix->scan_wgs;
+  sh.max_chunks = max_chunks_for(B, ix->scan_wgs);
+  sh.path = resolve_path(ix, B, nprobe, o);
+  sh.gather_cap = (o && (o->flags & SVT_OPT_MERGE_FROM_SLOTS)) ? 0 : kGatherCap;
+  sh.force_redo = (o && (o->flags & SVT_OPT_FORCE_REDO)) ? 1 : 0;
+  sh.TP = ix->tscan_wgs;
+  sh.XP = ix->xscan_wgs;
+  const size_t C = (size_t)sh.max_chunks;
+  size_t off = 0;
   auto take = [&](size_t bytes) {
-    size_t at = o;
-    o += align256(bytes);
+    size_t at = off;
+    off += align256(bytes);
     return at;
   };
   L.coarse_scores = take((size_t)B * nlist * sizeof(int32_t));
@@ -299,7 +333,7 @@ Layout layout(const svt_index *ix, int32_t B, int32_t nprobe, int32_t k) {
   L.hlo = take((size_t)B * sizeof(int32_t));
   L.hshift = take((size_t)B * sizeof(int32_t));
   L.ghist = take((size_t)B * kQHistBins * sizeof(uint32_t));
-  L.counter = take(3 * sizeof(uint32_t));
+  L.counter = take(8 * sizeof(uint32_t));
   L.slot_cnt = take(C * sizeof(int32_t));
   L.slot_min = take(C * sizeof(uint64_t));
   L.slot_keys = take(C * (size_t)k * sizeof(uint64_t));
@@ -307,64 +341,58 @@ Layout layout(const svt_index *ix, int32_t B, int32_t nprobe, int32_t k) {
   L.mcnt = take((size_t)B * sizeof(uint32_t));
   L.mkeys = take((size_t)B * kGatherCap * sizeof(uint64_t));
   L.stats = take((size_t)B * 2 * sizeof(int64_t));
-  // grouped path: units <= sum_c tiles_c * ceil(queries_c / kGMax), bounded two ways
-  const int64_t gpc = ((int64_t)B + kGMax - 1) / kGMax;
-  const int64_t u1 = ix->n_tiles * gpc;
-  const int64_t u2 = ix->n_tiles + ix->max_cluster_tiles * (((int64_t)B * nprobe + kGMax - 1) / kGMax);
-  const int64_t mu = std::max<int64_t>(1, std::min(u1, u2));
-  if (mu < (int64_t(1) << 31) - 256) {
-    L.max_units = (int32_t)mu;
-    const int64_t per_q = (int64_t)(kPoolBudget / 8 / (size_t)std::max(B, 1));
-    L.pool_cap = (int32_t)std::min(kPoolMaxKeys, std::max<int64_t>(16 * (int64_t)k, per_q));
+  if (sh.path != kPathQuery) {
+    const int64_t def = std::max<int64_t>(4096, ((int64_t)16 * k + 4095) / 4096 * 4096);
+    sh.pool_cap = (int32_t)((o && o->pool_keys > 0) ? o->pool_keys : def);
+    L.sthr = take((size_t)B * sizeof(int32_t));
+    L.redo = take((size_t)B * sizeof(int32_t));
+    L.pool_cnt = take((size_t)B * sizeof(uint32_t));
+    L.pool = take((size_t)B * (size_t)sh.pool_cap * sizeof(uint64_t));
+  }
+  if (sh.path == kPathTile) {
+    const int64_t blocks = ((int64_t)B + kTMembers - 1) / kTMembers;
+    sh.max_entries = (int32_t)std::max<int64_t>(1, std::min<int64_t>((int64_t)nlist * blocks, (int64_t)B * nprobe));
+    sh.max_tchunks = kTChunksPerWG * sh.TP + 2;
     L.gcnt = take(nlist * sizeof(int32_t));
     L.gfill = take(nlist * sizeof(int32_t));
     L.gstart = take((nlist + 1) * sizeof(int32_t));
-    L.ustart = take((nlist + 1) * sizeof(int32_t));
-    L.gq = take((size_t)B * nprobe * sizeof(int32_t));
-    L.units = take((size_t)L.max_units * sizeof(GUnit));
-    L.pool_cnt = take((size_t)B * sizeof(uint32_t));
-    L.pool = take((size_t)B * (size_t)L.pool_cap * sizeof(uint64_t));
+    L.estart = take((nlist + 1) * sizeof(int32_t));
+    L.uoff = take(nlist * sizeof(int32_t));
+    L.mrec = take((size_t)B * nprobe * sizeof(MRec));
+    L.entries = take((size_t)sh.max_entries * sizeof(UEntry));
+    L.ctab = take((size_t)sh.max_tchunks * sizeof(int32_t));
+    L.thdr = take(4 * sizeof(int32_t));
+    L.tblk = take(4 * kMaxPlanBlocks * sizeof(int64_t));
+    L.qdens = take((size_t)B * sizeof(float));
+    L.clog = take(nlist * sizeof(float));
+    L.ccost = take((nlist + 1) * sizeof(int64_t));
+    L.cstart_u = take((size_t)(sh.max_tchunks + 1) * sizeof(int32_t));
   }
-  L.total = o;
+  if (sh.path == kPathExh) {
+    const int64_t N = ix->dev.n_items;
+    const int64_t points = (N + kXStride - 1) / kXStride;   // sample pass: every kXStride-th position
+    sh.n_sblocks = (int32_t)((points + 63) / 64);            // runs of 64 points
+    sh.scap = 16 * sh.n_sblocks;                             // slots per query: one per lane and run
+    L.sbuf = take((size_t)B * (size_t)sh.scap * sizeof(int32_t));
+  }
+  L.total = off;
   return L;
 }
 
 // SVT_OK or the error code (message set)
-int check_search_args(const svt_index *ix, int32_t B, int32_t nprobe, int32_t k, const char *who) {
+int check_search_args(const svt_index *ix, int32_t B, int32_t nprobe, int32_t k, const svt_search_options *o,
+                      const char *who) {
   if (!ix || !is_live(ix) || ix->magic != kMagic) return fail(SVT_ESTATE, "%s: not a live index", who);
   if (B < 0 || B > 65535) return fail(SVT_EINVAL, "%s: n_queries %d out of [0, 65535]", who, B);
   if (nprobe < 1 || nprobe > ix->dev.nlist) return fail(SVT_EINVAL, "%s: nprobe %d out of [1, %d]", who, nprobe, ix->dev.nlist);
   if (k < 1 || k > SVT_MAX_K) return fail(SVT_EINVAL, "%s: k %d out of [1, %d]", who, k, SVT_MAX_K);
-  return SVT_OK;
+  return check_options(o, who);
 }
 
-}  // namespace
-
-extern "C" size_t svt_search_workspace_size(const svt_index *ix, int32_t n_queries, int32_t nprobe, int32_t k) {
-  g_err.clear();
-  if (check_search_args(ix, n_queries, nprobe, k, "svt_search_workspace_size") != SVT_OK) return 0;
-  return layout(ix, n_queries, nprobe, k).total;
-}
-
-extern "C" int svt_search(const svt_index *ix, int32_t B, const int8_t *queries, const uint64_t *masks,
-                          const float *query_scales, int32_t nprobe, int32_t k, int64_t *out_ids, int32_t *out_scores,
-                          float *out_fscores, int32_t *out_counts, int64_t *out_stats, void *workspace,
-                          size_t workspace_bytes, void *hip_stream) {
-  g_err.clear();
-  const int rc = check_search_args(ix, B, nprobe, k, "svt_search");
-  if (rc != SVT_OK) return rc;
-  if (B == 0) return SVT_OK;
-  if (!queries || !masks || !out_ids || !out_scores || !workspace)
-    return fail(SVT_EINVAL, "svt_search: NULL queries, masks, out_ids, out_scores or workspace");
-  if (((uintptr_t)workspace & 255) != 0) return fail(SVT_EINVAL, "svt_search: workspace not 256-byte aligned");
-  if (((uintptr_t)queries & 15) != 0) return fail(SVT_EINVAL, "svt_search: queries not 16-byte aligned");
-  if (((uintptr_t)masks & 7) != 0) return fail(SVT_EINVAL, "svt_search: masks not 8-byte aligned");
-  const Layout L = layout(ix, B, nprobe, k);
-  if (workspace_bytes < L.total)
-    return fail(SVT_EINVAL, "svt_search: workspace %zu bytes < required %zu", workspace_bytes, L.total);
-  hipStream_t s = (hipStream_t)hip_stream;
+Work carve(const Layout &L, void *workspace, int64_t *out_stats) {
   char *base = (char *)workspace;
-  Work w;
+  const SearchShape &sh = L.sh;
+  Work w{};
   w.coarse_scores = (int32_t *)(base + L.coarse_scores);
   w.probes = (int32_t *)(base + L.probes);
   w.seg = (int32_t *)(base + L.seg);
@@ -388,40 +416,36 @@ extern "C" int svt_search(const svt_index *ix, int32_t B, const int8_t *queries,
   w.mcnt = (uint32_t *)(base + L.mcnt);
   w.mkeys = (uint64_t *)(base + L.mkeys);
   w.stats = out_stats ? out_stats : (int64_t *)(base + L.stats);
-  // path: SVT_PATH=query|grouped forces one; otherwise batches of kGroupedMinBatch or more queries are
-  // grouped
-  int grouped = B >= kGroupedMinBatch ? 1 : 0;
-  if (const char *pe = getenv("SVT_PATH")) {
-    if (!strcmp(pe, "query")) grouped = 0;
-    else if (!strcmp(pe, "grouped")) grouped = 1;
-  }
-  if (L.max_units == 0) grouped = 0;
-  int32_t pool_cap = L.pool_cap;
-  if (const char *pc = getenv("SVT_POOL_CAP")) {   // smaller pools, to exercise the overflow fallback
-    const long v = strtol(pc, nullptr, 10);
-    if (v >= 1 && v < pool_cap) pool_cap = (int32_t)v;
-  }
-  w.gcnt = w.gfill = w.gstart = w.ustart = w.gq = nullptr;
-  w.units = nullptr;
-  w.pool_cnt = nullptr;
-  w.pool = nullptr;
-  if (grouped) {
-    w.gcnt = (int32_t *)(base + L.gcnt);
-    w.gfill = (int32_t *)(base + L.gfill);
-    w.gstart = (int32_t *)(base + L.gstart);
-    w.ustart = (int32_t *)(base + L.ustart);
-    w.gq = (int32_t *)(base + L.gq);
-    w.units = (GUnit *)(base + L.units);
+  if (sh.path != kPathQuery) {
+    w.sthr = (int32_t *)(base + L.sthr);
+    w.redo = (int32_t *)(base + L.redo);
     w.pool_cnt = (uint32_t *)(base + L.pool_cnt);
     w.pool = (uint64_t *)(base + L.pool);
   }
-  int32_t gather_cap = kGatherCap;
-  if (const char *gc = getenv("SVT_GATHER_CAP")) {   // fewer gathered keys, to exercise the merge from the slots
-    const long v = strtol(gc, nullptr, 10);
-    if (v >= 0 && v < gather_cap) gather_cap = (int32_t)v;
+  if (sh.path == kPathTile) {
+    w.gcnt = (int32_t *)(base + L.gcnt);
+    w.gfill = (int32_t *)(base + L.gfill);
+    w.gstart = (int32_t *)(base + L.gstart);
+    w.estart = (int32_t *)(base + L.estart);
+    w.uoff = (int32_t *)(base + L.uoff);
+    w.mrec = (MRec *)(base + L.mrec);
+    w.entries = (UEntry *)(base + L.entries);
+    w.ctab = (int32_t *)(base + L.ctab);
+    w.thdr = (int32_t *)(base + L.thdr);
+    w.tblk = (int64_t *)(base + L.tblk);
+    w.qdens = (float *)(base + L.qdens);
+    w.clog = (float *)(base + L.clog);
+    w.ccost = (int64_t *)(base + L.ccost);
+    w.cstart_u = (int32_t *)(base + L.cstart_u);
   }
-  SearchShape sh{B, nprobe, k, ix->scan_wgs, L.max_chunks, grouped, pool_cap, L.max_units, ix->gscan_wgs, gather_cap};
+  if (sh.path == kPathExh) w.sbuf = (int32_t *)(base + L.sbuf);
+  return w;
+}
 
+// Enqueue the search of a validated call on stream s.
+int enqueue_search(const svt_index *ix, const SearchShape &sh, const Work &w, const int8_t *queries,
+                   const uint64_t *masks, const float *query_scales, int64_t *out_ids, int32_t *out_scores,
+                   float *out_fscores, int32_t *out_counts, hipStream_t s) {
   const int prof_mode = g_prof_on.load(std::memory_order_relaxed);
   const bool prof = prof_mode != 0 && g_prof.searches < kMaxProfiledSearches;
   ProfState &ps = g_prof;
@@ -443,38 +467,79 @@ extern "C" int svt_search(const svt_index *ix, int32_t B, const int8_t *queries,
     if (!prof || (prof_mode == 2 && i != 3 && i != 4)) return hipSuccess;
     return hipEventRecord(ps.pool[ev0 + i], s);
   };
+  const DevIndex &dx = ix->dev;
   hipError_t e;
   if ((e = mark()) != hipSuccess) return fail_hip(e, "event");
-  if ((e = launch_coarse_keys(ix->dev, queries, B, w, s)) != hipSuccess) return fail_hip(e, "launch coarse_keys");
+  if ((e = launch_coarse_keys(dx, queries, sh.B, w, s)) != hipSuccess) return fail_hip(e, "launch coarse_keys");
   if ((e = mark()) != hipSuccess) return fail_hip(e, "event");
-  if ((e = launch_coarse_select(ix->dev, queries, masks, sh, w, s)) != hipSuccess)
-    return fail_hip(e, "launch coarse_select");
+  if ((e = launch_coarse_select(dx, queries, masks, sh, w, s)) != hipSuccess) return fail_hip(e, "launch coarse_select");
+  if (sh.path == kPathQuery && (e = launch_plan(dx, sh, w, 0, s)) != hipSuccess) return fail_hip(e, "launch plan");
   if ((e = mark()) != hipSuccess) return fail_hip(e, "event");
-  if (grouped && (e = launch_group_plan(ix->dev, sh, w, s)) != hipSuccess) return fail_hip(e, "launch group plan");
+  if (sh.path == kPathTile && (e = launch_tile_plan(dx, masks, sh, w, s)) != hipSuccess)
+    return fail_hip(e, "launch tile plan");
   if ((e = mark()) != hipSuccess) return fail_hip(e, "event");
-  if (grouped) {
-    if ((e = launch_gscan(ix->dev, queries, masks, sh, w, s)) != hipSuccess) return fail_hip(e, "launch gscan");
-    if ((e = mark()) != hipSuccess) return fail_hip(e, "event");
-    // queries whose pools overflowed, query by query (every other chunk and query returns at once)
-    if ((e = launch_scan(ix->dev, queries, masks, sh, w, s)) != hipSuccess) return fail_hip(e, "launch scan");
-    if ((e = launch_merge(ix->dev, query_scales, sh, w, out_ids, out_scores, out_fscores, out_counts, s)) !=
-        hipSuccess)
-      return fail_hip(e, "launch merge");
-    if ((e = mark()) != hipSuccess) return fail_hip(e, "event");
-    if ((e = launch_pool_merge(ix->dev, query_scales, sh, w, out_ids, out_scores, out_fscores, out_counts, s)) !=
-        hipSuccess)
-      return fail_hip(e, "launch pool merge");
-  } else {
-    if ((e = launch_scan(ix->dev, queries, masks, sh, w, s)) != hipSuccess) return fail_hip(e, "launch scan");
-    if ((e = mark()) != hipSuccess) return fail_hip(e, "event");
-    if ((e = mark()) != hipSuccess) return fail_hip(e, "event");
-    if ((e = launch_merge(ix->dev, query_scales, sh, w, out_ids, out_scores, out_fscores, out_counts, s)) !=
-        hipSuccess)
+  if (sh.path == kPathQuery) e = launch_scan(dx, queries, masks, sh, w, 0, s);
+  else if (sh.path == kPathTile) e = launch_tscan(dx, queries, sh, w, s);
+  else e = launch_exh_scan(dx, queries, masks, sh, w, s);
+  if (e != hipSuccess) return fail_hip(e, "launch scan");
+  if ((e = mark()) != hipSuccess) return fail_hip(e, "event");
+  if (sh.path != kPathQuery) {
+    // the queries whose pools cannot prove their top k, query by query (rare: a quarter of the scan's
+    // workgroups; the work list and chunk sizes follow that count)
+    SearchShape rs = sh;
+    rs.P = std::max(1, sh.P / 4);
+    if ((e = launch_plan(dx, rs, w, 1, s)) != hipSuccess) return fail_hip(e, "launch plan");
+    if ((e = launch_scan(dx, queries, masks, rs, w, 1, s)) != hipSuccess) return fail_hip(e, "launch scan");
+    if ((e = launch_merge(dx, query_scales, rs, w, 1, out_ids, out_scores, out_fscores, out_counts, s)) != hipSuccess)
       return fail_hip(e, "launch merge");
   }
   if ((e = mark()) != hipSuccess) return fail_hip(e, "event");
+  if (sh.path == kPathQuery)
+    e = launch_merge(dx, query_scales, sh, w, 0, out_ids, out_scores, out_fscores, out_counts, s);
+  else
+    e = launch_pool_merge(dx, query_scales, sh, w, out_ids, out_scores, out_fscores, out_counts, s);
+  if (e != hipSuccess) return fail_hip(e, "launch merge");
+  if ((e = mark()) != hipSuccess) return fail_hip(e, "event");
   if (prof) ++ps.searches;
   return SVT_OK;
+}
+
+// pointer checks shared by the search entry points; SVT_OK or SVT_EINVAL (message set)
+int check_search_ptrs(const int8_t *queries, const uint64_t *masks, const int64_t *out_ids, const int32_t *out_scores,
+                      const char *who) {
+  if (!queries || !masks || !out_ids || !out_scores)
+    return fail(SVT_EINVAL, "%s: NULL queries, masks, out_ids or out_scores", who);
+  if (((uintptr_t)queries & 15) != 0) return fail(SVT_EINVAL, "%s: queries not 16-byte aligned", who);
+  if (((uintptr_t)masks & 7) != 0) return fail(SVT_EINVAL, "%s: masks not 8-byte aligned", who);
+  return SVT_OK;
+}
+
+}  // namespace
+
+extern "C" size_t svt_search_workspace_size(const svt_index *ix, int32_t n_queries, int32_t nprobe, int32_t k,
+                                            const svt_search_options *opts) {
+  g_err.clear();
+  if (check_search_args(ix, n_queries, nprobe, k, opts, "svt_search_workspace_size") != SVT_OK) return 0;
+  return layout(ix, n_queries, nprobe, k, opts).total;
+}
+
+extern "C" int svt_search(const svt_index *ix, int32_t B, const int8_t *queries, const uint64_t *masks,
+                          const float *query_scales, int32_t nprobe, int32_t k, int64_t *out_ids, int32_t *out_scores,
+                          float *out_fscores, int32_t *out_counts, int64_t *out_stats, const svt_search_options *opts,
+                          void *workspace, size_t workspace_bytes, void *hip_stream) {
+  g_err.clear();
+  int rc = check_search_args(ix, B, nprobe, k, opts, "svt_search");
+  if (rc != SVT_OK) return rc;
+  if (B == 0) return SVT_OK;
+  if ((rc = check_search_ptrs(queries, masks, out_ids, out_scores, "svt_search")) != SVT_OK) return rc;
+  if (!workspace) return fail(SVT_EINVAL, "svt_search: NULL workspace");
+  if (((uintptr_t)workspace & 255) != 0) return fail(SVT_EINVAL, "svt_search: workspace not 256-byte aligned");
+  const Layout L = layout(ix, B, nprobe, k, opts);
+  if (workspace_bytes < L.total)
+    return fail(SVT_EINVAL, "svt_search: workspace %zu bytes < required %zu", workspace_bytes, L.total);
+  const Work w = carve(L, workspace, out_stats);
+  return enqueue_search(ix, L.sh, w, queries, masks, query_scales, out_ids, out_scores, out_fscores, out_counts,
+                        (hipStream_t)hip_stream);
 }
 
 extern "C" int svt_profile_enable(int on) {

@@ -61,6 +61,9 @@ struct Chunk {
 };
 
 constexpr int kCostSamples = kSelThreads;   // items sampled per query to estimate its filter density
+constexpr int kSampleMax = 8;               // tile path: samples per select thread, at most
+constexpr int64_t kSampleSpan = 256 << 10;  // tile path: one more sample per thread for each this many items
+constexpr int kSelElig = 2048;              // tile path: eligible samples the select scores (every stride-th)
 // Per-item work of the scan besides its bytes (filter, compaction, bookkeeping), in byte equivalents of
 // the chunk cost model.  Measured on the 80M-item catalogue at batch 256: 12 to 24 give the shortest
 // scan and merge (sparse filters get shorter chunks, dense ones fewer); 0.125 was 2.5 % slower in the
@@ -94,13 +97,53 @@ constexpr int kTailBand = SVT_TAIL_BAND;
 constexpr int kTailDiv = SVT_TAIL_DIV;
 static_assert(kTailBand >= 0 && kTailBand <= kPlanBands && kTailDiv >= 1, "tail region");
 
-// Grouped path: one unit of work is a tile of at most kGTile items of one probed cluster together
-// with a group of at most kGMax of the queries that probe that cluster (gq[q0..q1)).
-constexpr int kGTile = 4096;
-constexpr int kGMax = 16;
-constexpr int kGScanOcc = 4;         // grouped scan: workgroups per CU (4 independent waves each)
-struct GUnit {
-  int32_t c, lo, hi, q0, q1, pad0, pad1, pad2;   // items at positions [lo, hi) of cluster c
+// Tile path.  The batch's probed clusters form one union stream: for every probed cluster, in cluster
+// order, one entry per block of at most kTMembers of the queries probing it (a cluster probed by more
+// queries appears once per block).  The stream is cut into chunks that persistent workgroups take from
+// a queue; every item of an entry is tested against the masks of the entry's members and the rows of
+// the items any member accepts are gathered once and scored for each member that accepts them.
+constexpr int kTMembers = 16;        // queries of one union entry (member bits of a survivor: uint16)
+constexpr int kTWin = 64;            // union entries a workgroup stages in LDS at a time
+constexpr int kTWinMembers = 64;     // members of the staged entries (with their query vectors)
+#ifndef SVT_T_CHUNKS
+#define SVT_T_CHUNKS 8
+#endif
+constexpr int kTChunksPerWG = SVT_T_CHUNKS;   // chunks of the union stream per persistent workgroup
+// Chunks of the union stream are cut at equal estimated cost: per item of an entry, its signature bytes and
+// kTItemCost byte equivalents of other work, kTMemberCost per member; the rows of the fraction of items some
+// member accepts (from the members' sampled densities).
+#ifndef SVT_T_ROWS
+#define SVT_T_ROWS 48
+#endif
+#ifndef SVT_T_GROUPS
+#define SVT_T_GROUPS 5
+#endif
+constexpr int kTGroups = SVT_T_GROUPS;             // 64-item groups per wave per step
+constexpr int kTStep = kScanThreads * kTGroups;    // items per workgroup step, at most
+constexpr int kTItemCost = 16;
+constexpr int kTMemberCost = 2;
+// Speculative thresholds: a query's threshold is the score that an estimated kAlpha * k of its eligible
+// items reach, read off a sample of its items at rank at least kRMin; the pool keeps every candidate at
+// or above it.  A pool with fewer than k keys (threshold above the minimum) or more than it holds sends
+// its query to the query path.
+constexpr int kAlpha = 4;
+constexpr int kRMin = 16;
+// Exhaustive batches (nprobe == nlist): the catalogue is streamed once per block of kXQ queries and
+// scored with int8 MFMA (16x16x64).  The sample pass scores every kXStride-th item.
+constexpr int kXQ = 32;              // queries of one MFMA unit (two 16-row MFMA tiles)
+constexpr int kXStride = 256;        // sample pass: every kXStride-th position
+constexpr int kXChunk = 4096;        // items of one exhaustive unit
+constexpr int kXWaves = 4;           // waves of an exhaustive workgroup (each works on its own)
+constexpr int kXStage = 256;         // candidates a wave of the exhaustive kernel stages in LDS
+
+constexpr int kMaxPlanBlocks = 65536 / kSelThreads;   // blocks of kSelThreads clusters (nlist <= 65536)
+struct MRec {                        // one member of a union entry
+  uint64_t m0, m1;                   // request mask (m1 = 0 for 64-bit signatures)
+  int32_t thr, q;                    // speculative threshold, query index
+};
+struct UEntry {                      // one entry of the union stream
+  int32_t useg, len, pos0, mstart;   // stream offset, items, first position, first member in mrec
+  int32_t mcnt, pad0, pad1, pad2;    // members
 };
 
 // Per-search device workspace (carved by the host from the caller's buffer).
@@ -120,7 +163,7 @@ struct Work {
   int32_t *hlo;             // [B]          score at the lower edge of bin 1 of the query's histogram
   int32_t *hshift;          // [B]          bin width of that histogram is 2^hshift
   uint32_t *ghist;          // [B][kQHistBins] scores of every candidate any chunk accepted
-  uint32_t *counter;        // [3]          select completion counter, scan and grouped-scan queue heads
+  uint32_t *counter;        // [8]          queue heads (query scan, tile scan, exhaustive sample and scan)
   int32_t *slot_cnt;        // [max_chunks] candidates each chunk left
   uint64_t *slot_min;       // [max_chunks] smallest key of a slot holding k keys, else 0
   uint64_t *slot_keys;      // [max_chunks][k] those candidates (score/id keys)
@@ -128,24 +171,42 @@ struct Work {
   uint32_t *mcnt;           // [B]          slot keys at or above it (more than kGatherCap: not all kept)
   uint64_t *mkeys;          // [B][kGatherCap] those keys, gathered from the query's slots
   int64_t *stats;           // [B][2] scanned / eligible (caller buffer or workspace)
-  // grouped path (null when the search runs query by query)
-  int32_t *gcnt;            // [nlist]      queries probing each cluster
-  int32_t *gfill;           // [nlist]      fill cursor of each cluster's query list
-  int32_t *gstart;          // [nlist + 1]  each cluster's query list in gq
-  int32_t *ustart;          // [nlist + 1]  first unit of each cluster; ustart[nlist] = number of units
-  int32_t *gq;              // [B * nprobe] queries of every probed cluster, grouped by cluster
-  GUnit *units;             // [max_units]
+  // tile path (null on the query path)
+  int32_t *sthr;            // [B]          speculative threshold of each query
+  int32_t *redo;            // [B]          1: the query is redone on the query path
   uint32_t *pool_cnt;       // [B]          candidates offered to each query's pool (> pool_cap: overflow)
-  uint64_t *pool;           // [B][pool_cap] (score, position) keys of the candidates
+  uint64_t *pool;           // [B][pool_cap] (score, position) keys at or above the threshold
+  int32_t *gcnt;            // [nlist]      queries probing each cluster
+  int32_t *gfill;           // [nlist]      fill cursor of each cluster's member list
+  int32_t *gstart;          // [nlist + 1]  each cluster's members in mrec
+  int32_t *estart;          // [nlist + 1]  each cluster's first union entry
+  int32_t *uoff;            // [nlist]      union-stream offset of each cluster's first entry
+  MRec *mrec;               // [B * nprobe] members of every probed cluster, grouped by cluster
+  UEntry *entries;          // [max_entries]
+  int32_t *ctab;            // [max_tchunks] first entry of each chunk
+  int32_t *thdr;            // [4]          entries, union-stream length, chunks, 0
+  int64_t *tblk;            // [4 * kMaxPlanBlocks] per block of kSelThreads clusters: members, entries, items, cost
+  float *qdens;             // [B]          sampled fraction of the query's items that pass its mask
+  float *clog;              // [nlist]      sum over the cluster's members of log(1 - density)
+  int64_t *ccost;           // [nlist + 1]  prefix of the clusters' estimated costs
+  int32_t *cstart_u;        // [max_tchunks + 1] union-stream offset where each chunk starts
+  int32_t *sbuf;            // [B][scap]    exhaustive sample pass: per lane and run, the best eligible score
 };
+
+enum { kPathQuery = 0, kPathTile = 1, kPathExh = 2 };
 
 struct SearchShape {
   int32_t B, nprobe, k, P, max_chunks;
-  int32_t grouped;     // 1: grouped path with the query-by-query scan as fallback for overflowing pools
-  int32_t pool_cap;    // keys per query pool
-  int32_t max_units;
-  int32_t GP;          // persistent workgroups of the grouped scan
-  int32_t gather_cap;  // keys the merge gathers per query (at most kGatherCap)
+  int32_t path;         // kPath*
+  int32_t pool_cap;     // keys per query pool (tile and exhaustive paths)
+  int32_t max_entries;  // union entries (tile path)
+  int32_t max_tchunks;  // chunks of the union stream
+  int32_t TP;           // persistent workgroups of the tile scan
+  int32_t XP;           // workgroups of the exhaustive kernel
+  int32_t gather_cap;   // keys the merge gathers per query (at most kGatherCap)
+  int32_t force_redo;   // every threshold above any score (test of the redo branch)
+  int32_t scap;         // exhaustive: slots of a query's sample buffer (16 per run of 64 sampled points)
+  int32_t n_sblocks;    // exhaustive: runs of 64 sampled points
 };
 
 // most chunks a search can produce.  The costs of the queries add up to at most 4 P Tc.  Without a tail
@@ -155,27 +216,36 @@ inline int32_t max_chunks_for(int32_t B, int32_t P) {
   return kTailBand < kPlanBands ? 4 * kTailDiv * P + (kTailDiv + 1) * B + 1 : 4 * P + B + 1;
 }
 
-// launch wrappers (svt_kernels.hip); each returns hipSuccess or the launch error
-hipError_t launch_coarse_keys(const DevIndex &ix, const int8_t *queries, int32_t B, const Work &w,
-                              hipStream_t s);
+// launch wrappers (svt_kernels.hip, svt_tile.hip); each returns hipSuccess or the launch error
+hipError_t launch_coarse_keys(const DevIndex &ix, const int8_t *queries, int32_t B, const Work &w, hipStream_t s);
+// k_coarse_select: probes, stream layout, samples; tile path: speculative thresholds
 hipError_t launch_coarse_select(const DevIndex &ix, const int8_t *queries, const uint64_t *masks,
                                 const SearchShape &sh, const Work &w, hipStream_t s);
+// the query path's work list (k_plan_count, k_plan_chunks, k_plan_order); redo != 0 (tile path): the
+// queries whose pools cannot prove their top k are marked in w.redo, and only those get chunks
+hipError_t launch_plan(const DevIndex &ix, const SearchShape &sh, const Work &w, int redo, hipStream_t s);
+// k_scan; fallback != 0: the redo of the tile path (per-query statistics are not counted again)
 hipError_t launch_scan(const DevIndex &ix, const int8_t *queries, const uint64_t *masks, const SearchShape &sh,
-                       const Work &w, hipStream_t s);
-// launch_merge: k_merge_bound, k_merge_gather (query-by-query search only), then k_merge
+                       const Work &w, int fallback, hipStream_t s);
+// k_merge_bound, k_merge_gather, k_merge; fallback != 0: only the queries marked for redo, merged from
+// their chunks' slots (k_merge alone)
 hipError_t launch_merge(const DevIndex &ix, const float *query_scales, const SearchShape &sh, const Work &w,
-                        int64_t *out_ids, int32_t *out_scores, float *out_fscores, int32_t *out_counts,
+                        int fallback, int64_t *out_ids, int32_t *out_scores, float *out_fscores,
+                        int32_t *out_counts, hipStream_t s);
+// tile path (svt_tile.hip)
+hipError_t launch_tile_plan(const DevIndex &ix, const uint64_t *masks, const SearchShape &sh, const Work &w,
+                            hipStream_t s);
+hipError_t launch_tscan(const DevIndex &ix, const int8_t *queries, const SearchShape &sh, const Work &w,
                         hipStream_t s);
-// grouped path (svt_group.hip)
-hipError_t launch_group_plan(const DevIndex &ix, const SearchShape &sh, const Work &w, hipStream_t s);
-hipError_t launch_gscan(const DevIndex &ix, const int8_t *queries, const uint64_t *masks, const SearchShape &sh,
-                        const Work &w, hipStream_t s);
+hipError_t launch_exh_scan(const DevIndex &ix, const int8_t *queries, const uint64_t *masks,
+                           const SearchShape &sh, const Work &w, hipStream_t s);
 hipError_t launch_pool_merge(const DevIndex &ix, const float *query_scales, const SearchShape &sh, const Work &w,
                              int64_t *out_ids, int32_t *out_scores, float *out_fscores, int32_t *out_counts,
                              hipStream_t s);
-// resident scan workgroups per compute unit for this shape (0 if unknown)
+// resident workgroups per compute unit for this shape (0 if unknown)
 int scan_blocks_per_cu(int32_t dim, int32_t sig_words);
-int gscan_blocks_per_cu(int32_t dim, int32_t sig_words);
+int tscan_blocks_per_cu(int32_t dim, int32_t sig_words);
+int xscan_blocks_per_cu(int32_t dim, int32_t sig_words);
 hipError_t launch_scatter_rows(const int8_t *src_rows, const uint64_t *src_sigs, const int32_t *pos_of,
                                int64_t i0, int64_t n, int32_t dim, int32_t sig_words, int8_t *dst_rows,
                                uint64_t *dst_sigs, hipStream_t s);

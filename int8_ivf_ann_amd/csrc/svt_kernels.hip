@@ -9,6 +9,8 @@
 //   k_scan          the fused hot loop: Bloom filter -> int8 dot4 score -> per-workgroup top-k in LDS;
 //                   persistent workgroups take chunks from the queue; each chunk leaves at most k keys
 //   k_merge         per query: exact top-k over its chunks' keys (radix select), sorted, written out
+// The tile path (svt_tile.hip) replaces k_plan_* .. k_merge by a scan that reads each probed cluster once
+// per batch; the kernels here then redo the few queries whose candidate pools missed.
 //
 // Method: "SilverTorch - Index as Model" (Meta engineering post): probe the most promising clusters
 // first, filter only inside them with Bloom signatures and bit operations, score only survivors
@@ -36,15 +38,17 @@ template <int LPR>
 __global__ __launch_bounds__(256) void k_coarse_keys(const int8_t *__restrict__ centroids, int32_t nlist,
                                                      const int8_t *__restrict__ queries, int32_t B,
                                                      int32_t *__restrict__ scores, uint32_t *counter,
-                                                     int32_t *__restrict__ gcnt, int32_t *__restrict__ gfill) {
+                                                     int32_t *__restrict__ gcnt, int32_t *__restrict__ gfill,
+                                                     float *__restrict__ clog) {
   constexpr int D = 16 * LPR;
   __shared__ int4 qs[kCoarseQB][LPR];
   const int tid = threadIdx.x;
   const int b0 = blockIdx.y * kCoarseQB;
-  if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) { counter[0] = 0u; counter[1] = 0u; counter[2] = 0u; }
-  if (gcnt && blockIdx.y == 0 && blockIdx.x * 256 + tid < nlist) {   // grouped path: per-cluster counters
+  if (blockIdx.x == 0 && blockIdx.y == 0 && tid < 8) counter[tid] = 0u;
+  if (gcnt && blockIdx.y == 0 && blockIdx.x * 256 + tid < nlist) {   // tile path: per-cluster counters
     gcnt[blockIdx.x * 256 + tid] = 0;
     gfill[blockIdx.x * 256 + tid] = 0;
+    clog[blockIdx.x * 256 + tid] = 0.f;
   }
   for (int i = tid; i < kCoarseQB * LPR; i += 256) {
     int qi = i / LPR, ch = i % LPR;
@@ -104,9 +108,12 @@ __device__ __forceinline__ int32_t row_dot(const int4 *__restrict__ x, const int
 constexpr int kSelKR = 16;   // coarse keys a select thread keeps in registers (nlist <= kSelThreads * kSelKR)
 constexpr int kSelTwoLevel = kSelSegLds / 2 / kSelKR;   // largest nprobe the two-level selection stages
 
+// thr_mode (tile path): 0 no speculative threshold, 1 estimate it from the samples, 2 set it above every
+// score (every query with an eligible item is then redone on the query path)
 __global__ __launch_bounds__(kSelThreads) void k_coarse_select(DevIndex ix, const int8_t *__restrict__ queries,
                                                                 const uint64_t *__restrict__ masks, int32_t B,
-                                                                int32_t nprobe, Work w) {
+                                                                int32_t nprobe, int32_t k, int32_t pool_cap,
+                                                                int32_t thr_mode, Work w) {
   constexpr int NWV = kSelThreads / 64;
   __shared__ SelScratch sel;
   __shared__ int wave_tot[NWV + 1];
@@ -120,6 +127,10 @@ __global__ __launch_bounds__(kSelThreads) void k_coarse_select(DevIndex ix, cons
   __shared__ int32_t tcnt[kSelKR * NWV];         // probed clusters per (register slot, wave)
   __shared__ int smax_s;
   __shared__ int32_t tail_s;                     // stream offset of the first probed cluster in the tail bands
+  __shared__ struct {
+    int32_t pos[kSelElig];                       // tile path: eligible samples (position, score)
+    int32_t sc[kSelElig];
+  } se;
   const int tid = threadIdx.x, l = lane_id(), wv = tid / 64;
   const int b = blockIdx.x;
   const int nlist = ix.nlist;
@@ -128,6 +139,24 @@ __global__ __launch_bounds__(kSelThreads) void k_coarse_select(DevIndex ix, cons
   int32_t *seg = w.seg + (size_t)b * (nprobe + 1);
   int32_t *pb = w.pb + (size_t)b * nprobe;
   const bool in_lds = nprobe <= kSelSegLds;
+  const int32_t c_tail = (int32_t)(((int64_t)kTailBand * nlist + kPlanBands - 1) / kPlanBands);
+  if (tid == 0) tail_s = INT32_MAX;
+  int run = 0;   // items of the query's stream
+  if (nprobe == nlist) {
+    // every cluster probed: the probe list is every cluster in order, the stream is the position order
+    for (int r = tid; r < nlist; r += kSelThreads) {
+      const int32_t o0 = ix.offsets[r];
+      probes[r] = r;
+      seg[r] = o0;
+      pb[r] = 0;
+      if (in_lds) {
+        seg_lds[r] = o0;
+        su.pb[r] = 0;
+      }
+    }
+    run = ix.offsets[nlist];
+    if (tid == 0 && c_tail < nlist) tail_s = ix.offsets[c_tail];
+  } else {
   // --- the nprobe largest keys (keys are distinct: the cluster id is part of them)
   uint64_t T = 0;
   if (nlist <= kSelThreads * kSelKR) {
@@ -233,9 +262,6 @@ __global__ __launch_bounds__(kSelThreads) void k_coarse_select(DevIndex ix, cons
   }
   __syncthreads();
   // --- stream offsets: prefix of the probed clusters' sizes in probe order
-  const int32_t c_tail = (int32_t)(((int64_t)kTailBand * nlist + kPlanBands - 1) / kPlanBands);
-  if (tid == 0) tail_s = INT32_MAX;
-  int run = 0;
   for (int r0 = 0; r0 < nprobe; r0 += kSelThreads) {
     const int r = r0 + tid;
     int32_t c = 0, o0 = 0, sz = 0;
@@ -257,6 +283,7 @@ __global__ __launch_bounds__(kSelThreads) void k_coarse_select(DevIndex ix, cons
     }
     run += tot;
   }
+  }   // nprobe < nlist
   if (tid == 0) {
     seg[nprobe] = run;
     if (in_lds) seg_lds[nprobe] = run;
@@ -266,46 +293,99 @@ __global__ __launch_bounds__(kSelThreads) void k_coarse_select(DevIndex ix, cons
     if (w.stats) { w.stats[2 * (size_t)b] = 0; w.stats[2 * (size_t)b + 1] = 0; }
   }
   __syncthreads();
-  // evenly spaced samples of the query's probed items: their filter density sizes the query's share of
+  // Evenly spaced samples of the query's probed items: their filter density sizes the query's share of
   // the work list; their scores place the query's score histogram (the bins sit between the mean
-  // sample score and twice the largest margin above it)
-  int hit = 0, have = 0;
-  int32_t sc = 0;
-  if (run > 0) {
-    const int32_t t = (int32_t)((int64_t)tid * run / kCostSamples);
-    int32_t pos;
-    if (nprobe == nlist) {
-      pos = t;   // every cluster probed, in id order: the stream is the position order
-    } else {
-      int lo = 0, hi = nprobe - 1;   // largest j with seg[j] <= t
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        const int32_t sv = in_lds ? seg_lds[mid] : seg[mid];
-        if (sv <= t) lo = mid; else hi = mid - 1;
-      }
-      pos = (in_lds ? su.pb[lo] : pb[lo]) + t;
+  // sample score and twice the largest margin above it).
+  //   Query path: one sample per thread, every sample scored.
+  //   Tile path: m samples per thread, m growing with the stream (one more per kSampleSpan items, at
+  //   most kSampleMax), so that the threshold below rests on enough eligible samples.  The signatures of
+  //   a thread's samples are requested together; the eligible samples are compacted in LDS (every
+  //   stride-th of them when there are more than kSelElig) and scored by all threads, one row each in
+  //   most cases; the histogram sits on their scores.
+  const int m = thr_mode == 0 ? 1 : (int)((run + kSampleSpan - 1) / kSampleSpan < kSampleMax
+                                              ? ((run + kSampleSpan - 1) / kSampleSpan > 1 ? (run + kSampleSpan - 1) / kSampleSpan : 1)
+                                              : kSampleMax);
+  const int n_samp = m * kCostSamples;
+  const int4 *qr = reinterpret_cast<const int4 *>(queries + (size_t)b * ix.dim);
+  auto score_at = [&](int32_t pos) -> int32_t {
+    const int4 *xr = reinterpret_cast<const int4 *>(ix.items + (size_t)pos * ix.dim);
+    switch (ix.dim) {
+      case 16: return row_dot<1>(xr, qr);
+      case 32: return row_dot<2>(xr, qr);
+      case 64: return row_dot<4>(xr, qr);
+      case 128: return row_dot<8>(xr, qr);
+      default: return row_dot<16>(xr, qr);
     }
+  };
+  uint32_t hitm = 0u;        // bit i: sample i of this thread is eligible
+  int32_t pos[kSampleMax];
+  int have = 0;
+  int64_t ssum_t = 0;
+  int32_t mx = INT32_MIN;
+  if (run > 0) {
     uint64_t mk[2] = {0, 0};
     for (int u = 0; u < ix.sig_words; ++u) mk[u] = masks[(size_t)b * ix.sig_words + u];
-    const uint64_t *sg = ix.sigs + (size_t)pos * ix.sig_words;
-    hit = ix.sig_words == 2 ? passes<2>(sg, mk) : passes<1>(sg, mk);
-    const int4 *xr = reinterpret_cast<const int4 *>(ix.items + (size_t)pos * ix.dim);
-    const int4 *qr = reinterpret_cast<const int4 *>(queries + (size_t)b * ix.dim);
-    switch (ix.dim) {
-      case 16: sc = row_dot<1>(xr, qr); break;
-      case 32: sc = row_dot<2>(xr, qr); break;
-      case 64: sc = row_dot<4>(xr, qr); break;
-      case 128: sc = row_dot<8>(xr, qr); break;
-      default: sc = row_dot<16>(xr, qr); break;
+    uint64_t sgv[kSampleMax][2];
+#pragma unroll
+    for (int i = 0; i < kSampleMax; ++i) {
+      // sample j = i * kSelThreads + tid of n_samp; samples past m repeat the thread's first position
+      const int j = (i < m ? i : 0) * kSelThreads + tid;
+      const int32_t t = (int32_t)((int64_t)j * run / n_samp);
+      if (nprobe == nlist) {
+        pos[i] = t;   // every cluster probed, in id order: the stream is the position order
+      } else {
+        int lo = 0, hi = nprobe - 1;   // largest j with seg[j] <= t
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          const int32_t sv = in_lds ? seg_lds[mid] : seg[mid];
+          if (sv <= t) lo = mid; else hi = mid - 1;
+        }
+        pos[i] = (in_lds ? su.pb[lo] : pb[lo]) + t;
+      }
+      const uint64_t *sg = ix.sigs + (size_t)pos[i] * ix.sig_words;
+      sgv[i][0] = sg[0];
+      sgv[i][1] = ix.sig_words == 2 ? sg[1] : 0ull;
     }
-    have = 1;
+#pragma unroll
+    for (int i = 0; i < kSampleMax; ++i) {
+      const bool ok = i < m && (sgv[i][0] & mk[0]) == mk[0] && (sgv[i][1] & mk[1]) == mk[1];
+      hitm |= ok ? 1u << i : 0u;
+    }
+    if (thr_mode == 0) {   // query path: every sample scored
+      const int32_t sc = score_at(pos[0]);
+      have = 1;
+      ssum_t = sc;
+      mx = sc;
+    }
+  }
+  const int hit = __popc(hitm);
+  int hits;
+  const int hoff = block_excl_scan<kSelThreads>(hit, wave_tot, &hits);
+  // tile path: the eligible samples compacted in LDS (every stride-th one), then scored
+  const int stride = hits > kSelElig ? (hits + kSelElig - 1) / kSelElig : 1;
+  const int n_el = (hits + stride - 1) / stride;
+  if (thr_mode != 0) {
+    int rk = hoff;
+#pragma unroll
+    for (int i = 0; i < kSampleMax; ++i)
+      if ((hitm >> i) & 1u) {
+        if (rk % stride == 0) se.pos[rk / stride] = pos[i];
+        ++rk;
+      }
+    __syncthreads();
+    for (int e = tid; e < n_el; e += kSelThreads) {
+      const int32_t sc = score_at(se.pos[e]);
+      se.sc[e] = sc;
+      ++have;
+      ssum_t += sc;
+      mx = sc > mx ? sc : mx;
+    }
   }
   if (tid == 0) smax_s = INT32_MIN;
-  int hits;
-  block_excl_scan<kSelThreads>(hit, wave_tot, &hits);
+  int haves;
+  block_excl_scan<kSelThreads>(have, wave_tot, &haves);
   int64_t ssum;
-  block_excl_scan<kSelThreads>(have ? (int64_t)sc : (int64_t)0, wave_tot64, &ssum);
-  int32_t mx = have ? sc : INT32_MIN;
+  block_excl_scan<kSelThreads>(ssum_t, wave_tot64, &ssum);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     const int32_t t2 = __shfl_xor(mx, o);
@@ -313,14 +393,39 @@ __global__ __launch_bounds__(kSelThreads) void k_coarse_select(DevIndex ix, cons
   }
   if (l == 0) atomicMax(&smax_s, mx);
   for (int i = tid; i < kQHistBins; i += kSelThreads) w.ghist[(size_t)b * kQHistBins + i] = 0u;
+  if (thr_mode != 0) {
+    // Tile path: the speculative threshold.  The samples are evenly spaced over the query's stream, so
+    // r eligible samples at or above a score stand for about r * run / n_samp eligible items (each kept
+    // sample stands for stride eligible samples): the r-th best kept score, r for kAlpha * k items (at
+    // least kRMin), is the threshold.  A stream the pool can hold whole needs none.  The choice only
+    // decides how many candidates the pool receives; a pool that ends below k or above its capacity
+    // sends the query to the query path.
+    int32_t st = INT32_MIN;
+    if (run > pool_cap) {
+      const int64_t r0 = ((int64_t)kAlpha * k * n_samp + (int64_t)run * stride - 1) / ((int64_t)run * stride);
+      const int r = (int)(r0 > kRMin ? r0 : kRMin);
+      if (n_el >= r) {
+        __syncthreads();   // se.sc complete
+        const uint64_t T = block_select<kSelThreads>(
+            [&](auto f) {
+              for (int e = tid; e < n_el; e += kSelThreads) f(make_key(se.sc[e], (uint32_t)e));
+            },
+            r, sel);
+        st = key_score(T);
+      }
+    }
+    if (thr_mode == 2) st = INT32_MAX;
+    if (tid == 0) w.sthr[b] = st;
+  }
   __syncthreads();
   if (tid == 0) {
-    const double dens = (double)hits / kCostSamples;
+    const double dens = (double)hits / n_samp;
+    if (w.qdens) w.qdens[b] = (float)dens;
     w.qcost[b] = (int64_t)((double)run * (8.0 * ix.sig_words + dens * ix.dim + kItemCost)) + 1;
     w.qtail[2 * (size_t)b] = tail_s < run ? tail_s : run;
     int32_t lo = 0, shift = 0;
-    if (run > 0) {
-      lo = (int32_t)(ssum / kCostSamples);
+    if (haves > 0) {
+      lo = (int32_t)(ssum / haves);
       const int64_t hi = (int64_t)smax_s + ((int64_t)smax_s - lo) + 1;
       const uint32_t range = (uint32_t)(hi - lo);
       const int bits = range ? 32 - __clz((int)range) : 0;
@@ -340,15 +445,29 @@ __global__ __launch_bounds__(kSelThreads) void k_coarse_select(DevIndex ix, cons
 // the same time and the second reader finds the data in cache (Infinity Cache: every XCD works through
 // the same bands at the same time).
 
-__global__ __launch_bounds__(kSelThreads) void k_plan_count(int32_t B, int32_t P, Work w) {
+// Tile path (redo != 0): a pool proves its query's top k when it holds every candidate it was offered and
+// either its threshold admitted every eligible item or at least k candidates reached it (then the k-th
+// best score is at or above the threshold, so the top k are all in the pool); every other query is marked
+// for redo and only those get chunks.
+__global__ __launch_bounds__(kSelThreads) void k_plan_count(int32_t B, int32_t P, Work w, int32_t redo, int32_t k,
+                                                             uint32_t pool_cap) {
   __shared__ int wave_tot[kSelThreads / 64 + 1];
   __shared__ int64_t wave_tot64[kSelThreads / 64 + 1];
   const int tid = threadIdx.x;
+  auto marked = [&](int i) -> bool {   // tile path: query i is redone
+    const uint32_t c = w.pool_cnt[i];
+    return !(c <= pool_cap && (c >= (uint32_t)k || w.sthr[i] == INT32_MIN));
+  };
   int64_t total = 0;
   for (int i0 = 0; i0 < B; i0 += kSelThreads) {
     const int i = i0 + tid;
     int64_t tot;
-    block_excl_scan<kSelThreads>(i < B ? w.qcost[i] : (int64_t)0, wave_tot64, &tot);
+    bool take = i < B;
+    if (take && redo) {
+      take = marked(i);
+      w.redo[i] = take ? 1 : 0;
+    }
+    block_excl_scan<kSelThreads>(take ? w.qcost[i] : (int64_t)0, wave_tot64, &tot);
     total += tot;
   }
   // target cost of one chunk: four chunks per workgroup; when that is small, one chunk per workgroup
@@ -364,7 +483,9 @@ __global__ __launch_bounds__(kSelThreads) void k_plan_count(int32_t B, int32_t P
     const int i = i0 + tid;
     int32_t nch = 0;
     if (i < B) {
-      const int64_t len = w.qlen[i], cost = w.qcost[i];
+      // tile path: only the queries marked for redo get chunks
+      const bool skip = redo && !marked(i);
+      const int64_t len = skip ? 0 : w.qlen[i], cost = w.qcost[i];
       const int64_t ta = w.qtail[2 * (size_t)i];   // [0, ta): regular chunks; [ta, len): shorter ones
       int32_t na = 0;
       if (len > 0) {
@@ -518,10 +639,9 @@ struct ScanArgs {
   const uint64_t *masks;
   Work w;
   int32_t B, nprobe, k, P;
-  // fallback mode (grouped search): only queries whose candidate pool overflowed are scanned, without
-  // the histogram exchange (the grouped scan already counted their candidates) and without statistics
+  // redo of the tile path: only the queries marked for redo have chunks; their statistics were already
+  // counted by the tile scan
   int32_t fallback;
-  uint32_t pool_cap;
 };
 
 struct ScanLds {
@@ -769,16 +889,6 @@ __global__ __launch_bounds__(kScanThreads, kScanOcc) void k_scan(ScanArgs a) {
     if (tid == 0) next_c = (int)atomicAdd(&a.w.counter[1], 1u);
     const Chunk ch = a.w.chunks[c];
     const int q = ch.q;
-    if (a.fallback && a.w.pool_cnt[q] <= a.pool_cap) {   // this query's pool holds all its candidates
-      __syncthreads();   // every thread has read sm.next before it is replaced
-      if (tid == 0) {
-        a.w.slot_cnt[c] = 0;
-        a.w.slot_min[c] = 0ull;
-        sm.next = next_c;
-      }
-      __syncthreads();
-      continue;
-    }
     const int32_t ra = ch.lo, rb = ch.hi;
     const int32_t hlo = a.w.hlo[q];
     const int hsh = a.w.hshift[q];
@@ -1077,7 +1187,7 @@ __global__ __launch_bounds__(kScanThreads, kScanOcc) void k_scan(ScanArgs a) {
       }
       // histogram exchange after steps 2, 4, 8, ...: the bound converges within a few exchanges
       ++steps;
-      if (!a.fallback && steps >= 2 && (steps & (steps - 1)) == 0) {
+      if (steps >= 2 && (steps & (steps - 1)) == 0) {
         hist_push();
         pull = true;
       }
@@ -1095,7 +1205,7 @@ __global__ __launch_bounds__(kScanThreads, kScanOcc) void k_scan(ScanArgs a) {
       cnt_base += last;
     }
     // --- end of the chunk: its exact top k above the query's bound, published in slot c
-    if (!a.fallback) hist_push();
+    hist_push();
     // keys below the query's bound cannot be in its top k.  The branches below contain barriers, so
     // the block uses one value of the bound, read by one thread.
     if (tid == 0) sm.gbound = gthr > thr_s ? gthr : thr_s;
@@ -1210,8 +1320,7 @@ struct MergeArgs {
   const float *query_scales;
   float item_scale;
   int32_t B, k, P;
-  int32_t fallback;     // grouped search: only queries whose pool overflowed are merged here
-  uint32_t pool_cap;
+  int32_t fallback;     // redo of the tile path: only the queries marked for redo are merged here
   uint32_t gather_cap;  // keys gathered per query; a query with more is merged from its slots
   int64_t *out_ids;
   int32_t *out_scores;
@@ -1235,7 +1344,7 @@ __global__ __launch_bounds__(kSelThreads) void k_merge(MergeArgs a) {
   const int tid = threadIdx.x, l = lane_id();
   const int q = blockIdx.x;
   const int k = a.k;
-  if (a.fallback && a.w.pool_cnt[q] <= a.pool_cap) return;   // merged from its pool
+  if (a.fallback && a.w.redo[q] == 0) return;   // merged from its pool
   // the query's chunks, hence its slots, are cstart[q] .. cstart[q+1]-1 (contiguous in memory)
   const size_t s0 = (size_t)a.w.cstart[q];
   const int ns = a.w.cstart[q + 1] - a.w.cstart[q];
@@ -1447,11 +1556,11 @@ __global__ __launch_bounds__(256) void k_scatter_rows(const int8_t *__restrict__
 hipError_t launch_coarse_keys(const DevIndex &ix, const int8_t *queries, int32_t B, const Work &w, hipStream_t s) {
   dim3 grid((ix.nlist + 255) / 256, (B + kCoarseQB - 1) / kCoarseQB);
   switch (ix.dim) {
-    case 16: k_coarse_keys<1><<<grid, 256, 0, s>>>(ix.centroids, ix.nlist, queries, B, w.coarse_scores, w.counter, w.gcnt, w.gfill); break;
-    case 32: k_coarse_keys<2><<<grid, 256, 0, s>>>(ix.centroids, ix.nlist, queries, B, w.coarse_scores, w.counter, w.gcnt, w.gfill); break;
-    case 64: k_coarse_keys<4><<<grid, 256, 0, s>>>(ix.centroids, ix.nlist, queries, B, w.coarse_scores, w.counter, w.gcnt, w.gfill); break;
-    case 128: k_coarse_keys<8><<<grid, 256, 0, s>>>(ix.centroids, ix.nlist, queries, B, w.coarse_scores, w.counter, w.gcnt, w.gfill); break;
-    case 256: k_coarse_keys<16><<<grid, 256, 0, s>>>(ix.centroids, ix.nlist, queries, B, w.coarse_scores, w.counter, w.gcnt, w.gfill); break;
+    case 16: k_coarse_keys<1><<<grid, 256, 0, s>>>(ix.centroids, ix.nlist, queries, B, w.coarse_scores, w.counter, w.gcnt, w.gfill, w.clog); break;
+    case 32: k_coarse_keys<2><<<grid, 256, 0, s>>>(ix.centroids, ix.nlist, queries, B, w.coarse_scores, w.counter, w.gcnt, w.gfill, w.clog); break;
+    case 64: k_coarse_keys<4><<<grid, 256, 0, s>>>(ix.centroids, ix.nlist, queries, B, w.coarse_scores, w.counter, w.gcnt, w.gfill, w.clog); break;
+    case 128: k_coarse_keys<8><<<grid, 256, 0, s>>>(ix.centroids, ix.nlist, queries, B, w.coarse_scores, w.counter, w.gcnt, w.gfill, w.clog); break;
+    case 256: k_coarse_keys<16><<<grid, 256, 0, s>>>(ix.centroids, ix.nlist, queries, B, w.coarse_scores, w.counter, w.gcnt, w.gfill, w.clog); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -1459,8 +1568,13 @@ hipError_t launch_coarse_keys(const DevIndex &ix, const int8_t *queries, int32_t
 
 hipError_t launch_coarse_select(const DevIndex &ix, const int8_t *queries, const uint64_t *masks,
                                 const SearchShape &sh, const Work &w, hipStream_t s) {
-  k_coarse_select<<<sh.B, kSelThreads, 0, s>>>(ix, queries, masks, sh.B, sh.nprobe, w);
-  k_plan_count<<<1, kSelThreads, 0, s>>>(sh.B, sh.P, w);
+  const int thr_mode = sh.path != kPathTile ? 0 : (sh.force_redo ? 2 : 1);
+  k_coarse_select<<<sh.B, kSelThreads, 0, s>>>(ix, queries, masks, sh.B, sh.nprobe, sh.k, sh.pool_cap, thr_mode, w);
+  return hipGetLastError();
+}
+
+hipError_t launch_plan(const DevIndex &ix, const SearchShape &sh, const Work &w, int redo, hipStream_t s) {
+  k_plan_count<<<1, kSelThreads, 0, s>>>(sh.B, sh.P, w, redo, sh.k, (uint32_t)sh.pool_cap);
   k_plan_chunks<<<sh.B, 256, 0, s>>>(sh.B, sh.nprobe, ix.nlist, w);
   k_plan_order<<<1, kSelThreads, 0, s>>>(sh.B, w);
   return hipGetLastError();
@@ -1475,8 +1589,8 @@ static void scan_w(const ScanArgs &a, int W, hipStream_t s) {
 }
 
 hipError_t launch_scan(const DevIndex &ix, const int8_t *queries, const uint64_t *masks, const SearchShape &sh,
-                       const Work &w, hipStream_t s) {
-  ScanArgs a{ix, queries, masks, w, sh.B, sh.nprobe, sh.k, sh.P, sh.grouped, (uint32_t)sh.pool_cap};
+                       const Work &w, int fallback, hipStream_t s) {
+  ScanArgs a{ix, queries, masks, w, sh.B, sh.nprobe, sh.k, sh.P, fallback};
   switch (ix.dim) {
     case 16: scan_w<1>(a, ix.sig_words, s); break;
     case 32: scan_w<2>(a, ix.sig_words, s); break;
@@ -1508,11 +1622,11 @@ int scan_blocks_per_cu(int32_t dim, int32_t sig_words) {
 }
 
 hipError_t launch_merge(const DevIndex &ix, const float *query_scales, const SearchShape &sh, const Work &w,
-                        int64_t *out_ids, int32_t *out_scores, float *out_fscores, int32_t *out_counts,
-                        hipStream_t s) {
-  MergeArgs a{w, query_scales, ix.item_scale, sh.B, sh.k, sh.P, sh.grouped, (uint32_t)sh.pool_cap,
-              (uint32_t)sh.gather_cap, out_ids, out_scores, out_fscores, out_counts};
-  if (!sh.grouped) {
+                        int fallback, int64_t *out_ids, int32_t *out_scores, float *out_fscores,
+                        int32_t *out_counts, hipStream_t s) {
+  MergeArgs a{w, query_scales, ix.item_scale, sh.B, sh.k, sh.P, fallback, (uint32_t)sh.gather_cap, out_ids,
+              out_scores, out_fscores, out_counts};
+  if (!fallback) {   // the redo of the tile path (rare) merges straight from the chunks' slots
     k_merge_bound<<<sh.B, 64, 0, s>>>(w, sh.k);
     const int g = sh.max_chunks < kMergeGatherWGs ? sh.max_chunks : kMergeGatherWGs;
     k_merge_gather<<<g, 256, 0, s>>>(w, sh.B, sh.k, (uint32_t)sh.gather_cap);

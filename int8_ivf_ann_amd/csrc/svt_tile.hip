@@ -1,0 +1,1241 @@
+// svt_tile.hip - gfx950 kernels of the tile search path: each probed cluster is read once per batch for
+// every query that probes it.
+//
+//   k_gcount, k_tplan1, k_tplan2, k_gfill, k_tentries, k_tchunks
+//             the union stream: every probed cluster, in cluster order, once per block of at most
+//             kTMembers of the queries probing it (an entry); its members (mask, threshold, query); the
+//             stream cut into chunks of equal estimated cost
+//   k_tscan   persistent workgroups take chunks from a queue and walk them in steps; each item of an
+//             entry is tested against the masks of all the entry's members, the rows any member accepts
+//             are gathered once and scored (v_dot4) for each member that accepts them; a score at or
+//             above the member's threshold is a candidate for its query's pool
+//   k_xscan   nprobe == nlist: the whole catalogue is one stream shared by every query; it is read once
+//             per block of kXQ queries and scored with int8 MFMA (16x16x64), the masks applied to the
+//             products; a sample pass over every kXStride-th item gives the thresholds (k_xthr)
+// A query whose pool cannot prove its top k (fewer than k keys with a threshold above the minimum, or
+// more keys than the pool holds) is redone by the query-by-query kernels (marked by k_plan_count).
+//   k_pmerge  per query: the exact top k of its pool
+//
+// Method: "SilverTorch - Index as Model" (Meta engineering post): probe the most promising clusters,
+// filter inside them with Bloom signatures and bit operations, score the survivors with int8 dot
+// products ("dp4a" in the compute-cost-efficiency section), keep a large top-k on the device;
+// "Meta Andromeda" summary, System section: scoring is bound by memory bandwidth, so data are fetched
+// once and intermediates stay on chip.  The speculative thresholds, the union stream and the MFMA
+// layout are this library's design for CDNA4, not the pages'.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "svt_device.h"
+#include "svt_internal.h"
+
+namespace svt {
+
+// ------------------------------------------------------------------------------------------------
+// the union stream
+
+// queries probing each cluster, and the log of the fraction of the cluster's items no member accepts
+// (members taken as independent, each with its sampled density); gcnt, gfill and clog are zeroed by
+// k_coarse_keys
+__global__ __launch_bounds__(256) void k_gcount(const int32_t *__restrict__ probes, int32_t nprobe, Work w) {
+  const int b = blockIdx.x;
+  const float dens = w.qdens[b];
+  const float lg = log1pf(-(dens < 0.999f ? dens : 0.999f));
+  for (int j = threadIdx.x; j < nprobe; j += 256) {
+    const int c = probes[(size_t)b * nprobe + j];
+    atomicAdd(&w.gcnt[c], 1);
+    atomicAdd(&w.clog[c], lg);
+  }
+}
+
+// Each cluster's members in mrec (gstart), its first entry (estart), the union-stream offset of that entry
+// (uoff) and the prefix of the clusters' estimated costs (ccost): prefix sums over the clusters in two
+// launches.  k_tplan1: one thread per cluster, block prefixes and block totals.  k_tplan2: each
+// workgroup adds its block's offset (the sum of the blocks before it); one more writes the totals, the
+// stream's length and chunk count in thdr.
+__device__ __forceinline__ void tile_cluster(const DevIndex &ix, const Work &w, int c, int64_t v[4]) {
+  const int nq = w.gcnt[c];
+  const int size = ix.offsets[c + 1] - ix.offsets[c];
+  const int ne = (nq > 0 && size > 0) ? (nq + kTMembers - 1) / kTMembers : 0;
+  v[0] = nq;
+  v[1] = ne;
+  v[2] = (int64_t)ne * size;   // the union stream is shorter than 2^31 (checked by the host)
+  // estimated bytes and byte equivalents: signatures and per-item work of every entry, per-member
+  // tests, the rows of the items some member accepts
+  const double acc = ne > 0 ? 1.0 - (double)__expf(w.clog[c]) : 0.0;
+  v[3] = ne > 0 ? (int64_t)size * (ne * (8 * ix.sig_words + kTItemCost) + (int64_t)kTMemberCost * nq) +
+                      (int64_t)(acc * ix.dim * size) + 1
+                : 0;
+}
+
+__global__ __launch_bounds__(kSelThreads) void k_tplan1(DevIndex ix, Work w) {
+  __shared__ int64_t wave_tot[kSelThreads / 64 + 1];
+  const int c = blockIdx.x * kSelThreads + threadIdx.x;
+  int64_t v[4] = {0, 0, 0, 0};
+  if (c < ix.nlist) tile_cluster(ix, w, c, v);
+  int64_t pre[4], tot[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) pre[j] = block_excl_scan<kSelThreads>(v[j], wave_tot, &tot[j]);
+  if (c < ix.nlist) {
+    w.gstart[c] = (int32_t)pre[0];
+    w.estart[c] = (int32_t)pre[1];
+    w.uoff[c] = (int32_t)pre[2];
+    w.ccost[c] = pre[3];
+  }
+  if (threadIdx.x == 0)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w.tblk[4 * blockIdx.x + j] = tot[j];
+}
+
+__global__ __launch_bounds__(kSelThreads) void k_tplan2(DevIndex ix, int32_t P, Work w) {
+  __shared__ int64_t boff[4];
+  const int tid = threadIdx.x, l = lane_id();
+  const int nlist = ix.nlist;
+  const int nb = (nlist + kSelThreads - 1) / kSelThreads;
+  const int blk = blockIdx.x;
+  if (tid < 64) {   // this block's offsets (blocks before it), and the totals: one wave over the block sums
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      int64_t before = 0, all = 0;
+      for (int b0 = 0; b0 < nb; b0 += 64) {
+        const int b = b0 + l;
+        const int64_t x = b < nb ? w.tblk[4 * b + v] : 0;
+        const int64_t inc = wave_incl_scan(x);
+        const int64_t tot = __shfl(inc, 63);
+        const int64_t pre = __shfl(inc - x, (blk - b0) & 63);   // offset of block blk within this group
+        if (blk >= b0 && blk < b0 + 64) before = all + pre;
+        all += tot;
+      }
+      if (l == 0) boff[v] = blk < nb ? before : all;
+    }
+  }
+  __syncthreads();
+  if (blk < nb) {
+    const int c = blk * kSelThreads + tid;
+    if (blk > 0 && c < nlist) {
+      w.gstart[c] += (int32_t)boff[0];
+      w.estart[c] += (int32_t)boff[1];
+      w.uoff[c] += (int32_t)boff[2];
+      w.ccost[c] += boff[3];
+    }
+  } else if (tid == 0) {   // the last workgroup: totals and the stream's length and chunk count
+    w.gstart[nlist] = (int32_t)boff[0];
+    w.estart[nlist] = (int32_t)boff[1];
+    w.ccost[nlist] = boff[3];
+    const int32_t U = (int32_t)boff[2];
+    w.thdr[0] = (int32_t)boff[1];
+    w.thdr[1] = U;
+    w.thdr[2] = U > 0 ? kTChunksPerWG * P : 0;
+    w.thdr[3] = 0;
+  }
+}
+
+// Chunk i of the union stream starts where the estimated cost reaches i / n of the total: inside the
+// cluster whose cost range holds that point, at the same fraction of the cluster's union items (rounded
+// down to 64).  The starts ascend with i; a chunk may be empty.  ctab[i]: the entry holding the start.
+__global__ __launch_bounds__(256) void k_tchunks(DevIndex ix, int32_t max_tchunks, Work w) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  const int n = w.thdr[2];
+  const int32_t U = w.thdr[1];
+  if (i > n || i > max_tchunks) return;
+  if (i == n) {
+    w.cstart_u[n] = U;
+    return;
+  }
+  const int nlist = ix.nlist;
+  const int64_t total = w.ccost[nlist];
+  const int64_t target = (int64_t)((double)total * i / n);
+  int lo = 0, hi = nlist - 1;   // largest c with ccost[c] <= target: its cost range holds target
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (w.ccost[mid] <= target) lo = mid; else hi = mid - 1;
+  }
+  const int c = lo;
+  const int64_t cost = w.ccost[c + 1] - w.ccost[c];
+  const int32_t u0 = w.uoff[c];
+  const int32_t nu = (c + 1 < nlist ? w.uoff[c + 1] : U) - u0;
+  int32_t off = 0;
+  if (cost > 0 && nu > 0) {
+    off = (int32_t)((double)(target - w.ccost[c]) / (double)cost * (double)nu);
+    off = off < nu - 1 ? off : nu - 1;
+    off = off / 64 * 64;
+  }
+  const int size = ix.offsets[c + 1] - ix.offsets[c];
+  w.cstart_u[i] = u0 + off;
+  w.ctab[i] = w.estart[c] + (size > 0 ? off / size : 0);
+}
+
+// the members of each probed cluster: the request mask, speculative threshold and index of every query
+// probing it (their order inside a cluster is arbitrary; it changes no result)
+__global__ __launch_bounds__(256) void k_gfill(const int32_t *__restrict__ probes, const uint64_t *__restrict__ masks,
+                                               int32_t nprobe, int32_t W, Work w) {
+  const int b = blockIdx.x;
+  const uint64_t m0 = masks[(size_t)b * W], m1 = W == 2 ? masks[(size_t)b * W + 1] : 0ull;
+  const int32_t thr = w.sthr[b];
+  for (int j = threadIdx.x; j < nprobe; j += 256) {
+    const int c = probes[(size_t)b * nprobe + j];
+    const int slot = atomicAdd(&w.gfill[c], 1);
+    w.mrec[w.gstart[c] + slot] = MRec{m0, m1, thr, b};
+  }
+}
+
+// entry e: the cluster whose entries hold e and its member block
+__global__ __launch_bounds__(256) void k_tentries(DevIndex ix, int32_t max_entries, Work w) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  const int n_e = w.thdr[0];
+  if (e >= n_e || e >= max_entries) return;
+  const int nlist = ix.nlist;
+  int lo = 0, hi = nlist - 1;   // largest c with estart[c] <= e: the cluster that has entry e
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (w.estart[mid] <= e) lo = mid; else hi = mid - 1;
+  }
+  const int c = lo;
+  const int bi = e - w.estart[c];
+  const int32_t pos0 = ix.offsets[c], size = ix.offsets[c + 1] - pos0;
+  const int nq = w.gstart[c + 1] - w.gstart[c];
+  const int32_t useg = w.uoff[c] + bi * size;
+  const int mc = nq - bi * kTMembers < kTMembers ? nq - bi * kTMembers : kTMembers;
+  const int ms = w.gstart[c] + bi * kTMembers;
+  w.entries[e] = UEntry{useg, size, pos0, ms, mc, 0, 0, 0};
+}
+
+// ------------------------------------------------------------------------------------------------
+// k_tscan: the union stream, chunk by chunk.
+//
+// A workgroup walks a chunk in steps of kTStep items inside one entry (as k_scan walks a query's
+// stream): each wave loads 64 kTGroups signatures, tests them against the masks of every member of
+// the step's entry and compacts the items any member accepts, with the member bits, into LDS; after one
+// barrier the survivors are shared evenly among the waves, which gather their rows (LPR lanes per row,
+// 16-byte loads) with the query slice of each row's first member and score them with v_dot4; further
+// members of a row (rare) are scored from the same row registers.  The steps run as a software pipeline:
+// iteration i filters step i + 1, requests the signatures of step i + 2, passes the barrier, scores step
+// i and requests the rows of step i + 1.  Every load is issued unconditionally (clamped addresses,
+// masked lanes), so the compiler's wait counts stay exact.
+//
+// Candidates (score at or above the member's threshold) are staged in LDS with the slot of their
+// (entry visit, member) and go to the queries' pools at the end of the chunk, one pool reservation per
+// slot.  A candidate that finds the stage or the slot table full goes to its pool directly.  Per-slot
+// counters give the scanned and accepted items of each query.
+
+struct TScanArgs {
+  DevIndex ix;
+  const int8_t *queries;
+  Work w;
+  int32_t B, P;
+  uint32_t pool_cap;
+};
+
+constexpr int kTSlots = 256;         // (entry visit, member) slots of a chunk
+constexpr int kTStageWG = 768;       // candidates a workgroup stages per chunk
+constexpr int kTRowBatch = SVT_T_ROWS;   // rows a wave gathers together (its share of a dense step)
+
+struct TMember {                     // one member of a step's entry
+  uint64_t m0, m1;
+  int32_t thr, q, slot, pad;         // slot < 0: no slot (counts and candidates go to HBM directly)
+};
+
+template <int LPR>
+struct TScanLds {
+  uint16_t wl[3][kTStep];         // survivors of three consecutive steps (offset in the step)
+  uint16_t wq[3][kTStep];         //   and the members that accept them (bit j: member j)
+  int wcnt[2][kScanThreads / 64];    // survivors each wave found in a step, by step parity
+  TMember mt[4][kTMembers];          // members of the entry of step i in mt[i % 4]
+  int4 mqv[4][kTMembers][LPR];       //   and their query vectors
+  // window of the chunk's entries: stream range clipped to the chunk, position base (pos = pb + t),
+  // first member in wm, member count, first member in mrec
+  int32_t e_t0[kTWin], e_t1[kTWin], e_pb[kTWin], e_m[kTWin], e_mc[kTWin], e_ms[kTWin];
+  int e_n;
+  MRec wm[kTWinMembers];             // members of the window's entries
+  int4 wqv[kTWinMembers][LPR];       //   and their query vectors
+  int32_t sq[kTSlots];               // query of each slot
+  uint32_t scount[kTSlots];          // candidates staged for each slot
+  uint32_t sbase[kTSlots];           // their pool position, reserved at the flush
+  uint32_t selig[kTSlots];           // items the slot's member accepted
+  uint32_t sscan[kTSlots];           // items of the slot's entry visit
+  uint64_t skey[kTStageWG];          // staged candidates: (score, position) keys
+  uint16_t sslot[kTStageWG];         //   their slot (0xFFFF: not staged)
+  uint16_t srank[kTStageWG];         //   their rank among the slot's staged candidates
+  int stage_n;
+  int next;
+};
+
+template <int LPR, int W>
+__global__ __launch_bounds__(kScanThreads, kScanOcc) void k_tscan(TScanArgs a) {
+  constexpr int D = 16 * LPR;
+  constexpr int RPI = 64 / LPR;                   // rows covered by one 16-byte load per lane
+  constexpr int R0 = kTRowBatch / RPI;
+  constexpr int R = R0 < 1 ? 1 : (R0 > 8 ? 8 : R0);   // row loads per lane in one batch
+  constexpr int RB = R * RPI;                     // rows a wave requests together
+  constexpr int NWV = kScanThreads / 64;
+  __shared__ TScanLds<LPR> sm;
+  const int tid = threadIdx.x, l = lane_id(), wv = tid / 64, sub = l % LPR;
+  const int n_chunks = a.w.thdr[2];
+  const int n_ent = a.w.thdr[0];
+  const uint32_t cap = a.pool_cap;
+  int64_t *stats = a.w.stats;
+  if (tid == 0) {
+    sm.next = (int)atomicAdd(&a.w.counter[3], 1u);
+    sm.stage_n = 0;
+  }
+  for (int i = tid; i < kTSlots; i += kScanThreads) {
+    sm.scount[i] = 0u;
+    sm.selig[i] = 0u;
+  }
+  __syncthreads();
+  for (;;) {
+    const int ci = __builtin_amdgcn_readfirstlane(sm.next);
+    if (ci >= n_chunks) break;
+    int next_c = 0;
+    if (tid == 0) next_c = (int)atomicAdd(&a.w.counter[3], 1u);
+    const int32_t ra = a.w.cstart_u[ci], rb = a.w.cstart_u[ci + 1];
+    int jwin = a.w.ctab[ci];
+    if (ra >= rb) {   // an empty chunk
+      __syncthreads();   // every thread has read sm.next before it is replaced
+      if (tid == 0) sm.next = next_c;
+      __syncthreads();
+      continue;
+    }
+    // the chunk's entries from jwin on, as many as kTWin entries and kTWinMembers members allow
+    auto load_window = [&]() {   // all threads
+      __syncthreads();
+      if (wv == 0) {
+        UEntry E{0, 0, 0, 0, 0, 0, 0, 0};
+        const bool have = jwin + l < n_ent && l < kTWin;
+        if (have) E = a.w.entries[jwin + l];
+        const bool valid = have && E.useg < rb;   // entries are in stream order: a prefix of the lanes
+        const int mc = valid ? E.mcnt : 0;
+        const int inc = wave_incl_scan(mc);
+        const bool fit = valid && inc <= kTWinMembers;
+        const int n = __popcll(__ballot(fit));
+        if (fit) {
+          sm.e_t0[l] = ra > E.useg ? ra : E.useg;
+          sm.e_t1[l] = rb < E.useg + E.len ? rb : E.useg + E.len;
+          sm.e_pb[l] = E.pos0 - E.useg;
+          sm.e_m[l] = inc - mc;
+          sm.e_mc[l] = mc;
+          sm.e_ms[l] = E.mstart;
+        }
+        if (l == 0) sm.e_n = n;
+      }
+      __syncthreads();
+      const int n = sm.e_n;
+      const int nm = n > 0 ? sm.e_m[n - 1] + sm.e_mc[n - 1] : 0;
+      // members and their query vectors: thread t copies part t % LPR of member t / LPR
+      for (int mp = tid; mp < nm * LPR; mp += kScanThreads) {
+        const int m = mp / LPR, part = mp % LPR;
+        int lo = 0, hi = n - 1;   // the entry of window member m: largest i with e_m[i] <= m
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (sm.e_m[mid] <= m) lo = mid; else hi = mid - 1;
+        }
+        const MRec rec = a.w.mrec[sm.e_ms[lo] + (m - sm.e_m[lo])];
+        if (part == 0) sm.wm[m] = rec;
+        sm.wqv[m][part] = reinterpret_cast<const int4 *>(a.queries + (size_t)rec.q * D)[part];
+      }
+      __syncthreads();
+    };
+    struct Cursor {
+      int w;            // entry in the LDS window; -1: chunk finished
+      int32_t st, t1;   // step start / entry end, in stream offsets
+      int32_t pbase;    // position = pbase + stream offset
+    };
+    auto seek = [&](Cursor &cu) {   // all threads; from entry cu.w: the first entry with items left
+      for (;;) {
+        for (; cu.w < sm.e_n; ++cu.w) {
+          const int32_t t0 = sm.e_t0[cu.w], t1 = sm.e_t1[cu.w];
+          if (t0 < t1) {
+            cu.st = t0;
+            cu.t1 = t1;
+            cu.pbase = sm.e_pb[cu.w];
+            return;
+          }
+        }
+        const int nx = jwin + sm.e_n;   // window exhausted: another one if the chunk continues
+        if (sm.e_n == 0 || nx >= n_ent || a.w.entries[nx].useg >= rb) {
+          cu.w = -1;
+          return;
+        }
+        jwin = nx;
+        load_window();
+        cu.w = 0;
+      }
+    };
+    auto advance = [&](Cursor &cu) {
+      cu.st += kTStep;
+      if (cu.st >= cu.t1) {
+        ++cu.w;
+        seek(cu);
+      }
+    };
+    // The member table of the step at cursor cu, in mt[mtb] (wave 0 writes it; a barrier follows before
+    // any use).  A new entry visit takes a slot per member; a visit without slots counts to HBM.
+    int nsl = 0;        // slots taken in this chunk (the same value in every thread)
+    int last_eg = -1;   // entry of the last step whose table was built
+    int slot_base = 0;
+    // The member table copies everything a step needs from the window (LDS to LDS, no memory loads in
+    // the step pipeline), so that the window can be replaced while the step is still in flight.
+    auto build_mt = [&](const Cursor &cu, int mtb) -> int {
+      if (cu.w < 0) return 0;
+      const int mc = sm.e_mc[cu.w];
+      if (tid < mc * LPR) sm.mqv[mtb][tid / LPR][tid % LPR] = sm.wqv[sm.e_m[cu.w] + tid / LPR][tid % LPR];
+      const int eg = jwin + cu.w;
+      const bool fresh = eg != last_eg;
+      if (fresh) {
+        slot_base = nsl;
+        nsl += mc;
+        last_eg = eg;
+      }
+      if (wv == 0 && l < mc) {
+        const MRec m = sm.wm[sm.e_m[cu.w] + l];
+        const int s = slot_base + l < kTSlots ? slot_base + l : -1;
+        sm.mt[mtb][l] = TMember{m.m0, m.m1, m.thr, m.q, s, 0};
+        if (fresh) {
+          const uint32_t items = (uint32_t)(sm.e_t1[cu.w] - sm.e_t0[cu.w]);
+          if (s >= 0) {
+            sm.sq[s] = m.q;
+            sm.sscan[s] = items;
+          } else if (stats) {
+            atomicAdd((unsigned long long *)&stats[2 * (size_t)m.q], (unsigned long long)items);
+          }
+        }
+      }
+      return mc;
+    };
+    uint64_t sg[kTGroups][W];
+    int32_t sg_n = 0, sg_p0 = 0;
+    auto load_sigs = [&](const Cursor &cu) {
+      sg_n = cu.w >= 0 ? ((cu.t1 - cu.st) < kTStep ? (cu.t1 - cu.st) : kTStep) : 0;
+      const int32_t p0 = cu.w >= 0 ? cu.pbase + cu.st : 0;
+      sg_p0 = p0;
+      const int32_t last = sg_n > 0 ? sg_n - 1 : 0;
+#pragma unroll
+      for (int gi = 0; gi < kTGroups; ++gi) {
+        const int i = gi * kScanThreads + wv * 64 + l;
+        const int32_t p = p0 + (i < last ? i : last);
+        if constexpr (W == 2) {
+          const ulonglong2 v = reinterpret_cast<const ulonglong2 *>(a.ix.sigs)[p];
+          sg[gi][0] = v.x;
+          sg[gi][1] = v.y;
+        } else {
+          sg[gi][0] = a.ix.sigs[p];
+        }
+      }
+    };
+    struct Share {           // wave wv scores survivors [rbeg, rend) of a step's concatenated lists
+      int pre[NWV + 1];
+      int rbeg, rend;
+    };
+    auto share = [&](int par) -> Share {
+      Share s;
+      s.pre[0] = 0;
+#pragma unroll
+      for (int i = 0; i < NWV; ++i) s.pre[i + 1] = s.pre[i] + sm.wcnt[par][i];
+      const int total = s.pre[NWV];
+      const int per = (total + NWV - 1) / NWV;
+      s.rbeg = wv * per;
+      s.rend = s.rbeg + per < total ? s.rbeg + per : total;
+      return s;
+    };
+    auto surv_at = [&](const Share &s, int r) -> int {   // index of survivor r in its buffer
+      int adj = 0;
+#pragma unroll
+      for (int i = 1; i < NWV; ++i) adj = r >= s.pre[i] ? i * 64 * kTGroups - s.pre[i] : adj;
+      return r + adj;
+    };
+    // the step in sg, tested against the mc members of mt[mtb], into wl/wq[buf]; returns this wave's
+    // survivors
+    auto filter = [&](int buf, int mtb, int mc) -> int {
+      uint32_t qm[kTGroups];
+#pragma unroll
+      for (int gi = 0; gi < kTGroups; ++gi) qm[gi] = 0u;
+      for (int j = 0; j < mc; ++j) {
+        const uint64_t m0 = sm.mt[mtb][j].m0, m1 = sm.mt[mtb][j].m1;
+        int cnt = 0;
+#pragma unroll
+        for (int gi = 0; gi < kTGroups; ++gi) {
+          const int i = gi * kScanThreads + wv * 64 + l;
+          bool pass = i < sg_n && ((sg[gi][0] & m0) == m0);
+          if constexpr (W == 2) pass = pass && ((sg[gi][1] & m1) == m1);
+          qm[gi] |= pass ? 1u << j : 0u;
+          cnt += __popcll(__ballot(pass));
+        }
+        if (stats && l == 0 && cnt > 0) {
+          const int s = sm.mt[mtb][j].slot;
+          if (s >= 0)
+            atomicAdd(&sm.selig[s], (uint32_t)cnt);
+          else
+            atomicAdd((unsigned long long *)&stats[2 * (size_t)sm.mt[mtb][j].q + 1], (unsigned long long)cnt);
+        }
+      }
+      int nw = 0;
+#pragma unroll
+      for (int gi = 0; gi < kTGroups; ++gi) {
+        const int i = gi * kScanThreads + wv * 64 + l;
+        const uint64_t bal = __ballot(qm[gi] != 0u);
+        if (qm[gi] != 0u) {
+          const int o = wv * 64 * kTGroups + nw + mbcnt(bal);
+          sm.wl[buf][o] = (uint16_t)i;
+          sm.wq[buf][o] = (uint16_t)qm[gi];
+        }
+        nw += __popcll(bal);
+      }
+      return nw;
+    };
+    int4 x[R];
+    uint32_t qmv[R];
+    // rows of the batch at r0
+    auto load_rows = [&](int32_t p0, int buf, const Share &s, int r0) {
+#pragma unroll
+      for (int u = 0; u < R; ++u) {
+        const int r = r0 + u * RPI + l / LPR;
+        const bool valid = r < s.rend;
+        const int idx = valid ? surv_at(s, r) : 0;
+        const uint32_t qm = valid ? (uint32_t)sm.wq[buf][idx] : 0u;
+        const int32_t p = p0 + (valid ? (int)sm.wl[buf][idx] : 0);
+        qmv[u] = qm;
+        x[u] = reinterpret_cast<const int4 *>(a.ix.items + (size_t)p * D)[sub];
+      }
+    };
+    // a candidate of member j (lanes with ok): staged with its slot, or written to the pool directly.
+    // The row's position is read back from the survivor list only here (candidates are rare).
+    auto offer = [&](bool ok, int32_t score, int32_t p0, int buf, const Share &s, int r, const TMember &m) {
+      const uint64_t b = __ballot(ok);
+      if (b == 0ull) return;
+      const int32_t pos = p0 + (ok ? (int)sm.wl[buf][surv_at(s, r)] : 0);
+      int at = 0;
+      if (l == 0) at = atomicAdd(&sm.stage_n, __popcll(b));
+      at = __builtin_amdgcn_readfirstlane(at);
+      if (ok) {
+        const int e = at + mbcnt(b);
+        const uint64_t key = pos_key(score, pos);
+        bool direct = true;
+        if (e < kTStageWG) {
+          if (m.slot >= 0) {
+            sm.skey[e] = key;
+            sm.sslot[e] = (uint16_t)m.slot;
+            sm.srank[e] = (uint16_t)atomicAdd(&sm.scount[m.slot], 1u);
+            direct = false;
+          } else {
+            sm.sslot[e] = 0xFFFFu;
+          }
+        }
+        if (direct) {
+          const uint32_t o = atomicAdd(&a.w.pool_cnt[m.q], 1u);
+          if (o < cap) a.w.pool[(size_t)m.q * cap + o] = key;
+        }
+      }
+    };
+    auto score_rows = [&](int32_t p0, int buf, int mtb, const Share &s, int r0) {
+      int32_t acc0[R];
+#pragma unroll
+      for (int u = 0; u < R; ++u) {
+        const int j = qmv[u] ? __builtin_ctz(qmv[u]) : 0;
+        acc0[u] = group_sum<LPR>(dot16(x[u], sm.mqv[mtb][j][sub], 0));
+      }
+#pragma unroll
+      for (int u = 0; u < R; ++u) {
+        uint32_t qm = qmv[u];
+        int32_t acc = acc0[u];
+        for (;;) {
+          const int j = qm ? __builtin_ctz(qm) : 0;
+          const TMember m = sm.mt[mtb][j];
+          offer(qm != 0u && sub == 0 && acc >= m.thr, acc, p0, buf, s, r0 + u * RPI + l / LPR, m);
+          qm &= qm - 1u;
+          if (__ballot(qm != 0u) == 0ull) break;
+          // a further member accepts this row: the same row against its query vector
+          const int j2 = qm ? __builtin_ctz(qm) : 0;
+          acc = group_sum<LPR>(dot16(x[u], sm.mqv[mtb][j2][sub], 0));
+        }
+      }
+    };
+
+    load_window();
+    Cursor cur{0, 0, 0, 0};
+    seek(cur);
+    // prologue: step 0's member table and signatures, filter; step 1's; step 0's first rows
+    int mc_sg = build_mt(cur, 0);
+    load_sigs(cur);
+    if (cur.w >= 0) advance(cur);
+    __syncthreads();   // mt[0]
+    int32_t p0_i = sg_p0;
+    {
+      const int nw = filter(0, 0, mc_sg);
+      if (l == 0) sm.wcnt[0][wv] = nw;
+    }
+    mc_sg = build_mt(cur, 1);
+    load_sigs(cur);
+    if (cur.w >= 0) advance(cur);
+    __syncthreads();
+    Share sh_i = share(0);
+    if (sh_i.rbeg < sh_i.rend) load_rows(p0_i, 0, sh_i, sh_i.rbeg);
+    for (int i = 0;; ++i) {
+      const bool more = sg_n > 0;   // step i + 1 exists (the same for every thread)
+      const int32_t p0_n = sg_p0;
+      const int bi = i % 3, bn = (i + 1) % 3;
+      if (more) {
+        const int nw = filter(bn, (i + 1) & 3, mc_sg);   // waits for step i + 1's signatures only
+        if (l == 0) sm.wcnt[(i + 1) & 1][wv] = nw;
+        mc_sg = build_mt(cur, (i + 2) & 3);
+        load_sigs(cur);
+        if (cur.w >= 0) advance(cur);
+      }
+      __syncthreads();
+      Share sh_n;
+      if (more) sh_n = share((i + 1) & 1);
+      // --- score step i
+      if (sh_i.rbeg < sh_i.rend) score_rows(p0_i, bi, i & 3, sh_i, sh_i.rbeg);
+      for (int r0 = sh_i.rbeg + RB; r0 < sh_i.rend; r0 += RB) {   // dense filters: further batches
+        load_rows(p0_i, bi, sh_i, r0);
+        score_rows(p0_i, bi, i & 3, sh_i, r0);
+      }
+      if (!more) break;
+      if (sh_n.rbeg < sh_n.rend) load_rows(p0_n, bn, sh_n, sh_n.rbeg);   // step i + 1's first rows
+      sh_i = sh_n;
+      p0_i = p0_n;
+    }
+    __syncthreads();
+    // --- end of the chunk: one pool reservation per slot, then the staged keys; the slots' counts
+    const int ns = nsl < kTSlots ? nsl : kTSlots;
+    const int n_st = sm.stage_n < kTStageWG ? sm.stage_n : kTStageWG;
+    for (int s = tid; s < ns; s += kScanThreads) {
+      const uint32_t c = sm.scount[s];
+      const int q = sm.sq[s];
+      if (c) sm.sbase[s] = atomicAdd(&a.w.pool_cnt[q], c);
+      if (stats) {
+        if (sm.selig[s]) atomicAdd((unsigned long long *)&stats[2 * (size_t)q + 1], (unsigned long long)sm.selig[s]);
+        if (sm.sscan[s]) atomicAdd((unsigned long long *)&stats[2 * (size_t)q], (unsigned long long)sm.sscan[s]);
+      }
+    }
+    __syncthreads();
+    for (int e = tid; e < n_st; e += kScanThreads) {
+      const int s = sm.sslot[e];
+      if (s != 0xFFFF) {
+        const uint32_t o = sm.sbase[s] + sm.srank[e];
+        if (o < cap) a.w.pool[(size_t)sm.sq[s] * cap + o] = sm.skey[e];
+      }
+    }
+    __syncthreads();
+    for (int s = tid; s < ns; s += kScanThreads) {
+      sm.scount[s] = 0u;
+      sm.selig[s] = 0u;
+    }
+    if (tid == 0) {
+      sm.stage_n = 0;
+      sm.next = next_c;
+    }
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------------------------------------------
+// k_xscan: nprobe == nlist.  Every query's stream is the whole catalogue in position order, so one read
+// of a 64-item block serves a block of kXQ queries: v_mfma_i32_16x16x64_i8 multiplies 16 queries by 16
+// items per K slice of 64 bytes.  Lane layout (gfx950, 16x16x64 int8): lane l supplies row l % 16 of each
+// operand with K bytes 16 (l / 16) .. + 15 of the slice, and receives C[4 (l / 16) + r][l % 16], r = 0..3.
+// Items are the columns, queries the rows: lane l holds 4 queries x 1 item per (query tile, item tile),
+// and tests those items' signatures against those queries' masks after the product.
+//
+// Each wave of a workgroup works alone: it takes units (a run of items x a query block) from a queue
+// and walks the run in 64-item steps, the next step's rows and signatures loaded while the current one is
+// scored.  Candidates are staged per wave in LDS (with their rank among the wave's candidates of their
+// query) and go to the pools with one reservation per query.  SAMPLE: the run is one 64-item block per
+// Sample pass: the run is 64 consecutive points of the every-kXStride-th-position stream; each lane keeps
+// its best eligible score per query and writes it to the query's sample buffer (one slot per lane and run).
+
+struct XScanArgs {
+  DevIndex ix;
+  const int8_t *queries;
+  const uint64_t *masks;
+  Work w;
+  int32_t B, n_units, n_qb;
+  uint32_t cap;       // pool keys (main pass) or sample-buffer entries (sample pass) per query
+};
+
+struct XWave {
+  uint32_t mk[kXQ][4];       // request masks of the block's queries (32-bit words)
+  int32_t sc[32][64];        // a step's scores, when it has candidates (entry 8 t + 4 t2 + r, lane)
+  uint64_t key[kXStage];     // staged candidates: (score, position) keys
+  uint8_t qi[kXStage];       //   their query within the block
+  uint16_t rank[kXStage];    //   their rank among the staged candidates of that query
+  uint32_t cnt[kXQ];         // staged candidates per query of the block
+  uint32_t base[kXQ];        // pool positions reserved at a flush
+};
+
+// Order of LDS accesses between the lanes of one wave (its LDS operations complete in order; this keeps
+// the compiler from moving them across each other).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int KS, int W, bool SAMPLE>
+__global__ __launch_bounds__(64 * kXWaves) void k_xscan(XScanArgs a) {
+  __shared__ XWave xw[kXWaves];
+  const int l = lane_id(), wv = threadIdx.x / 64;
+  XWave &S = xw[wv];
+  const int dim = a.ix.dim;
+  const int64_t N = a.ix.n_items;
+  // the stream walked: every position, or (sample pass) every kXStride-th
+  const int64_t NP = SAMPLE ? (N + kXStride - 1) / kXStride : N;
+  const int lr = l & 15, lg = l >> 4;   // operand row (query or item) and K group of this lane
+  uint32_t *qctr = &a.w.counter[SAMPLE ? 4 : 5];
+  if (l < kXQ) S.cnt[l] = 0u;
+  int stage_n = 0;
+  for (;;) {
+    int u = 0;
+    if (l == 0) u = (int)atomicAdd(qctr, 1u);
+    u = __shfl(u, 0);
+    if (u >= a.n_units) break;
+    const int qb = u % a.n_qb, run = u / a.n_qb;
+    const int64_t p_begin = (int64_t)run * (SAMPLE ? 64 : kXChunk);
+    const int64_t p_lim = p_begin + (SAMPLE ? 64 : kXChunk);
+    const int64_t p_end = p_lim < NP ? p_lim : NP;
+    const int q0 = qb * kXQ;
+    // query operands: rows q0 + 16 t2 + lr, K bytes 64 ks + 16 lg .. + 15 (zero beyond dim or B)
+    int4 aop[2][KS];
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+      const int q = q0 + 16 * t2 + lr;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int off = 64 * ks + 16 * lg;
+        const bool ok = q < a.B && off < dim;
+        const int4 v = reinterpret_cast<const int4 *>(a.queries + (size_t)(q < a.B ? q : 0) * dim +
+                                                      (off < dim ? off : 0))[0];
+        aop[t2][ks] = ok ? v : make_int4(0, 0, 0, 0);
+      }
+    }
+    // the masks and thresholds of this lane's result rows: queries q0 + 16 t2 + 4 lg + r.  A row past
+    // the batch never offers a candidate (threshold above every score) and its count is not written.
+    constexpr int MW = 2 * W;   // 32-bit words of a mask
+    int32_t th[2][4];
+    uint32_t ec[2][4];
+    // the block's masks in the wave's LDS (lane j < kXQ writes query q0 + j's)
+    wave_lds_sync();
+    if (l < kXQ) {
+      const int qc = q0 + l < a.B ? q0 + l : 0;
+#pragma unroll
+      for (int ww = 0; ww < W; ++ww) {
+        const uint64_t m = a.masks[(size_t)qc * W + ww];
+        S.mk[l][2 * ww] = (uint32_t)m;
+        S.mk[l][2 * ww + 1] = (uint32_t)(m >> 32);
+      }
+    }
+    wave_lds_sync();
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int q = q0 + 16 * t2 + 4 * lg + r;
+        th[t2][r] = q < a.B ? (SAMPLE ? INT32_MIN : a.w.sthr[q]) : INT32_MAX;
+        ec[t2][r] = 0u;   // sample pass: the lane's best eligible score
+        if constexpr (SAMPLE) ec[t2][r] = (uint32_t)INT32_MIN;
+      }
+    // one step: rows of 4 item tiles (item p0 + 16 t + lr) and one 32-bit word of each item's signature
+    // per lane (word lg; the lanes of the other groups hold the others)
+    typedef int4 StepRows[4][KS];
+    typedef uint32_t StepSigs[4];
+    auto load_step = [&](int64_t p0, StepRows &Bo, StepSigs &NS) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int64_t idx = p0 + 16 * t + lr < NP ? p0 + 16 * t + lr : NP - 1;
+        const int64_t p = SAMPLE ? idx * kXStride : idx;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const int off = 64 * ks + 16 * lg;
+          Bo[t][ks] = reinterpret_cast<const int4 *>(a.ix.items + (size_t)p * dim + (off < dim ? off : 0))[0];
+        }
+        NS[t] = reinterpret_cast<const uint32_t *>(a.ix.sigs)[(size_t)p * MW + (lg % MW)];
+      }
+    };
+    auto flush = [&]() {
+      wave_lds_sync();
+      if (l < kXQ) {
+        const uint32_t c = S.cnt[l];
+        uint32_t b = 0u;
+        if (c && q0 + l < a.B) b = atomicAdd(&a.w.pool_cnt[q0 + l], c);
+        S.base[l] = b;
+        S.cnt[l] = 0u;
+      }
+      wave_lds_sync();
+      for (int e = l; e < stage_n; e += 64) {
+        const int qi = S.qi[e];
+        const uint32_t o = S.base[qi] + S.rank[e];
+        const size_t q = (size_t)(q0 + qi);
+        if (o < a.cap) a.w.pool[q * a.cap + o] = S.key[e];
+      }
+      wave_lds_sync();
+      stage_n = 0;
+    };
+    // score the step in Bo/NS (items p0 ..), count the eligible items, offer the candidates.  FULL: the
+    // step lies wholly inside the run (no item to mask).
+    auto score_step = [&](int64_t p0, const StepRows &Bo, const StepSigs &SG, auto full) {
+      typedef int v4i __attribute__((ext_vector_type(4)));
+      constexpr bool FULL = decltype(full)::value;
+      uint32_t cbits = 0u;   // bit (8 t + 4 t2 + r): candidate
+      v4i acc[4][2];
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) {
+          v4i c = {0, 0, 0, 0};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            const v4i av = {aop[t2][ks].x, aop[t2][ks].y, aop[t2][ks].z, aop[t2][ks].w};
+            const v4i bv = {Bo[t][ks].x, Bo[t][ks].y, Bo[t][ks].z, Bo[t][ks].w};
+            c = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bv, c, 0, 0, 0);
+          }
+          acc[t][t2] = c;
+        }
+      // the complemented signature words of item lr of each tile (an item passes a mask when no mask bit
+      // falls on a zero of its signature), gathered from the lanes of the other groups
+      uint32_t ns[4][MW];
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int ww = 0; ww < MW; ++ww) ns[t][ww] = ~(uint32_t)__shfl((int)SG[t], lr + 16 * ww);
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          uint32_t mq[MW];   // the mask of this lane's query 16 t2 + 4 lg + r
+#pragma unroll
+          for (int ww = 0; ww < MW; ++ww) mq[ww] = S.mk[16 * t2 + 4 * lg + r][ww];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const bool item_ok = FULL || p0 + 16 * t + lr < p_end;
+            uint32_t x = 0u;
+#pragma unroll
+            for (int ww = 0; ww < MW; ++ww) x |= mq[ww] & ns[t][ww];
+            const bool el = item_ok && x == 0u;
+            if constexpr (SAMPLE) {
+              const int32_t cur = (int32_t)ec[t2][r], sc = acc[t][t2][r];
+              ec[t2][r] = (uint32_t)(el && sc > cur ? sc : cur);
+            } else {
+              ec[t2][r] += el ? 1u : 0u;
+              const bool cand = el && acc[t][t2][r] >= th[t2][r];
+              cbits |= cand ? 1u << (8 * t + 4 * t2 + r) : 0u;
+            }
+          }
+      }
+      if constexpr (SAMPLE) return;
+      if (__ballot(cbits != 0u) == 0ull) return;
+      // rare: the step's scores go to LDS and its candidates are staged in one loop over the result
+      // entries
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) S.sc[8 * t + 4 * t2 + r][l] = acc[t][t2][r];
+      wave_lds_sync();
+#pragma unroll 1
+      for (int c = 0; c < 32; ++c) {
+        const bool cand = (cbits >> c) & 1u;
+        const uint64_t b = __ballot(cand);
+        if (b == 0ull) continue;
+        if (stage_n + 64 > kXStage) flush();
+        if (cand) {
+          const int t = c >> 3, t2 = (c >> 2) & 1, r = c & 3;
+          const int e = stage_n + mbcnt(b);
+          const int qi = 16 * t2 + 4 * lg + r;
+          const int32_t score = S.sc[c][l];
+          const int32_t pos = (int32_t)(p0 + 16 * t + lr);
+          S.key[e] = pos_key(score, pos);
+          S.qi[e] = (uint8_t)qi;
+          S.rank[e] = (uint16_t)atomicAdd(&S.cnt[qi], 1u);
+        }
+        stage_n += __popcll(b);
+      }
+      wave_lds_sync();
+    };
+    using Full = std::integral_constant<bool, true>;
+    using Part = std::integral_constant<bool, false>;
+    auto score_any = [&](int64_t p0, const StepRows &Bo, const StepSigs &SG) {
+      if (p0 + 64 <= p_end)
+        score_step(p0, Bo, SG, Full{});
+      else
+        score_step(p0, Bo, SG, Part{});
+    };
+    // triple-buffered walk over three named buffers: the loads of steps s + 1 and s + 2 are in flight
+    // while step s is scored (a request past the run repeats the run's first step)
+    StepRows ra, rb, rc;
+    StepSigs sa, sb, sc;
+    int64_t p0 = p_begin;
+    auto ahead = [&](int64_t p) { return p < p_end ? p : p_begin; };
+    load_step(p0, ra, sa);
+    load_step(ahead(p0 + 64), rb, sb);
+    for (;;) {
+      if (p0 >= p_end) break;
+      load_step(ahead(p0 + 128), rc, sc);
+      score_any(p0, ra, sa);
+      p0 += 64;
+      if (p0 >= p_end) break;
+      load_step(ahead(p0 + 128), ra, sa);
+      score_any(p0, rb, sb);
+      p0 += 64;
+      if (p0 >= p_end) break;
+      load_step(ahead(p0 + 128), rb, sb);
+      score_any(p0, rc, sc);
+      p0 += 64;
+    }
+    if (stage_n > 0) flush();
+    if (SAMPLE) {
+      // the lane's best eligible score of each of its queries over this run: slot 16 run + lr
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int q = q0 + 16 * t2 + 4 * lg + r;
+          if (q < a.B) a.w.sbuf[(size_t)q * a.cap + 16 * run + lr] = (int32_t)ec[t2][r];
+        }
+    }
+    // eligible items of each query of the block, summed over the 16 lanes that hold its items
+    if (!SAMPLE && a.w.stats) {
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          uint32_t v = ec[t2][r];
+          v += __shfl_xor(v, 1);
+          v += __shfl_xor(v, 2);
+          v += __shfl_xor(v, 4);
+          v += __shfl_xor(v, 8);
+          const int q = q0 + 16 * t2 + 4 * lg + r;
+          if (lr == 0 && q < a.B && v)
+            atomicAdd((unsigned long long *)&a.w.stats[2 * (size_t)q + 1], (unsigned long long)v);
+        }
+    }
+  }
+}
+
+// Thresholds from the sample pass.  Every slot of a query's sample buffer holds the best eligible score
+// among a few sampled items (INT32_MIN when none passed), the slots covering disjoint items.  Each thread
+// takes the best of its slots; the r-th best of those per-thread maxima is the threshold, r for kAlpha * k
+// items over the whole catalogue (at least kRMin): r distinct sampled items score at or above it.  With
+// r far below the thread count it sits close to the r-th best sample.  No threshold when the pool holds
+// the whole catalogue or fewer than r threads saw an eligible sample.  Also the scanned count of every
+// query (the whole catalogue).
+__global__ __launch_bounds__(kSelThreads) void k_xthr(Work w, int64_t n_items, int32_t k, int32_t pool_cap,
+                                                      int32_t scap, int32_t n_points, int32_t force) {
+  __shared__ SelScratch sel;
+  __shared__ int wave_tot[kSelThreads / 64 + 1];
+  const int q = blockIdx.x, tid = threadIdx.x;
+  const int32_t *sb = w.sbuf + (size_t)q * scap;
+  int32_t st = INT32_MIN;
+  int r = 0;
+  if (n_items > pool_cap && n_points > 0) {
+    const int64_t r0 = ((int64_t)kAlpha * k * n_points + n_items - 1) / n_items;
+    r = (int)(r0 > kRMin ? r0 : kRMin);
+  }
+  if (r > 0 && r <= kSelThreads) {   // uniform over the block
+    int32_t mx = INT32_MIN;
+    for (int i0 = tid; i0 < scap; i0 += 8 * kSelThreads) {
+      int32_t v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = i0 + u * kSelThreads < scap ? sb[i0 + u * kSelThreads] : INT32_MIN;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) mx = v[u] > mx ? v[u] : mx;
+    }
+    int have;
+    block_excl_scan<kSelThreads>(mx != INT32_MIN ? 1 : 0, wave_tot, &have);
+    if (have >= r) {
+      const uint64_t T = block_select<kSelThreads>(
+          [&](auto f) {
+            if (mx != INT32_MIN) f(make_key(mx, (uint32_t)tid));
+          },
+          r, sel);
+      st = key_score(T);
+    }
+  }
+  if (force) st = INT32_MAX;
+  if (tid == 0) {
+    w.sthr[q] = st;
+    if (w.stats) w.stats[2 * (size_t)q] = w.qlen[q];
+  }
+}
+
+// ------------------------------------------------------------------------------------------------
+// k_pmerge: one workgroup per query whose pool proves its top k.  The k-th best (score, position) key
+// fixes the k-th best score; every key at that score or above becomes a (score, id) key, and the exact
+// top k of those is sorted and written.  A pool of at most kPoolLds keys is staged in LDS with one
+// batch of loads per thread and merged there; a larger one is read from HBM at each step.
+
+struct PMergeArgs {
+  DevIndex ix;
+  Work w;
+  const float *query_scales;
+  float item_scale;
+  int32_t B, k;
+  uint32_t pool_cap;
+  int64_t *out_ids;
+  int32_t *out_scores;
+  float *out_fscores;
+  int32_t *out_counts;
+};
+
+constexpr int kPoolLds = 12 * kSelThreads;   // pool keys merged in LDS (96 KB)
+static_assert(kPoolLds >= kMergeCap, "the LDS merge holds at least the staging capacity");
+
+// Keep the keys >= lo of cand[0..n) (n <= kPoolLds), in place, as (score, id) keys when to_id; returns
+// the count kept.  Each thread reads its keys (and their ids) before the block scan's barriers and
+// writes them after.
+__device__ __forceinline__ int pool_keep(uint64_t *cand, int n, uint64_t lo, bool to_id, const int32_t *perm,
+                                         int *wave_tot) {
+  constexpr int PER = kPoolLds / kSelThreads;
+  const int tid = threadIdx.x;
+  uint64_t kv[PER];
+  uint32_t idv[PER];
+  int keep = 0;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int i = u * kSelThreads + tid;
+    kv[u] = i < n ? cand[i] : 0ull;
+    const bool k_ = i < n && kv[u] >= lo;
+    keep += k_ ? 1 : 0;
+    idv[u] = (k_ && to_id) ? (uint32_t)perm[(uint32_t)kv[u]] : 0u;
+  }
+  int tot;
+  int off = block_excl_scan<kSelThreads>(keep, wave_tot, &tot);   // barriers inside
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int i = u * kSelThreads + tid;
+    if (i < n && kv[u] >= lo)
+      cand[off++] = to_id ? make_key((int32_t)((uint32_t)(kv[u] >> 32) ^ 0x80000000u), idv[u]) : kv[u];
+  }
+  __syncthreads();
+  return tot;
+}
+
+__global__ __launch_bounds__(kSelThreads) void k_pmerge(PMergeArgs a) {
+  __shared__ SelScratch sel;
+  __shared__ uint64_t cand[kPoolLds];
+  __shared__ int wave_tot[kSelThreads / 64 + 1];
+  __shared__ int ncand;
+  const int q = blockIdx.x, tid = threadIdx.x, k = a.k;
+  if (a.w.redo[q]) return;   // merged by the query path
+  const int n = (int)a.w.pool_cnt[q];
+  uint64_t *pool = a.w.pool + (size_t)q * a.pool_cap;
+  const int nout = n < k ? n : k;
+  int m;
+  if (n <= kPoolLds) {
+    constexpr int PER = kPoolLds / kSelThreads;
+    uint64_t v[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int i = u * kSelThreads + tid;
+      v[u] = i < n ? pool[i] : 0ull;
+    }
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int i = u * kSelThreads + tid;
+      if (i < n) cand[i] = v[u];
+    }
+    __syncthreads();
+    m = n;
+    if (n > k) {
+      const uint64_t T = block_select<kSelThreads>(
+          [&](auto f) {
+            for (int i = tid; i < n; i += kSelThreads) f(cand[i]);
+          },
+          k, sel);
+      // every key with the k-th best score or better, as (score, id) keys
+      m = pool_keep(cand, n, (T >> 32) << 32, true, a.ix.perm, wave_tot);
+      if (m > k) {
+        const uint64_t Tk = block_select<kSelThreads>(
+            [&](auto f) {
+              for (int i = tid; i < m; i += kSelThreads) f(cand[i]);
+            },
+            k, sel);
+        m = pool_keep(cand, m, Tk, false, a.ix.perm, wave_tot);   // exactly k distinct keys
+      }
+    } else {
+      m = pool_keep(cand, n, 0ull, true, a.ix.perm, wave_tot);
+    }
+  } else {
+    // a pool larger than LDS: select in HBM
+    const uint64_t T = block_select<kSelThreads>(
+        [&](auto f) {
+          for (int i = tid; i < n; i += kSelThreads) f(pool[i]);
+        },
+        k, sel);
+    const uint64_t lo = (T >> 32) << 32;   // the smallest key with the k-th best score
+    // keys at or above lo become (score, id) keys in place; their upper half, the score, is unchanged
+    for (int i = tid; i < n; i += kSelThreads) {
+      const uint64_t v = pool[i];
+      if (v >= lo) pool[i] = make_key((int32_t)((uint32_t)(v >> 32) ^ 0x80000000u), (uint32_t)a.ix.perm[(uint32_t)v]);
+    }
+    if (tid == 0) ncand = 0;
+    __syncthreads();
+    for (int i = tid; i < n; i += kSelThreads) {
+      const uint64_t v = pool[i];
+      if (v >= lo) {
+        const int o = atomicAdd(&ncand, 1);
+        if (o < kPoolLds) cand[o] = v;
+      }
+    }
+    __syncthreads();
+    m = ncand;
+    if (m > kPoolLds) {
+      // heavy ties at the k-th score: select among the converted keys in the pool
+      const uint64_t Tk = block_select<kSelThreads>(
+          [&](auto f) {
+            for (int i = tid; i < n; i += kSelThreads) {
+              const uint64_t v = pool[i];
+              if (v >= lo) f(v);
+            }
+          },
+          k, sel);
+      if (tid == 0) ncand = 0;
+      __syncthreads();
+      for (int i = tid; i < n; i += kSelThreads) {
+        const uint64_t v = pool[i];
+        if (v >= lo && v >= Tk) cand[atomicAdd(&ncand, 1)] = v;   // exactly k distinct keys
+      }
+      __syncthreads();
+      m = k;
+    } else if (m > k) {
+      const uint64_t Tk = block_select<kSelThreads>(
+          [&](auto f) {
+            for (int i = tid; i < m; i += kSelThreads) f(cand[i]);
+          },
+          k, sel);
+      m = pool_keep(cand, m, Tk, false, a.ix.perm, wave_tot);
+    }
+  }
+  emit_sorted<kSelThreads>(cand, m, nout, q, k, a.query_scales, a.item_scale, a.out_ids, a.out_scores,
+                           a.out_fscores);
+  if (tid == 0 && a.out_counts) a.out_counts[q] = nout;
+}
+
+// ------------------------------------------------------------------------------------------------
+// launch wrappers
+
+hipError_t launch_tile_plan(const DevIndex &ix, const uint64_t *masks, const SearchShape &sh, const Work &w,
+                            hipStream_t s) {
+  k_gcount<<<sh.B, 256, 0, s>>>(w.probes, sh.nprobe, w);
+  k_tplan1<<<(ix.nlist + kSelThreads - 1) / kSelThreads, kSelThreads, 0, s>>>(ix, w);
+  k_tplan2<<<(ix.nlist + kSelThreads - 1) / kSelThreads + 1, kSelThreads, 0, s>>>(ix, sh.TP, w);
+  k_gfill<<<sh.B, 256, 0, s>>>(w.probes, masks, sh.nprobe, ix.sig_words, w);
+  k_tentries<<<(sh.max_entries + 255) / 256, 256, 0, s>>>(ix, sh.max_entries, w);
+  k_tchunks<<<(sh.max_tchunks + 256) / 256, 256, 0, s>>>(ix, sh.max_tchunks, w);
+  return hipGetLastError();
+}
+
+template <int LPR>
+static void tscan_w(const TScanArgs &a, int W, hipStream_t s) {
+  if (W == 2)
+    k_tscan<LPR, 2><<<a.P, kScanThreads, 0, s>>>(a);
+  else
+    k_tscan<LPR, 1><<<a.P, kScanThreads, 0, s>>>(a);
+}
+
+hipError_t launch_tscan(const DevIndex &ix, const int8_t *queries, const SearchShape &sh, const Work &w,
+                        hipStream_t s) {
+  TScanArgs a{ix, queries, w, sh.B, sh.TP, (uint32_t)sh.pool_cap};
+  switch (ix.dim) {
+    case 16: tscan_w<1>(a, ix.sig_words, s); break;
+    case 32: tscan_w<2>(a, ix.sig_words, s); break;
+    case 64: tscan_w<4>(a, ix.sig_words, s); break;
+    case 128: tscan_w<8>(a, ix.sig_words, s); break;
+    case 256: tscan_w<16>(a, ix.sig_words, s); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int LPR>
+static int tscan_occ_w(int W) {
+  int n = 0;
+  hipError_t e = W == 2 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_tscan<LPR, 2>, kScanThreads, 0)
+                        : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_tscan<LPR, 1>, kScanThreads, 0);
+  return e == hipSuccess ? n : 0;
+}
+
+int tscan_blocks_per_cu(int32_t dim, int32_t sig_words) {
+  switch (dim) {
+    case 16: return tscan_occ_w<1>(sig_words);
+    case 32: return tscan_occ_w<2>(sig_words);
+    case 64: return tscan_occ_w<4>(sig_words);
+    case 128: return tscan_occ_w<8>(sig_words);
+    case 256: return tscan_occ_w<16>(sig_words);
+    default: return 0;
+  }
+}
+
+template <int KS, bool SAMPLE>
+static void xscan_w(const XScanArgs &a, int W, int grid, hipStream_t s) {
+  if (W == 2)
+    k_xscan<KS, 2, SAMPLE><<<grid, 64 * kXWaves, 0, s>>>(a);
+  else
+    k_xscan<KS, 1, SAMPLE><<<grid, 64 * kXWaves, 0, s>>>(a);
+}
+
+template <bool SAMPLE>
+static hipError_t xscan_dim(const XScanArgs &a, int dim, int W, int grid, hipStream_t s) {
+  switch (dim) {
+    case 16:
+    case 32:
+    case 64: xscan_w<1, SAMPLE>(a, W, grid, s); break;
+    case 128: xscan_w<2, SAMPLE>(a, W, grid, s); break;
+    case 256: xscan_w<4, SAMPLE>(a, W, grid, s); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipSuccess;
+}
+
+int xscan_blocks_per_cu(int32_t dim, int32_t sig_words) {
+  int n = 0;
+  hipError_t e = hipSuccess;
+  const bool w2 = sig_words == 2;
+  switch (dim) {
+    case 16:
+    case 32:
+    case 64:
+      e = w2 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_xscan<1, 2, false>, 64 * kXWaves, 0)
+             : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_xscan<1, 1, false>, 64 * kXWaves, 0);
+      break;
+    case 128:
+      e = w2 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_xscan<2, 2, false>, 64 * kXWaves, 0)
+             : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_xscan<2, 1, false>, 64 * kXWaves, 0);
+      break;
+    case 256:
+      e = w2 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_xscan<4, 2, false>, 64 * kXWaves, 0)
+             : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_xscan<4, 1, false>, 64 * kXWaves, 0);
+      break;
+    default: return 0;
+  }
+  return e == hipSuccess ? n : 0;
+}
+
+hipError_t launch_exh_scan(const DevIndex &ix, const int8_t *queries, const uint64_t *masks,
+                           const SearchShape &sh, const Work &w, hipStream_t s) {
+  const int n_qb = (sh.B + kXQ - 1) / kXQ;
+  const int64_t N = ix.n_items;
+  // sample pass, thresholds, main pass
+  XScanArgs as{ix, queries, masks, w, sh.B, sh.n_sblocks * n_qb, n_qb, (uint32_t)sh.scap};
+  hipError_t e = xscan_dim<true>(as, ix.dim, ix.sig_words, sh.XP, s);
+  if (e != hipSuccess) return e;
+  k_xthr<<<sh.B, kSelThreads, 0, s>>>(w, N, sh.k, sh.pool_cap, sh.scap, (int32_t)((N + kXStride - 1) / kXStride),
+                                      sh.force_redo);
+  const int64_t runs = (N + kXChunk - 1) / kXChunk;
+  XScanArgs am{ix, queries, masks, w, sh.B, (int32_t)(runs * n_qb), n_qb, (uint32_t)sh.pool_cap};
+  e = xscan_dim<false>(am, ix.dim, ix.sig_words, sh.XP, s);
+  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+hipError_t launch_pool_merge(const DevIndex &ix, const float *query_scales, const SearchShape &sh, const Work &w,
+                             int64_t *out_ids, int32_t *out_scores, float *out_fscores, int32_t *out_counts,
+                             hipStream_t s) {
+  PMergeArgs a{ix, w, query_scales, ix.item_scale, sh.B, sh.k, (uint32_t)sh.pool_cap, out_ids, out_scores,
+               out_fscores, out_counts};
+  k_pmerge<<<sh.B, kSelThreads, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace svt

@@ -18,6 +18,9 @@ LIB_PATH = os.path.join(_HERE, "libsvt.so")
 SVT_OK, SVT_EINVAL, SVT_ENOMEM, SVT_EDEVICE, SVT_EUNSUPPORTED, SVT_ESTATE = 0, -1, -2, -3, -4, -5
 SVT_MAX_K = 2048
 SVT_MAX_SIG_WORDS = 2
+SVT_PATH_AUTO, SVT_PATH_QUERY, SVT_PATH_TILE = 0, 1, 2
+SVT_OPT_MERGE_FROM_SLOTS, SVT_OPT_FORCE_REDO = 1, 2
+_PATHS = {"auto": SVT_PATH_AUTO, "query": SVT_PATH_QUERY, "tile": SVT_PATH_TILE}
 
 #: every symbol include/svt.h declares
 EXPORTED = ("svt_index_upload", "svt_index_free", "svt_index_info", "svt_search_workspace_size", "svt_search",
@@ -44,6 +47,25 @@ class svt_index_desc(ctypes.Structure):
     ]
 
 
+class svt_search_options(ctypes.Structure):
+    _fields_ = [
+        ("path", ctypes.c_int32),
+        ("pool_keys", ctypes.c_int32),
+        ("flags", ctypes.c_uint32),
+        ("reserved", ctypes.c_int32 * 5),
+    ]
+
+
+def make_options(path="auto", pool_keys: int = 0, flags: int = 0) -> svt_search_options:
+    """Search options: path "auto" | "query" | "tile" (or an SVT_PATH_* value), pool_keys (tile path,
+    0 = default), flags (OR of SVT_OPT_*)."""
+    o = svt_search_options()
+    o.path = _PATHS[path] if isinstance(path, str) else int(path)
+    o.pool_keys = int(pool_keys)
+    o.flags = int(flags)
+    return o
+
+
 _lib = None
 
 
@@ -57,11 +79,11 @@ def lib():
     L = ctypes.CDLL(LIB_PATH)
     vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     L.svt_index_upload.argtypes = [ctypes.POINTER(svt_index_desc), vp, ctypes.POINTER(vp)]
-    L.svt_index_free.argtypes = [vp]
+    L.svt_index_free.argtypes = [vp, vp]
     L.svt_index_info.argtypes = [vp, vp, vp, vp, vp]
-    L.svt_search_workspace_size.argtypes = [vp, i32, i32, i32]
+    L.svt_search_workspace_size.argtypes = [vp, i32, i32, i32, vp]
     L.svt_search_workspace_size.restype = sz
-    L.svt_search.argtypes = [vp, i32, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.svt_search.argtypes = [vp, i32, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.svt_last_error.restype = ctypes.c_char_p
     L.svt_bloom_mask.argtypes = [vp, i32, i32, i32, vp]
     L.svt_bloom_sign.argtypes = [vp, i64, i32, i32, i32, vp, i32]
@@ -95,6 +117,32 @@ def _stream_ptr(stream):
     import torch
     s = stream if stream is not None else torch.cuda.current_stream()
     return ctypes.c_void_p(s.cuda_stream)
+
+
+def _opt_ptr(opts):
+    return None if opts is None else ctypes.byref(opts)
+
+
+def _check_tensor(name, t, dtypes, shape, device=None, nullable=False):
+    """The C side cannot see dtypes, shapes or strides: a wrong tensor would be read or written out of
+    bounds on the device.  Raise ValueError unless t is a contiguous tensor of one of ``dtypes`` with
+    exactly ``shape``, on ``device`` (when given)."""
+    if t is None:
+        if nullable:
+            return
+        raise ValueError(f"{name}: required")
+    if not hasattr(t, "data_ptr") or not hasattr(t, "dtype"):
+        raise ValueError(f"{name}: expected a torch tensor, got {type(t).__name__}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name}: dtype {t.dtype} not in {[str(d) for d in dtypes]}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)} != {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: not contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name}: on {t.device}, expected {device}")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: not a device tensor")
 
 
 # ------------------------------------------------------------------------------------------------
@@ -133,8 +181,9 @@ def svt_index_upload(items: np.ndarray, sigs: np.ndarray, list_of: np.ndarray, c
     return h
 
 
-def svt_index_free(handle) -> None:
-    _check(lib().svt_index_free(handle))
+def svt_index_free(handle, stream=None) -> None:
+    """Free an index after synchronising ``stream`` (the stream its searches ran on)."""
+    _check(lib().svt_index_free(handle, _stream_ptr(stream)))
 
 
 def svt_index_info(handle) -> Tuple[int, int, int, int]:
@@ -144,9 +193,9 @@ def svt_index_info(handle) -> Tuple[int, int, int, int]:
     return n.value, d.value, w.value, nl.value
 
 
-def svt_search_workspace_size(handle, n_queries: int, nprobe: int, k: int) -> int:
-    sz = lib().svt_search_workspace_size(handle, n_queries, nprobe, k)
-    if sz == 0 and n_queries >= 0:
+def svt_search_workspace_size(handle, n_queries: int, nprobe: int, k: int, opts=None) -> int:
+    sz = lib().svt_search_workspace_size(handle, n_queries, nprobe, k, _opt_ptr(opts))
+    if sz == 0:
         err = svt_last_error()
         if err:
             raise SvtError(SVT_EINVAL, err)
@@ -154,13 +203,20 @@ def svt_search_workspace_size(handle, n_queries: int, nprobe: int, k: int) -> in
 
 
 def svt_search(handle, queries, masks, nprobe: int, k: int, query_scales=None, out_ids=None, out_scores=None,
-               out_fscores=None, out_counts=None, out_stats=None, workspace=None, stream=None):
+               out_fscores=None, out_counts=None, out_stats=None, workspace=None, stream=None, opts=None):
     """queries: int8 [B, d] cuda tensor; masks: uint64 (or int64) [B, W] cuda tensor.
     Returns (ids int64 [B,k], scores int32 [B,k], fscores f32 [B,k], counts int32 [B], stats int64 [B,2]);
-    outputs are allocated with torch unless passed in.  Asynchronous on ``stream``."""
+    outputs are allocated with torch unless passed in.  Asynchronous on ``stream``.  ``opts``: a
+    svt_search_options (see make_options) or None."""
     import torch
+    n, dim, W, _ = svt_index_info(handle)
+    if not hasattr(queries, "shape") or len(queries.shape) != 2:
+        raise ValueError("queries: expected a 2-D tensor [B, dim]")
     B = int(queries.shape[0])
     dev = queries.device
+    _check_tensor("queries", queries, (torch.int8,), (B, dim))
+    _check_tensor("masks", masks, (torch.int64, torch.uint64), (B, W), dev)
+    _check_tensor("query_scales", query_scales, (torch.float32,), (B,), dev, nullable=True)
     if out_ids is None:
         out_ids = torch.empty((B, k), dtype=torch.int64, device=dev)
     if out_scores is None:
@@ -171,12 +227,19 @@ def svt_search(handle, queries, masks, nprobe: int, k: int, query_scales=None, o
         out_counts = torch.empty((B,), dtype=torch.int32, device=dev)
     if out_stats is None:
         out_stats = torch.empty((B, 2), dtype=torch.int64, device=dev)
+    _check_tensor("out_ids", out_ids, (torch.int64,), (B, k), dev)
+    _check_tensor("out_scores", out_scores, (torch.int32,), (B, k), dev)
+    _check_tensor("out_fscores", out_fscores, (torch.float32,), (B, k), dev)
+    _check_tensor("out_counts", out_counts, (torch.int32,), (B,), dev)
+    _check_tensor("out_stats", out_stats, (torch.int64,), (B, 2), dev)
     if workspace is None:
-        nbytes = svt_search_workspace_size(handle, B, nprobe, k) if B > 0 else 0
+        nbytes = svt_search_workspace_size(handle, B, nprobe, k, opts) if B > 0 else 0
         workspace = torch.empty((max(nbytes, 256),), dtype=torch.uint8, device=dev)
+    _check_tensor("workspace", workspace, (torch.uint8,), (workspace.numel(),), dev)
     _check(lib().svt_search(handle, B, _t_ptr(queries), _t_ptr(masks), _t_ptr(query_scales), nprobe, k,
                             _t_ptr(out_ids), _t_ptr(out_scores), _t_ptr(out_fscores), _t_ptr(out_counts),
-                            _t_ptr(out_stats), _t_ptr(workspace), int(workspace.numel()), _stream_ptr(stream)))
+                            _t_ptr(out_stats), _opt_ptr(opts), _t_ptr(workspace), int(workspace.numel()),
+                            _stream_ptr(stream)))
     return out_ids, out_scores, out_fscores, out_counts, out_stats
 
 
@@ -204,21 +267,23 @@ class Index:
         self.n_items, self.dim, self.sig_words, self.nlist = svt_index_info(self.handle)
         self._ws = None
 
-    def workspace(self, n_queries: int, nprobe: int, k: int):
+    def workspace(self, n_queries: int, nprobe: int, k: int, opts=None):
         import torch
-        nbytes = max(256, svt_search_workspace_size(self.handle, n_queries, nprobe, k))
+        nbytes = max(256, svt_search_workspace_size(self.handle, n_queries, nprobe, k, opts))
         if self._ws is None or self._ws.numel() < nbytes:
+            self._ws = None
             self._ws = torch.empty((nbytes,), dtype=torch.uint8, device="cuda")
         return self._ws
 
-    def search(self, queries, masks, nprobe: int, k: int, query_scales=None, stream=None, **outs):
-        ws = self.workspace(int(queries.shape[0]), nprobe, k) if int(queries.shape[0]) > 0 else None
+    def search(self, queries, masks, nprobe: int, k: int, query_scales=None, stream=None, opts=None, **outs):
+        B = int(queries.shape[0])
+        ws = self.workspace(B, nprobe, k, opts) if B > 0 else None
         return svt_search(self.handle, queries, masks, nprobe, k, query_scales=query_scales, workspace=ws,
-                          stream=stream, **outs)
+                          stream=stream, opts=opts, **outs)
 
-    def close(self):
+    def close(self, stream=None):
         if self.handle is not None:
-            svt_index_free(self.handle)
+            svt_index_free(self.handle, stream)
             self.handle = None
 
     def __del__(self):

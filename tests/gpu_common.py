@@ -20,12 +20,12 @@ def say(*a):
     sys.stdout.flush()
 
 
-def gpu_search(ix, queries, masks, nprobe, k, query_scales=None):
+def gpu_search(ix, queries, masks, nprobe, k, query_scales=None, opts=None):
     import torch
     q = torch.from_numpy(np.ascontiguousarray(queries, np.int8)).cuda()
     m = torch.from_numpy(np.ascontiguousarray(masks, np.uint64).view(np.int64)).cuda()
     qs = None if query_scales is None else torch.from_numpy(np.ascontiguousarray(query_scales, np.float32)).cuda()
-    ids, sc, fs, cnt, st = ix.search(q, m, nprobe, k, query_scales=qs)
+    ids, sc, fs, cnt, st = ix.search(q, m, nprobe, k, query_scales=qs, opts=opts)
     torch.cuda.synchronize()
     return ids.cpu().numpy(), sc.cpu().numpy(), fs.cpu().numpy(), cnt.cpu().numpy(), st.cpu().numpy()
 
@@ -48,10 +48,12 @@ def compare(got, ref, k, label=""):
     assert np.all(ids[~valid] == -1) and np.all(sc[~valid] == INT32_MIN), f"{label}: id/score padding"
 
 
-def check_invariants(items, sigs, list_of, got, masks, queries, k):
+def check_invariants(items, sigs, list_of, got, masks, queries, k, centroids=None, nprobe=None):
     """Properties that hold at any size: rows sorted by (score desc, id asc), ids unique, every id
-    eligible, every score the exact dot product."""
+    eligible, every score the exact dot product, and (given the centroids) every id in one of the
+    query's probed clusters as the oracle's coarse step picks them."""
     ids, sc, fs, cnt, st = got
+    orc = oracle.Oracle() if centroids is not None else None
     for b in range(ids.shape[0]):
         n = int(cnt[b])
         i, s = ids[b, :n], sc[b, :n].astype(np.int64)
@@ -61,6 +63,9 @@ def check_invariants(items, sigs, list_of, got, masks, queries, k):
         if n:
             assert np.all((sigs[i] & masks[b]) == masks[b])
             assert np.array_equal(items[i].astype(np.int64) @ queries[b].astype(np.int64), s)
+            if orc is not None:
+                probes, _ = orc.coarse(centroids, queries[b], nprobe)
+                assert np.all(np.isin(list_of[i], probes)), f"query {b}: an id outside the probed clusters"
 
 
 def oracle_search(items, sigs, list_of, cent, scale, queries, masks, nprobe, k, query_scales=None, threads=8):

@@ -78,10 +78,46 @@ def test_upload_argument_errors(L):
 
 def test_search_rejects_dead_index(L):
     bogus = ctypes.c_void_p(0x1000)
-    assert L.svt_search(bogus, 1, None, None, None, 1, 1, None, None, None, None, None, None, 0, None) == svt.SVT_ESTATE
-    assert L.svt_search_workspace_size(bogus, 1, 1, 1) == 0
-    assert L.svt_index_free(bogus) == svt.SVT_ESTATE
-    assert L.svt_index_free(None) == svt.SVT_OK
+    assert L.svt_search(bogus, 1, None, None, None, 1, 1, None, None, None, None, None, None, None, 0,
+                        None) == svt.SVT_ESTATE
+    assert L.svt_search_workspace_size(bogus, 1, 1, 1, None) == 0
+    assert "not a live index" in svt.svt_last_error()
+    assert L.svt_index_free(bogus, None) == svt.SVT_ESTATE
+    assert L.svt_index_free(None, None) == svt.SVT_OK
+
+
+def test_options_struct_layout():
+    # 8 words: path, pool_keys, flags, 5 reserved (must stay in step with include/svt.h)
+    assert ctypes.sizeof(svt.svt_search_options) == 32
+    o = svt.make_options("tile", 64, svt.SVT_OPT_FORCE_REDO)
+    assert (o.path, o.pool_keys, o.flags) == (svt.SVT_PATH_TILE, 64, 2)
+    assert list(o.reserved) == [0] * 5
+    hdr = open(os.path.join(ROOT, "include", "svt.h")).read()
+    for name, v in (("SVT_PATH_AUTO", 0), ("SVT_PATH_QUERY", 1), ("SVT_PATH_TILE", 2)):
+        assert re.search(rf"{name} = {v}\b", hdr), name
+    assert re.search(r"#define SVT_OPT_MERGE_FROM_SLOTS 1u", hdr)
+    assert re.search(r"#define SVT_OPT_FORCE_REDO 2u", hdr)
+
+
+def test_binding_rejects_bad_tensors():
+    """The binding checks dtype, shape, contiguity and device before any pointer reaches the C side
+    (which cannot see them): wrong tensors raise ValueError."""
+    import torch
+    ck = svt._check_tensor
+    q = torch.zeros((4, 64), dtype=torch.int8)
+    with pytest.raises(ValueError, match="dtype"):
+        ck("queries", q.to(torch.int16), (torch.int8,), (4, 64))
+    with pytest.raises(ValueError, match="shape"):
+        ck("queries", torch.zeros((4, 128), dtype=torch.int8), (torch.int8,), (4, 64))
+    with pytest.raises(ValueError, match="contiguous"):
+        ck("queries", torch.zeros((64, 4), dtype=torch.int8).t(), (torch.int8,), (4, 64))
+    with pytest.raises(ValueError, match="device"):
+        ck("queries", q, (torch.int8,), (4, 64))
+    with pytest.raises(ValueError, match="required"):
+        ck("masks", None, (torch.int64,), (4, 2))
+    ck("query_scales", None, (torch.float32,), (4,), nullable=True)
+    with pytest.raises(ValueError, match="torch tensor"):
+        ck("out_ids", np.zeros((4, 8), np.int64), (torch.int64,), (4, 8))
 
 
 def test_profile_modes(L):

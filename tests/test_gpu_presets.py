@@ -1,6 +1,7 @@
-"""GPU vs oracle on the five workload presets at their full sizes, in the launch configuration the
-benchmark times.  The 1M and 10M presets are compared on every query; the 80M presets on a sample
-of queries the oracle computes one by one, plus size-independent invariants on every query."""
+"""GPU vs oracle on the workload presets at their full sizes, in the launch configuration the benchmark
+times: every query of every batch is compared element by element with the oracle, on both search paths
+(query by query, and the tile path that reads each probed cluster once per batch), and checked for the
+size-independent invariants (order, uniqueness, eligibility, exact scores, probe-set membership)."""
 import time
 
 import numpy as np
@@ -49,22 +50,25 @@ class Preset:
         assert np.array_equal(masks, o_masks)
         return qs.queries, masks
 
-    def check(self, B, offset, sample=None, nprobe=None, k=None, label=""):
+    def check(self, B, offset, nprobe=None, k=None, label="", paths=("query", "tile")):
+        from int8_ivf_ann_amd import svt as svt_mod
         nprobe = nprobe or self.cfg["nprobe"]
         k = k or self.cfg["k"]
         q, masks = self.batch(B, offset)
         t = time.time()
-        got = gpu_search(self.ix, q, masks, nprobe, k)
-        say(f"{label}: B={B} gpu search {1e3 * (time.time() - t):.1f} ms (incl. copies); "
-            f"eligible/query median {int(np.median(got[4][:, 1]))}")
-        rows = np.arange(B) if sample is None else np.asarray(sample)
-        t = time.time()
         ref = oracle.Oracle().search(self.cat.items, self.sigs, self.cat.list_of, self.cat.centroids,
-                                     self.cat.item_scale, q[rows], masks[rows], nprobe, k, n_threads=16)
-        say(f"{label}: oracle on {len(rows)} queries {time.time() - t:.1f}s")
-        compare(tuple(a[rows] for a in got), ref, k, label)
-        check_invariants(self.cat.items, self.sigs, self.cat.list_of, got, masks, q, k)
-        return got
+                                     self.cat.item_scale, q, masks, nprobe, k, n_threads=16)
+        say(f"{label}: oracle on {B} queries {time.time() - t:.1f}s; eligible/query median "
+            f"{int(np.median(ref[4][:, 1]))}")
+        for path in paths:
+            opts = svt_mod.make_options(path)
+            t = time.time()
+            got = gpu_search(self.ix, q, masks, nprobe, k, opts=opts)
+            say(f"{label} [{path}]: B={B} gpu search {1e3 * (time.time() - t):.1f} ms (incl. copies)")
+            compare(got, ref, k, f"{label} [{path}]")
+            check_invariants(self.cat.items, self.sigs, self.cat.list_of, got, masks, q, k, self.cat.centroids,
+                             nprobe)
+        return ref
 
     def close(self):
         self.ix.close()
@@ -93,6 +97,10 @@ def test_1m_batch8(p1m):
     p1m.check(8, 100, label="1m-b8")
 
 
+def test_1m_batch64(p1m):
+    p1m.check(64, 300, label="1m-b64")
+
+
 def test_10m_batch64(p10m):
     p10m.check(64, 0, label="10m-b64")
 
@@ -101,7 +109,5 @@ def test_10m_batch64_other(p10m):
     p10m.check(64, 5000, label="10m-b64-2")
 
 
-def test_10m_batch64_query_path(p10m, monkeypatch):
-    """Batches of this size are grouped by default; the query-by-query path at full size too."""
-    monkeypatch.setenv("SVT_PATH", "query")
-    p10m.check(64, 10_000, label="10m-b64-query-path")
+def test_10m_batch256(p10m):
+    p10m.check(256, 10_000, label="10m-b256")
