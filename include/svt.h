@@ -174,6 +174,27 @@ int svt_search(const svt_index *ix, int32_t n_queries, const int8_t *queries, co
                float *out_fscores, int32_t *out_counts, int64_t *out_stats, const svt_search_options *opts,
                void *workspace, size_t workspace_bytes, void *hip_stream);
 
+/*
+ * svt_search_noalloc - svt_search without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Arguments, results and errors are those of svt_search; the workspace is a static device array of
+ * SVT_NOALLOC_SCRATCH_BYTES bytes inside the library, one per GPU, held until the process ends.
+ * The call allocates no device memory: on its first call on a GPU it looks up that GPU's copy of the
+ * array (hipGetSymbolAddress), and it records no stage-timing events.
+ *   Errors, besides those of svt_search: SVT_EINVAL when this call's svt_search_workspace_size exceeds
+ *   SVT_NOALLOC_SCRATCH_BYTES, or when the current device is not the one the index was uploaded on;
+ *   SVT_EDEVICE when the array's address cannot be obtained.
+ * Concurrency: every call on one GPU uses the same array, which keeps the previous call's contents (the
+ * search clears what it needs).  Calls whose executions overlap on one GPU (two streams, two threads
+ * or two processes' work in flight at once) race on it and may return wrong results: serialise them,
+ * e.g. issue them all on one stream.
+ */
+#define SVT_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+int svt_search_noalloc(const svt_index *ix, int32_t n_queries, const int8_t *queries, const uint64_t *masks,
+                       const float *query_scales, int32_t nprobe, int32_t k, int64_t *out_ids, int32_t *out_scores,
+                       float *out_fscores, int32_t *out_counts, int64_t *out_stats, const svt_search_options *opts,
+                       void *hip_stream);
+
 /* svt_last_error - message of the last failed call on this thread ("" if none). */
 const char *svt_last_error(void);
 

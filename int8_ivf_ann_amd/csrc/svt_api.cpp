@@ -26,14 +26,19 @@ namespace {
 
 thread_local std::string g_err;
 
-int fail(int code, const char *fmt, ...) {
+int vfail(int code, const char *fmt, va_list ap) {
   char buf[512];
-  va_list ap;
-  va_start(ap, fmt);
   vsnprintf(buf, sizeof buf, fmt, ap);
-  va_end(ap);
   g_err = buf;
   return code;
+}
+
+int fail(int code, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  const int r = vfail(code, fmt, ap);
+  va_end(ap);
+  return r;
 }
 
 int fail_hip(hipError_t e, const char *what) {
@@ -445,8 +450,8 @@ Work carve(const Layout &L, void *workspace, int64_t *out_stats) {
 // Enqueue the search of a validated call on stream s.
 int enqueue_search(const svt_index *ix, const SearchShape &sh, const Work &w, const int8_t *queries,
                    const uint64_t *masks, const float *query_scales, int64_t *out_ids, int32_t *out_scores,
-                   float *out_fscores, int32_t *out_counts, hipStream_t s) {
-  const int prof_mode = g_prof_on.load(std::memory_order_relaxed);
+                   float *out_fscores, int32_t *out_counts, bool record_events, hipStream_t s) {
+  const int prof_mode = record_events ? g_prof_on.load(std::memory_order_relaxed) : 0;
   const bool prof = prof_mode != 0 && g_prof.searches < kMaxProfiledSearches;
   ProfState &ps = g_prof;
   int ev0 = 0, evn = 0;
@@ -516,6 +521,45 @@ int check_search_ptrs(const int8_t *queries, const uint64_t *masks, const int64_
 
 }  // namespace
 
+namespace svt {
+
+int report(int code, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  const int r = vfail(code, fmt, ap);
+  va_end(ap);
+  return r;
+}
+
+int search_size(const svt_index *ix, int32_t B, int32_t nprobe, int32_t k, const svt_search_options *opts,
+                const char *who, size_t *bytes, int *device) {
+  const int rc = check_search_args(ix, B, nprobe, k, opts, who);
+  if (rc != SVT_OK) return rc;
+  *bytes = layout(ix, B, nprobe, k, opts).total;
+  *device = ix->device;
+  return SVT_OK;
+}
+
+int search_into(const svt_index *ix, int32_t B, const int8_t *queries, const uint64_t *masks,
+                const float *query_scales, int32_t nprobe, int32_t k, int64_t *out_ids, int32_t *out_scores,
+                float *out_fscores, int32_t *out_counts, int64_t *out_stats, const svt_search_options *opts,
+                void *workspace, size_t workspace_bytes, void *hip_stream, bool record_events, const char *who) {
+  int rc = check_search_args(ix, B, nprobe, k, opts, who);
+  if (rc != SVT_OK) return rc;
+  if (B == 0) return SVT_OK;
+  if ((rc = check_search_ptrs(queries, masks, out_ids, out_scores, who)) != SVT_OK) return rc;
+  if (!workspace) return fail(SVT_EINVAL, "%s: NULL workspace", who);
+  if (((uintptr_t)workspace & 255) != 0) return fail(SVT_EINVAL, "%s: workspace not 256-byte aligned", who);
+  const Layout L = layout(ix, B, nprobe, k, opts);
+  if (workspace_bytes < L.total)
+    return fail(SVT_EINVAL, "%s: workspace %zu bytes < required %zu", who, workspace_bytes, L.total);
+  const Work w = carve(L, workspace, out_stats);
+  return enqueue_search(ix, L.sh, w, queries, masks, query_scales, out_ids, out_scores, out_fscores, out_counts,
+                        record_events, (hipStream_t)hip_stream);
+}
+
+}  // namespace svt
+
 extern "C" size_t svt_search_workspace_size(const svt_index *ix, int32_t n_queries, int32_t nprobe, int32_t k,
                                             const svt_search_options *opts) {
   g_err.clear();
@@ -528,18 +572,8 @@ extern "C" int svt_search(const svt_index *ix, int32_t B, const int8_t *queries,
                           float *out_fscores, int32_t *out_counts, int64_t *out_stats, const svt_search_options *opts,
                           void *workspace, size_t workspace_bytes, void *hip_stream) {
   g_err.clear();
-  int rc = check_search_args(ix, B, nprobe, k, opts, "svt_search");
-  if (rc != SVT_OK) return rc;
-  if (B == 0) return SVT_OK;
-  if ((rc = check_search_ptrs(queries, masks, out_ids, out_scores, "svt_search")) != SVT_OK) return rc;
-  if (!workspace) return fail(SVT_EINVAL, "svt_search: NULL workspace");
-  if (((uintptr_t)workspace & 255) != 0) return fail(SVT_EINVAL, "svt_search: workspace not 256-byte aligned");
-  const Layout L = layout(ix, B, nprobe, k, opts);
-  if (workspace_bytes < L.total)
-    return fail(SVT_EINVAL, "svt_search: workspace %zu bytes < required %zu", workspace_bytes, L.total);
-  const Work w = carve(L, workspace, out_stats);
-  return enqueue_search(ix, L.sh, w, queries, masks, query_scales, out_ids, out_scores, out_fscores, out_counts,
-                        (hipStream_t)hip_stream);
+  return search_into(ix, B, queries, masks, query_scales, nprobe, k, out_ids, out_scores, out_fscores, out_counts,
+                     out_stats, opts, workspace, workspace_bytes, hip_stream, true, "svt_search");
 }
 
 extern "C" int svt_profile_enable(int on) {

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "svt.h"
+
 namespace svt {
 
 constexpr int kMaxK = 2048;          // largest top-k (SVT_MAX_K)
@@ -249,5 +251,18 @@ int xscan_blocks_per_cu(int32_t dim, int32_t sig_words);
 hipError_t launch_scatter_rows(const int8_t *src_rows, const uint64_t *src_sigs, const int32_t *pos_of,
                                int64_t i0, int64_t n, int32_t dim, int32_t sig_words, int8_t *dst_rows,
                                uint64_t *dst_sigs, hipStream_t s);
+
+// host side of the search entry points (svt_api.cpp)
+// sets the thread's last-error message; returns code
+int report(int code, const char *fmt, ...);
+// validates the arguments of a search; on SVT_OK, its workspace bytes and the device the index lives on
+int search_size(const svt_index *ix, int32_t B, int32_t nprobe, int32_t k, const svt_search_options *opts,
+                const char *who, size_t *bytes, int *device);
+// validates a search and enqueues it on hip_stream with the given workspace; record_events == false: no
+// stage-timing events even when timing is on (the event pool would have to grow)
+int search_into(const svt_index *ix, int32_t B, const int8_t *queries, const uint64_t *masks,
+                const float *query_scales, int32_t nprobe, int32_t k, int64_t *out_ids, int32_t *out_scores,
+                float *out_fscores, int32_t *out_counts, int64_t *out_stats, const svt_search_options *opts,
+                void *workspace, size_t workspace_bytes, void *hip_stream, bool record_events, const char *who);
 
 }  // namespace svt

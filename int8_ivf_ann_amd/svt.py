@@ -20,11 +20,12 @@ SVT_MAX_K = 2048
 SVT_MAX_SIG_WORDS = 2
 SVT_PATH_AUTO, SVT_PATH_QUERY, SVT_PATH_TILE = 0, 1, 2
 SVT_OPT_MERGE_FROM_SLOTS, SVT_OPT_FORCE_REDO = 1, 2
+SVT_NOALLOC_SCRATCH_BYTES = 256 << 20
 _PATHS = {"auto": SVT_PATH_AUTO, "query": SVT_PATH_QUERY, "tile": SVT_PATH_TILE}
 
 #: every symbol include/svt.h declares
 EXPORTED = ("svt_index_upload", "svt_index_free", "svt_index_info", "svt_search_workspace_size", "svt_search",
-            "svt_last_error", "svt_bloom_mask", "svt_bloom_sign", "svt_profile_enable", "svt_profile_read")
+            "svt_search_noalloc", "svt_last_error", "svt_bloom_mask", "svt_bloom_sign", "svt_profile_enable", "svt_profile_read")
 
 
 class SvtError(RuntimeError):
@@ -84,6 +85,7 @@ def lib():
     L.svt_search_workspace_size.argtypes = [vp, i32, i32, i32, vp]
     L.svt_search_workspace_size.restype = sz
     L.svt_search.argtypes = [vp, i32, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.svt_search_noalloc.argtypes = [vp, i32, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp]
     L.svt_last_error.restype = ctypes.c_char_p
     L.svt_bloom_mask.argtypes = [vp, i32, i32, i32, vp]
     L.svt_bloom_sign.argtypes = [vp, i64, i32, i32, i32, vp, i32]
@@ -202,12 +204,9 @@ def svt_search_workspace_size(handle, n_queries: int, nprobe: int, k: int, opts=
     return int(sz)
 
 
-def svt_search(handle, queries, masks, nprobe: int, k: int, query_scales=None, out_ids=None, out_scores=None,
-               out_fscores=None, out_counts=None, out_stats=None, workspace=None, stream=None, opts=None):
-    """queries: int8 [B, d] cuda tensor; masks: uint64 (or int64) [B, W] cuda tensor.
-    Returns (ids int64 [B,k], scores int32 [B,k], fscores f32 [B,k], counts int32 [B], stats int64 [B,2]);
-    outputs are allocated with torch unless passed in.  Asynchronous on ``stream``.  ``opts``: a
-    svt_search_options (see make_options) or None."""
+def _search_tensors(handle, queries, masks, k, query_scales, out_ids, out_scores, out_fscores, out_counts,
+                    out_stats):
+    """Checks the search tensors and allocates the outputs not passed in; returns (B, dev, outputs)."""
     import torch
     n, dim, W, _ = svt_index_info(handle)
     if not hasattr(queries, "shape") or len(queries.shape) != 2:
@@ -232,15 +231,37 @@ def svt_search(handle, queries, masks, nprobe: int, k: int, query_scales=None, o
     _check_tensor("out_fscores", out_fscores, (torch.float32,), (B, k), dev)
     _check_tensor("out_counts", out_counts, (torch.int32,), (B,), dev)
     _check_tensor("out_stats", out_stats, (torch.int64,), (B, 2), dev)
+    return B, dev, (out_ids, out_scores, out_fscores, out_counts, out_stats)
+
+
+def svt_search(handle, queries, masks, nprobe: int, k: int, query_scales=None, out_ids=None, out_scores=None,
+               out_fscores=None, out_counts=None, out_stats=None, workspace=None, stream=None, opts=None):
+    """queries: int8 [B, d] cuda tensor; masks: uint64 (or int64) [B, W] cuda tensor.
+    Returns (ids int64 [B,k], scores int32 [B,k], fscores f32 [B,k], counts int32 [B], stats int64 [B,2]);
+    outputs are allocated with torch unless passed in.  Asynchronous on ``stream``.  ``opts``: a
+    svt_search_options (see make_options) or None."""
+    import torch
+    B, dev, outs = _search_tensors(handle, queries, masks, k, query_scales, out_ids, out_scores, out_fscores,
+                                   out_counts, out_stats)
     if workspace is None:
         nbytes = svt_search_workspace_size(handle, B, nprobe, k, opts) if B > 0 else 0
         workspace = torch.empty((max(nbytes, 256),), dtype=torch.uint8, device=dev)
     _check_tensor("workspace", workspace, (torch.uint8,), (workspace.numel(),), dev)
     _check(lib().svt_search(handle, B, _t_ptr(queries), _t_ptr(masks), _t_ptr(query_scales), nprobe, k,
-                            _t_ptr(out_ids), _t_ptr(out_scores), _t_ptr(out_fscores), _t_ptr(out_counts),
-                            _t_ptr(out_stats), _opt_ptr(opts), _t_ptr(workspace), int(workspace.numel()),
+                            *[_t_ptr(t) for t in outs], _opt_ptr(opts), _t_ptr(workspace), int(workspace.numel()),
                             _stream_ptr(stream)))
-    return out_ids, out_scores, out_fscores, out_counts, out_stats
+    return outs
+
+
+def svt_search_noalloc(handle, queries, masks, nprobe: int, k: int, query_scales=None, out_ids=None,
+                       out_scores=None, out_fscores=None, out_counts=None, out_stats=None, stream=None, opts=None):
+    """svt_search with the library's static scratch as workspace (the C call allocates no device memory;
+    outputs not passed in are still allocated here, by torch).  Searches on one GPU must not overlap."""
+    B, dev, outs = _search_tensors(handle, queries, masks, k, query_scales, out_ids, out_scores, out_fscores,
+                                   out_counts, out_stats)
+    _check(lib().svt_search_noalloc(handle, B, _t_ptr(queries), _t_ptr(masks), _t_ptr(query_scales), nprobe, k,
+                                    *[_t_ptr(t) for t in outs], _opt_ptr(opts), _stream_ptr(stream)))
+    return outs
 
 
 def svt_profile_enable(on) -> None:

@@ -82,6 +82,9 @@ def test_search_rejects_dead_index(L):
                         None) == svt.SVT_ESTATE
     assert L.svt_search_workspace_size(bogus, 1, 1, 1, None) == 0
     assert "not a live index" in svt.svt_last_error()
+    assert L.svt_search_noalloc(bogus, 1, None, None, None, 1, 1, None, None, None, None, None, None,
+                                None) == svt.SVT_ESTATE
+    assert "not a live index" in svt.svt_last_error()
     assert L.svt_index_free(bogus, None) == svt.SVT_ESTATE
     assert L.svt_index_free(None, None) == svt.SVT_OK
 
@@ -97,6 +100,8 @@ def test_options_struct_layout():
         assert re.search(rf"{name} = {v}\b", hdr), name
     assert re.search(r"#define SVT_OPT_MERGE_FROM_SLOTS 1u", hdr)
     assert re.search(r"#define SVT_OPT_FORCE_REDO 2u", hdr)
+    assert re.search(r"#define SVT_NOALLOC_SCRATCH_BYTES \(\(size_t\)256 << 20\)", hdr)
+    assert svt.SVT_NOALLOC_SCRATCH_BYTES == 256 << 20
 
 
 def test_binding_rejects_bad_tensors():
