@@ -134,8 +134,15 @@ constexpr int kRMin = 16;
 // scored with int8 MFMA (16x16x64).  The sample pass scores every kXStride-th item.
 constexpr int kXQ = 32;              // queries of one MFMA unit (two 16-row MFMA tiles)
 constexpr int kXStride = 256;        // sample pass: every kXStride-th position
-constexpr int kXChunk = 4096;        // items of one exhaustive unit
 constexpr int kXWaves = 4;           // waves of an exhaustive workgroup (each works on its own)
+#ifndef SVT_X_BUFFERS
+#define SVT_X_BUFFERS 2
+#endif
+#ifndef SVT_X_OCC
+#define SVT_X_OCC 3
+#endif
+constexpr int kXBuffers = SVT_X_BUFFERS;   // steps of the exhaustive scan in registers (in flight + scored)
+constexpr int kXOcc = SVT_X_OCC;           // its waves per SIMD the compiler is asked to fit
 constexpr int kXStage = 256;         // candidates a wave of the exhaustive kernel stages in LDS
 
 constexpr int kMaxPlanBlocks = 65536 / kSelThreads;   // blocks of kSelThreads clusters (nlist <= 65536)

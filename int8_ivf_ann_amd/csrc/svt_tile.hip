@@ -26,6 +26,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "svt_device.h"
@@ -632,25 +633,29 @@ __global__ __launch_bounds__(kScanThreads, kScanOcc) void k_tscan(TScanArgs a) {
 
 // ------------------------------------------------------------------------------------------------
 // k_xscan: nprobe == nlist.  Every query's stream is the whole catalogue in position order, so one read
-// of a 64-item block serves a block of kXQ queries: v_mfma_i32_16x16x64_i8 multiplies 16 queries by 16
+// of a 64-item step serves a block of kXQ queries: v_mfma_i32_16x16x64_i8 multiplies 16 queries by 16
 // items per K slice of 64 bytes.  Lane layout (gfx950, 16x16x64 int8): lane l supplies row l % 16 of each
 // operand with K bytes 16 (l / 16) .. + 15 of the slice, and receives C[4 (l / 16) + r][l % 16], r = 0..3.
 // Items are the columns, queries the rows: lane l holds 4 queries x 1 item per (query tile, item tile),
 // and tests those items' signatures against those queries' masks after the product.
 //
-// Each wave of a workgroup works alone: it takes units (a run of items x a query block) from a queue
-// and walks the run in 64-item steps, the next step's rows and signatures loaded while the current one is
-// scored.  Candidates are staged per wave in LDS (with their rank among the wave's candidates of their
-// query) and go to the pools with one reservation per query.  SAMPLE: the run is one 64-item block per
-// Sample pass: the run is 64 consecutive points of the every-kXStride-th-position stream; each lane keeps
-// its best eligible score per query and writes it to the query's sample buffer (one slot per lane and run).
+// Each wave works alone, on one query block and a fixed share of the steps: step s of the stream goes to
+// the wave with part s mod parts, so the waves of the grid walk the catalogue together and each has the
+// same number of steps.  A step's rows and signatures come through buffer loads whose resource starts at
+// the step and ends with the catalogue: the per-lane offsets are constants, and items past the end read as
+// zero without a memory access.  The loads of the next XNB - 1 steps are in flight while a step is scored
+// (XNB register buffers, the loop unrolled XNB times, every load unconditional).  Candidates are staged per
+// wave in LDS with their rank among the wave's staged candidates of their query and go to the pools with
+// one reservation per query.
+// SAMPLE: the stream is every kXStride-th position; each lane keeps its best eligible score per query over
+// a step and writes it to the query's sample buffer (one slot per lane and step).
 
 struct XScanArgs {
   DevIndex ix;
   const int8_t *queries;
   const uint64_t *masks;
   Work w;
-  int32_t B, n_units, n_qb;
+  int32_t B, n_qb;
   uint32_t cap;       // pool keys (main pass) or sample-buffer entries (sample pass) per query
 };
 
@@ -672,230 +677,235 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// raw buffer resource over [base, base + bytes) (gfx9 word 3: 32-bit data format, no swizzle)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void *base, int64_t bytes) {
+  const int n = bytes <= 0 ? 0 : (bytes < 0x7FFFFFFF ? (int)bytes : 0x7FFFFFFF);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n, 0x00020000);
+}
+
 template <int KS, int W, bool SAMPLE>
-__global__ __launch_bounds__(64 * kXWaves) void k_xscan(XScanArgs a) {
+__global__ __launch_bounds__(64 * kXWaves, kXOcc) void k_xscan(XScanArgs a) {
+  constexpr int XNB = KS >= 4 ? 2 : kXBuffers;   // step buffers in registers
+  constexpr int IS = SAMPLE ? kXStride : 1;   // catalogue positions between stream items
+  constexpr int MW = 2 * W;                   // 32-bit words of a mask
   __shared__ XWave xw[kXWaves];
-  const int l = lane_id(), wv = threadIdx.x / 64;
+  const int l = lane_id();
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
   XWave &S = xw[wv];
   const int dim = a.ix.dim;
   const int64_t N = a.ix.n_items;
-  // the stream walked: every position, or (sample pass) every kXStride-th
-  const int64_t NP = SAMPLE ? (N + kXStride - 1) / kXStride : N;
+  const int64_t NP = (N + IS - 1) / IS;        // stream length
+  const int64_t n_steps = (NP + 63) / 64;
+  const int gw = blockIdx.x * kXWaves + wv;
+  const int parts = (int)(gridDim.x * kXWaves) / a.n_qb;   // the launch gives every block at least one
+  if (gw >= parts * a.n_qb) return;   // waves work alone: no workgroup barrier follows
+  const int qb = gw % a.n_qb, part = gw / a.n_qb;
+  const int64_t my_steps = part < n_steps ? (n_steps - part + parts - 1) / parts : 0;
   const int lr = l & 15, lg = l >> 4;   // operand row (query or item) and K group of this lane
-  uint32_t *qctr = &a.w.counter[SAMPLE ? 4 : 5];
-  if (l < kXQ) S.cnt[l] = 0u;
-  int stage_n = 0;
-  for (;;) {
-    int u = 0;
-    if (l == 0) u = (int)atomicAdd(qctr, 1u);
-    u = __shfl(u, 0);
-    if (u >= a.n_units) break;
-    const int qb = u % a.n_qb, run = u / a.n_qb;
-    const int64_t p_begin = (int64_t)run * (SAMPLE ? 64 : kXChunk);
-    const int64_t p_lim = p_begin + (SAMPLE ? 64 : kXChunk);
-    const int64_t p_end = p_lim < NP ? p_lim : NP;
-    const int q0 = qb * kXQ;
-    // query operands: rows q0 + 16 t2 + lr, K bytes 64 ks + 16 lg .. + 15 (zero beyond dim or B)
-    int4 aop[2][KS];
+  const int q0 = qb * kXQ;
+  // query operands: rows q0 + 16 t2 + lr, K bytes 64 ks + 16 lg .. + 15 (zero beyond dim or B)
+  int4 aop[2][KS];
 #pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2) {
-      const int q = q0 + 16 * t2 + lr;
+  for (int t2 = 0; t2 < 2; ++t2) {
+    const int q = q0 + 16 * t2 + lr;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int off = 64 * ks + 16 * lg;
+      const bool ok = q < a.B && off < dim;
+      const int4 v = reinterpret_cast<const int4 *>(a.queries + (size_t)(q < a.B ? q : 0) * dim +
+                                                    (off < dim ? off : 0))[0];
+      aop[t2][ks] = ok ? v : make_int4(0, 0, 0, 0);
+    }
+  }
+  // the block's masks in the wave's LDS (lane j < kXQ writes query q0 + j's); this lane's result rows are
+  // queries q0 + 16 t2 + 4 lg + r.  A row past the batch never offers a candidate (threshold above every
+  // score) and its count is not written.
+  if (l < kXQ) {
+    const int qc = q0 + l < a.B ? q0 + l : 0;
+#pragma unroll
+    for (int ww = 0; ww < W; ++ww) {
+      const uint64_t m = a.masks[(size_t)qc * W + ww];
+      S.mk[l][2 * ww] = (uint32_t)m;
+      S.mk[l][2 * ww + 1] = (uint32_t)(m >> 32);
+    }
+    S.cnt[l] = 0u;
+  }
+  wave_lds_sync();
+  int32_t th[2][4];
+  uint32_t ec[2][4];   // eligible items per query (sample pass: the lane's best eligible score of the step)
+#pragma unroll
+  for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int q = q0 + 16 * t2 + 4 * lg + r;
+      th[t2][r] = q < a.B ? (SAMPLE ? INT32_MIN : a.w.sthr[q]) : INT32_MAX;
+      ec[t2][r] = SAMPLE ? (uint32_t)INT32_MIN : 0u;
+    }
+  // byte offsets of this lane's parts of a step: rows of items 16 t + lr (K bytes 64 ks + 16 lg) and
+  // signature word lg % MW of the same items
+  uint32_t roff[4][KS], soff[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const uint32_t item = (uint32_t)((16 * t + lr) * IS);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int off = 64 * ks + 16 * lg;
+      roff[t][ks] = item * (uint32_t)dim + (uint32_t)(off < dim ? off : 0);
+    }
+    soff[t] = item * (uint32_t)(8 * W) + 4u * (uint32_t)(lg % MW);
+  }
+  typedef int4 StepRows[4][KS];
+  typedef uint32_t StepSigs[4];
+  // the j-th step of this wave (j may run past its share: such a step lies past the catalogue and reads
+  // zeros without touching memory)
+  auto load_step = [&](int64_t j, StepRows &Bo, StepSigs &NS) {
+    const int64_t first = (part + j * parts) * 64 * IS;   // catalogue position of the step's item 0
+    const int64_t valid = N - first;
+    const int64_t at = valid > 0 ? first : 0;
+    const __amdgpu_buffer_rsrc_t rr = raw_rsrc(a.ix.items + at * dim, valid * dim);
+    const __amdgpu_buffer_rsrc_t rs = raw_rsrc(a.ix.sigs + at * W, valid * (8 * W));
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const int off = 64 * ks + 16 * lg;
-        const bool ok = q < a.B && off < dim;
-        const int4 v = reinterpret_cast<const int4 *>(a.queries + (size_t)(q < a.B ? q : 0) * dim +
-                                                      (off < dim ? off : 0))[0];
-        aop[t2][ks] = ok ? v : make_int4(0, 0, 0, 0);
+        typedef int v4i __attribute__((ext_vector_type(4)));
+        const v4i v = __builtin_amdgcn_raw_buffer_load_b128(rr, roff[t][ks], 0, 0);
+        Bo[t][ks] = make_int4(v.x, v.y, v.z, v.w);
       }
+      NS[t] = __builtin_amdgcn_raw_buffer_load_b32(rs, soff[t], 0, 0);
     }
-    // the masks and thresholds of this lane's result rows: queries q0 + 16 t2 + 4 lg + r.  A row past
-    // the batch never offers a candidate (threshold above every score) and its count is not written.
-    constexpr int MW = 2 * W;   // 32-bit words of a mask
-    int32_t th[2][4];
-    uint32_t ec[2][4];
-    // the block's masks in the wave's LDS (lane j < kXQ writes query q0 + j's)
+  };
+  int stage_n = 0;
+  auto flush = [&]() {
     wave_lds_sync();
     if (l < kXQ) {
-      const int qc = q0 + l < a.B ? q0 + l : 0;
-#pragma unroll
-      for (int ww = 0; ww < W; ++ww) {
-        const uint64_t m = a.masks[(size_t)qc * W + ww];
-        S.mk[l][2 * ww] = (uint32_t)m;
-        S.mk[l][2 * ww + 1] = (uint32_t)(m >> 32);
-      }
+      const uint32_t c = S.cnt[l];
+      uint32_t b = 0u;
+      if (c && q0 + l < a.B) b = atomicAdd(&a.w.pool_cnt[q0 + l], c);
+      S.base[l] = b;
+      S.cnt[l] = 0u;
     }
     wave_lds_sync();
+    for (int e = l; e < stage_n; e += 64) {
+      const int qi = S.qi[e];
+      const uint32_t o = S.base[qi] + S.rank[e];
+      const size_t q = (size_t)(q0 + qi);
+      if (o < a.cap) a.w.pool[q * a.cap + o] = S.key[e];
+    }
+    wave_lds_sync();
+    stage_n = 0;
+  };
+  // score the wave's j-th step (rows and signatures in Bo / SG): count the eligible items, offer the
+  // candidates (sample pass: keep the best eligible score and write it to the sample buffer)
+  auto score_step = [&](int64_t j, const StepRows &Bo, const StepSigs &SG) {
+    typedef int v4i __attribute__((ext_vector_type(4)));
+    const int64_t s = part + j * parts;
+    const int64_t p0 = s * 64;   // stream index of the step's item 0
+    uint32_t cbits = 0u;         // bit (8 t + 4 t2 + r): candidate
+    v4i acc[4][2];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) {
+        v4i c = {0, 0, 0, 0};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const v4i av = {aop[t2][ks].x, aop[t2][ks].y, aop[t2][ks].z, aop[t2][ks].w};
+          const v4i bv = {Bo[t][ks].x, Bo[t][ks].y, Bo[t][ks].z, Bo[t][ks].w};
+          c = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bv, c, 0, 0, 0);
+        }
+        acc[t][t2] = c;
+      }
+    // the complemented signature words of item lr of each tile (an item passes a mask when no mask bit
+    // falls on a zero of its signature), gathered from the lanes of the other groups
+    uint32_t ns[4][MW];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int ww = 0; ww < MW; ++ww) ns[t][ww] = ~(uint32_t)__shfl((int)SG[t], lr + 16 * ww);
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int q = q0 + 16 * t2 + 4 * lg + r;
-        th[t2][r] = q < a.B ? (SAMPLE ? INT32_MIN : a.w.sthr[q]) : INT32_MAX;
-        ec[t2][r] = 0u;   // sample pass: the lane's best eligible score
-        if constexpr (SAMPLE) ec[t2][r] = (uint32_t)INT32_MIN;
-      }
-    // one step: rows of 4 item tiles (item p0 + 16 t + lr) and one 32-bit word of each item's signature
-    // per lane (word lg; the lanes of the other groups hold the others)
-    typedef int4 StepRows[4][KS];
-    typedef uint32_t StepSigs[4];
-    auto load_step = [&](int64_t p0, StepRows &Bo, StepSigs &NS) {
+        uint32_t mq[MW];   // the mask of this lane's query 16 t2 + 4 lg + r
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int64_t idx = p0 + 16 * t + lr < NP ? p0 + 16 * t + lr : NP - 1;
-        const int64_t p = SAMPLE ? idx * kXStride : idx;
+        for (int ww = 0; ww < MW; ++ww) mq[ww] = S.mk[16 * t2 + 4 * lg + r][ww];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const int off = 64 * ks + 16 * lg;
-          Bo[t][ks] = reinterpret_cast<const int4 *>(a.ix.items + (size_t)p * dim + (off < dim ? off : 0))[0];
-        }
-        NS[t] = reinterpret_cast<const uint32_t *>(a.ix.sigs)[(size_t)p * MW + (lg % MW)];
-      }
-    };
-    auto flush = [&]() {
-      wave_lds_sync();
-      if (l < kXQ) {
-        const uint32_t c = S.cnt[l];
-        uint32_t b = 0u;
-        if (c && q0 + l < a.B) b = atomicAdd(&a.w.pool_cnt[q0 + l], c);
-        S.base[l] = b;
-        S.cnt[l] = 0u;
-      }
-      wave_lds_sync();
-      for (int e = l; e < stage_n; e += 64) {
-        const int qi = S.qi[e];
-        const uint32_t o = S.base[qi] + S.rank[e];
-        const size_t q = (size_t)(q0 + qi);
-        if (o < a.cap) a.w.pool[q * a.cap + o] = S.key[e];
-      }
-      wave_lds_sync();
-      stage_n = 0;
-    };
-    // score the step in Bo/NS (items p0 ..), count the eligible items, offer the candidates.  FULL: the
-    // step lies wholly inside the run (no item to mask).
-    auto score_step = [&](int64_t p0, const StepRows &Bo, const StepSigs &SG, auto full) {
-      typedef int v4i __attribute__((ext_vector_type(4)));
-      constexpr bool FULL = decltype(full)::value;
-      uint32_t cbits = 0u;   // bit (8 t + 4 t2 + r): candidate
-      v4i acc[4][2];
+        for (int t = 0; t < 4; ++t) {
+          const bool item_ok = p0 + 16 * t + lr < NP;
+          uint32_t x = 0u;
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2) {
-          v4i c = {0, 0, 0, 0};
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks) {
-            const v4i av = {aop[t2][ks].x, aop[t2][ks].y, aop[t2][ks].z, aop[t2][ks].w};
-            const v4i bv = {Bo[t][ks].x, Bo[t][ks].y, Bo[t][ks].z, Bo[t][ks].w};
-            c = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bv, c, 0, 0, 0);
+          for (int ww = 0; ww < MW; ++ww) x |= mq[ww] & ns[t][ww];
+          const bool el = item_ok && x == 0u;
+          if constexpr (SAMPLE) {
+            const int32_t cur = (int32_t)ec[t2][r], sc = acc[t][t2][r];
+            ec[t2][r] = (uint32_t)(el && sc > cur ? sc : cur);
+          } else {
+            ec[t2][r] += el ? 1u : 0u;
+            const bool cand = el && acc[t][t2][r] >= th[t2][r];
+            cbits |= cand ? 1u << (8 * t + 4 * t2 + r) : 0u;
           }
-          acc[t][t2] = c;
         }
-      // the complemented signature words of item lr of each tile (an item passes a mask when no mask bit
-      // falls on a zero of its signature), gathered from the lanes of the other groups
-      uint32_t ns[4][MW];
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int ww = 0; ww < MW; ++ww) ns[t][ww] = ~(uint32_t)__shfl((int)SG[t], lr + 16 * ww);
-#pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          uint32_t mq[MW];   // the mask of this lane's query 16 t2 + 4 lg + r
-#pragma unroll
-          for (int ww = 0; ww < MW; ++ww) mq[ww] = S.mk[16 * t2 + 4 * lg + r][ww];
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const bool item_ok = FULL || p0 + 16 * t + lr < p_end;
-            uint32_t x = 0u;
-#pragma unroll
-            for (int ww = 0; ww < MW; ++ww) x |= mq[ww] & ns[t][ww];
-            const bool el = item_ok && x == 0u;
-            if constexpr (SAMPLE) {
-              const int32_t cur = (int32_t)ec[t2][r], sc = acc[t][t2][r];
-              ec[t2][r] = (uint32_t)(el && sc > cur ? sc : cur);
-            } else {
-              ec[t2][r] += el ? 1u : 0u;
-              const bool cand = el && acc[t][t2][r] >= th[t2][r];
-              cbits |= cand ? 1u << (8 * t + 4 * t2 + r) : 0u;
-            }
-          }
       }
-      if constexpr (SAMPLE) return;
-      if (__ballot(cbits != 0u) == 0ull) return;
-      // rare: the step's scores go to LDS and its candidates are staged in one loop over the result
-      // entries
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) S.sc[8 * t + 4 * t2 + r][l] = acc[t][t2][r];
-      wave_lds_sync();
-#pragma unroll 1
-      for (int c = 0; c < 32; ++c) {
-        const bool cand = (cbits >> c) & 1u;
-        const uint64_t b = __ballot(cand);
-        if (b == 0ull) continue;
-        if (stage_n + 64 > kXStage) flush();
-        if (cand) {
-          const int t = c >> 3, t2 = (c >> 2) & 1, r = c & 3;
-          const int e = stage_n + mbcnt(b);
-          const int qi = 16 * t2 + 4 * lg + r;
-          const int32_t score = S.sc[c][l];
-          const int32_t pos = (int32_t)(p0 + 16 * t + lr);
-          S.key[e] = pos_key(score, pos);
-          S.qi[e] = (uint8_t)qi;
-          S.rank[e] = (uint16_t)atomicAdd(&S.cnt[qi], 1u);
-        }
-        stage_n += __popcll(b);
-      }
-      wave_lds_sync();
-    };
-    using Full = std::integral_constant<bool, true>;
-    using Part = std::integral_constant<bool, false>;
-    auto score_any = [&](int64_t p0, const StepRows &Bo, const StepSigs &SG) {
-      if (p0 + 64 <= p_end)
-        score_step(p0, Bo, SG, Full{});
-      else
-        score_step(p0, Bo, SG, Part{});
-    };
-    // triple-buffered walk over three named buffers: the loads of steps s + 1 and s + 2 are in flight
-    // while step s is scored (a request past the run repeats the run's first step)
-    StepRows ra, rb, rc;
-    StepSigs sa, sb, sc;
-    int64_t p0 = p_begin;
-    auto ahead = [&](int64_t p) { return p < p_end ? p : p_begin; };
-    load_step(p0, ra, sa);
-    load_step(ahead(p0 + 64), rb, sb);
-    for (;;) {
-      if (p0 >= p_end) break;
-      load_step(ahead(p0 + 128), rc, sc);
-      score_any(p0, ra, sa);
-      p0 += 64;
-      if (p0 >= p_end) break;
-      load_step(ahead(p0 + 128), ra, sa);
-      score_any(p0, rb, sb);
-      p0 += 64;
-      if (p0 >= p_end) break;
-      load_step(ahead(p0 + 128), rb, sb);
-      score_any(p0, rc, sc);
-      p0 += 64;
-    }
-    if (stage_n > 0) flush();
-    if (SAMPLE) {
-      // the lane's best eligible score of each of its queries over this run: slot 16 run + lr
+    if constexpr (SAMPLE) {
+      // slot 16 s + lr of each of the lane's queries: its best eligible score among the step's items
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int q = q0 + 16 * t2 + 4 * lg + r;
-          if (q < a.B) a.w.sbuf[(size_t)q * a.cap + 16 * run + lr] = (int32_t)ec[t2][r];
+          if (q < a.B && s < n_steps) a.w.sbuf[(size_t)q * a.cap + 16 * s + lr] = (int32_t)ec[t2][r];
+          ec[t2][r] = (uint32_t)INT32_MIN;
         }
+      return;
     }
+    if (__ballot(cbits != 0u) == 0ull) return;
+    // rare: the step's scores go to LDS and its candidates are staged in one loop over the result entries
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) S.sc[8 * t + 4 * t2 + r][l] = acc[t][t2][r];
+    wave_lds_sync();
+#pragma unroll 1
+    for (int c = 0; c < 32; ++c) {
+      const bool cand = (cbits >> c) & 1u;
+      const uint64_t b = __ballot(cand);
+      if (b == 0ull) continue;
+      if (stage_n + 64 > kXStage) flush();
+      if (cand) {
+        const int t = c >> 3, t2 = (c >> 2) & 1, r = c & 3;
+        const int e = stage_n + mbcnt(b);
+        const int qi = 16 * t2 + 4 * lg + r;
+        const int32_t score = S.sc[c][l];
+        const int32_t pos = (int32_t)(p0 + 16 * t + lr);
+        S.key[e] = pos_key(score, pos);
+        S.qi[e] = (uint8_t)qi;
+        S.rank[e] = (uint16_t)atomicAdd(&S.cnt[qi], 1u);
+      }
+      stage_n += __popcll(b);
+    }
+    wave_lds_sync();
+  };
+  // the walk: XNB - 1 steps in flight ahead of the one scored
+  StepRows rows[XNB];
+  StepSigs sigs[XNB];
+#pragma unroll
+  for (int b = 0; b < XNB - 1; ++b) load_step(b, rows[b], sigs[b]);
+  const int64_t n_iter = (my_steps + XNB - 1) / XNB;
+  for (int64_t it = 0; it < n_iter; ++it) {
+#pragma unroll
+    for (int b = 0; b < XNB; ++b) {
+      const int64_t j = it * XNB + b;
+      load_step(j + XNB - 1, rows[(b + XNB - 1) % XNB], sigs[(b + XNB - 1) % XNB]);
+      score_step(j, rows[b], sigs[b]);   // past the share: zero rows, no item in range
+    }
+  }
+  if constexpr (!SAMPLE) {
+    if (stage_n > 0) flush();
     // eligible items of each query of the block, summed over the 16 lanes that hold its items
-    if (!SAMPLE && a.w.stats) {
+    if (a.w.stats) {
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
@@ -1216,15 +1226,16 @@ hipError_t launch_exh_scan(const DevIndex &ix, const int8_t *queries, const uint
                            const SearchShape &sh, const Work &w, hipStream_t s) {
   const int n_qb = (sh.B + kXQ - 1) / kXQ;
   const int64_t N = ix.n_items;
+  // every query block needs a wave: at least n_qb waves in the grid
+  const int grid = std::max(sh.XP, (n_qb + kXWaves - 1) / kXWaves);
   // sample pass, thresholds, main pass
-  XScanArgs as{ix, queries, masks, w, sh.B, sh.n_sblocks * n_qb, n_qb, (uint32_t)sh.scap};
-  hipError_t e = xscan_dim<true>(as, ix.dim, ix.sig_words, sh.XP, s);
+  XScanArgs as{ix, queries, masks, w, sh.B, n_qb, (uint32_t)sh.scap};
+  hipError_t e = xscan_dim<true>(as, ix.dim, ix.sig_words, grid, s);
   if (e != hipSuccess) return e;
   k_xthr<<<sh.B, kSelThreads, 0, s>>>(w, N, sh.k, sh.pool_cap, sh.scap, (int32_t)((N + kXStride - 1) / kXStride),
                                       sh.force_redo);
-  const int64_t runs = (N + kXChunk - 1) / kXChunk;
-  XScanArgs am{ix, queries, masks, w, sh.B, (int32_t)(runs * n_qb), n_qb, (uint32_t)sh.pool_cap};
-  e = xscan_dim<false>(am, ix.dim, ix.sig_words, sh.XP, s);
+  XScanArgs am{ix, queries, masks, w, sh.B, n_qb, (uint32_t)sh.pool_cap};
+  e = xscan_dim<false>(am, ix.dim, ix.sig_words, grid, s);
   if (e != hipSuccess) return e;
   return hipGetLastError();
 }

@@ -112,6 +112,17 @@ def test_random_shapes(svt, opts, d, W):
         _run(svt, opts, items, sigs, cl, cent, 3.0, q, masks, nprobe, k, f"rand-d{d}-W{W}-{nprobe}-{k}")
 
 
+def test_exhaustive_several_query_blocks(svt, opts):
+    # nprobe == nlist with 70 queries: three blocks of 32 on the MFMA scan, the last one ragged; 20011
+    # items leave a partial last step, and far fewer steps than waves
+    rng = np.random.default_rng(31)
+    items, sigs, cl, cent = P.small_catalogue(rng, n=20011, d=64, nlist=20, W=2)
+    q = rng.integers(-127, 128, (70, 64)).astype(np.int8)
+    masks = P.random_masks(rng, 70, 2, nbits_max=2)
+    _run(svt, opts, items, sigs, cl, cent, 2.0, q, masks, 20, 100, "exh-70q-k100")
+    _run(svt, opts, items, sigs, cl, cent, 2.0, q, masks, 20, 2048, "exh-70q-k2048")
+
+
 def test_large_k_many_candidates(svt, opts):
     # every query keeps ~40k candidates: LDS lists are cut many times and the merge selects
     rng = np.random.default_rng(7)
