@@ -8,9 +8,14 @@ before the timed region starts.  The default workload is the 80M-item catalogue 
 
 Printed: one JSON line on stdout (progress goes to stderr) with
   value        eligible (query, item) pairs scored per second over the timed steps
-  roofline     the scan kernel's algorithmic bytes per launch / its average duration (HIP events on the
-               search stream over the timed region) against the 8 TB/s HBM peak
-  cpu_baseline the CPU oracle timed on a bounded sample of the same workload on the host cores
+  roofline     the scan kernel of the path taken (k_scan, k_tscan or k_xscan): algorithmic bytes per launch
+               / its average duration (HIP events on the search stream over the timed region) against the
+               8 TB/s HBM peak; also the same bytes per whole step (step_frac), the streaming-read rate
+               measured in the same run (read_ceiling) and the fabric traffic of the last counter run
+               taken on the current sources (traffic, else null)
+  cpu_baseline the CPU oracle timed on bounded samples of the same workload, on up to 16 host threads and
+               on one thread, with the host's thread count and CPU model
+  latency      (batch 1 by default) p50 / p99 of single searches over 1000 distinct queries
 """
 from __future__ import annotations
 
@@ -51,20 +56,55 @@ def parse():
     ap.add_argument("--print-sha", action="store_true", help="print the hash of the kernel sources and exit")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="run one device copy of this many MiB after the timed region (counter calibration)")
+    ap.add_argument("--latency-queries", type=int, default=None,
+                    help="searches timed one by one for latency percentiles (default: 1000 at batch 1, else 0)")
+    ap.add_argument("--no-read-ceiling", action="store_true", help="skip the streaming-read probe")
     return ap.parse_args()
 
 
 def kernel_source_hash() -> str:
-    """Hash of the code the scan kernel is built from (its source, the shared device helpers and the
-    constants), with comments removed and whitespace collapsed, so that a comment edit keeps it."""
+    """Hash of everything the search kernels are built from: every source of the library (kernels, device
+    helpers, constants, the host code that sets launch shapes and paths) with comments removed and
+    whitespace collapsed, so that a comment edit keeps it, plus the compiler flags."""
+    from int8_ivf_ann_amd import build
     h = hashlib.sha256()
-    for f in ("svt_kernels.hip", "svt_device.h", "svt_internal.h"):
-        with open(os.path.join(ROOT, "int8_ivf_ann_amd", "csrc", f)) as fh:
+    csrc = os.path.join(ROOT, "int8_ivf_ann_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if not f.endswith((".hip", ".h", ".cpp")):
+            continue
+        with open(os.path.join(csrc, f)) as fh:
             src = fh.read()
         src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
         src = re.sub(r"//[^\n]*", " ", src)
-        h.update(" ".join(src.split()).encode())
+        h.update(f.encode() + b"\0" + " ".join(src.split()).encode())
+    h.update(" ".join(build.COMMON[:4] + build.DEVICE_FLAGS + [build.ARCH]).encode())
     return h.hexdigest()[:16]
+
+
+def read_ceiling_gbs(torch, gib: int = 4, reps: int = 5) -> float:
+    """Streaming-read rate of this GPU: torch's sum over a gib-GiB int64 tensor, best of reps."""
+    x = torch.ones((gib << 30) // 8, dtype=torch.int64, device="cuda")
+    best = 0.0
+    for _ in range(reps + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        s = x.sum()
+        e1.record()
+        e1.synchronize()
+        best = max(best, x.numel() * 8 / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del x, s
+    return best
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def algorithmic_bytes(cat, sigs_sorted, offsets, queries, masks, nprobe, W, d):
@@ -150,8 +190,10 @@ def main():
         batches.append(dict(q=qs.queries, m=masks, q_d=torch.from_numpy(qs.queries).cuda(),
                             m_d=torch.from_numpy(masks.view(np.int64)).cuda()))
     opts = svt.make_options(args.path)
+    path = svt.svt_search_path(ix.handle, B, nprobe, k, opts)
+    kernel = {"query": "k_scan", "tile": "k_tscan", "exhaustive": "k_xscan"}[path]
     ws = ix.workspace(B, nprobe, k, opts)
-    log(f"[bench] workspace {ws.numel() / 2**20:.1f} MiB (path {args.path})")
+    log(f"[bench] workspace {ws.numel() / 2**20:.1f} MiB (path {args.path}: {path}, scan kernel {kernel})")
     outs = dict(out_ids=torch.empty((B, k), dtype=torch.int64, device="cuda"),
                 out_scores=torch.empty((B, k), dtype=torch.int32, device="cuda"),
                 out_fscores=torch.empty((B, k), dtype=torch.float32, device="cuda"),
@@ -195,6 +237,46 @@ def main():
     log(f"[bench] {args.steps} steps in {elapsed * 1e3:.2f} ms; stages of a separate profiled pass (ms/step): "
         + ", ".join(f"{kname} {v / max(n_stage, 1):.4f}" for kname, v in stage_ms.items()))
 
+    # latency: searches of one batch timed one by one (distinct queries), host wall clock around the
+    # search and a synchronisation, and HIP events on the search stream
+    lat = None
+    n_lat = args.latency_queries if args.latency_queries is not None else (1000 if B == 1 else 0)
+    if n_lat > 0:
+        ql = synth.queries(cat, n_lat * B, offset=args.batches * B)
+        ml = np.stack([svt.svt_bloom_mask(ql.required(b), h, W) for b in range(n_lat * B)])
+        ql_d = torch.from_numpy(ql.queries).cuda()
+        ml_d = torch.from_numpy(ml.view(np.int64)).cuda()
+        st_l = torch.empty((B, 2), dtype=torch.int64, device="cuda")
+        host_ms, dev_ms, evs = [], [], []
+        for i in range(n_lat + 5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            ts = time.perf_counter()
+            e0.record()
+            svt.svt_search(ix.handle, ql_d[(i % n_lat) * B:(i % n_lat + 1) * B], ml_d[(i % n_lat) * B:(i % n_lat + 1) * B],
+                           nprobe, k, workspace=ws, out_stats=st_l, opts=opts, **outs)
+            e1.record()
+            torch.cuda.synchronize()
+            if i >= 5:   # the first searches of new queries warm the caches
+                host_ms.append((time.perf_counter() - ts) * 1e3)
+                evs.append((e0, e1))
+        dev_ms = [a.elapsed_time(b) for a, b in evs]
+        pct = lambda v, p: float(np.percentile(np.asarray(v), p))
+        lat = {"searches": n_lat, "batch": B,
+               "host_ms": {"p50": pct(host_ms, 50), "p99": pct(host_ms, 99), "mean": float(np.mean(host_ms))},
+               "device_ms": {"p50": pct(dev_ms, 50), "p99": pct(dev_ms, 99), "mean": float(np.mean(dev_ms))},
+               "note": "host: wall clock of the search call plus a stream synchronisation; device: HIP events "
+                       "recorded on the search stream before and after the search"}
+        log(f"[bench] latency over {n_lat} searches of batch {B}: host p50 {lat['host_ms']['p50']:.4f} ms "
+            f"p99 {lat['host_ms']['p99']:.4f} ms; device p50 {lat['device_ms']['p50']:.4f} ms "
+            f"p99 {lat['device_ms']['p99']:.4f} ms")
+        del ql_d, ml_d
+
+    ceiling = None
+    if not args.no_read_ceiling:
+        ceiling = read_ceiling_gbs(torch)
+        log(f"[bench] streaming-read ceiling (torch sum over 4 GiB): {ceiling:.1f} GB/s")
+
     if args.copy_calibration_mb > 0:
         # a plain copy of known size, for scaling hardware byte counters (read + write of n bytes each)
         nb = args.copy_calibration_mb << 20
@@ -225,7 +307,7 @@ def main():
         f"{np.mean([a[4] for a in alg]):.0f} distinct clusters) in {scan_ms:.4f} ms -> {achieved:.1f} GB/s")
 
     traffic = None
-    tpath = args.traffic or os.path.join(ROOT, "profiles", f"traffic_k_scan_{name}_b{B}.md")
+    tpath = args.traffic or os.path.join(ROOT, "profiles", f"traffic_{kernel}_{name}_b{B}.md")
     if os.path.exists(tpath):
         from int8_ivf_ann_amd.rocprof_summary import read_traffic
         tj = read_traffic(tpath)
@@ -238,21 +320,34 @@ def main():
     if not args.no_cpu_baseline:
         import oracle
         orc = oracle.Oracle()
-        threads = max(1, min(16, os.cpu_count() or 1))
+        nproc = os.cpu_count() or 1
+        threads = max(1, min(16, nproc))   # the GPU's share of the host: at most 16 threads
         bt = batches[0]
-        # one query first, to size a sample of about args.cpu_seconds of CPU work
+        # one query first, to size samples of about args.cpu_seconds of work on all threads and a third of
+        # that on one thread
         ts = time.perf_counter()
-        orc.search(cat.items, sigs, cat.list_of, cat.centroids, cat.item_scale, bt["q"][:1], bt["m"][:1], nprobe, k)
+        orc.search(cat.items, sigs, cat.list_of, cat.centroids, cat.item_scale, bt["q"][:1], bt["m"][:1], nprobe, k,
+                   n_threads=1)
         one = time.perf_counter() - ts
-        n_s = int(min(B, max(threads, round(args.cpu_seconds / max(one, 1e-6)))))
-        ts = time.perf_counter()
-        _, _, _, _, st = orc.search(cat.items, sigs, cat.list_of, cat.centroids, cat.item_scale, bt["q"][:n_s],
-                                    bt["m"][:n_s], nprobe, k, n_threads=threads)
-        cs = time.perf_counter() - ts
-        cpu = {"value": float(st[:, 1].sum() / cs), "unit": "items/s", "cores": threads, "kind": "oracle",
-               "sample": f"first {n_s} queries of batch 0 of the same workload ({int(st[:, 1].sum())} eligible pairs, "
-                         f"{cs:.2f} s wall on {threads} threads)"}
-        log(f"[bench] cpu oracle: {cpu['value']:.3e} items/s on {threads} threads ({n_s} queries, {cs:.2f}s)")
+
+        def run(n_q, n_thr):
+            ts = time.perf_counter()
+            _, _, _, _, st = orc.search(cat.items, sigs, cat.list_of, cat.centroids, cat.item_scale, bt["q"][:n_q],
+                                        bt["m"][:n_q], nprobe, k, n_threads=n_thr)
+            return int(st[:, 1].sum()), time.perf_counter() - ts
+
+        n_1 = int(min(B, max(1, round(args.cpu_seconds / 3 / max(one, 1e-6)))))
+        e1, c1 = run(n_1, 1)
+        n_s = int(min(B, max(threads, round(args.cpu_seconds * threads / max(one, 1e-6)))))
+        e_s, cs = run(n_s, threads)
+        cpu = {"value": float(e_s / cs), "unit": "items/s", "cores": threads, "threads": threads, "kind": "oracle",
+               "sample": f"first {n_s} queries of batch 0 of the same workload ({e_s} eligible pairs, "
+                         f"{cs:.2f} s wall on {threads} threads)",
+               "nproc": nproc, "cpu_model": cpu_model(),
+               "single_thread": {"value": float(e1 / c1), "unit": "items/s", "threads": 1,
+                                 "sample": f"first {n_1} queries of batch 0 ({e1} eligible pairs, {c1:.2f} s wall)"}}
+        log(f"[bench] cpu oracle: {cpu['value']:.3e} items/s on {threads} threads ({n_s} queries, {cs:.2f}s); "
+            f"{e1 / c1:.3e} items/s on 1 thread ({n_1} queries, {c1:.2f}s); nproc {nproc}, {cpu['cpu_model']}")
 
     wl = (f"{name}: {cat.n_items} items, d={d}, nlist={cfg['nlist']} "
           f"({'Zipf ' + str(cfg['cluster_zipf']) if cfg['cluster_zipf'] else 'uniform'} cluster sizes), "
@@ -276,10 +371,21 @@ def main():
         "items_scanned_per_s": steps_scanned / elapsed,
         "stage_ms_per_step": {kname: v / max(n_stage, 1) for kname, v in stage_ms.items()},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "kernel": "k_scan",
-                     "algorithmic_bytes_per_launch": alg_per_launch},
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "traffic_kind": "fabric bytes per launch: FETCH_SIZE + WRITE_SIZE (L2-to-fabric requests, "
+                                     "Infinity Cache hits included), each scaled by the same counter over a "
+                                     "device copy of known size",
+                     "kernel": kernel, "path": path,
+                     "algorithmic_bytes_per_launch": alg_per_launch,
+                     "scan_ms": scan_ms,
+                     "step_achieved": alg_per_launch / (elapsed / args.steps) / 1e9,
+                     "step_frac": alg_per_launch / (elapsed / args.steps) / 1e9 / HBM_PEAK_GBS,
+                     "read_ceiling": ceiling,
+                     "frac_of_read_ceiling": (achieved / ceiling) if ceiling else None},
         "cpu_baseline": cpu,
     }
+    if lat is not None:
+        line["latency"] = lat
     print(json.dumps(line), flush=True)
     ix.close()
 

@@ -109,7 +109,7 @@ int svt_index_info(const svt_index *ix, int64_t *n_items, int32_t *dim, int32_t 
  *                   candidates (with a threshold above the minimum) or overflows is redone on the query
  *                   path, so the result stays exact whatever the data.
  */
-enum { SVT_PATH_AUTO = 0, SVT_PATH_QUERY = 1, SVT_PATH_TILE = 2 };
+enum { SVT_PATH_AUTO = 0, SVT_PATH_QUERY = 1, SVT_PATH_TILE = 2, SVT_PATH_EXHAUSTIVE = 3 };
 
 /* svt_search_options.flags */
 #define SVT_OPT_MERGE_FROM_SLOTS 1u  /* query path: the merge reads every chunk's slot instead of the keys
@@ -143,6 +143,14 @@ typedef struct {
  */
 size_t svt_search_workspace_size(const svt_index *ix, int32_t n_queries, int32_t nprobe, int32_t k,
                                  const svt_search_options *opts);
+
+/*
+ * svt_search_path - the path a search with these sizes and options takes: SVT_PATH_QUERY, SVT_PATH_TILE
+ * or SVT_PATH_EXHAUSTIVE (the tile path's MFMA scan of the whole catalogue, nprobe == nlist).  It depends
+ * on the index, n_queries, nprobe and the options only, never on query values.  No device work.
+ * Errors (negative return): those of svt_search_workspace_size's arguments (SVT_EINVAL, SVT_ESTATE).
+ */
+int svt_search_path(const svt_index *ix, int32_t n_queries, int32_t nprobe, int32_t k, const svt_search_options *opts);
 
 /*
  * svt_search - batched fused search (steps 1-4 above), asynchronous on hip_stream.

@@ -265,9 +265,10 @@ struct Layout {
   SearchShape sh;
 };
 
-// Batches of at least this many queries take the tile path by default (their queries share enough
-// probed clusters for one read per batch to pay for the work list and the pools).
-constexpr int32_t kTileMinBatch = 32;
+// Batches of at least this many queries take the tile path by default: their queries share enough
+// probed clusters for one read per batch to pay for the union work list and the pools (at 80M items,
+// nprobe 64, the query path is faster at 32 queries and the tile path at 256).
+constexpr int32_t kTileMinBatch = 128;
 // The union stream is indexed with 32-bit offsets.
 constexpr int64_t kMaxUnion = (int64_t(1) << 31) - (int64_t(1) << 20);
 
@@ -357,7 +358,7 @@ Layout layout(const svt_index *ix, int32_t B, int32_t nprobe, int32_t k, const s
   if (sh.path == kPathTile) {
     const int64_t blocks = ((int64_t)B + kTMembers - 1) / kTMembers;
     sh.max_entries = (int32_t)std::max<int64_t>(1, std::min<int64_t>((int64_t)nlist * blocks, (int64_t)B * nprobe));
-    sh.max_tchunks = kTChunksPerWG * sh.TP + 2;
+    sh.max_tchunks = kTChunksPerWave * kTWaves * sh.TP + 2;
     L.gcnt = take(nlist * sizeof(int32_t));
     L.gfill = take(nlist * sizeof(int32_t));
     L.gstart = take((nlist + 1) * sizeof(int32_t));
@@ -565,6 +566,18 @@ extern "C" size_t svt_search_workspace_size(const svt_index *ix, int32_t n_queri
   g_err.clear();
   if (check_search_args(ix, n_queries, nprobe, k, opts, "svt_search_workspace_size") != SVT_OK) return 0;
   return layout(ix, n_queries, nprobe, k, opts).total;
+}
+
+extern "C" int svt_search_path(const svt_index *ix, int32_t n_queries, int32_t nprobe, int32_t k,
+                               const svt_search_options *opts) {
+  g_err.clear();
+  const int rc = check_search_args(ix, n_queries, nprobe, k, opts, "svt_search_path");
+  if (rc != SVT_OK) return rc;
+  switch (resolve_path(ix, n_queries, nprobe, opts)) {
+    case kPathTile: return SVT_PATH_TILE;
+    case kPathExh: return SVT_PATH_EXHAUSTIVE;
+    default: return SVT_PATH_QUERY;
+  }
 }
 
 extern "C" int svt_search(const svt_index *ix, int32_t B, const int8_t *queries, const uint64_t *masks,

@@ -101,27 +101,30 @@ static_assert(kTailBand >= 0 && kTailBand <= kPlanBands && kTailDiv >= 1, "tail 
 
 // Tile path.  The batch's probed clusters form one union stream: for every probed cluster, in cluster
 // order, one entry per block of at most kTMembers of the queries probing it (a cluster probed by more
-// queries appears once per block).  The stream is cut into chunks that persistent workgroups take from
-// a queue; every item of an entry is tested against the masks of the entry's members and the rows of
-// the items any member accepts are gathered once and scored for each member that accepts them.
+// queries appears once per block).  The stream is cut into chunks that the waves of persistent workgroups
+// take from a queue; every item of an entry is tested against the masks of the entry's members and the
+// rows of the items any member accepts are gathered once and scored for each member that accepts them.
 constexpr int kTMembers = 16;        // queries of one union entry (member bits of a survivor: uint16)
-constexpr int kTWin = 64;            // union entries a workgroup stages in LDS at a time
-constexpr int kTWinMembers = 64;     // members of the staged entries (with their query vectors)
+constexpr int kTWaves = kScanThreads / 64;   // waves of a tile-scan workgroup (each works alone)
 #ifndef SVT_T_CHUNKS
-#define SVT_T_CHUNKS 8
+#define SVT_T_CHUNKS 4
 #endif
-constexpr int kTChunksPerWG = SVT_T_CHUNKS;   // chunks of the union stream per persistent workgroup
+constexpr int kTChunksPerWave = SVT_T_CHUNKS;   // chunks of the union stream per wave of the scan
+#ifndef SVT_T_GROUPS
+#define SVT_T_GROUPS 4
+#endif
+constexpr int kTGroups = SVT_T_GROUPS;   // 64-item signature groups of one filter step
+#ifndef SVT_T_ROWLOADS
+#define SVT_T_ROWLOADS 6
+#endif
+constexpr int kTRowLoads = SVT_T_ROWLOADS;   // 16-byte row loads per lane of one scored batch
+#ifndef SVT_T_OCC
+#define SVT_T_OCC 3
+#endif
+constexpr int kTOcc = SVT_T_OCC;             // tile-scan waves per SIMD the compiler is asked to fit
 // Chunks of the union stream are cut at equal estimated cost: per item of an entry, its signature bytes and
 // kTItemCost byte equivalents of other work, kTMemberCost per member; the rows of the fraction of items some
 // member accepts (from the members' sampled densities).
-#ifndef SVT_T_ROWS
-#define SVT_T_ROWS 48
-#endif
-#ifndef SVT_T_GROUPS
-#define SVT_T_GROUPS 5
-#endif
-constexpr int kTGroups = SVT_T_GROUPS;             // 64-item groups per wave per step
-constexpr int kTStep = kScanThreads * kTGroups;    // items per workgroup step, at most
 constexpr int kTItemCost = 16;
 constexpr int kTMemberCost = 2;
 // Speculative thresholds: a query's threshold is the score that an estimated kAlpha * k of its eligible

@@ -128,7 +128,7 @@ __global__ __launch_bounds__(kSelThreads) void k_tplan2(DevIndex ix, int32_t P, 
     const int32_t U = (int32_t)boff[2];
     w.thdr[0] = (int32_t)boff[1];
     w.thdr[1] = U;
-    w.thdr[2] = U > 0 ? kTChunksPerWG * P : 0;
+    w.thdr[2] = U > 0 ? kTChunksPerWave * kTWaves * P : 0;
     w.thdr[3] = 0;
   }
 }
@@ -203,23 +203,38 @@ __global__ __launch_bounds__(256) void k_tentries(DevIndex ix, int32_t max_entri
   w.entries[e] = UEntry{useg, size, pos0, ms, mc, 0, 0, 0};
 }
 
+// Order of LDS accesses between the lanes of one wave (its LDS operations complete in order; this keeps
+// the compiler from moving them across each other).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// raw buffer resource over [base, base + bytes) (gfx9 word 3: 32-bit data format, no swizzle)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void *base, int64_t bytes) {
+  const int n = bytes <= 0 ? 0 : (bytes < 0x7FFFFFFF ? (int)bytes : 0x7FFFFFFF);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n, 0x00020000);
+}
+
 // ------------------------------------------------------------------------------------------------
 // k_tscan: the union stream, chunk by chunk.
 //
-// A workgroup walks a chunk in steps of kTStep items inside one entry (as k_scan walks a query's
-// stream): each wave loads 64 kTGroups signatures, tests them against the masks of every member of
-// the step's entry and compacts the items any member accepts, with the member bits, into LDS; after one
-// barrier the survivors are shared evenly among the waves, which gather their rows (LPR lanes per row,
-// 16-byte loads) with the query slice of each row's first member and score them with v_dot4; further
-// members of a row (rare) are scored from the same row registers.  The steps run as a software pipeline:
-// iteration i filters step i + 1, requests the signatures of step i + 2, passes the barrier, scores step
-// i and requests the rows of step i + 1.  Every load is issued unconditionally (clamped addresses,
-// masked lanes), so the compiler's wait counts stay exact.
+// Each wave works alone: it takes a chunk from the queue, stages the chunk's entries (a window of them,
+// with their members and query vectors) in its part of LDS and walks them in filter steps of 64 kTGroups
+// items inside one entry.  A step's signatures are tested against the masks of every member of the entry;
+// the items any member accepts go, with their member bits, into the wave's FIFO of survivors.  Every
+// iteration then requests the rows of the next batch of FIFO survivors (LPR lanes per row, 16-byte loads)
+// and scores the batch requested one iteration earlier against the query vector of each member that
+// accepts the row (v_dot4).  The signatures of the next step are requested after each filter, so
+// signatures and rows both have one iteration to arrive; every load is issued in every iteration (a
+// signature resource clipped to the step, so that items past it read as zero without a memory access;
+// lanes without a row re-read the batch's first row), which keeps the compiler's wait counts exact.
+// A new step is taken only while the FIFO has room for all of its items besides the batch in flight.
 //
-// Candidates (score at or above the member's threshold) are staged in LDS with the slot of their
-// (entry visit, member) and go to the queries' pools at the end of the chunk, one pool reservation per
-// slot.  A candidate that finds the stage or the slot table full goes to its pool directly.  Per-slot
-// counters give the scanned and accepted items of each query.
+// Candidates (score at or above the member's threshold) are staged in LDS with the slot of their (entry
+// visit, member) and go to the queries' pools when the stage fills and at the end of the chunk, one pool
+// reservation per slot.  Per-slot counters give the scanned and accepted items of each query.
 
 struct TScanArgs {
   DevIndex ix;
@@ -229,405 +244,347 @@ struct TScanArgs {
   uint32_t pool_cap;
 };
 
-constexpr int kTSlots = 256;         // (entry visit, member) slots of a chunk
-constexpr int kTStageWG = 768;       // candidates a workgroup stages per chunk
-constexpr int kTRowBatch = SVT_T_ROWS;   // rows a wave gathers together (its share of a dense step)
-
-struct TMember {                     // one member of a step's entry
-  uint64_t m0, m1;
-  int32_t thr, q, slot, pad;         // slot < 0: no slot (counts and candidates go to HBM directly)
-};
+constexpr int kTF = 512;             // survivors a wave's FIFO holds (a ring)
+constexpr int kTWinW = 16;           // entries of a wave's window
+constexpr int kTWinMW = 32;          // members of those entries
+constexpr int kTSlotsW = 64;         // (entry visit, member) slots of a wave's chunk
+constexpr int kTStageW = 192;        // candidates a wave stages before it writes them to the pools
+constexpr uint32_t kNoSlot = 0xFFu;
+static_assert(kTWinMW >= kTMembers && kTWinMW <= 256 && kTSlotsW < 255, "survivor metadata fields");
 
 template <int LPR>
-struct TScanLds {
-  uint16_t wl[3][kTStep];         // survivors of three consecutive steps (offset in the step)
-  uint16_t wq[3][kTStep];         //   and the members that accept them (bit j: member j)
-  int wcnt[2][kScanThreads / 64];    // survivors each wave found in a step, by step parity
-  TMember mt[4][kTMembers];          // members of the entry of step i in mt[i % 4]
-  int4 mqv[4][kTMembers][LPR];       //   and their query vectors
-  // window of the chunk's entries: stream range clipped to the chunk, position base (pos = pb + t),
-  // first member in wm, member count, first member in mrec
-  int32_t e_t0[kTWin], e_t1[kTWin], e_pb[kTWin], e_m[kTWin], e_mc[kTWin], e_ms[kTWin];
-  int e_n;
-  MRec wm[kTWinMembers];             // members of the window's entries
-  int4 wqv[kTWinMembers][LPR];       //   and their query vectors
-  int32_t sq[kTSlots];               // query of each slot
-  uint32_t scount[kTSlots];          // candidates staged for each slot
-  uint32_t sbase[kTSlots];           // their pool position, reserved at the flush
-  uint32_t selig[kTSlots];           // items the slot's member accepted
-  uint32_t sscan[kTSlots];           // items of the slot's entry visit
-  uint64_t skey[kTStageWG];          // staged candidates: (score, position) keys
-  uint16_t sslot[kTStageWG];         //   their slot (0xFFFF: not staged)
-  uint16_t srank[kTStageWG];         //   their rank among the slot's staged candidates
-  int stage_n;
-  int next;
+struct TWaveLds {
+  // the window: stream range of each entry clipped to the chunk, position base (pos = pb + t), first
+  // window member, member count, first member in mrec
+  int32_t e_t0[kTWinW], e_t1[kTWinW], e_pb[kTWinW], e_m[kTWinW], e_mc[kTWinW], e_ms[kTWinW];
+  MRec wm[kTWinMW];                  // members of the window's entries
+  int4 wqv[kTWinMW][LPR];            //   and their query vectors
+  int32_t fpos[kTF];                 // survivors: position
+  uint32_t fmeta[kTF];               //   member bits | first window member << 16 | first slot << 24
+  int32_t sq[kTSlotsW];              // query of each slot
+  uint32_t scount[kTSlotsW];         // candidates staged for each slot
+  uint32_t sbase[kTSlotsW];          // their pool position, reserved at a flush
+  uint32_t selig[kTSlotsW];          // items the slot's member accepted
+  uint32_t sscan[kTSlotsW];          // items of the slot's entry visit
+  uint64_t skey[kTStageW];           // staged candidates: (score, position) keys
+  uint8_t sslot[kTStageW];           //   their slot
+  uint16_t srank[kTStageW];          //   their rank among the slot's staged candidates
 };
 
 template <int LPR, int W>
-__global__ __launch_bounds__(kScanThreads, kScanOcc) void k_tscan(TScanArgs a) {
+__global__ __launch_bounds__(kScanThreads, kTOcc) void k_tscan(TScanArgs a) {
   constexpr int D = 16 * LPR;
-  constexpr int RPI = 64 / LPR;                   // rows covered by one 16-byte load per lane
-  constexpr int R0 = kTRowBatch / RPI;
-  constexpr int R = R0 < 1 ? 1 : (R0 > 8 ? 8 : R0);   // row loads per lane in one batch
-  constexpr int RB = R * RPI;                     // rows a wave requests together
-  constexpr int NWV = kScanThreads / 64;
-  __shared__ TScanLds<LPR> sm;
-  const int tid = threadIdx.x, l = lane_id(), wv = tid / 64, sub = l % LPR;
+  constexpr int RPI = 64 / LPR;        // rows covered by one 16-byte load per lane
+  constexpr int R = kTRowLoads;
+  constexpr int RB = R * RPI;          // rows of one batch
+  constexpr int G = kTGroups;
+  constexpr int GS = 64 * G;           // items of one filter step
+  static_assert(RB <= kTF && GS <= kTF, "FIFO");
+  __shared__ TWaveLds<LPR> lds[kTWaves];
+  const int l = lane_id(), sub = l % LPR;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+  TWaveLds<LPR> &S = lds[wv];
   const int n_chunks = a.w.thdr[2];
   const int n_ent = a.w.thdr[0];
   const uint32_t cap = a.pool_cap;
   int64_t *stats = a.w.stats;
-  if (tid == 0) {
-    sm.next = (int)atomicAdd(&a.w.counter[3], 1u);
-    sm.stage_n = 0;
+  for (int i = l; i < kTSlotsW; i += 64) {
+    S.scount[i] = 0u;
+    S.selig[i] = 0u;
   }
-  for (int i = tid; i < kTSlots; i += kScanThreads) {
-    sm.scount[i] = 0u;
-    sm.selig[i] = 0u;
-  }
-  __syncthreads();
-  for (;;) {
-    const int ci = __builtin_amdgcn_readfirstlane(sm.next);
-    if (ci >= n_chunks) break;
-    int next_c = 0;
-    if (tid == 0) next_c = (int)atomicAdd(&a.w.counter[3], 1u);
-    const int32_t ra = a.w.cstart_u[ci], rb = a.w.cstart_u[ci + 1];
-    int jwin = a.w.ctab[ci];
-    if (ra >= rb) {   // an empty chunk
-      __syncthreads();   // every thread has read sm.next before it is replaced
-      if (tid == 0) sm.next = next_c;
-      __syncthreads();
-      continue;
+  int stage_n = 0;   // staged candidates (the same value in every lane)
+  int nsl = 0;       // slots taken in the chunk
+  // staged candidates to their pools: one reservation per slot with staged keys, then the keys
+  auto flush = [&]() {
+    wave_lds_sync();
+    const int ns = nsl < kTSlotsW ? nsl : kTSlotsW;
+    for (int s = l; s < ns; s += 64) {
+      const uint32_t c = S.scount[s];
+      if (c) S.sbase[s] = atomicAdd(&a.w.pool_cnt[S.sq[s]], c);
+      S.scount[s] = 0u;
     }
-    // the chunk's entries from jwin on, as many as kTWin entries and kTWinMembers members allow
-    auto load_window = [&]() {   // all threads
-      __syncthreads();
-      if (wv == 0) {
-        UEntry E{0, 0, 0, 0, 0, 0, 0, 0};
-        const bool have = jwin + l < n_ent && l < kTWin;
-        if (have) E = a.w.entries[jwin + l];
-        const bool valid = have && E.useg < rb;   // entries are in stream order: a prefix of the lanes
-        const int mc = valid ? E.mcnt : 0;
-        const int inc = wave_incl_scan(mc);
-        const bool fit = valid && inc <= kTWinMembers;
-        const int n = __popcll(__ballot(fit));
-        if (fit) {
-          sm.e_t0[l] = ra > E.useg ? ra : E.useg;
-          sm.e_t1[l] = rb < E.useg + E.len ? rb : E.useg + E.len;
-          sm.e_pb[l] = E.pos0 - E.useg;
-          sm.e_m[l] = inc - mc;
-          sm.e_mc[l] = mc;
-          sm.e_ms[l] = E.mstart;
-        }
-        if (l == 0) sm.e_n = n;
+    wave_lds_sync();
+    for (int e = l; e < stage_n; e += 64) {
+      const int s = S.sslot[e];
+      const uint32_t o = S.sbase[s] + S.srank[e];
+      if (o < cap) a.w.pool[(size_t)S.sq[s] * cap + o] = S.skey[e];
+    }
+    wave_lds_sync();
+    stage_n = 0;
+  };
+  for (;;) {
+    int ci = 0;
+    if (l == 0) ci = (int)atomicAdd(&a.w.counter[3], 1u);
+    ci = __builtin_amdgcn_readfirstlane(__shfl(ci, 0));
+    if (ci >= n_chunks) break;
+    const int32_t ra = a.w.cstart_u[ci], rb = a.w.cstart_u[ci + 1];
+    if (ra >= rb) continue;
+    int jwin = a.w.ctab[ci];
+    int e_n = 0;   // entries in the window
+    // the chunk's entries from jwin on, as many as kTWinW entries and kTWinMW members allow
+    auto load_window = [&]() {
+      UEntry E{0, 0, 0, 0, 0, 0, 0, 0};
+      const bool have = jwin + l < n_ent && l < kTWinW;
+      if (have) E = a.w.entries[jwin + l];
+      const bool valid = have && E.useg < rb;   // entries are in stream order: a prefix of the lanes
+      const int mc = valid ? E.mcnt : 0;
+      const int inc = wave_incl_scan(mc);
+      const bool fit = valid && inc <= kTWinMW;
+      const int n = __popcll(__ballot(fit));
+      wave_lds_sync();
+      if (fit) {
+        S.e_t0[l] = ra > E.useg ? ra : E.useg;
+        S.e_t1[l] = rb < E.useg + E.len ? rb : E.useg + E.len;
+        S.e_pb[l] = E.pos0 - E.useg;
+        S.e_m[l] = inc - mc;
+        S.e_mc[l] = mc;
+        S.e_ms[l] = E.mstart;
       }
-      __syncthreads();
-      const int n = sm.e_n;
-      const int nm = n > 0 ? sm.e_m[n - 1] + sm.e_mc[n - 1] : 0;
-      // members and their query vectors: thread t copies part t % LPR of member t / LPR
-      for (int mp = tid; mp < nm * LPR; mp += kScanThreads) {
+      const int nm = n > 0 ? __shfl(inc, n - 1) : 0;
+      wave_lds_sync();
+      // members and their query vectors: lane t copies part t % LPR of member t / LPR
+      for (int mp = l; mp < nm * LPR; mp += 64) {
         const int m = mp / LPR, part = mp % LPR;
         int lo = 0, hi = n - 1;   // the entry of window member m: largest i with e_m[i] <= m
         while (lo < hi) {
           const int mid = (lo + hi + 1) >> 1;
-          if (sm.e_m[mid] <= m) lo = mid; else hi = mid - 1;
+          if (S.e_m[mid] <= m) lo = mid; else hi = mid - 1;
         }
-        const MRec rec = a.w.mrec[sm.e_ms[lo] + (m - sm.e_m[lo])];
-        if (part == 0) sm.wm[m] = rec;
-        sm.wqv[m][part] = reinterpret_cast<const int4 *>(a.queries + (size_t)rec.q * D)[part];
+        const MRec rec = a.w.mrec[S.e_ms[lo] + (m - S.e_m[lo])];
+        if (part == 0) S.wm[m] = rec;
+        S.wqv[m][part] = reinterpret_cast<const int4 *>(a.queries + (size_t)rec.q * D)[part];
       }
-      __syncthreads();
+      wave_lds_sync();
+      e_n = n;
     };
-    struct Cursor {
-      int w;            // entry in the LDS window; -1: chunk finished
-      int32_t st, t1;   // step start / entry end, in stream offsets
-      int32_t pbase;    // position = pbase + stream offset
-    };
-    auto seek = [&](Cursor &cu) {   // all threads; from entry cu.w: the first entry with items left
-      for (;;) {
-        for (; cu.w < sm.e_n; ++cu.w) {
-          const int32_t t0 = sm.e_t0[cu.w], t1 = sm.e_t1[cu.w];
-          if (t0 < t1) {
-            cu.st = t0;
-            cu.t1 = t1;
-            cu.pbase = sm.e_pb[cu.w];
-            return;
+    // cursor: entry cw of the window, next step at stream offset cst, entry end ct1, position base cpb;
+    // the entry visit's first window member, member count and first slot
+    int cw = 0;
+    int32_t cst = 0, ct1 = 0, cpb = 0;
+    int cmb = 0, cmc = 0;
+    uint32_t cslot = kNoSlot;
+    // from entry cw on: the first entry of the window with items left (cw == e_n: none); a new entry visit
+    // takes a slot per member (a visit without slots counts to HBM)
+    auto seek = [&]() {
+      for (; cw < e_n; ++cw) {
+        const int32_t t0 = __builtin_amdgcn_readfirstlane(S.e_t0[cw]);
+        const int32_t t1 = __builtin_amdgcn_readfirstlane(S.e_t1[cw]);
+        if (t0 < t1) {
+          cst = t0;
+          ct1 = t1;
+          cpb = __builtin_amdgcn_readfirstlane(S.e_pb[cw]);
+          cmb = __builtin_amdgcn_readfirstlane(S.e_m[cw]);
+          cmc = __builtin_amdgcn_readfirstlane(S.e_mc[cw]);
+          const bool fits = nsl + cmc <= kTSlotsW;
+          cslot = fits ? (uint32_t)nsl : kNoSlot;
+          if (l < cmc) {
+            const int q = S.wm[cmb + l].q;
+            if (fits) {
+              S.sq[nsl + l] = q;
+              S.sscan[nsl + l] = (uint32_t)(t1 - t0);
+            } else if (stats) {
+              atomicAdd((unsigned long long *)&stats[2 * (size_t)q], (unsigned long long)(t1 - t0));
+            }
           }
-        }
-        const int nx = jwin + sm.e_n;   // window exhausted: another one if the chunk continues
-        if (sm.e_n == 0 || nx >= n_ent || a.w.entries[nx].useg >= rb) {
-          cu.w = -1;
+          if (fits) nsl += cmc;
+          wave_lds_sync();
           return;
         }
-        jwin = nx;
-        load_window();
-        cu.w = 0;
       }
     };
-    auto advance = [&](Cursor &cu) {
-      cu.st += kTStep;
-      if (cu.st >= cu.t1) {
-        ++cu.w;
-        seek(cu);
-      }
-    };
-    // The member table of the step at cursor cu, in mt[mtb] (wave 0 writes it; a barrier follows before
-    // any use).  A new entry visit takes a slot per member; a visit without slots counts to HBM.
-    int nsl = 0;        // slots taken in this chunk (the same value in every thread)
-    int last_eg = -1;   // entry of the last step whose table was built
-    int slot_base = 0;
-    // The member table copies everything a step needs from the window (LDS to LDS, no memory loads in
-    // the step pipeline), so that the window can be replaced while the step is still in flight.
-    auto build_mt = [&](const Cursor &cu, int mtb) -> int {
-      if (cu.w < 0) return 0;
-      const int mc = sm.e_mc[cu.w];
-      if (tid < mc * LPR) sm.mqv[mtb][tid / LPR][tid % LPR] = sm.wqv[sm.e_m[cu.w] + tid / LPR][tid % LPR];
-      const int eg = jwin + cu.w;
-      const bool fresh = eg != last_eg;
-      if (fresh) {
-        slot_base = nsl;
-        nsl += mc;
-        last_eg = eg;
-      }
-      if (wv == 0 && l < mc) {
-        const MRec m = sm.wm[sm.e_m[cu.w] + l];
-        const int s = slot_base + l < kTSlots ? slot_base + l : -1;
-        sm.mt[mtb][l] = TMember{m.m0, m.m1, m.thr, m.q, s, 0};
-        if (fresh) {
-          const uint32_t items = (uint32_t)(sm.e_t1[cu.w] - sm.e_t0[cu.w]);
-          if (s >= 0) {
-            sm.sq[s] = m.q;
-            sm.sscan[s] = items;
-          } else if (stats) {
-            atomicAdd((unsigned long long *)&stats[2 * (size_t)m.q], (unsigned long long)items);
-          }
-        }
-      }
-      return mc;
-    };
-    uint64_t sg[kTGroups][W];
-    int32_t sg_n = 0, sg_p0 = 0;
-    auto load_sigs = [&](const Cursor &cu) {
-      sg_n = cu.w >= 0 ? ((cu.t1 - cu.st) < kTStep ? (cu.t1 - cu.st) : kTStep) : 0;
-      const int32_t p0 = cu.w >= 0 ? cu.pbase + cu.st : 0;
-      sg_p0 = p0;
-      const int32_t last = sg_n > 0 ? sg_n - 1 : 0;
+    load_window();
+    seek();
+    // the step whose signatures are in flight: position of its first item, items, members, slot
+    bool sg_live = false;
+    int32_t fs_p0 = 0, fs_n = 0;
+    int fs_mb = 0, fs_mc = 0;
+    uint32_t fs_slot = kNoSlot;
+    uint64_t sg[G][W];
+    // request the signatures of the step at the cursor (or, with take false, of nothing: the loads read
+    // zeros without touching memory)
+    auto request_sigs = [&](bool take) {
+      const int32_t n = take ? (ct1 - cst < GS ? ct1 - cst : GS) : 0;
+      const int32_t p0 = cpb + cst;
+      const __amdgpu_buffer_rsrc_t rs = raw_rsrc(a.ix.sigs + (take ? (size_t)p0 * W : 0), (int64_t)n * (8 * W));
 #pragma unroll
-      for (int gi = 0; gi < kTGroups; ++gi) {
-        const int i = gi * kScanThreads + wv * 64 + l;
-        const int32_t p = p0 + (i < last ? i : last);
+      for (int g = 0; g < G; ++g) {
+        const uint32_t off = (uint32_t)(g * 64 + l) * (8u * W);
         if constexpr (W == 2) {
-          const ulonglong2 v = reinterpret_cast<const ulonglong2 *>(a.ix.sigs)[p];
-          sg[gi][0] = v.x;
-          sg[gi][1] = v.y;
+          typedef int v4i __attribute__((ext_vector_type(4)));
+          const v4i v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+          sg[g][0] = (uint64_t)(uint32_t)v.x | ((uint64_t)(uint32_t)v.y << 32);
+          sg[g][1] = (uint64_t)(uint32_t)v.z | ((uint64_t)(uint32_t)v.w << 32);
         } else {
-          sg[gi][0] = a.ix.sigs[p];
+          typedef int v2i __attribute__((ext_vector_type(2)));
+          const v2i v = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0);
+          sg[g][0] = (uint64_t)(uint32_t)v.x | ((uint64_t)(uint32_t)v.y << 32);
+        }
+      }
+      if (take) {
+        sg_live = true;
+        fs_p0 = p0;
+        fs_n = n;
+        fs_mb = cmb;
+        fs_mc = cmc;
+        fs_slot = cslot;
+        cst += n;
+        if (cst >= ct1) {
+          ++cw;
+          seek();
         }
       }
     };
-    struct Share {           // wave wv scores survivors [rbeg, rend) of a step's concatenated lists
-      int pre[NWV + 1];
-      int rbeg, rend;
-    };
-    auto share = [&](int par) -> Share {
-      Share s;
-      s.pre[0] = 0;
+    uint32_t head = 0, tail = 0;   // FIFO ring positions (uniform)
+    uint32_t bhead = 0;            // first FIFO position of the batch in flight
+    // the step in sg against the members of its entry; its survivors to the FIFO
+    auto filter = [&]() {
 #pragma unroll
-      for (int i = 0; i < NWV; ++i) s.pre[i + 1] = s.pre[i] + sm.wcnt[par][i];
-      const int total = s.pre[NWV];
-      const int per = (total + NWV - 1) / NWV;
-      s.rbeg = wv * per;
-      s.rend = s.rbeg + per < total ? s.rbeg + per : total;
-      return s;
-    };
-    auto surv_at = [&](const Share &s, int r) -> int {   // index of survivor r in its buffer
-      int adj = 0;
-#pragma unroll
-      for (int i = 1; i < NWV; ++i) adj = r >= s.pre[i] ? i * 64 * kTGroups - s.pre[i] : adj;
-      return r + adj;
-    };
-    // the step in sg, tested against the mc members of mt[mtb], into wl/wq[buf]; returns this wave's
-    // survivors
-    auto filter = [&](int buf, int mtb, int mc) -> int {
-      uint32_t qm[kTGroups];
-#pragma unroll
-      for (int gi = 0; gi < kTGroups; ++gi) qm[gi] = 0u;
-      for (int j = 0; j < mc; ++j) {
-        const uint64_t m0 = sm.mt[mtb][j].m0, m1 = sm.mt[mtb][j].m1;
-        int cnt = 0;
-#pragma unroll
-        for (int gi = 0; gi < kTGroups; ++gi) {
-          const int i = gi * kScanThreads + wv * 64 + l;
-          bool pass = i < sg_n && ((sg[gi][0] & m0) == m0);
-          if constexpr (W == 2) pass = pass && ((sg[gi][1] & m1) == m1);
-          qm[gi] |= pass ? 1u << j : 0u;
-          cnt += __popcll(__ballot(pass));
-        }
-        if (stats && l == 0 && cnt > 0) {
-          const int s = sm.mt[mtb][j].slot;
-          if (s >= 0)
-            atomicAdd(&sm.selig[s], (uint32_t)cnt);
-          else
-            atomicAdd((unsigned long long *)&stats[2 * (size_t)sm.mt[mtb][j].q + 1], (unsigned long long)cnt);
-        }
-      }
-      int nw = 0;
-#pragma unroll
-      for (int gi = 0; gi < kTGroups; ++gi) {
-        const int i = gi * kScanThreads + wv * 64 + l;
-        const uint64_t bal = __ballot(qm[gi] != 0u);
-        if (qm[gi] != 0u) {
-          const int o = wv * 64 * kTGroups + nw + mbcnt(bal);
-          sm.wl[buf][o] = (uint16_t)i;
-          sm.wq[buf][o] = (uint16_t)qm[gi];
-        }
-        nw += __popcll(bal);
-      }
-      return nw;
-    };
-    int4 x[R];
-    uint32_t qmv[R];
-    // rows of the batch at r0
-    auto load_rows = [&](int32_t p0, int buf, const Share &s, int r0) {
-#pragma unroll
-      for (int u = 0; u < R; ++u) {
-        const int r = r0 + u * RPI + l / LPR;
-        const bool valid = r < s.rend;
-        const int idx = valid ? surv_at(s, r) : 0;
-        const uint32_t qm = valid ? (uint32_t)sm.wq[buf][idx] : 0u;
-        const int32_t p = p0 + (valid ? (int)sm.wl[buf][idx] : 0);
-        qmv[u] = qm;
-        x[u] = reinterpret_cast<const int4 *>(a.ix.items + (size_t)p * D)[sub];
-      }
-    };
-    // a candidate of member j (lanes with ok): staged with its slot, or written to the pool directly.
-    // The row's position is read back from the survivor list only here (candidates are rare).
-    auto offer = [&](bool ok, int32_t score, int32_t p0, int buf, const Share &s, int r, const TMember &m) {
-      const uint64_t b = __ballot(ok);
-      if (b == 0ull) return;
-      const int32_t pos = p0 + (ok ? (int)sm.wl[buf][surv_at(s, r)] : 0);
-      int at = 0;
-      if (l == 0) at = atomicAdd(&sm.stage_n, __popcll(b));
-      at = __builtin_amdgcn_readfirstlane(at);
-      if (ok) {
-        const int e = at + mbcnt(b);
-        const uint64_t key = pos_key(score, pos);
-        bool direct = true;
-        if (e < kTStageWG) {
-          if (m.slot >= 0) {
-            sm.skey[e] = key;
-            sm.sslot[e] = (uint16_t)m.slot;
-            sm.srank[e] = (uint16_t)atomicAdd(&sm.scount[m.slot], 1u);
-            direct = false;
-          } else {
-            sm.sslot[e] = 0xFFFFu;
+      for (int g = 0; g < G; ++g) {
+        const int i = g * 64 + l;
+        uint32_t qm = 0u;
+        for (int j = 0; j < fs_mc; ++j) {
+          const uint64_t m0 = S.wm[fs_mb + j].m0;
+          bool pass = i < fs_n && ((sg[g][0] & m0) == m0);
+          if constexpr (W == 2) {
+            const uint64_t m1 = S.wm[fs_mb + j].m1;
+            pass = pass && ((sg[g][1] & m1) == m1);
+          }
+          qm |= pass ? 1u << j : 0u;
+          if (stats) {
+            const int cnt = __popcll(__ballot(pass));
+            if (l == 0 && cnt > 0) {
+              if (fs_slot != kNoSlot)
+                S.selig[fs_slot + j] += (uint32_t)cnt;
+              else
+                atomicAdd((unsigned long long *)&stats[2 * (size_t)S.wm[fs_mb + j].q + 1], (unsigned long long)cnt);
+            }
           }
         }
-        if (direct) {
-          const uint32_t o = atomicAdd(&a.w.pool_cnt[m.q], 1u);
-          if (o < cap) a.w.pool[(size_t)m.q * cap + o] = key;
+        const uint64_t bal = __ballot(qm != 0u);
+        if (qm != 0u) {
+          const uint32_t o = (tail + (uint32_t)mbcnt(bal)) & (kTF - 1);
+          S.fpos[o] = fs_p0 + i;
+          S.fmeta[o] = qm | ((uint32_t)fs_mb << 16) | (fs_slot << 24);
+        }
+        tail += (uint32_t)__popcll(bal);
+      }
+      sg_live = false;
+    };
+    int4 xa[R], xb[R];
+    uint32_t ma[R], mb[R];
+    // request the rows of the next batch (n of them) into x / mt
+    auto request_rows = [&](int4 (&x)[R], uint32_t (&mt)[R]) -> int {
+      const int n = (int)(tail - head) < RB ? (int)(tail - head) : RB;
+      wave_lds_sync();
+      const int32_t first = n > 0 ? S.fpos[head & (kTF - 1)] : 0;
+#pragma unroll
+      for (int u = 0; u < R; ++u) {
+        const int ri = u * RPI + l / LPR;
+        const bool valid = ri < n;
+        const uint32_t o = (head + (uint32_t)ri) & (kTF - 1);
+        const int32_t pos = valid ? S.fpos[o] : first;
+        mt[u] = valid ? S.fmeta[o] : 0u;
+        x[u] = reinterpret_cast<const int4 *>(a.ix.items + (size_t)pos * D)[sub];
+      }
+      bhead = head;
+      head += (uint32_t)n;
+      return n;
+    };
+    // a candidate of a member (lanes with ok): staged with its slot; a member without a slot goes to its
+    // pool directly
+    auto offer = [&](bool ok, int32_t score, uint32_t bpos, uint32_t slot0, int j, int q) {
+      if (__ballot(ok) == 0ull) return;
+      if (stage_n + 64 > kTStageW) flush();
+      const uint64_t b = __ballot(ok);
+      if (ok) {
+        const int32_t pos = S.fpos[bpos & (kTF - 1)];
+        const uint64_t key = pos_key(score, pos);
+        if (slot0 != kNoSlot) {
+          const int e = stage_n + mbcnt(b);
+          const uint32_t s = slot0 + (uint32_t)j;
+          S.skey[e] = key;
+          S.sslot[e] = (uint8_t)s;
+          S.srank[e] = (uint16_t)atomicAdd(&S.scount[s], 1u);
+        } else {
+          const uint32_t o = atomicAdd(&a.w.pool_cnt[q], 1u);
+          if (o < cap) a.w.pool[(size_t)q * cap + o] = key;
         }
       }
+      stage_n += __popcll(b);   // a lane without a slot leaves an unused stage entry (no harm)
+      wave_lds_sync();
     };
-    auto score_rows = [&](int32_t p0, int buf, int mtb, const Share &s, int r0) {
-      int32_t acc0[R];
+    // score the batch in x / mt (rows of FIFO positions bh ..)
+    auto score_rows = [&](const int4 (&x)[R], const uint32_t (&mt)[R], uint32_t bh) {
 #pragma unroll
       for (int u = 0; u < R; ++u) {
-        const int j = qmv[u] ? __builtin_ctz(qmv[u]) : 0;
-        acc0[u] = group_sum<LPR>(dot16(x[u], sm.mqv[mtb][j][sub], 0));
-      }
-#pragma unroll
-      for (int u = 0; u < R; ++u) {
-        uint32_t qm = qmv[u];
-        int32_t acc = acc0[u];
+        const uint32_t meta = mt[u];
+        uint32_t qm = meta & 0xFFFFu;
+        const int mb0 = (int)((meta >> 16) & 0xFFu);
+        const uint32_t slot0 = meta >> 24;
+        const uint32_t bpos = bh + (uint32_t)(u * RPI + l / LPR);
+        int j = qm ? __builtin_ctz(qm) : 0;
+        int32_t acc = group_sum<LPR>(dot16(x[u], S.wqv[mb0 + j][sub], 0));
         for (;;) {
-          const int j = qm ? __builtin_ctz(qm) : 0;
-          const TMember m = sm.mt[mtb][j];
-          offer(qm != 0u && sub == 0 && acc >= m.thr, acc, p0, buf, s, r0 + u * RPI + l / LPR, m);
+          const MRec &m = S.wm[mb0 + j];
+          offer(qm != 0u && sub == 0 && acc >= m.thr, acc, bpos, slot0, j, m.q);
           qm &= qm - 1u;
           if (__ballot(qm != 0u) == 0ull) break;
           // a further member accepts this row: the same row against its query vector
-          const int j2 = qm ? __builtin_ctz(qm) : 0;
-          acc = group_sum<LPR>(dot16(x[u], sm.mqv[mtb][j2][sub], 0));
+          j = qm ? __builtin_ctz(qm) : 0;
+          acc = group_sum<LPR>(dot16(x[u], S.wqv[mb0 + j][sub], 0));
         }
       }
     };
-
-    load_window();
-    Cursor cur{0, 0, 0, 0};
-    seek(cur);
-    // prologue: step 0's member table and signatures, filter; step 1's; step 0's first rows
-    int mc_sg = build_mt(cur, 0);
-    load_sigs(cur);
-    if (cur.w >= 0) advance(cur);
-    __syncthreads();   // mt[0]
-    int32_t p0_i = sg_p0;
-    {
-      const int nw = filter(0, 0, mc_sg);
-      if (l == 0) sm.wcnt[0][wv] = nw;
-    }
-    mc_sg = build_mt(cur, 1);
-    load_sigs(cur);
-    if (cur.w >= 0) advance(cur);
-    __syncthreads();
-    Share sh_i = share(0);
-    if (sh_i.rbeg < sh_i.rend) load_rows(p0_i, 0, sh_i, sh_i.rbeg);
-    for (int i = 0;; ++i) {
-      const bool more = sg_n > 0;   // step i + 1 exists (the same for every thread)
-      const int32_t p0_n = sg_p0;
-      const int bi = i % 3, bn = (i + 1) % 3;
-      if (more) {
-        const int nw = filter(bn, (i + 1) & 3, mc_sg);   // waits for step i + 1's signatures only
-        if (l == 0) sm.wcnt[(i + 1) & 1][wv] = nw;
-        mc_sg = build_mt(cur, (i + 2) & 3);
-        load_sigs(cur);
-        if (cur.w >= 0) advance(cur);
+    // room for a new step: its items at most, besides the survivors not yet scored
+    auto room = [&]() { return (int)(tail - bhead) <= kTF - GS; };
+    auto more_steps = [&]() { return cw < e_n; };
+    // the walk; each iteration: filter the step in flight, request the next step's signatures and the next
+    // batch's rows, score the batch requested one iteration earlier
+    int nb = 0;           // rows of the batch in flight
+    for (int u = 0; u < R; ++u) mb[u] = 0u;   // the first iteration scores an empty batch
+    uint32_t bh_prev = 0;
+    auto iteration = [&](int4 (&xr)[R], uint32_t (&mr)[R], const int4 (&xs)[R], const uint32_t (&ms)[R]) -> bool {
+      if (sg_live) filter();
+      request_sigs(more_steps() && room());
+      const uint32_t bh_s = bh_prev;
+      const int nr = request_rows(xr, mr);
+      bh_prev = bhead;
+      nb = nr;
+      score_rows(xs, ms, bh_s);   // also an empty batch: every path reads the rows it requested
+      return !sg_live && nr == 0 && head == tail && !more_steps();
+    };
+    for (;;) {
+      for (;;) {
+        // iterations in pairs, so that the rows requested into xa are always read before the loop ends
+        // (an iteration after the one that found nothing left does nothing)
+        (void)iteration(xa, ma, xb, mb);
+        if (iteration(xb, mb, xa, ma)) break;
       }
-      __syncthreads();
-      Share sh_n;
-      if (more) sh_n = share((i + 1) & 1);
-      // --- score step i
-      if (sh_i.rbeg < sh_i.rend) score_rows(p0_i, bi, i & 3, sh_i, sh_i.rbeg);
-      for (int r0 = sh_i.rbeg + RB; r0 < sh_i.rend; r0 += RB) {   // dense filters: further batches
-        load_rows(p0_i, bi, sh_i, r0);
-        score_rows(p0_i, bi, i & 3, sh_i, r0);
-      }
-      if (!more) break;
-      if (sh_n.rbeg < sh_n.rend) load_rows(p0_n, bn, sh_n, sh_n.rbeg);   // step i + 1's first rows
-      sh_i = sh_n;
-      p0_i = p0_n;
+      // the window is done (every survivor scored: the FIFO is empty and no batch is in flight); the chunk
+      // may continue in the next one
+      if (!(e_n > 0 && jwin + e_n < n_ent && a.w.entries[jwin + e_n].useg < rb)) break;
+      jwin += e_n;
+      load_window();
+      cw = 0;
+      seek();
     }
-    __syncthreads();
-    // --- end of the chunk: one pool reservation per slot, then the staged keys; the slots' counts
-    const int ns = nsl < kTSlots ? nsl : kTSlots;
-    const int n_st = sm.stage_n < kTStageWG ? sm.stage_n : kTStageWG;
-    for (int s = tid; s < ns; s += kScanThreads) {
-      const uint32_t c = sm.scount[s];
-      const int q = sm.sq[s];
-      if (c) sm.sbase[s] = atomicAdd(&a.w.pool_cnt[q], c);
-      if (stats) {
-        if (sm.selig[s]) atomicAdd((unsigned long long *)&stats[2 * (size_t)q + 1], (unsigned long long)sm.selig[s]);
-        if (sm.sscan[s]) atomicAdd((unsigned long long *)&stats[2 * (size_t)q], (unsigned long long)sm.sscan[s]);
+    // end of the chunk: staged candidates to the pools, the slots' counts to the statistics
+    if (stage_n > 0) flush();
+    const int ns = nsl < kTSlotsW ? nsl : kTSlotsW;
+    if (stats) {
+      for (int s = l; s < ns; s += 64) {
+        const int q = S.sq[s];
+        if (S.selig[s]) atomicAdd((unsigned long long *)&stats[2 * (size_t)q + 1], (unsigned long long)S.selig[s]);
+        if (S.sscan[s]) atomicAdd((unsigned long long *)&stats[2 * (size_t)q], (unsigned long long)S.sscan[s]);
       }
     }
-    __syncthreads();
-    for (int e = tid; e < n_st; e += kScanThreads) {
-      const int s = sm.sslot[e];
-      if (s != 0xFFFF) {
-        const uint32_t o = sm.sbase[s] + sm.srank[e];
-        if (o < cap) a.w.pool[(size_t)sm.sq[s] * cap + o] = sm.skey[e];
-      }
+    wave_lds_sync();
+    for (int s = l; s < ns; s += 64) {
+      S.scount[s] = 0u;
+      S.selig[s] = 0u;
     }
-    __syncthreads();
-    for (int s = tid; s < ns; s += kScanThreads) {
-      sm.scount[s] = 0u;
-      sm.selig[s] = 0u;
-    }
-    if (tid == 0) {
-      sm.stage_n = 0;
-      sm.next = next_c;
-    }
-    __syncthreads();
+    nsl = 0;
+    wave_lds_sync();
   }
 }
 
@@ -668,20 +625,6 @@ struct XWave {
   uint32_t cnt[kXQ];         // staged candidates per query of the block
   uint32_t base[kXQ];        // pool positions reserved at a flush
 };
-
-// Order of LDS accesses between the lanes of one wave (its LDS operations complete in order; this keeps
-// the compiler from moving them across each other).
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-// raw buffer resource over [base, base + bytes) (gfx9 word 3: 32-bit data format, no swizzle)
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void *base, int64_t bytes) {
-  const int n = bytes <= 0 ? 0 : (bytes < 0x7FFFFFFF ? (int)bytes : 0x7FFFFFFF);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n, 0x00020000);
-}
 
 template <int KS, int W, bool SAMPLE>
 __global__ __launch_bounds__(64 * kXWaves, kXOcc) void k_xscan(XScanArgs a) {

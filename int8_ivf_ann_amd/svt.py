@@ -18,14 +18,14 @@ LIB_PATH = os.path.join(_HERE, "libsvt.so")
 SVT_OK, SVT_EINVAL, SVT_ENOMEM, SVT_EDEVICE, SVT_EUNSUPPORTED, SVT_ESTATE = 0, -1, -2, -3, -4, -5
 SVT_MAX_K = 2048
 SVT_MAX_SIG_WORDS = 2
-SVT_PATH_AUTO, SVT_PATH_QUERY, SVT_PATH_TILE = 0, 1, 2
+SVT_PATH_AUTO, SVT_PATH_QUERY, SVT_PATH_TILE, SVT_PATH_EXHAUSTIVE = 0, 1, 2, 3
 SVT_OPT_MERGE_FROM_SLOTS, SVT_OPT_FORCE_REDO = 1, 2
 SVT_NOALLOC_SCRATCH_BYTES = 256 << 20
 _PATHS = {"auto": SVT_PATH_AUTO, "query": SVT_PATH_QUERY, "tile": SVT_PATH_TILE}
 
 #: every symbol include/svt.h declares
-EXPORTED = ("svt_index_upload", "svt_index_free", "svt_index_info", "svt_search_workspace_size", "svt_search",
-            "svt_search_noalloc", "svt_last_error", "svt_bloom_mask", "svt_bloom_sign", "svt_profile_enable", "svt_profile_read")
+EXPORTED = ("svt_index_upload", "svt_index_free", "svt_index_info", "svt_search_workspace_size", "svt_search_path",
+            "svt_search", "svt_search_noalloc", "svt_last_error", "svt_bloom_mask", "svt_bloom_sign", "svt_profile_enable", "svt_profile_read")
 
 
 class SvtError(RuntimeError):
@@ -84,6 +84,7 @@ def lib():
     L.svt_index_info.argtypes = [vp, vp, vp, vp, vp]
     L.svt_search_workspace_size.argtypes = [vp, i32, i32, i32, vp]
     L.svt_search_workspace_size.restype = sz
+    L.svt_search_path.argtypes = [vp, i32, i32, i32, vp]
     L.svt_search.argtypes = [vp, i32, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.svt_search_noalloc.argtypes = [vp, i32, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp]
     L.svt_last_error.restype = ctypes.c_char_p
@@ -202,6 +203,14 @@ def svt_search_workspace_size(handle, n_queries: int, nprobe: int, k: int, opts=
         if err:
             raise SvtError(SVT_EINVAL, err)
     return int(sz)
+
+
+def svt_search_path(handle, n_queries: int, nprobe: int, k: int, opts=None) -> str:
+    """The path a search of these sizes takes: "query", "tile" or "exhaustive"."""
+    rc = lib().svt_search_path(handle, n_queries, nprobe, k, _opt_ptr(opts))
+    if rc < 0:
+        raise SvtError(rc, svt_last_error())
+    return {SVT_PATH_QUERY: "query", SVT_PATH_TILE: "tile", SVT_PATH_EXHAUSTIVE: "exhaustive"}[rc]
 
 
 def _search_tensors(handle, queries, masks, k, query_scales, out_ids, out_scores, out_fscores, out_counts,

@@ -84,6 +84,7 @@ def test_search_rejects_dead_index(L):
     assert "not a live index" in svt.svt_last_error()
     assert L.svt_search_noalloc(bogus, 1, None, None, None, 1, 1, None, None, None, None, None, None,
                                 None) == svt.SVT_ESTATE
+    assert L.svt_search_path(bogus, 1, 1, 1, None) == svt.SVT_ESTATE
     assert "not a live index" in svt.svt_last_error()
     assert L.svt_index_free(bogus, None) == svt.SVT_ESTATE
     assert L.svt_index_free(None, None) == svt.SVT_OK
@@ -96,7 +97,7 @@ def test_options_struct_layout():
     assert (o.path, o.pool_keys, o.flags) == (svt.SVT_PATH_TILE, 64, 2)
     assert list(o.reserved) == [0] * 5
     hdr = open(os.path.join(ROOT, "include", "svt.h")).read()
-    for name, v in (("SVT_PATH_AUTO", 0), ("SVT_PATH_QUERY", 1), ("SVT_PATH_TILE", 2)):
+    for name, v in (("SVT_PATH_AUTO", 0), ("SVT_PATH_QUERY", 1), ("SVT_PATH_TILE", 2), ("SVT_PATH_EXHAUSTIVE", 3)):
         assert re.search(rf"{name} = {v}\b", hdr), name
     assert re.search(r"#define SVT_OPT_MERGE_FROM_SLOTS 1u", hdr)
     assert re.search(r"#define SVT_OPT_FORCE_REDO 2u", hdr)

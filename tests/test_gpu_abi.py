@@ -116,3 +116,18 @@ def test_free_twice_is_rejected(env):
     svt.svt_index_free(h)
     with pytest.raises(svt.SvtError):
         svt.svt_index_free(h)
+
+
+def test_search_path(env):
+    svt, ix, q, m, outs, ws, B, k = env
+    nlist = ix.nlist
+    assert svt.svt_search_path(ix.handle, 1, 4, k) == "query"
+    assert svt.svt_search_path(ix.handle, 32, 4, k) == "query"
+    assert svt.svt_search_path(ix.handle, 128, 4, k) == "tile"
+    assert svt.svt_search_path(ix.handle, 32, 4, k, svt.make_options("query")) == "query"
+    assert svt.svt_search_path(ix.handle, 3, 4, k, svt.make_options("tile")) == "tile"
+    assert svt.svt_search_path(ix.handle, 2, nlist, k) == "exhaustive"
+    assert svt.svt_search_path(ix.handle, 1, nlist, k, svt.make_options("tile")) == "exhaustive"
+    assert svt.svt_search_path(ix.handle, 1, nlist, k) == "query"
+    with pytest.raises(svt.SvtError):
+        svt.svt_search_path(ix.handle, 1, nlist + 1, k)
