@@ -115,11 +115,11 @@ constexpr int kTChunksPerWave = SVT_T_CHUNKS;   // chunks of the union stream pe
 #endif
 constexpr int kTGroups = SVT_T_GROUPS;   // 64-item signature groups of one filter step
 #ifndef SVT_T_ROWLOADS
-#define SVT_T_ROWLOADS 6
+#define SVT_T_ROWLOADS 4
 #endif
 constexpr int kTRowLoads = SVT_T_ROWLOADS;   // 16-byte row loads per lane of one scored batch
 #ifndef SVT_T_OCC
-#define SVT_T_OCC 3
+#define SVT_T_OCC 4
 #endif
 constexpr int kTOcc = SVT_T_OCC;             // tile-scan waves per SIMD the compiler is asked to fit
 // Chunks of the union stream are cut at equal estimated cost: per item of an entry, its signature bytes and
@@ -131,7 +131,10 @@ constexpr int kTMemberCost = 2;
 // items reach, read off a sample of its items at rank at least kRMin; the pool keeps every candidate at
 // or above it.  A pool with fewer than k keys (threshold above the minimum) or more than it holds sends
 // its query to the query path.
-constexpr int kAlpha = 4;
+#ifndef SVT_ALPHA
+#define SVT_ALPHA 4
+#endif
+constexpr int kAlpha = SVT_ALPHA;
 constexpr int kRMin = 16;
 // Exhaustive batches (nprobe == nlist): the catalogue is streamed once per block of kXQ queries and
 // scored with int8 MFMA (16x16x64).  The sample pass scores every kXStride-th item.

@@ -244,11 +244,17 @@ struct TScanArgs {
   uint32_t pool_cap;
 };
 
+#ifndef SVT_T_WIN_MEMBERS
+#define SVT_T_WIN_MEMBERS 16
+#endif
+#ifndef SVT_T_STAGE
+#define SVT_T_STAGE 160
+#endif
 constexpr int kTF = 512;             // survivors a wave's FIFO holds (a ring)
 constexpr int kTWinW = 16;           // entries of a wave's window
-constexpr int kTWinMW = 32;          // members of those entries
+constexpr int kTWinMW = SVT_T_WIN_MEMBERS;   // members of those entries
 constexpr int kTSlotsW = 64;         // (entry visit, member) slots of a wave's chunk
-constexpr int kTStageW = 192;        // candidates a wave stages before it writes them to the pools
+constexpr int kTStageW = SVT_T_STAGE;        // candidates a wave stages before it writes them to the pools
 constexpr uint32_t kNoSlot = 0xFFu;
 static_assert(kTWinMW >= kTMembers && kTWinMW <= 256 && kTSlotsW < 255, "survivor metadata fields");
 
@@ -494,7 +500,7 @@ __global__ __launch_bounds__(kScanThreads, kTOcc) void k_tscan(TScanArgs a) {
     // pool directly
     auto offer = [&](bool ok, int32_t score, uint32_t bpos, uint32_t slot0, int j, int q) {
       if (__ballot(ok) == 0ull) return;
-      if (stage_n + 64 > kTStageW) flush();
+      if (stage_n + 64 > kTStageW) flush();   // rare: an iteration with more candidates than the stage holds
       const uint64_t b = __ballot(ok);
       if (ok) {
         const int32_t pos = S.fpos[bpos & (kTF - 1)];
@@ -544,6 +550,9 @@ __global__ __launch_bounds__(kScanThreads, kTOcc) void k_tscan(TScanArgs a) {
     for (int u = 0; u < R; ++u) mb[u] = 0u;   // the first iteration scores an empty batch
     uint32_t bh_prev = 0;
     auto iteration = [&](int4 (&xr)[R], uint32_t (&mr)[R], const int4 (&xs)[R], const uint32_t (&ms)[R]) -> bool {
+      // a stage past half full is written out here, where the loads in flight are the ones this iteration
+      // consumes next anyway (the flush waits for every load of the wave)
+      if (stage_n > kTStageW / 2) flush();
       if (sg_live) filter();
       request_sigs(more_steps() && room());
       const uint32_t bh_s = bh_prev;
