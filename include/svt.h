@@ -45,7 +45,8 @@ enum {
   SVT_ENOMEM = -2,       /* device or host allocation failed                                        */
   SVT_EDEVICE = -3,      /* a HIP runtime call or kernel launch failed                              */
   SVT_EUNSUPPORTED = -4, /* valid but unsupported shape (dimension, signature width)                 */
-  SVT_ESTATE = -5        /* object in the wrong state (freed or foreign index)                       */
+  SVT_ESTATE = -5,       /* object in the wrong state (freed or foreign index, not updatable)        */
+  SVT_ENOSPACE = -6      /* an insert finds no free slot in its cluster                              */
 };
 
 #define SVT_MAX_K 2048        /* largest top-k per query                                            */
@@ -81,6 +82,47 @@ typedef struct {
  */
 int svt_index_upload(const svt_index_desc *desc, void *hip_stream, svt_index **out);
 
+/*
+ * svt_index_upload_updatable - svt_index_upload for an index that takes in-place updates afterwards
+ * (svt_index_insert, svt_index_delete, svt_index_resign): the freshness of "SilverTorch - Index as
+ * Model" (index freshness section), where the index tensors receive a continuous stream of small,
+ * targeted in-place updates between full snapshots.
+ * Each cluster gets max(slack_min, ceil(slack_frac * its item count)) free slots after its items; a free
+ * slot holds the reserved signature with every bit set (which no filter passes, whatever the mask) and
+ * the id -1, so searches scan it at the cost of its signature and never return it.  Ids of later
+ * inserts are any unused ids in [0, id_capacity).  The host keeps a record of the layout (an int32 per
+ * id and per free slot) that places each update.
+ *   id_capacity  n_items <= id_capacity < 2^31
+ *   slack_min    >= 0;  slack_frac  in [0, 64]
+ * Other arguments, errors and ownership as svt_index_upload; also SVT_EINVAL for a bad id_capacity or
+ * slack, or more than 2^31 slots.  Items whose signature has every bit set are rejected (SVT_EINVAL) by
+ * both uploads: that signature marks free slots.
+ */
+int svt_index_upload_updatable(const svt_index_desc *d, int64_t id_capacity, int32_t slack_min, float slack_frac,
+                               void *hip_stream, svt_index **out);
+
+/*
+ * In-place updates of an updatable index (same section of the same page).  Each call takes a batch from
+ * host memory, checks all of it (on any error nothing changes), chooses the slots on the host, copies
+ * the batch to the device, applies it with one kernel on hip_stream and synchronises that stream before
+ * returning.  Searches see the index as of the updates enqueued before them on their stream: searches
+ * in flight on other streams must not overlap an update.  A search after the updates returns exactly
+ * what a search of the updated catalogue (the items present, with their current signatures) returns.
+ *   svt_index_insert  n items: ids (unused, distinct), rows [n][dim] int8, sigs [n][sig_words], list_of
+ *                     [n] cluster of each; each goes to a free slot of its cluster (lowest slot first)
+ *   svt_index_delete  n present, distinct ids: their slots become free
+ *   svt_index_resign  n present, distinct ids: their signatures become sigs [n][sig_words]
+ * All pointers are host pointers.  Errors: SVT_ESTATE (freed index, or one not uploaded as updatable),
+ * SVT_EINVAL (n < 0, NULL pointer with n > 0, an id out of range, repeated, already present (insert) or
+ * absent (delete, resign), a cluster out of range, a reserved signature), SVT_ENOSPACE (a cluster without
+ * enough free slots for the batch), SVT_ENOMEM / SVT_EDEVICE (device staging or kernel; the index is then
+ * undefined).  n == 0 is a no-op.
+ */
+int svt_index_insert(svt_index *ix, int32_t n, const int64_t *ids, const int8_t *rows, const uint64_t *sigs,
+                     const int32_t *list_of, void *hip_stream);
+int svt_index_delete(svt_index *ix, int32_t n, const int64_t *ids, void *hip_stream);
+int svt_index_resign(svt_index *ix, int32_t n, const int64_t *ids, const uint64_t *sigs, void *hip_stream);
+
 /* svt_index_free - release an index and its device memory.
  * hip_stream: the stream the caller's searches on this index ran on (NULL = the default stream); the
  * call synchronises that stream before freeing.  Searches enqueued on other streams must have
@@ -89,7 +131,8 @@ int svt_index_upload(const svt_index_desc *desc, void *hip_stream, svt_index **o
  * SVT_EDEVICE if the stream synchronisation fails (the index is then still freed). */
 int svt_index_free(svt_index *ix, void *hip_stream);
 
-/* svt_index_info - shape of an uploaded index; any output pointer may be NULL. */
+/* svt_index_info - shape of an uploaded index (n_items: the items present, not free slots); any output
+ * pointer may be NULL. */
 int svt_index_info(const svt_index *ix, int64_t *n_items, int32_t *dim, int32_t *sig_words, int32_t *nlist);
 
 /*

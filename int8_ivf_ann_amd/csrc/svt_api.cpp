@@ -6,6 +6,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -86,7 +87,17 @@ struct svt_index {
   uint64_t *d_sigs = nullptr;
   int32_t *d_perm = nullptr;
   int32_t *d_offsets = nullptr;
+  int32_t *d_live = nullptr;
   int8_t *d_centroids = nullptr;
+  int64_t n_live = 0;                          // items (not free slots)
+  // updatable index: the host's record of the layout, which chooses every update's slot
+  bool updatable = false;
+  int64_t id_capacity = 0;
+  std::vector<int32_t> slot_of;                // [id_capacity] slot of each id (-1: not in the index)
+  std::vector<int32_t> offsets_h;              // [nlist + 1] cluster slot ranges
+  std::vector<std::vector<int32_t>> free_h;    // free slots of each cluster (a stack, lowest slot on top)
+  void *d_stage = nullptr;                     // device staging of an update batch
+  size_t stage_bytes = 0;
   int32_t scan_wgs;                 // persistent workgroups of the query-by-query scan
   int32_t tscan_wgs;                // persistent workgroups of the tile scan
   int32_t xscan_wgs;                // workgroups of the exhaustive MFMA scan
@@ -100,36 +111,68 @@ static void free_index_memory(svt_index *ix) {
   if (ix->d_sigs) (void)hipFree(ix->d_sigs);
   if (ix->d_perm) (void)hipFree(ix->d_perm);
   if (ix->d_offsets) (void)hipFree(ix->d_offsets);
+  if (ix->d_live) (void)hipFree(ix->d_live);
   if (ix->d_centroids) (void)hipFree(ix->d_centroids);
+  if (ix->d_stage) (void)hipFree(ix->d_stage);
 }
 
-extern "C" int svt_index_upload(const svt_index_desc *d, void *hip_stream, svt_index **out) {
-  g_err.clear();
-  if (!d || !out) return fail(SVT_EINVAL, "svt_index_upload: NULL desc or out");
+namespace {
+
+bool sig_reserved(const uint64_t *sig, int32_t W) {
+  uint64_t a = ~0ull;
+  for (int32_t u = 0; u < W; ++u) a &= sig[u];
+  return a == ~0ull;
+}
+
+// Upload; with updatable, each cluster gets max(slack_min, ceil(slack_frac * size)) free slots after its
+// items and the host keeps the layout record that places later updates.
+int upload(const svt_index_desc *d, bool updatable, int64_t id_capacity, int32_t slack_min, float slack_frac,
+           void *hip_stream, svt_index **out, const char *who) {
+  if (!d || !out) return fail(SVT_EINVAL, "%s: NULL desc or out", who);
   *out = nullptr;
   if (d->n_items < 0 || d->n_items >= (int64_t(1) << 31))
-    return fail(SVT_EINVAL, "svt_index_upload: n_items %lld out of [0, 2^31)", (long long)d->n_items);
-  if (!supported_dim(d->dim)) return fail(SVT_EUNSUPPORTED, "svt_index_upload: dim %d not in {16,32,64,128,256}", d->dim);
+    return fail(SVT_EINVAL, "%s: n_items %lld out of [0, 2^31)", who, (long long)d->n_items);
+  if (!supported_dim(d->dim)) return fail(SVT_EUNSUPPORTED, "%s: dim %d not in {16,32,64,128,256}", who, d->dim);
   if (d->sig_words != 1 && d->sig_words != 2)
-    return fail(SVT_EUNSUPPORTED, "svt_index_upload: sig_words %d not in {1,2}", d->sig_words);
-  if (d->nlist < 1 || d->nlist > 65536) return fail(SVT_EINVAL, "svt_index_upload: nlist %d out of [1, 65536]", d->nlist);
-  if (!(d->item_scale > 0.f)) return fail(SVT_EINVAL, "svt_index_upload: item_scale must be > 0");
-  if (!d->centroids) return fail(SVT_EINVAL, "svt_index_upload: NULL centroids");
+    return fail(SVT_EUNSUPPORTED, "%s: sig_words %d not in {1,2}", who, d->sig_words);
+  if (d->nlist < 1 || d->nlist > 65536) return fail(SVT_EINVAL, "%s: nlist %d out of [1, 65536]", who, d->nlist);
+  if (!(d->item_scale > 0.f)) return fail(SVT_EINVAL, "%s: item_scale must be > 0", who);
+  if (!d->centroids) return fail(SVT_EINVAL, "%s: NULL centroids", who);
   if (d->n_items > 0 && (!d->items || !d->sigs || !d->list_of))
-    return fail(SVT_EINVAL, "svt_index_upload: NULL items, sigs or list_of");
+    return fail(SVT_EINVAL, "%s: NULL items, sigs or list_of", who);
   const int64_t n = d->n_items;
   const int32_t dim = d->dim, W = d->sig_words, nlist = d->nlist;
   hipStream_t s = (hipStream_t)hip_stream;
 
-  // host: cluster sizes, offsets, stable cluster-contiguous order
-  std::vector<int32_t> offsets(nlist + 1, 0);
+  if (updatable) {
+    if (id_capacity < n || id_capacity > INT32_MAX)
+      return fail(SVT_EINVAL, "%s: id_capacity %lld out of [n_items, 2^31)", who, (long long)id_capacity);
+    if (slack_min < 0 || !(slack_frac >= 0.f) || slack_frac > 64.f)
+      return fail(SVT_EINVAL, "%s: slack_min %d < 0 or slack_frac %g out of [0, 64]", who, slack_min, (double)slack_frac);
+  }
+
+  // host: cluster sizes, slot ranges (items, then free slots), stable cluster-contiguous order
+  std::vector<int64_t> size(nlist, 0);
   for (int64_t i = 0; i < n; ++i) {
     const int32_t c = d->list_of[i];
-    if (c < 0 || c >= nlist) return fail(SVT_EINVAL, "svt_index_upload: list_of[%lld] = %d out of range", (long long)i, c);
-    ++offsets[c + 1];
+    if (c < 0 || c >= nlist) return fail(SVT_EINVAL, "%s: list_of[%lld] = %d out of range", who, (long long)i, c);
+    ++size[c];
+    if (sig_reserved(d->sigs + (size_t)i * W, W))
+      return fail(SVT_EINVAL, "%s: item %lld has every signature bit set (reserved for free slots)", who, (long long)i);
   }
-  for (int32_t c = 0; c < nlist; ++c) offsets[c + 1] += offsets[c];
-  std::vector<int32_t> perm((size_t)n), pos_of((size_t)n);
+  std::vector<int32_t> offsets(nlist + 1, 0);
+  {
+    int64_t at = 0;
+    for (int32_t c = 0; c < nlist; ++c) {
+      offsets[c] = (int32_t)at;
+      const int64_t slack = updatable ? std::max<int64_t>(slack_min, (int64_t)std::ceil((double)slack_frac * size[c])) : 0;
+      at += size[c] + slack;
+      if (at >= (int64_t(1) << 31)) return fail(SVT_EINVAL, "%s: more than 2^31 slots", who);
+    }
+    offsets[nlist] = (int32_t)at;
+  }
+  const int64_t n_slots = offsets[nlist];
+  std::vector<int32_t> perm((size_t)n_slots, -1), pos_of((size_t)n), live((size_t)nlist);
   {
     std::vector<int32_t> cur(offsets.begin(), offsets.end() - 1);
     for (int64_t i = 0; i < n; ++i) {
@@ -137,10 +180,11 @@ extern "C" int svt_index_upload(const svt_index_desc *d, void *hip_stream, svt_i
       perm[(size_t)p] = (int32_t)i;
       pos_of[(size_t)i] = p;
     }
+    for (int32_t c = 0; c < nlist; ++c) live[(size_t)c] = (int32_t)size[c];
   }
 
   svt_index *ix = new (std::nothrow) svt_index();
-  if (!ix) return fail(SVT_ENOMEM, "svt_index_upload: host allocation");
+  if (!ix) return fail(SVT_ENOMEM, "%s: host allocation", who);
   ix->magic = kMagic;
   hipError_t e = hipGetDevice(&ix->device);
   if (e != hipSuccess) { delete ix; return fail_hip(e, "hipGetDevice"); }
@@ -168,19 +212,29 @@ extern "C" int svt_index_upload(const svt_index_desc *d, void *hip_stream, svt_i
     delete ix;
     return fail_hip(err, what);
   };
-  const size_t nb = (size_t)std::max<int64_t>(n, 1);
+  const size_t nb = (size_t)std::max<int64_t>(n_slots, 1);
   if ((e = hipMalloc(&ix->d_items, nb * dim)) != hipSuccess) return cleanup_fail(e, "hipMalloc(items)");
   if ((e = hipMalloc(&ix->d_sigs, nb * W * sizeof(uint64_t))) != hipSuccess) return cleanup_fail(e, "hipMalloc(sigs)");
   if ((e = hipMalloc(&ix->d_perm, nb * sizeof(int32_t))) != hipSuccess) return cleanup_fail(e, "hipMalloc(perm)");
   if ((e = hipMalloc(&ix->d_offsets, (nlist + 1) * sizeof(int32_t))) != hipSuccess) return cleanup_fail(e, "hipMalloc(offsets)");
+  if ((e = hipMalloc(&ix->d_live, (size_t)nlist * sizeof(int32_t))) != hipSuccess) return cleanup_fail(e, "hipMalloc(live)");
   if ((e = hipMalloc(&ix->d_centroids, (size_t)nlist * dim)) != hipSuccess) return cleanup_fail(e, "hipMalloc(centroids)");
   if ((e = hipMemcpyAsync(ix->d_offsets, offsets.data(), (nlist + 1) * sizeof(int32_t), hipMemcpyHostToDevice, s)) != hipSuccess)
     return cleanup_fail(e, "copy offsets");
+  if ((e = hipMemcpyAsync(ix->d_live, live.data(), (size_t)nlist * sizeof(int32_t), hipMemcpyHostToDevice, s)) != hipSuccess)
+    return cleanup_fail(e, "copy live counts");
   if ((e = hipMemcpyAsync(ix->d_centroids, d->centroids, (size_t)nlist * dim, hipMemcpyHostToDevice, s)) != hipSuccess)
     return cleanup_fail(e, "copy centroids");
+  if (n_slots > n) {
+    // free slots: the reserved signature, zero rows (the items' slots are overwritten below)
+    if ((e = hipMemsetAsync(ix->d_sigs, 0xFF, (size_t)n_slots * W * sizeof(uint64_t), s)) != hipSuccess)
+      return cleanup_fail(e, "fill free slots");
+    if ((e = hipMemsetAsync(ix->d_items, 0, (size_t)n_slots * dim, s)) != hipSuccess) return cleanup_fail(e, "fill free slots");
+  }
+  if (n_slots > 0 &&
+      (e = hipMemcpyAsync(ix->d_perm, perm.data(), (size_t)n_slots * sizeof(int32_t), hipMemcpyHostToDevice, s)) != hipSuccess)
+    return cleanup_fail(e, "copy perm");
   if (n > 0) {
-    if ((e = hipMemcpyAsync(ix->d_perm, perm.data(), (size_t)n * sizeof(int32_t), hipMemcpyHostToDevice, s)) != hipSuccess)
-      return cleanup_fail(e, "copy perm");
     // rows and signatures: staged in bounded chunks, scattered on the device to their positions
     if ((e = hipMalloc(&d_pos_of, (size_t)n * sizeof(int32_t))) != hipSuccess) return cleanup_fail(e, "hipMalloc(pos_of)");
     if ((e = hipMemcpyAsync(d_pos_of, pos_of.data(), (size_t)n * sizeof(int32_t), hipMemcpyHostToDevice, s)) != hipSuccess)
@@ -209,18 +263,43 @@ extern "C" int svt_index_upload(const svt_index_desc *d, void *hip_stream, svt_i
   ix->dev.sigs = ix->d_sigs;
   ix->dev.perm = ix->d_perm;
   ix->dev.offsets = ix->d_offsets;
+  ix->dev.live = ix->d_live;
   ix->dev.centroids = ix->d_centroids;
-  ix->dev.n_items = n;
+  ix->dev.n_items = n_slots;
   ix->dev.dim = dim;
   ix->dev.sig_words = W;
   ix->dev.nlist = nlist;
   ix->dev.item_scale = d->item_scale;
+  ix->n_live = n;
+  if (updatable) {
+    ix->updatable = true;
+    ix->id_capacity = id_capacity;
+    ix->slot_of.assign((size_t)id_capacity, -1);
+    for (int64_t i = 0; i < n; ++i) ix->slot_of[(size_t)i] = pos_of[(size_t)i];
+    ix->offsets_h = offsets;
+    ix->free_h.resize((size_t)nlist);
+    for (int32_t c = 0; c < nlist; ++c)
+      for (int32_t p = offsets[c + 1] - 1; p >= offsets[c] + (int32_t)size[c]; --p) ix->free_h[(size_t)c].push_back(p);
+  }
   {
     std::lock_guard<std::mutex> lk(g_live_mu);
     g_live.insert(ix);
   }
   *out = ix;
   return SVT_OK;
+}
+
+}  // namespace
+
+extern "C" int svt_index_upload(const svt_index_desc *d, void *hip_stream, svt_index **out) {
+  g_err.clear();
+  return upload(d, false, 0, 0, 0.f, hip_stream, out, "svt_index_upload");
+}
+
+extern "C" int svt_index_upload_updatable(const svt_index_desc *d, int64_t id_capacity, int32_t slack_min,
+                                          float slack_frac, void *hip_stream, svt_index **out) {
+  g_err.clear();
+  return upload(d, true, id_capacity, slack_min, slack_frac, hip_stream, out, "svt_index_upload_updatable");
 }
 
 extern "C" int svt_index_free(svt_index *ix, void *hip_stream) {
@@ -243,11 +322,147 @@ extern "C" int svt_index_free(svt_index *ix, void *hip_stream) {
 extern "C" int svt_index_info(const svt_index *ix, int64_t *n_items, int32_t *dim, int32_t *sig_words, int32_t *nlist) {
   g_err.clear();
   if (!ix || !is_live(ix)) return fail(SVT_ESTATE, "svt_index_info: not a live index");
-  if (n_items) *n_items = ix->dev.n_items;
+  if (n_items) *n_items = ix->n_live;
   if (dim) *dim = ix->dev.dim;
   if (sig_words) *sig_words = ix->dev.sig_words;
   if (nlist) *nlist = ix->dev.nlist;
   return SVT_OK;
+}
+
+namespace {
+
+// The checks every update batch shares; SVT_OK or the error (message set)
+int check_update(svt_index *ix, int32_t n, const int64_t *ids, const char *who) {
+  if (!ix || !is_live(ix) || ix->magic != kMagic) return fail(SVT_ESTATE, "%s: not a live index", who);
+  if (!ix->updatable) return fail(SVT_ESTATE, "%s: the index was not uploaded as updatable", who);
+  if (n < 0) return fail(SVT_EINVAL, "%s: n %d < 0", who, n);
+  if (n > 0 && !ids) return fail(SVT_EINVAL, "%s: NULL ids", who);
+  return SVT_OK;
+}
+
+// ids of one batch: each in [0, id_capacity), no id twice, each present (present) or absent (!present)
+int check_ids(svt_index *ix, int32_t n, const int64_t *ids, bool present, const char *who) {
+  std::vector<int64_t> sorted(ids, ids + n);
+  std::sort(sorted.begin(), sorted.end());
+  for (int32_t i = 0; i < n; ++i) {
+    const int64_t id = sorted[(size_t)i];
+    if (id < 0 || id >= ix->id_capacity)
+      return fail(SVT_EINVAL, "%s: id %lld out of [0, %lld)", who, (long long)id, (long long)ix->id_capacity);
+    if (i > 0 && sorted[(size_t)i - 1] == id) return fail(SVT_EINVAL, "%s: id %lld twice in one batch", who, (long long)id);
+    const bool in = ix->slot_of[(size_t)id] >= 0;
+    if (in != present)
+      return fail(SVT_EINVAL, "%s: id %lld is %s the index", who, (long long)id, in ? "already in" : "not in");
+  }
+  return SVT_OK;
+}
+
+int32_t cluster_of_slot(const svt_index *ix, int32_t p) {
+  return (int32_t)(std::upper_bound(ix->offsets_h.begin(), ix->offsets_h.end(), p) - ix->offsets_h.begin()) - 1;
+}
+
+// Stage a batch (ops, then rows, then signatures) on the device, apply it on s and wait for it.
+int apply_updates(svt_index *ix, const std::vector<UpdOp> &ops, const int8_t *rows, const uint64_t *sigs,
+                  hipStream_t s, const char *who) {
+  const int32_t n = (int32_t)ops.size(), dim = ix->dev.dim, W = ix->dev.sig_words;
+  const size_t ob = align256((size_t)n * sizeof(UpdOp));
+  const size_t rb = rows ? align256((size_t)n * dim) : 0;
+  const size_t sb = sigs ? (size_t)n * W * sizeof(uint64_t) : 0;
+  const size_t need = ob + rb + sb;
+  hipError_t e;
+  if (need > ix->stage_bytes) {
+    // the previous batch finished before its call returned: the old staging is idle
+    if (ix->d_stage) (void)hipFree(ix->d_stage);
+    ix->d_stage = nullptr;
+    ix->stage_bytes = 0;
+    if ((e = hipMalloc(&ix->d_stage, need)) != hipSuccess) return fail_hip(e, who);
+    ix->stage_bytes = need;
+  }
+  char *base = (char *)ix->d_stage;
+  if ((e = hipMemcpyAsync(base, ops.data(), (size_t)n * sizeof(UpdOp), hipMemcpyHostToDevice, s)) != hipSuccess)
+    return fail_hip(e, who);
+  if (rows && (e = hipMemcpyAsync(base + ob, rows, (size_t)n * dim, hipMemcpyHostToDevice, s)) != hipSuccess)
+    return fail_hip(e, who);
+  if (sigs && (e = hipMemcpyAsync(base + ob + rb, sigs, sb, hipMemcpyHostToDevice, s)) != hipSuccess)
+    return fail_hip(e, who);
+  if ((e = launch_updates(ix->d_items, ix->d_sigs, ix->d_perm, ix->d_live, (const UpdOp *)base, n,
+                          rows ? (const int8_t *)(base + ob) : nullptr,
+                          sigs ? (const uint64_t *)(base + ob + rb) : nullptr, dim, W, s)) != hipSuccess)
+    return fail_hip(e, who);
+  if ((e = hipStreamSynchronize(s)) != hipSuccess) return fail_hip(e, who);
+  return SVT_OK;
+}
+
+}  // namespace
+
+extern "C" int svt_index_insert(svt_index *ix, int32_t n, const int64_t *ids, const int8_t *rows, const uint64_t *sigs,
+                                const int32_t *list_of, void *hip_stream) {
+  g_err.clear();
+  const char *who = "svt_index_insert";
+  int rc = check_update(ix, n, ids, who);
+  if (rc != SVT_OK || n == 0) return rc;
+  if (!rows || !sigs || !list_of) return fail(SVT_EINVAL, "%s: NULL rows, sigs or list_of", who);
+  if ((rc = check_ids(ix, n, ids, false, who)) != SVT_OK) return rc;
+  const int32_t nlist = ix->dev.nlist, W = ix->dev.sig_words;
+  std::vector<int32_t> want((size_t)nlist, 0);
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t c = list_of[i];
+    if (c < 0 || c >= nlist) return fail(SVT_EINVAL, "%s: list_of[%d] = %d out of range", who, i, c);
+    if (sig_reserved(sigs + (size_t)i * W, W))
+      return fail(SVT_EINVAL, "%s: item %d has every signature bit set (reserved for free slots)", who, i);
+    if (++want[(size_t)c] > (int32_t)ix->free_h[(size_t)c].size())
+      return fail(SVT_ENOSPACE, "%s: cluster %d has %zu free slots, the batch needs more (upload with more slack)", who,
+                  c, ix->free_h[(size_t)c].size());
+  }
+  std::vector<UpdOp> ops((size_t)n);
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t c = list_of[i];
+    const int32_t p = ix->free_h[(size_t)c].back();
+    ix->free_h[(size_t)c].pop_back();
+    ix->slot_of[(size_t)ids[i]] = p;
+    ops[(size_t)i] = UpdOp{p, (int32_t)ids[i], c, kUpdInsert};
+  }
+  ix->n_live += n;
+  return apply_updates(ix, ops, rows, sigs, (hipStream_t)hip_stream, who);
+}
+
+extern "C" int svt_index_delete(svt_index *ix, int32_t n, const int64_t *ids, void *hip_stream) {
+  g_err.clear();
+  const char *who = "svt_index_delete";
+  int rc = check_update(ix, n, ids, who);
+  if (rc != SVT_OK || n == 0) return rc;
+  if ((rc = check_ids(ix, n, ids, true, who)) != SVT_OK) return rc;
+  std::vector<UpdOp> ops((size_t)n);
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t p = ix->slot_of[(size_t)ids[i]];
+    const int32_t c = cluster_of_slot(ix, p);
+    ops[(size_t)i] = UpdOp{p, -1, c, kUpdDelete};
+    ix->slot_of[(size_t)ids[i]] = -1;
+  }
+  // freed slots go back on top of their clusters' stacks, lowest slot last pushed
+  std::vector<UpdOp> by_slot(ops);
+  std::sort(by_slot.begin(), by_slot.end(), [](const UpdOp &a, const UpdOp &b) { return a.pos > b.pos; });
+  for (const UpdOp &op : by_slot) ix->free_h[(size_t)op.cluster].push_back(op.pos);
+  ix->n_live -= n;
+  return apply_updates(ix, ops, nullptr, nullptr, (hipStream_t)hip_stream, who);
+}
+
+extern "C" int svt_index_resign(svt_index *ix, int32_t n, const int64_t *ids, const uint64_t *sigs, void *hip_stream) {
+  g_err.clear();
+  const char *who = "svt_index_resign";
+  int rc = check_update(ix, n, ids, who);
+  if (rc != SVT_OK || n == 0) return rc;
+  if (!sigs) return fail(SVT_EINVAL, "%s: NULL sigs", who);
+  if ((rc = check_ids(ix, n, ids, true, who)) != SVT_OK) return rc;
+  const int32_t W = ix->dev.sig_words;
+  for (int32_t i = 0; i < n; ++i)
+    if (sig_reserved(sigs + (size_t)i * W, W))
+      return fail(SVT_EINVAL, "%s: signature %d has every bit set (reserved for free slots)", who, i);
+  std::vector<UpdOp> ops((size_t)n);
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t p = ix->slot_of[(size_t)ids[i]];
+    ops[(size_t)i] = UpdOp{p, (int32_t)ids[i], cluster_of_slot(ix, p), kUpdResign};
+  }
+  return apply_updates(ix, ops, nullptr, sigs, (hipStream_t)hip_stream, who);
 }
 
 // ------------------------------------------------------------------------------------------------

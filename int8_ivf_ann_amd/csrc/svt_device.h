@@ -39,6 +39,12 @@ __device__ __forceinline__ int32_t group_sum(int32_t v) {
   return v;
 }
 
+// A free slot of an updatable index holds the reserved signature with every bit set, which no live item
+// has: the filter rejects it whatever the mask (a mask of zero passes every live item).
+__device__ __forceinline__ bool sig_live(uint64_t s0, uint64_t s1, int sig_words) {
+  return (s0 & (sig_words == 2 ? s1 : ~0ull)) != ~0ull;
+}
+
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
 
 // number of set bits of `mask` below this lane

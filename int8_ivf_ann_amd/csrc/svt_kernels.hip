@@ -82,14 +82,6 @@ __global__ __launch_bounds__(256) void k_coarse_keys(const int8_t *__restrict__ 
 // The work list follows in four small kernels (k_plan_*): every query's stream is cut into chunks of
 // about equal estimated cost, so that a dense filter does not leave one workgroup with far more bytes.
 
-template <int W>
-__device__ __forceinline__ bool passes(const uint64_t *__restrict__ sig, const uint64_t *mk) {
-  bool ok = true;
-#pragma unroll
-  for (int u = 0; u < W; ++u) ok = ok && ((sig[u] & mk[u]) == mk[u]);
-  return ok;
-}
-
 // <x, q> over NCH 16-byte parts, every part requested before any is used
 template <int NCH>
 __device__ __forceinline__ int32_t row_dot(const int4 *__restrict__ x, const int4 *__restrict__ q) {
@@ -127,6 +119,7 @@ __global__ __launch_bounds__(kSelThreads) void k_coarse_select(DevIndex ix, cons
   __shared__ int32_t tcnt[kSelKR * NWV];         // probed clusters per (register slot, wave)
   __shared__ int smax_s;
   __shared__ int32_t tail_s;                     // stream offset of the first probed cluster in the tail bands
+  __shared__ unsigned long long live_s;          // live items of the probed clusters
   __shared__ struct {
     int32_t pos[kSelElig];                       // tile path: eligible samples (position, score)
     int32_t sc[kSelElig];
@@ -140,12 +133,17 @@ __global__ __launch_bounds__(kSelThreads) void k_coarse_select(DevIndex ix, cons
   int32_t *pb = w.pb + (size_t)b * nprobe;
   const bool in_lds = nprobe <= kSelSegLds;
   const int32_t c_tail = (int32_t)(((int64_t)kTailBand * nlist + kPlanBands - 1) / kPlanBands);
-  if (tid == 0) tail_s = INT32_MAX;
+  if (tid == 0) {
+    tail_s = INT32_MAX;
+    live_s = 0ull;
+  }
   int run = 0;   // items of the query's stream
+  int64_t my_live = 0;   // live items of the probed clusters this thread visits
   if (nprobe == nlist) {
     // every cluster probed: the probe list is every cluster in order, the stream is the position order
     for (int r = tid; r < nlist; r += kSelThreads) {
       const int32_t o0 = ix.offsets[r];
+      my_live += ix.live[r];
       probes[r] = r;
       seg[r] = o0;
       pb[r] = 0;
@@ -269,6 +267,7 @@ __global__ __launch_bounds__(kSelThreads) void k_coarse_select(DevIndex ix, cons
       c = in_lds ? seg_lds[r] : probes[r];
       o0 = ix.offsets[c];
       sz = ix.offsets[c + 1] - o0;
+      my_live += ix.live[c];
     }
     int tot;
     const int pre = block_excl_scan<kSelThreads>(sz, wave_tot, &tot);
@@ -284,13 +283,23 @@ __global__ __launch_bounds__(kSelThreads) void k_coarse_select(DevIndex ix, cons
     run += tot;
   }
   }   // nprobe < nlist
+  {
+    // the items the search scans for this query: the live items of its probed clusters (the stream also
+    // holds the free slots of an updatable index, which no filter passes)
+    unsigned long long v = (unsigned long long)my_live;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    __syncthreads();
+    if (l == 0 && v) atomicAdd(&live_s, v);
+    __syncthreads();
+  }
   if (tid == 0) {
     seg[nprobe] = run;
     if (in_lds) seg_lds[nprobe] = run;
     w.qlen[b] = run;
     w.thr[b] = INT32_MIN;
     if (w.pool_cnt) w.pool_cnt[b] = 0u;
-    if (w.stats) { w.stats[2 * (size_t)b] = 0; w.stats[2 * (size_t)b + 1] = 0; }
+    if (w.stats) { w.stats[2 * (size_t)b] = (int64_t)live_s; w.stats[2 * (size_t)b + 1] = 0; }
   }
   __syncthreads();
   // Evenly spaced samples of the query's probed items: their filter density sizes the query's share of
@@ -348,7 +357,8 @@ __global__ __launch_bounds__(kSelThreads) void k_coarse_select(DevIndex ix, cons
     }
 #pragma unroll
     for (int i = 0; i < kSampleMax; ++i) {
-      const bool ok = i < m && (sgv[i][0] & mk[0]) == mk[0] && (sgv[i][1] & mk[1]) == mk[1];
+      const bool ok = i < m && (sgv[i][0] & mk[0]) == mk[0] && (sgv[i][1] & mk[1]) == mk[1] &&
+                      sig_live(sgv[i][0], sgv[i][1], ix.sig_words);
       hitm |= ok ? 1u << i : 0u;
     }
     if (thr_mode == 0) {   // query path: every sample scored
@@ -1060,7 +1070,7 @@ __global__ __launch_bounds__(kScanThreads, kScanOcc) void k_scan(ScanArgs a) {
 #pragma unroll
       for (int gi = 0; gi < kScanGroups; ++gi) {
         const int i = gi * kScanThreads + wv * 64 + l;
-        bool pass = i < sg_n;
+        bool pass = i < sg_n && sig_live(sg[gi][0], sg[gi][W - 1], W);
 #pragma unroll
         for (int u = 0; u < W; ++u) pass = pass && ((sg[gi][u] & mk[u]) == mk[u]);
         const uint64_t bal = __ballot(pass);
@@ -1221,11 +1231,10 @@ __global__ __launch_bounds__(kScanThreads, kScanOcc) void k_scan(ScanArgs a) {
       a.w.slot_min[c] = kth;
       sm.next = next_c;
     }
-    // per-query counters: items scanned by this chunk, items that passed the filter
+    // per-query counter: items that passed the filter (n_elig is uniform across the wave: one add per
+    // wave); the scanned items are counted by k_coarse_select
     if (a.w.stats && !a.fallback) {
-      // n_elig is uniform across the wave: one add per wave
       if (l == 0) atomicAdd((unsigned long long *)&a.w.stats[2 * (size_t)q + 1], (unsigned long long)n_elig);
-      if (tid == 0) atomicAdd((unsigned long long *)&a.w.stats[2 * (size_t)q], (unsigned long long)(rb - ra));
     }
     __syncthreads();
   }
@@ -1550,6 +1559,40 @@ __global__ __launch_bounds__(256) void k_scatter_rows(const int8_t *__restrict__
   for (int u = c; u < sig_words; u += chunks) dst_sigs[p * sig_words + u] = src_sigs[r * sig_words + u];
 }
 
+// Updates of an updatable index, one thread per 16-byte chunk of a row ("SilverTorch - Index as Model",
+// index freshness section: a stream of small in-place updates to the index tensors between snapshots).
+// Insert: the row, signature and id go to the free slot the host chose, the cluster's live count grows.
+// Delete: the slot's signature becomes the free-slot signature (every bit set) and its id -1.  Re-sign:
+// the slot's signature is replaced.  Every update of one batch writes a different slot.
+__global__ __launch_bounds__(256) void k_updates(int8_t *__restrict__ items, uint64_t *__restrict__ sigs,
+                                                 int32_t *__restrict__ perm, int32_t *__restrict__ live,
+                                                 const UpdOp *__restrict__ ops, int32_t n,
+                                                 const int8_t *__restrict__ rows, const uint64_t *__restrict__ new_sigs,
+                                                 int32_t chunks, int32_t sig_words) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t i = t / chunks;
+  const int c = (int)(t % chunks);
+  if (i >= n) return;
+  const UpdOp op = ops[i];
+  const int64_t p = op.pos;
+  if (op.kind == kUpdInsert)   // rows is NULL unless the batch inserts
+    reinterpret_cast<int4 *>(items)[p * chunks + c] = reinterpret_cast<const int4 *>(rows)[i * chunks + c];
+  if (op.kind == kUpdDelete) {
+    for (int u = c; u < sig_words; u += chunks) sigs[p * sig_words + u] = ~0ull;
+  } else {   // new_sigs is NULL in a batch of deletes only
+    for (int u = c; u < sig_words; u += chunks) sigs[p * sig_words + u] = new_sigs[i * sig_words + u];
+  }
+  if (c == 0) {
+    if (op.kind == kUpdInsert) {
+      perm[p] = op.id;
+      atomicAdd(&live[op.cluster], 1);
+    } else if (op.kind == kUpdDelete) {
+      perm[p] = -1;
+      atomicAdd(&live[op.cluster], -1);
+    }
+  }
+}
+
 // ------------------------------------------------------------------------------------------------
 // launch wrappers
 
@@ -1632,6 +1675,16 @@ hipError_t launch_merge(const DevIndex &ix, const float *query_scales, const Sea
     k_merge_gather<<<g, 256, 0, s>>>(w, sh.B, sh.k, (uint32_t)sh.gather_cap);
   }
   k_merge<<<sh.B, kSelThreads, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_updates(int8_t *items, uint64_t *sigs, int32_t *perm, int32_t *live, const UpdOp *ops, int32_t n,
+                          const int8_t *rows, const uint64_t *new_sigs, int32_t dim, int32_t sig_words, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int32_t chunks = dim / 16;
+  const int64_t threads = (int64_t)n * chunks;
+  k_updates<<<(unsigned)((threads + 255) / 256), 256, 0, s>>>(items, sigs, perm, live, ops, n, rows, new_sigs, chunks,
+                                                                sig_words);
   return hipGetLastError();
 }
 

@@ -234,7 +234,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void *base, int
 //
 // Candidates (score at or above the member's threshold) are staged in LDS with the slot of their (entry
 // visit, member) and go to the queries' pools when the stage fills and at the end of the chunk, one pool
-// reservation per slot.  Per-slot counters give the scanned and accepted items of each query.
+// reservation per slot.  Per-slot counters give the accepted items of each query.
 
 struct TScanArgs {
   DevIndex ix;
@@ -271,7 +271,6 @@ struct TWaveLds {
   uint32_t scount[kTSlotsW];         // candidates staged for each slot
   uint32_t sbase[kTSlotsW];          // their pool position, reserved at a flush
   uint32_t selig[kTSlotsW];          // items the slot's member accepted
-  uint32_t sscan[kTSlotsW];          // items of the slot's entry visit
   uint64_t skey[kTStageW];           // staged candidates: (score, position) keys
   uint8_t sslot[kTStageW];           //   their slot
   uint16_t srank[kTStageW];          //   their rank among the slot's staged candidates
@@ -383,15 +382,7 @@ __global__ __launch_bounds__(kScanThreads, kTOcc) void k_tscan(TScanArgs a) {
           cmc = __builtin_amdgcn_readfirstlane(S.e_mc[cw]);
           const bool fits = nsl + cmc <= kTSlotsW;
           cslot = fits ? (uint32_t)nsl : kNoSlot;
-          if (l < cmc) {
-            const int q = S.wm[cmb + l].q;
-            if (fits) {
-              S.sq[nsl + l] = q;
-              S.sscan[nsl + l] = (uint32_t)(t1 - t0);
-            } else if (stats) {
-              atomicAdd((unsigned long long *)&stats[2 * (size_t)q], (unsigned long long)(t1 - t0));
-            }
-          }
+          if (l < cmc && fits) S.sq[nsl + l] = S.wm[cmb + l].q;
           if (fits) nsl += cmc;
           wave_lds_sync();
           return;
@@ -447,10 +438,11 @@ __global__ __launch_bounds__(kScanThreads, kTOcc) void k_tscan(TScanArgs a) {
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         const int i = g * 64 + l;
+        const bool live = i < fs_n && sig_live(sg[g][0], sg[g][W - 1], W);
         uint32_t qm = 0u;
         for (int j = 0; j < fs_mc; ++j) {
           const uint64_t m0 = S.wm[fs_mb + j].m0;
-          bool pass = i < fs_n && ((sg[g][0] & m0) == m0);
+          bool pass = live && ((sg[g][0] & m0) == m0);
           if constexpr (W == 2) {
             const uint64_t m1 = S.wm[fs_mb + j].m1;
             pass = pass && ((sg[g][1] & m1) == m1);
@@ -584,7 +576,6 @@ __global__ __launch_bounds__(kScanThreads, kTOcc) void k_tscan(TScanArgs a) {
       for (int s = l; s < ns; s += 64) {
         const int q = S.sq[s];
         if (S.selig[s]) atomicAdd((unsigned long long *)&stats[2 * (size_t)q + 1], (unsigned long long)S.selig[s]);
-        if (S.sscan[s]) atomicAdd((unsigned long long *)&stats[2 * (size_t)q], (unsigned long long)S.sscan[s]);
       }
     }
     wave_lds_sync();
@@ -771,10 +762,17 @@ __global__ __launch_bounds__(64 * kXWaves, kXOcc) void k_xscan(XScanArgs a) {
     // the complemented signature words of item lr of each tile (an item passes a mask when no mask bit
     // falls on a zero of its signature), gathered from the lanes of the other groups
     uint32_t ns[4][MW];
+    bool live[4];   // a free slot (every signature bit set) is eligible for no query
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < 4; ++t) {
+      uint32_t any = 0u;
 #pragma unroll
-      for (int ww = 0; ww < MW; ++ww) ns[t][ww] = ~(uint32_t)__shfl((int)SG[t], lr + 16 * ww);
+      for (int ww = 0; ww < MW; ++ww) {
+        ns[t][ww] = ~(uint32_t)__shfl((int)SG[t], lr + 16 * ww);
+        any |= ns[t][ww];
+      }
+      live[t] = any != 0u;
+    }
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
@@ -784,7 +782,7 @@ __global__ __launch_bounds__(64 * kXWaves, kXOcc) void k_xscan(XScanArgs a) {
         for (int ww = 0; ww < MW; ++ww) mq[ww] = S.mk[16 * t2 + 4 * lg + r][ww];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          const bool item_ok = p0 + 16 * t + lr < NP;
+          const bool item_ok = p0 + 16 * t + lr < NP && live[t];
           uint32_t x = 0u;
 #pragma unroll
           for (int ww = 0; ww < MW; ++ww) x |= mq[ww] & ns[t][ww];
@@ -880,8 +878,7 @@ __global__ __launch_bounds__(64 * kXWaves, kXOcc) void k_xscan(XScanArgs a) {
 // takes the best of its slots; the r-th best of those per-thread maxima is the threshold, r for kAlpha * k
 // items over the whole catalogue (at least kRMin): r distinct sampled items score at or above it.  With
 // r far below the thread count it sits close to the r-th best sample.  No threshold when the pool holds
-// the whole catalogue or fewer than r threads saw an eligible sample.  Also the scanned count of every
-// query (the whole catalogue).
+// the whole catalogue or fewer than r threads saw an eligible sample.
 __global__ __launch_bounds__(kSelThreads) void k_xthr(Work w, int64_t n_items, int32_t k, int32_t pool_cap,
                                                       int32_t scap, int32_t n_points, int32_t force) {
   __shared__ SelScratch sel;
@@ -915,10 +912,7 @@ __global__ __launch_bounds__(kSelThreads) void k_xthr(Work w, int64_t n_items, i
     }
   }
   if (force) st = INT32_MAX;
-  if (tid == 0) {
-    w.sthr[q] = st;
-    if (w.stats) w.stats[2 * (size_t)q] = w.qlen[q];
-  }
+  if (tid == 0) w.sthr[q] = st;
 }
 
 // ------------------------------------------------------------------------------------------------

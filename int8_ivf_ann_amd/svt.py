@@ -15,7 +15,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsvt.so")
 
-SVT_OK, SVT_EINVAL, SVT_ENOMEM, SVT_EDEVICE, SVT_EUNSUPPORTED, SVT_ESTATE = 0, -1, -2, -3, -4, -5
+SVT_OK, SVT_EINVAL, SVT_ENOMEM, SVT_EDEVICE, SVT_EUNSUPPORTED, SVT_ESTATE, SVT_ENOSPACE = 0, -1, -2, -3, -4, -5, -6
 SVT_MAX_K = 2048
 SVT_MAX_SIG_WORDS = 2
 SVT_PATH_AUTO, SVT_PATH_QUERY, SVT_PATH_TILE, SVT_PATH_EXHAUSTIVE = 0, 1, 2, 3
@@ -24,7 +24,8 @@ SVT_NOALLOC_SCRATCH_BYTES = 256 << 20
 _PATHS = {"auto": SVT_PATH_AUTO, "query": SVT_PATH_QUERY, "tile": SVT_PATH_TILE}
 
 #: every symbol include/svt.h declares
-EXPORTED = ("svt_index_upload", "svt_index_free", "svt_index_info", "svt_search_workspace_size", "svt_search_path",
+EXPORTED = ("svt_index_upload", "svt_index_upload_updatable", "svt_index_insert", "svt_index_delete",
+            "svt_index_resign", "svt_index_free", "svt_index_info", "svt_search_workspace_size", "svt_search_path",
             "svt_search", "svt_search_noalloc", "svt_last_error", "svt_bloom_mask", "svt_bloom_sign", "svt_profile_enable", "svt_profile_read")
 
 
@@ -80,6 +81,11 @@ def lib():
     L = ctypes.CDLL(LIB_PATH)
     vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     L.svt_index_upload.argtypes = [ctypes.POINTER(svt_index_desc), vp, ctypes.POINTER(vp)]
+    L.svt_index_upload_updatable.argtypes = [ctypes.POINTER(svt_index_desc), i64, i32, ctypes.c_float, vp,
+                                             ctypes.POINTER(vp)]
+    L.svt_index_insert.argtypes = [vp, i32, vp, vp, vp, vp, vp]
+    L.svt_index_delete.argtypes = [vp, i32, vp, vp]
+    L.svt_index_resign.argtypes = [vp, i32, vp, vp, vp]
     L.svt_index_free.argtypes = [vp, vp]
     L.svt_index_info.argtypes = [vp, vp, vp, vp, vp]
     L.svt_search_workspace_size.argtypes = [vp, i32, i32, i32, vp]
@@ -165,9 +171,7 @@ def svt_bloom_sign(token_keys: np.ndarray, n_hashes: int, sig_words: int, n_thre
     return out
 
 
-def svt_index_upload(items: np.ndarray, sigs: np.ndarray, list_of: np.ndarray, centroids: np.ndarray,
-                     item_scale: float, stream=None) -> ctypes.c_void_p:
-    """Host arrays -> device index handle (the current torch device)."""
+def _desc(items, sigs, list_of, centroids, item_scale):
     items = np.ascontiguousarray(items, np.int8)
     sigs = np.ascontiguousarray(sigs, np.uint64)
     list_of = np.ascontiguousarray(list_of, np.int32)
@@ -179,9 +183,56 @@ def svt_index_upload(items: np.ndarray, sigs: np.ndarray, list_of: np.ndarray, c
     d.nlist = centroids.shape[0]
     d.items, d.sigs, d.list_of, d.centroids = (_np_ptr(items), _np_ptr(sigs), _np_ptr(list_of), _np_ptr(centroids))
     d.item_scale = float(item_scale)
+    return d, (items, sigs, list_of, centroids)   # the arrays stay alive while d is used
+
+
+def svt_index_upload(items: np.ndarray, sigs: np.ndarray, list_of: np.ndarray, centroids: np.ndarray,
+                     item_scale: float, stream=None) -> ctypes.c_void_p:
+    """Host arrays -> device index handle (the current torch device)."""
+    d, keep = _desc(items, sigs, list_of, centroids, item_scale)
     h = ctypes.c_void_p()
     _check(lib().svt_index_upload(ctypes.byref(d), _stream_ptr(stream), ctypes.byref(h)))
     return h
+
+
+def svt_index_upload_updatable(items, sigs, list_of, centroids, item_scale: float, id_capacity: int,
+                               slack_min: int = 0, slack_frac: float = 0.0, stream=None) -> ctypes.c_void_p:
+    """Host arrays -> an index that takes in-place inserts, deletes and re-signs (free slots per cluster:
+    max(slack_min, ceil(slack_frac * size)); later ids in [0, id_capacity))."""
+    d, keep = _desc(items, sigs, list_of, centroids, item_scale)
+    h = ctypes.c_void_p()
+    _check(lib().svt_index_upload_updatable(ctypes.byref(d), int(id_capacity), int(slack_min), float(slack_frac),
+                                            _stream_ptr(stream), ctypes.byref(h)))
+    return h
+
+
+def _ids(ids):
+    return np.ascontiguousarray(ids, np.int64).reshape(-1)
+
+
+def svt_index_insert(handle, ids, rows, sigs, list_of, stream=None) -> None:
+    """Insert items (host arrays: ids [n], rows [n, dim] int8, sigs [n, W] uint64, list_of [n])."""
+    ids = _ids(ids)
+    n = ids.shape[0]
+    _, dim, W, _ = svt_index_info(handle)
+    rows = np.ascontiguousarray(rows, np.int8).reshape(n, dim)
+    sigs = np.ascontiguousarray(sigs, np.uint64).reshape(n, W)
+    list_of = np.ascontiguousarray(list_of, np.int32).reshape(n)
+    _check(lib().svt_index_insert(handle, n, _np_ptr(ids), _np_ptr(rows), _np_ptr(sigs), _np_ptr(list_of),
+                                  _stream_ptr(stream)))
+
+
+def svt_index_delete(handle, ids, stream=None) -> None:
+    ids = _ids(ids)
+    _check(lib().svt_index_delete(handle, ids.shape[0], _np_ptr(ids), _stream_ptr(stream)))
+
+
+def svt_index_resign(handle, ids, sigs, stream=None) -> None:
+    ids = _ids(ids)
+    n = ids.shape[0]
+    _, _, W, _ = svt_index_info(handle)
+    sigs = np.ascontiguousarray(sigs, np.uint64).reshape(n, W)
+    _check(lib().svt_index_resign(handle, n, _np_ptr(ids), _np_ptr(sigs), _stream_ptr(stream)))
 
 
 def svt_index_free(handle, stream=None) -> None:
@@ -292,8 +343,13 @@ class Index:
     """Convenience owner of an uploaded index: ``Index(items, sigs, list_of, centroids, scale)``,
     ``search(queries, masks, nprobe, k)`` with torch device tensors, ``close()``."""
 
-    def __init__(self, items, sigs, list_of, centroids, item_scale, stream=None):
-        self.handle = svt_index_upload(items, sigs, list_of, centroids, item_scale, stream)
+    def __init__(self, items, sigs, list_of, centroids, item_scale, stream=None, id_capacity=None, slack_min=0,
+                 slack_frac=0.0):
+        if id_capacity is None:
+            self.handle = svt_index_upload(items, sigs, list_of, centroids, item_scale, stream)
+        else:   # updatable
+            self.handle = svt_index_upload_updatable(items, sigs, list_of, centroids, item_scale, id_capacity,
+                                                     slack_min, slack_frac, stream)
         self.n_items, self.dim, self.sig_words, self.nlist = svt_index_info(self.handle)
         self._ws = None
 
@@ -310,6 +366,17 @@ class Index:
         ws = self.workspace(B, nprobe, k, opts) if B > 0 else None
         return svt_search(self.handle, queries, masks, nprobe, k, query_scales=query_scales, workspace=ws,
                           stream=stream, opts=opts, **outs)
+
+    def insert(self, ids, rows, sigs, list_of, stream=None):
+        svt_index_insert(self.handle, ids, rows, sigs, list_of, stream)
+        self.n_items = svt_index_info(self.handle)[0]
+
+    def delete(self, ids, stream=None):
+        svt_index_delete(self.handle, ids, stream)
+        self.n_items = svt_index_info(self.handle)[0]
+
+    def resign(self, ids, sigs, stream=None):
+        svt_index_resign(self.handle, ids, sigs, stream)
 
     def close(self, stream=None):
         if self.handle is not None:

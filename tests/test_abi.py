@@ -76,6 +76,24 @@ def test_upload_argument_errors(L):
     assert "NULL" in svt.svt_last_error()
 
 
+def test_upload_rejects_reserved_signature_and_bad_slack(L):
+    # a signature with every bit set marks free slots: no item may have it (checked before any device work)
+    h = ctypes.c_void_p()
+    items = np.zeros((3, 16), np.int8)
+    sigs = np.array([[1, 2], [~np.uint64(0), ~np.uint64(0)], [3, 4]], np.uint64)
+    cl = np.zeros(3, np.int32)
+    cent = np.zeros((2, 16), np.int8)
+    d, keep = svt._desc(items, sigs, cl, cent, 1.0)
+    assert L.svt_index_upload(ctypes.byref(d), None, ctypes.byref(h)) == svt.SVT_EINVAL
+    assert "every signature bit set" in svt.svt_last_error()
+    sigs[1, 1] = 7   # one word with every bit set is an ordinary signature; the bad slack is caught first
+    d, keep = svt._desc(items, sigs, cl, cent, 1.0)
+    assert L.svt_index_upload_updatable(ctypes.byref(d), 2, 0, 0.0, None, ctypes.byref(h)) == svt.SVT_EINVAL
+    assert "id_capacity" in svt.svt_last_error()
+    assert L.svt_index_upload_updatable(ctypes.byref(d), 10, -1, 0.0, None, ctypes.byref(h)) == svt.SVT_EINVAL
+    assert L.svt_index_upload_updatable(ctypes.byref(d), 10, 0, -0.5, None, ctypes.byref(h)) == svt.SVT_EINVAL
+
+
 def test_search_rejects_dead_index(L):
     bogus = ctypes.c_void_p(0x1000)
     assert L.svt_search(bogus, 1, None, None, None, 1, 1, None, None, None, None, None, None, None, 0,
@@ -85,6 +103,10 @@ def test_search_rejects_dead_index(L):
     assert L.svt_search_noalloc(bogus, 1, None, None, None, 1, 1, None, None, None, None, None, None,
                                 None) == svt.SVT_ESTATE
     assert L.svt_search_path(bogus, 1, 1, 1, None) == svt.SVT_ESTATE
+    one = np.zeros(1, np.int64)
+    assert L.svt_index_delete(bogus, 1, one.ctypes.data, None) == svt.SVT_ESTATE
+    assert L.svt_index_resign(bogus, 1, one.ctypes.data, one.ctypes.data, None) == svt.SVT_ESTATE
+    assert L.svt_index_insert(bogus, 1, one.ctypes.data, None, None, None, None) == svt.SVT_ESTATE
     assert "not a live index" in svt.svt_last_error()
     assert L.svt_index_free(bogus, None) == svt.SVT_ESTATE
     assert L.svt_index_free(None, None) == svt.SVT_OK
@@ -101,6 +123,7 @@ def test_options_struct_layout():
         assert re.search(rf"{name} = {v}\b", hdr), name
     assert re.search(r"#define SVT_OPT_MERGE_FROM_SLOTS 1u", hdr)
     assert re.search(r"#define SVT_OPT_FORCE_REDO 2u", hdr)
+    assert re.search(r"SVT_ENOSPACE = -6", hdr) and svt.SVT_ENOSPACE == -6
     assert re.search(r"#define SVT_NOALLOC_SCRATCH_BYTES \(\(size_t\)256 << 20\)", hdr)
     assert svt.SVT_NOALLOC_SCRATCH_BYTES == 256 << 20
 
