@@ -38,6 +38,9 @@ def load(path: Optional[str] = None):
     lib.oracle_coarse.argtypes = [vp, i32, i32, vp, i32, vp, vp]
     lib.oracle_dequant.argtypes = [i32, ctypes.c_float, ctypes.c_float]
     lib.oracle_dequant.restype = ctypes.c_float
+    lib.oracle_search_groups.argtypes = [vp, vp, vp, i64, i32, i32, vp, i32, ctypes.c_float, i32, vp, vp, i32, vp,
+                                         i32, i32, vp, vp, vp, vp, vp, i32]
+    lib.oracle_search_groups.restype = i32
     lib.oracle_search.argtypes = [vp, vp, vp, i64, i32, i32, vp, i32, ctypes.c_float, i32, vp, vp, vp,
                                   i32, i32, vp, vp, vp, vp, vp, i32]
     lib.oracle_search.restype = ctypes.c_int
@@ -92,7 +95,8 @@ class Oracle:
     def search(self, items, sigs, list_of, centroids, item_scale, queries, masks, nprobe, k,
                query_scales=None, n_threads: int = 1):
         """Returns (ids int64 [B,k], scores int32 [B,k], fscores f32 [B,k], counts int32 [B],
-        stats int64 [B,2] = (items scanned in probed clusters, eligible items scored))."""
+        stats int64 [B,2] = (items scanned in probed clusters, eligible items scored)).  masks is
+        [B, W], or [B, G, W] for requests of G masks (an item is eligible when it passes any)."""
         items = np.ascontiguousarray(items, np.int8)
         sigs = np.ascontiguousarray(sigs, np.uint64)
         list_of = np.ascontiguousarray(list_of, np.int32)
@@ -109,9 +113,14 @@ class Oracle:
         fs = np.empty((b, k), np.float32)
         cnt = np.empty(b, np.int32)
         st = np.empty((b, 2), np.int64)
-        rc = self.lib.oracle_search(_p(items), _p(sigs), _p(list_of), n, d, w, _p(centroids), nlist,
-                                    ctypes.c_float(item_scale), b, _p(queries), _p(masks), _p(qs), nprobe, k,
-                                    _p(ids), _p(sc), _p(fs), _p(cnt), _p(st), n_threads)
+        if masks.ndim == 3:
+            rc = self.lib.oracle_search_groups(_p(items), _p(sigs), _p(list_of), n, d, w, _p(centroids), nlist,
+                                               ctypes.c_float(item_scale), b, _p(queries), _p(masks), masks.shape[1],
+                                               _p(qs), nprobe, k, _p(ids), _p(sc), _p(fs), _p(cnt), _p(st), n_threads)
+        else:
+            rc = self.lib.oracle_search(_p(items), _p(sigs), _p(list_of), n, d, w, _p(centroids), nlist,
+                                        ctypes.c_float(item_scale), b, _p(queries), _p(masks), _p(qs), nprobe, k,
+                                        _p(ids), _p(sc), _p(fs), _p(cnt), _p(st), n_threads)
         if rc != 0:
             raise ValueError("oracle_search: invalid arguments")
         return ids, sc, fs, cnt, st

@@ -159,6 +159,7 @@ typedef struct {
   int32_t dim, sig_words;
   const int8_t *centroids; int32_t nlist; float item_scale;
   const int8_t *queries; const uint64_t *masks; const float *query_scales;
+  int32_t mask_groups;
   int32_t nprobe, k;
   int64_t *out_ids; int32_t *out_scores; float *out_fscores; int32_t *out_counts; int64_t *out_stats;
   int32_t q0, q1;
@@ -167,7 +168,8 @@ typedef struct {
 static void search_one(const job *J, int32_t b, char *probed, int32_t *probes, cand **buf, int64_t *cap) {
   const int32_t d = J->dim, W = J->sig_words;
   const int8_t *q = J->queries + (size_t)b * d;
-  const uint64_t *mask = J->masks + (size_t)b * W;
+  const int32_t G = J->mask_groups;
+  const uint64_t *mask = J->masks + (size_t)b * G * W;   /* G masks of W words */
   /* 1. coarse */
   oracle_coarse(J->centroids, J->nlist, d, q, J->nprobe, probes, NULL);
   memset(probed, 0, (size_t)J->nlist);
@@ -181,7 +183,15 @@ static void search_one(const job *J, int32_t b, char *probed, int32_t *probes, c
   for (int64_t i = 0; i < J->n_items; ++i) {
     if (!probed[J->list_of[i]]) continue;
     ++scanned;
-    if (!eligible(J->sigs + (size_t)i * W, mask, W)) continue;
+    /* a request of several masks (targeting rules, "Meta Andromeda" summary, System section: the
+     * targeting matcher): reading = an item is eligible when it passes at least one of them */
+    int ok = 0;
+#if ORACLE_MUTANT == 8
+    for (int32_t g = 0; g < 1 && !ok; ++g) ok = eligible(J->sigs + (size_t)i * W, mask + (size_t)g * W, W);
+#else
+    for (int32_t g = 0; g < G && !ok; ++g) ok = eligible(J->sigs + (size_t)i * W, mask + (size_t)g * W, W);
+#endif
+    if (!ok) continue;
     if (n == *cap) {
       *cap = *cap ? *cap * 2 : 4096;
       *buf = (cand *)realloc(*buf, sizeof(cand) * (size_t)*cap);
@@ -221,16 +231,19 @@ static void *search_worker(void *arg) {
   return NULL;
 }
 
-/* Full search for n_queries queries.  Outputs [n_queries][k] with padding id -1, score INT32_MIN,
- * fscore -inf past count.  out_stats (nullable) receives per query: items scanned in the probed
- * clusters, eligible items scored.  Queries are split over n_threads threads (no other change).
- * Returns 0, or -1 on invalid arguments.                                                          */
-int oracle_search(const int8_t *items, const uint64_t *sigs, const int32_t *list_of, int64_t n_items,
-                  int32_t dim, int32_t sig_words, const int8_t *centroids, int32_t nlist, float item_scale,
-                  int32_t n_queries, const int8_t *queries, const uint64_t *masks, const float *query_scales,
-                  int32_t nprobe, int32_t k, int64_t *out_ids, int32_t *out_scores, float *out_fscores,
-                  int32_t *out_counts, int64_t *out_stats, int32_t n_threads) {
-  if (n_queries < 0 || nprobe < 1 || nprobe > nlist || k < 1 || dim < 1 || sig_words < 1) return -1;
+/* Full search for n_queries queries, each with mask_groups masks of sig_words words ([n_queries]
+ * [mask_groups][sig_words]); an item is eligible when it passes any of its query's masks.  Outputs
+ * [n_queries][k] with padding id -1, score INT32_MIN, fscore -inf past count.  out_stats (nullable)
+ * receives per query: items scanned in the probed clusters, eligible items scored.  Queries are split
+ * over n_threads threads (no other change).  Returns 0, or -1 on invalid arguments.               */
+int oracle_search_groups(const int8_t *items, const uint64_t *sigs, const int32_t *list_of, int64_t n_items,
+                         int32_t dim, int32_t sig_words, const int8_t *centroids, int32_t nlist, float item_scale,
+                         int32_t n_queries, const int8_t *queries, const uint64_t *masks, int32_t mask_groups,
+                         const float *query_scales, int32_t nprobe, int32_t k, int64_t *out_ids,
+                         int32_t *out_scores, float *out_fscores, int32_t *out_counts, int64_t *out_stats,
+                         int32_t n_threads) {
+  if (n_queries < 0 || nprobe < 1 || nprobe > nlist || k < 1 || dim < 1 || sig_words < 1 || mask_groups < 1)
+    return -1;
   if (n_queries == 0) return 0;
   int32_t nt = n_threads < 1 ? 1 : n_threads;
   if (nt > n_queries) nt = n_queries;
@@ -241,6 +254,7 @@ int oracle_search(const int8_t *items, const uint64_t *sigs, const int32_t *list
     J->items = items; J->sigs = sigs; J->list_of = list_of; J->n_items = n_items;
     J->dim = dim; J->sig_words = sig_words; J->centroids = centroids; J->nlist = nlist;
     J->item_scale = item_scale; J->queries = queries; J->masks = masks; J->query_scales = query_scales;
+    J->mask_groups = mask_groups;
     J->nprobe = nprobe; J->k = k; J->out_ids = out_ids; J->out_scores = out_scores;
     J->out_fscores = out_fscores; J->out_counts = out_counts; J->out_stats = out_stats;
     J->q0 = (int32_t)((int64_t)n_queries * t / nt);
@@ -250,4 +264,15 @@ int oracle_search(const int8_t *items, const uint64_t *sigs, const int32_t *list
   for (int32_t t = 0; t < nt; ++t) pthread_join(th[t], NULL);
   free(jobs); free(th);
   return 0;
+}
+
+/* The same with one mask per query ([n_queries][sig_words]).                                     */
+int oracle_search(const int8_t *items, const uint64_t *sigs, const int32_t *list_of, int64_t n_items,
+                  int32_t dim, int32_t sig_words, const int8_t *centroids, int32_t nlist, float item_scale,
+                  int32_t n_queries, const int8_t *queries, const uint64_t *masks, const float *query_scales,
+                  int32_t nprobe, int32_t k, int64_t *out_ids, int32_t *out_scores, float *out_fscores,
+                  int32_t *out_counts, int64_t *out_stats, int32_t n_threads) {
+  return oracle_search_groups(items, sigs, list_of, n_items, dim, sig_words, centroids, nlist, item_scale, n_queries,
+                              queries, masks, 1, query_scales, nprobe, k, out_ids, out_scores, out_fscores,
+                              out_counts, out_stats, n_threads);
 }

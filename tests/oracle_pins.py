@@ -41,7 +41,10 @@ def exhaustive_topk(items, sigs, queries, masks, k, allowed=None):
     cnt = np.zeros(B, np.int64)
     X = items.astype(np.int64)
     for b in range(B):
-        ok = np.all((sigs & masks[b]) == masks[b], axis=1)
+        mb = masks[b] if masks.ndim == 3 else masks[b][None, :]   # [G, W]: eligible under any of them
+        ok = np.zeros(sigs.shape[0], bool)
+        for m in mb:
+            ok |= np.all((sigs & m) == m, axis=1)
         if allowed is not None:
             ok &= allowed[b]
         cand = np.nonzero(ok)[0]
@@ -191,6 +194,45 @@ def pin_ivf_restriction(orc, seed=3, W=2):
         assert np.array_equal(ids, rids) and np.array_equal(sc.astype(np.int64), rsc) and np.array_equal(cnt, rcnt)
 
 
+def pin_mask_groups(orc, seed=12, W=2):
+    """Requests of several masks: an item is eligible when it passes any of them.  Against the numpy
+    reference (the union of each mask's eligible set), at nprobe = nlist and, restricted to the probed
+    clusters, at nprobe < nlist; one group reproduces the one-mask search; a group with every bit set
+    matches nothing here (no item has that signature); the order of the groups does not matter."""
+    rng = np.random.default_rng(seed)
+    items, sigs, cl, cent = small_catalogue(rng, n=4000, d=32, nlist=20, W=W, empty_clusters=2)
+    assert not np.any(np.all(sigs == ~np.uint64(0), axis=1))
+    B, G, k = 6, 3, 80
+    q = rng.integers(-127, 128, (B, 32)).astype(np.int8)
+    masks = np.stack([random_masks(rng, B, W, nbits_max=4) for _ in range(G)], axis=1)   # [B, G, W]
+    masks[2, 1] = 0          # one group of query 2 makes every item eligible
+    ids, sc, fs, cnt, st = orc.search(items, sigs, cl, cent, 1.0, q, masks, 20, k)
+    rids, rsc, rcnt = exhaustive_topk(items, sigs, q, masks, k)
+    assert np.array_equal(ids, rids) and np.array_equal(sc.astype(np.int64), rsc) and np.array_equal(cnt, rcnt)
+    for b in range(B):
+        ok = np.zeros(items.shape[0], bool)
+        for m in masks[b]:
+            ok |= np.all((sigs & m) == m, axis=1)
+        assert st[b, 1] == ok.sum(), "eligible count of a several-mask request"
+    for nprobe in (1, 5):
+        ids, sc, fs, cnt, st = orc.search(items, sigs, cl, cent, 1.0, q, masks, nprobe, k)
+        allowed = np.zeros((B, items.shape[0]), bool)
+        for b in range(B):
+            ref = cent.astype(np.int64) @ q[b].astype(np.int64)
+            allowed[b] = np.isin(cl, np.lexsort((np.arange(20), -ref))[:nprobe])
+        rids, rsc, rcnt = exhaustive_topk(items, sigs, q, masks, k, allowed)
+        assert np.array_equal(ids, rids) and np.array_equal(sc.astype(np.int64), rsc) and np.array_equal(cnt, rcnt)
+    one = orc.search(items, sigs, cl, cent, 1.0, q, masks[:, :1, :], 5, k)
+    plain = orc.search(items, sigs, cl, cent, 1.0, q, np.ascontiguousarray(masks[:, 0, :]), 5, k)
+    assert all(np.array_equal(a, b) for a, b in zip(one, plain))
+    padded = np.concatenate([masks, np.full((B, 1, W), ~np.uint64(0))], axis=1)
+    with_pad = orc.search(items, sigs, cl, cent, 1.0, q, padded, 5, k)
+    base = orc.search(items, sigs, cl, cent, 1.0, q, masks, 5, k)
+    assert all(np.array_equal(a, b) for a, b in zip(with_pad, base))
+    perm = orc.search(items, sigs, cl, cent, 1.0, q, np.ascontiguousarray(masks[:, ::-1, :]), 5, k)
+    assert all(np.array_equal(a, b) for a, b in zip(perm, base))
+
+
 def pin_padding(orc, seed=4):
     rng = np.random.default_rng(seed)
     items, sigs, cl, cent = small_catalogue(rng, n=200, d=16, nlist=4)
@@ -304,5 +346,6 @@ def pin_mask_helper(orc):
         assert np.all(np.unpackbits(singles.view(np.uint8), axis=1).sum(axis=1) <= h)
 
 
-ALL_PINS = [pin_splitmix64, pin_handworked, pin_exhaustive, pin_probe_set, pin_ivf_restriction, pin_padding,
+ALL_PINS = [pin_splitmix64, pin_handworked, pin_exhaustive, pin_probe_set, pin_ivf_restriction, pin_mask_groups,
+            pin_padding,
             pin_dequant, pin_bloom, pin_bloom_mapping, pin_mask_helper]

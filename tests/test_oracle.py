@@ -36,6 +36,10 @@ def test_ivf_is_restricted_exhaustive(orc):
     P.pin_ivf_restriction(orc)
 
 
+def test_mask_groups(orc):
+    P.pin_mask_groups(orc)
+
+
 def test_padding(orc):
     P.pin_padding(orc)
 

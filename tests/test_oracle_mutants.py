@@ -16,6 +16,7 @@ MUTANTS = {
     5: "dot product drops the last dimension",
     6: "Bloom bit index taken from the wrong bits",
     7: "dequantisation ignores the query scale",
+    8: "a request of several masks tests only its first one",
 }
 
 
