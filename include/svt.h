@@ -169,14 +169,22 @@ enum { SVT_PATH_AUTO = 0, SVT_PATH_QUERY = 1, SVT_PATH_TILE = 2, SVT_PATH_EXHAUS
  *   pool_keys  tile path: candidate keys kept per query (0 = default, 16 k rounded up to 4096); a
  *              smaller value makes more pools overflow (their queries are redone)
  *   flags      OR of SVT_OPT_* above
+ *   mask_groups  G in [0, SVT_MAX_MASK_GROUPS]: each query brings G request masks ([B][G][sig_words]) and an
+ *              item is eligible when its signature passes at least one of them (a targeting rule set as a
+ *              disjunction of conjunctive masks, "Meta Andromeda" summary, System section: the targeting
+ *              matcher).  A mask with every bit set passes no item: it pads a query with fewer masks.
+ *              0 is the same as 1.
  * Errors (returned by the calls that take the options): SVT_EINVAL for an unknown path, a negative
- * pool_keys, unknown flag bits or non-zero reserved words.
+ * pool_keys, unknown flag bits, mask_groups out of range or non-zero reserved words.
  */
+#define SVT_MAX_MASK_GROUPS 4  /* masks per request at most                                            */
+
 typedef struct {
   int32_t path;
   int32_t pool_keys;
   uint32_t flags;
-  int32_t reserved[5];   /* must be 0 */
+  int32_t mask_groups;   /* masks per query (0 or 1: one); an item is eligible when it passes any of them */
+  int32_t reserved[4];   /* must be 0 */
 } svt_search_options;
 
 /*
@@ -198,7 +206,8 @@ int svt_search_path(const svt_index *ix, int32_t n_queries, int32_t nprobe, int3
 /*
  * svt_search - batched fused search (steps 1-4 above), asynchronous on hip_stream.
  *   queries       device, [n_queries][dim] int8, row-major, 16-byte aligned
- *   masks         device, [n_queries][sig_words] uint64 request masks (see svt_bloom_mask), 8-byte aligned
+ *   masks         device, [n_queries][G][sig_words] uint64 request masks (see svt_bloom_mask; G = the options'
+ *                 mask_groups, 1 by default), 8-byte aligned
  *   query_scales  device, [n_queries] float > 0, or NULL to use the index's item_scale
  *   nprobe        1 <= nprobe <= nlist
  *   k             1 <= k <= SVT_MAX_K

@@ -487,21 +487,26 @@ constexpr int32_t kTileMinBatch = 128;
 // The union stream is indexed with 32-bit offsets.
 constexpr int64_t kMaxUnion = (int64_t(1) << 31) - (int64_t(1) << 20);
 
-bool tile_fits(const svt_index *ix, int32_t B, int32_t nprobe) {
-  const int64_t blocks = ((int64_t)B + kTMembers - 1) / kTMembers;
-  return ix->dev.n_items * blocks < kMaxUnion && (int64_t)B * nprobe < kMaxUnion;
+int32_t mask_groups(const svt_search_options *o) { return (o && o->mask_groups > 1) ? o->mask_groups : 1; }
+// members per (query, probed cluster) on the tile path
+int32_t tile_groups(int32_t G) { return G <= 1 ? 1 : (G <= 2 ? 2 : 4); }
+
+bool tile_fits(const svt_index *ix, int32_t B, int32_t nprobe, int32_t GT) {
+  const int64_t blocks = ((int64_t)B * GT + kTMembers - 1) / kTMembers;
+  return ix->dev.n_items * blocks < kMaxUnion && (int64_t)B * nprobe * GT < kMaxUnion;
 }
 
 int resolve_path(const svt_index *ix, int32_t B, int32_t nprobe, const svt_search_options *o) {
   const int want = o ? o->path : SVT_PATH_AUTO;
   if (want == SVT_PATH_QUERY || ix->dev.n_items == 0) return kPathQuery;
   const bool exh = nprobe == ix->dev.nlist;
+  const int32_t GT = tile_groups(mask_groups(o));
   if (want == SVT_PATH_TILE) {
     if (exh) return kPathExh;
-    return tile_fits(ix, B, nprobe) ? kPathTile : kPathQuery;
+    return tile_fits(ix, B, nprobe, GT) ? kPathTile : kPathQuery;
   }
   if (exh && B >= 2) return kPathExh;
-  if (B >= kTileMinBatch && tile_fits(ix, B, nprobe)) return kPathTile;
+  if (B >= kTileMinBatch && tile_fits(ix, B, nprobe, GT)) return kPathTile;
   return kPathQuery;
 }
 
@@ -513,7 +518,9 @@ int check_options(const svt_search_options *o, const char *who) {
   if (o->pool_keys < 0) return fail(SVT_EINVAL, "%s: pool_keys %d < 0", who, o->pool_keys);
   if (o->flags & ~(SVT_OPT_MERGE_FROM_SLOTS | SVT_OPT_FORCE_REDO))
     return fail(SVT_EINVAL, "%s: unknown flag bits 0x%x", who, o->flags);
-  for (int i = 0; i < 5; ++i)
+  if (o->mask_groups < 0 || o->mask_groups > SVT_MAX_MASK_GROUPS)
+    return fail(SVT_EINVAL, "%s: mask_groups %d out of [0, %d]", who, o->mask_groups, SVT_MAX_MASK_GROUPS);
+  for (int i = 0; i < 4; ++i)
     if (o->reserved[i] != 0) return fail(SVT_EINVAL, "%s: reserved word %d is not 0", who, i);
   return SVT_OK;
 }
@@ -532,6 +539,8 @@ Layout layout(const svt_index *ix, int32_t B, int32_t nprobe, int32_t k, const s
   sh.force_redo = (o && (o->flags & SVT_OPT_FORCE_REDO)) ? 1 : 0;
   sh.TP = ix->tscan_wgs;
   sh.XP = ix->xscan_wgs;
+  sh.G = mask_groups(o);
+  sh.GT = tile_groups(sh.G);
   const size_t C = (size_t)sh.max_chunks;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -571,15 +580,16 @@ Layout layout(const svt_index *ix, int32_t B, int32_t nprobe, int32_t k, const s
     L.pool = take((size_t)B * (size_t)sh.pool_cap * sizeof(uint64_t));
   }
   if (sh.path == kPathTile) {
-    const int64_t blocks = ((int64_t)B + kTMembers - 1) / kTMembers;
-    sh.max_entries = (int32_t)std::max<int64_t>(1, std::min<int64_t>((int64_t)nlist * blocks, (int64_t)B * nprobe));
+    const int64_t blocks = ((int64_t)B * sh.GT + kTMembers - 1) / kTMembers;
+    sh.max_entries =
+        (int32_t)std::max<int64_t>(1, std::min<int64_t>((int64_t)nlist * blocks, (int64_t)B * nprobe * sh.GT));
     sh.max_tchunks = kTChunksPerWave * kTWaves * sh.TP + 2;
     L.gcnt = take(nlist * sizeof(int32_t));
     L.gfill = take(nlist * sizeof(int32_t));
     L.gstart = take((nlist + 1) * sizeof(int32_t));
     L.estart = take((nlist + 1) * sizeof(int32_t));
     L.uoff = take(nlist * sizeof(int32_t));
-    L.mrec = take((size_t)B * nprobe * sizeof(MRec));
+    L.mrec = take((size_t)B * nprobe * sh.GT * sizeof(MRec));
     L.entries = take((size_t)sh.max_entries * sizeof(UEntry));
     L.ctab = take((size_t)sh.max_tchunks * sizeof(int32_t));
     L.thdr = take(4 * sizeof(int32_t));

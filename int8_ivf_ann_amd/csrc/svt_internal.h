@@ -214,6 +214,8 @@ struct Work {
 
 enum { kPathQuery = 0, kPathTile = 1, kPathExh = 2 };
 
+constexpr int kMaxGroups = 4;   // masks per query (SVT_MAX_MASK_GROUPS)
+
 struct SearchShape {
   int32_t B, nprobe, k, P, max_chunks;
   int32_t path;         // kPath*
@@ -226,6 +228,9 @@ struct SearchShape {
   int32_t force_redo;   // every threshold above any score (test of the redo branch)
   int32_t scap;         // exhaustive: slots of a query's sample buffer (16 per run of 64 sampled points)
   int32_t n_sblocks;    // exhaustive: runs of 64 sampled points
+  int32_t G;            // request masks per query (masks [B][G][sig_words])
+  int32_t GT;           // tile path: members per (query, probed cluster), G rounded up to 1, 2 or 4 (a power of
+                        // two dividing kTMembers, so that a query's members never straddle two entries)
 };
 
 // most chunks a search can produce.  The costs of the queries add up to at most 4 P Tc.  Without a tail

@@ -103,9 +103,9 @@ constexpr int kSelTwoLevel = kSelSegLds / 2 / kSelKR;   // largest nprobe the tw
 // thr_mode (tile path): 0 no speculative threshold, 1 estimate it from the samples, 2 set it above every
 // score (every query with an eligible item is then redone on the query path)
 __global__ __launch_bounds__(kSelThreads) void k_coarse_select(DevIndex ix, const int8_t *__restrict__ queries,
-                                                                const uint64_t *__restrict__ masks, int32_t B,
-                                                                int32_t nprobe, int32_t k, int32_t pool_cap,
-                                                                int32_t thr_mode, Work w) {
+                                                                const uint64_t *__restrict__ masks, int32_t G,
+                                                                int32_t B, int32_t nprobe, int32_t k,
+                                                                int32_t pool_cap, int32_t thr_mode, Work w) {
   constexpr int NWV = kSelThreads / 64;
   __shared__ SelScratch sel;
   __shared__ int wave_tot[NWV + 1];
@@ -332,8 +332,12 @@ __global__ __launch_bounds__(kSelThreads) void k_coarse_select(DevIndex ix, cons
   int64_t ssum_t = 0;
   int32_t mx = INT32_MIN;
   if (run > 0) {
-    uint64_t mk[2] = {0, 0};
-    for (int u = 0; u < ix.sig_words; ++u) mk[u] = masks[(size_t)b * ix.sig_words + u];
+    uint64_t mk[kMaxGroups][2];   // the query's G masks (a sample is eligible under any of them)
+#pragma unroll
+    for (int g = 0; g < kMaxGroups; ++g) {
+      mk[g][0] = g < G ? masks[((size_t)b * G + g) * ix.sig_words] : 0ull;
+      mk[g][1] = (g < G && ix.sig_words == 2) ? masks[((size_t)b * G + g) * ix.sig_words + 1] : 0ull;
+    }
     uint64_t sgv[kSampleMax][2];
 #pragma unroll
     for (int i = 0; i < kSampleMax; ++i) {
@@ -357,8 +361,11 @@ __global__ __launch_bounds__(kSelThreads) void k_coarse_select(DevIndex ix, cons
     }
 #pragma unroll
     for (int i = 0; i < kSampleMax; ++i) {
-      const bool ok = i < m && (sgv[i][0] & mk[0]) == mk[0] && (sgv[i][1] & mk[1]) == mk[1] &&
-                      sig_live(sgv[i][0], sgv[i][1], ix.sig_words);
+      bool any = false;
+#pragma unroll
+      for (int g = 0; g < kMaxGroups; ++g)
+        any = any || (g < G && (sgv[i][0] & mk[g][0]) == mk[g][0] && (sgv[i][1] & mk[g][1]) == mk[g][1]);
+      const bool ok = i < m && any && sig_live(sgv[i][0], sgv[i][1], ix.sig_words);
       hitm |= ok ? 1u << i : 0u;
     }
     if (thr_mode == 0) {   // query path: every sample scored
@@ -652,6 +659,7 @@ struct ScanArgs {
   // redo of the tile path: only the queries marked for redo have chunks; their statistics were already
   // counted by the tile scan
   int32_t fallback;
+  int32_t G;   // masks per query: an item passes when it passes any of them
 };
 
 struct ScanLds {
@@ -906,9 +914,11 @@ __global__ __launch_bounds__(kScanThreads, kScanOcc) void k_scan(ScanArgs a) {
     int32_t *thr_q = a.w.thr + q;
     // query vector slice held by this lane, request mask
     const int4 qv = reinterpret_cast<const int4 *>(a.queries + (size_t)q * D)[sub];
-    uint64_t mk[W];
+    uint64_t mk[kMaxGroups][W];   // the query's masks (groups past G are never tested)
 #pragma unroll
-    for (int i = 0; i < W; ++i) mk[i] = a.masks[(size_t)q * W + i];
+    for (int g = 0; g < kMaxGroups; ++g)
+#pragma unroll
+      for (int i = 0; i < W; ++i) mk[g][i] = g < a.G ? a.masks[((size_t)q * a.G + g) * W + i] : 0ull;
     for (int i = tid; i < kQHistBins; i += kScanThreads) sm.qh[i] = 0u;
     if (tid == 0) sm.cnt = 0;
     // thr_s: proven bound of this workgroup (trims, histogram pulls); gthr: the query's global bound
@@ -1070,9 +1080,19 @@ __global__ __launch_bounds__(kScanThreads, kScanOcc) void k_scan(ScanArgs a) {
 #pragma unroll
       for (int gi = 0; gi < kScanGroups; ++gi) {
         const int i = gi * kScanThreads + wv * 64 + l;
-        bool pass = i < sg_n && sig_live(sg[gi][0], sg[gi][W - 1], W);
+        bool any = true;
 #pragma unroll
-        for (int u = 0; u < W; ++u) pass = pass && ((sg[gi][u] & mk[u]) == mk[u]);
+        for (int u = 0; u < W; ++u) any = any && ((sg[gi][u] & mk[0][u]) == mk[0][u]);
+#pragma unroll
+        for (int g = 1; g < kMaxGroups; ++g) {
+          if (g < a.G) {
+            bool pg = true;
+#pragma unroll
+            for (int u = 0; u < W; ++u) pg = pg && ((sg[gi][u] & mk[g][u]) == mk[g][u]);
+            any = any || pg;
+          }
+        }
+        const bool pass = i < sg_n && any && sig_live(sg[gi][0], sg[gi][W - 1], W);
         const uint64_t bal = __ballot(pass);
         if (pass) sm.wl[buf][wv * 64 * kScanGroups + nw + mbcnt(bal)] = (uint16_t)i;
         nw += __popcll(bal);
@@ -1612,7 +1632,8 @@ hipError_t launch_coarse_keys(const DevIndex &ix, const int8_t *queries, int32_t
 hipError_t launch_coarse_select(const DevIndex &ix, const int8_t *queries, const uint64_t *masks,
                                 const SearchShape &sh, const Work &w, hipStream_t s) {
   const int thr_mode = sh.path != kPathTile ? 0 : (sh.force_redo ? 2 : 1);
-  k_coarse_select<<<sh.B, kSelThreads, 0, s>>>(ix, queries, masks, sh.B, sh.nprobe, sh.k, sh.pool_cap, thr_mode, w);
+  k_coarse_select<<<sh.B, kSelThreads, 0, s>>>(ix, queries, masks, sh.G, sh.B, sh.nprobe, sh.k, sh.pool_cap,
+                                                thr_mode, w);
   return hipGetLastError();
 }
 
@@ -1633,7 +1654,7 @@ static void scan_w(const ScanArgs &a, int W, hipStream_t s) {
 
 hipError_t launch_scan(const DevIndex &ix, const int8_t *queries, const uint64_t *masks, const SearchShape &sh,
                        const Work &w, int fallback, hipStream_t s) {
-  ScanArgs a{ix, queries, masks, w, sh.B, sh.nprobe, sh.k, sh.P, fallback};
+  ScanArgs a{ix, queries, masks, w, sh.B, sh.nprobe, sh.k, sh.P, fallback, sh.G};
   switch (ix.dim) {
     case 16: scan_w<1>(a, ix.sig_words, s); break;
     case 32: scan_w<2>(a, ix.sig_words, s); break;

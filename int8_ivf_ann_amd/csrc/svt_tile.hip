@@ -40,13 +40,14 @@ namespace svt {
 // queries probing each cluster, and the log of the fraction of the cluster's items no member accepts
 // (members taken as independent, each with its sampled density); gcnt, gfill and clog are zeroed by
 // k_coarse_keys
-__global__ __launch_bounds__(256) void k_gcount(const int32_t *__restrict__ probes, int32_t nprobe, Work w) {
+__global__ __launch_bounds__(256) void k_gcount(const int32_t *__restrict__ probes, int32_t nprobe, int32_t GT,
+                                                Work w) {
   const int b = blockIdx.x;
   const float dens = w.qdens[b];
   const float lg = log1pf(-(dens < 0.999f ? dens : 0.999f));
   for (int j = threadIdx.x; j < nprobe; j += 256) {
     const int c = probes[(size_t)b * nprobe + j];
-    atomicAdd(&w.gcnt[c], 1);
+    atomicAdd(&w.gcnt[c], GT);   // one member per mask (GT of them, see k_gfill)
     atomicAdd(&w.clog[c], lg);
   }
 }
@@ -168,17 +169,22 @@ __global__ __launch_bounds__(256) void k_tchunks(DevIndex ix, int32_t max_tchunk
   w.ctab[i] = w.estart[c] + (size > 0 ? off / size : 0);
 }
 
-// the members of each probed cluster: the request mask, speculative threshold and index of every query
-// probing it (their order inside a cluster is arbitrary; it changes no result)
+// the members of each probed cluster: for every query probing it, GT consecutive members, one per request
+// mask (masks past the query's G pass nothing: every bit set), with the query's speculative threshold and
+// index.  The slots of a query's members start at a multiple of GT, and GT divides kTMembers, so they lie
+// in one entry, aligned.  The order of the queries inside a cluster is arbitrary; it changes no result.
 __global__ __launch_bounds__(256) void k_gfill(const int32_t *__restrict__ probes, const uint64_t *__restrict__ masks,
-                                               int32_t nprobe, int32_t W, Work w) {
+                                               int32_t nprobe, int32_t W, int32_t G, int32_t GT, Work w) {
   const int b = blockIdx.x;
-  const uint64_t m0 = masks[(size_t)b * W], m1 = W == 2 ? masks[(size_t)b * W + 1] : 0ull;
   const int32_t thr = w.sthr[b];
   for (int j = threadIdx.x; j < nprobe; j += 256) {
     const int c = probes[(size_t)b * nprobe + j];
-    const int slot = atomicAdd(&w.gfill[c], 1);
-    w.mrec[w.gstart[c] + slot] = MRec{m0, m1, thr, b};
+    const int slot = atomicAdd(&w.gfill[c], GT);
+    for (int g = 0; g < GT; ++g) {
+      const uint64_t *m = masks + ((size_t)b * G + (g < G ? g : 0)) * W;
+      const uint64_t m0 = g < G ? m[0] : ~0ull, m1 = g < G ? (W == 2 ? m[1] : 0ull) : ~0ull;
+      w.mrec[w.gstart[c] + slot + g] = MRec{m0, m1, thr, b};
+    }
   }
 }
 
@@ -242,6 +248,7 @@ struct TScanArgs {
   Work w;
   int32_t B, P;
   uint32_t pool_cap;
+  int32_t GT;   // consecutive members per query (one per request mask), aligned in an entry
 };
 
 #ifndef SVT_T_WIN_MEMBERS
@@ -293,6 +300,8 @@ __global__ __launch_bounds__(kScanThreads, kTOcc) void k_tscan(TScanArgs a) {
   const int n_ent = a.w.thdr[0];
   const uint32_t cap = a.pool_cap;
   int64_t *stats = a.w.stats;
+  const int GT = a.GT;
+  const uint32_t gmask = (1u << GT) - 1u;   // the member bits of one query, at its first member
   for (int i = l; i < kTSlotsW; i += 64) {
     S.scount[i] = 0u;
     S.selig[i] = 0u;
@@ -448,8 +457,11 @@ __global__ __launch_bounds__(kScanThreads, kTOcc) void k_tscan(TScanArgs a) {
             pass = pass && ((sg[g][1] & m1) == m1);
           }
           qm |= pass ? 1u << j : 0u;
-          if (stats) {
-            const int cnt = __popcll(__ballot(pass));
+        }
+        if (stats) {
+          // an item counts once per query: when any of the query's members (its masks) accepts it
+          for (int j = 0; j < fs_mc; j += GT) {
+            const int cnt = __popcll(__ballot((qm & (gmask << j)) != 0u));
             if (l == 0 && cnt > 0) {
               if (fs_slot != kNoSlot)
                 S.selig[fs_slot + j] += (uint32_t)cnt;
@@ -525,7 +537,7 @@ __global__ __launch_bounds__(kScanThreads, kTOcc) void k_tscan(TScanArgs a) {
         for (;;) {
           const MRec &m = S.wm[mb0 + j];
           offer(qm != 0u && sub == 0 && acc >= m.thr, acc, bpos, slot0, j, m.q);
-          qm &= qm - 1u;
+          qm &= ~(gmask << (j & ~(GT - 1)));   // the query of member j is done, whichever of its masks passed
           if (__ballot(qm != 0u) == 0ull) break;
           // a further member accepts this row: the same row against its query vector
           j = qm ? __builtin_ctz(qm) : 0;
@@ -614,10 +626,12 @@ struct XScanArgs {
   Work w;
   int32_t B, n_qb;
   uint32_t cap;       // pool keys (main pass) or sample-buffer entries (sample pass) per query
+  int32_t G;          // masks per query (an item is eligible under any of them)
 };
 
 struct XWave {
-  uint32_t mk[kXQ][4];       // request masks of the block's queries (32-bit words)
+  uint32_t mk[kXQ][4];                     // first request mask of the block's queries (32-bit words)
+  uint32_t mkx[kXQ][kMaxGroups - 1][4];    //   and their further masks
   int32_t sc[32][64];        // a step's scores, when it has candidates (entry 8 t + 4 t2 + r, lane)
   uint64_t key[kXStage];     // staged candidates: (score, position) keys
   uint8_t qi[kXStage];       //   their query within the block
@@ -626,7 +640,7 @@ struct XWave {
   uint32_t base[kXQ];        // pool positions reserved at a flush
 };
 
-template <int KS, int W, bool SAMPLE>
+template <int KS, int W, bool SAMPLE, bool MULTI>
 __global__ __launch_bounds__(64 * kXWaves, kXOcc) void k_xscan(XScanArgs a) {
   constexpr int XNB = KS >= 4 ? 2 : kXBuffers;   // step buffers in registers
   constexpr int IS = SAMPLE ? kXStride : 1;   // catalogue positions between stream items
@@ -665,12 +679,14 @@ __global__ __launch_bounds__(64 * kXWaves, kXOcc) void k_xscan(XScanArgs a) {
   // score) and its count is not written.
   if (l < kXQ) {
     const int qc = q0 + l < a.B ? q0 + l : 0;
+    for (int g = 0; g < a.G; ++g)
 #pragma unroll
-    for (int ww = 0; ww < W; ++ww) {
-      const uint64_t m = a.masks[(size_t)qc * W + ww];
-      S.mk[l][2 * ww] = (uint32_t)m;
-      S.mk[l][2 * ww + 1] = (uint32_t)(m >> 32);
-    }
+      for (int ww = 0; ww < W; ++ww) {
+        const uint64_t m = a.masks[((size_t)qc * a.G + g) * W + ww];
+        uint32_t *dst = g == 0 ? S.mk[l] : S.mkx[l][g - 1];
+        dst[2 * ww] = (uint32_t)m;
+        dst[2 * ww + 1] = (uint32_t)(m >> 32);
+      }
     S.cnt[l] = 0u;
   }
   wave_lds_sync();
@@ -777,16 +793,26 @@ __global__ __launch_bounds__(64 * kXWaves, kXOcc) void k_xscan(XScanArgs a) {
     for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        uint32_t mq[MW];   // the mask of this lane's query 16 t2 + 4 lg + r
+        uint32_t mq[MW];   // the first mask of this lane's query 16 t2 + 4 lg + r
+        const int qi = 16 * t2 + 4 * lg + r;
 #pragma unroll
-        for (int ww = 0; ww < MW; ++ww) mq[ww] = S.mk[16 * t2 + 4 * lg + r][ww];
+        for (int ww = 0; ww < MW; ++ww) mq[ww] = S.mk[qi][ww];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           const bool item_ok = p0 + 16 * t + lr < NP && live[t];
           uint32_t x = 0u;
 #pragma unroll
           for (int ww = 0; ww < MW; ++ww) x |= mq[ww] & ns[t][ww];
-          const bool el = item_ok && x == 0u;
+          bool pass = x == 0u;
+          if constexpr (MULTI) {
+            for (int g = 1; g < a.G; ++g) {   // further masks of the query: eligible under any of them
+              uint32_t xg = 0u;
+#pragma unroll
+              for (int ww = 0; ww < MW; ++ww) xg |= S.mkx[qi][g - 1][ww] & ns[t][ww];
+              pass = pass || xg == 0u;
+            }
+          }
+          const bool el = item_ok && pass;
           if constexpr (SAMPLE) {
             const int32_t cur = (int32_t)ec[t2][r], sc = acc[t][t2][r];
             ec[t2][r] = (uint32_t)(el && sc > cur ? sc : cur);
@@ -1073,10 +1099,10 @@ __global__ __launch_bounds__(kSelThreads) void k_pmerge(PMergeArgs a) {
 
 hipError_t launch_tile_plan(const DevIndex &ix, const uint64_t *masks, const SearchShape &sh, const Work &w,
                             hipStream_t s) {
-  k_gcount<<<sh.B, 256, 0, s>>>(w.probes, sh.nprobe, w);
+  k_gcount<<<sh.B, 256, 0, s>>>(w.probes, sh.nprobe, sh.GT, w);
   k_tplan1<<<(ix.nlist + kSelThreads - 1) / kSelThreads, kSelThreads, 0, s>>>(ix, w);
   k_tplan2<<<(ix.nlist + kSelThreads - 1) / kSelThreads + 1, kSelThreads, 0, s>>>(ix, sh.TP, w);
-  k_gfill<<<sh.B, 256, 0, s>>>(w.probes, masks, sh.nprobe, ix.sig_words, w);
+  k_gfill<<<sh.B, 256, 0, s>>>(w.probes, masks, sh.nprobe, ix.sig_words, sh.G, sh.GT, w);
   k_tentries<<<(sh.max_entries + 255) / 256, 256, 0, s>>>(ix, sh.max_entries, w);
   k_tchunks<<<(sh.max_tchunks + 256) / 256, 256, 0, s>>>(ix, sh.max_tchunks, w);
   return hipGetLastError();
@@ -1092,7 +1118,7 @@ static void tscan_w(const TScanArgs &a, int W, hipStream_t s) {
 
 hipError_t launch_tscan(const DevIndex &ix, const int8_t *queries, const SearchShape &sh, const Work &w,
                         hipStream_t s) {
-  TScanArgs a{ix, queries, w, sh.B, sh.TP, (uint32_t)sh.pool_cap};
+  TScanArgs a{ix, queries, w, sh.B, sh.TP, (uint32_t)sh.pool_cap, sh.GT};
   switch (ix.dim) {
     case 16: tscan_w<1>(a, ix.sig_words, s); break;
     case 32: tscan_w<2>(a, ix.sig_words, s); break;
@@ -1125,10 +1151,14 @@ int tscan_blocks_per_cu(int32_t dim, int32_t sig_words) {
 
 template <int KS, bool SAMPLE>
 static void xscan_w(const XScanArgs &a, int W, int grid, hipStream_t s) {
-  if (W == 2)
-    k_xscan<KS, 2, SAMPLE><<<grid, 64 * kXWaves, 0, s>>>(a);
-  else
-    k_xscan<KS, 1, SAMPLE><<<grid, 64 * kXWaves, 0, s>>>(a);
+  const bool multi = a.G > 1;   // requests of several masks: a variant, so that one mask costs nothing more
+  if (W == 2) {
+    if (multi) k_xscan<KS, 2, SAMPLE, true><<<grid, 64 * kXWaves, 0, s>>>(a);
+    else k_xscan<KS, 2, SAMPLE, false><<<grid, 64 * kXWaves, 0, s>>>(a);
+  } else {
+    if (multi) k_xscan<KS, 1, SAMPLE, true><<<grid, 64 * kXWaves, 0, s>>>(a);
+    else k_xscan<KS, 1, SAMPLE, false><<<grid, 64 * kXWaves, 0, s>>>(a);
+  }
 }
 
 template <bool SAMPLE>
@@ -1152,16 +1182,16 @@ int xscan_blocks_per_cu(int32_t dim, int32_t sig_words) {
     case 16:
     case 32:
     case 64:
-      e = w2 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_xscan<1, 2, false>, 64 * kXWaves, 0)
-             : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_xscan<1, 1, false>, 64 * kXWaves, 0);
+      e = w2 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_xscan<1, 2, false, false>, 64 * kXWaves, 0)
+             : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_xscan<1, 1, false, false>, 64 * kXWaves, 0);
       break;
     case 128:
-      e = w2 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_xscan<2, 2, false>, 64 * kXWaves, 0)
-             : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_xscan<2, 1, false>, 64 * kXWaves, 0);
+      e = w2 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_xscan<2, 2, false, false>, 64 * kXWaves, 0)
+             : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_xscan<2, 1, false, false>, 64 * kXWaves, 0);
       break;
     case 256:
-      e = w2 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_xscan<4, 2, false>, 64 * kXWaves, 0)
-             : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_xscan<4, 1, false>, 64 * kXWaves, 0);
+      e = w2 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_xscan<4, 2, false, false>, 64 * kXWaves, 0)
+             : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_xscan<4, 1, false, false>, 64 * kXWaves, 0);
       break;
     default: return 0;
   }
@@ -1175,12 +1205,12 @@ hipError_t launch_exh_scan(const DevIndex &ix, const int8_t *queries, const uint
   // every query block needs a wave: at least n_qb waves in the grid
   const int grid = std::max(sh.XP, (n_qb + kXWaves - 1) / kXWaves);
   // sample pass, thresholds, main pass
-  XScanArgs as{ix, queries, masks, w, sh.B, n_qb, (uint32_t)sh.scap};
+  XScanArgs as{ix, queries, masks, w, sh.B, n_qb, (uint32_t)sh.scap, sh.G};
   hipError_t e = xscan_dim<true>(as, ix.dim, ix.sig_words, grid, s);
   if (e != hipSuccess) return e;
   k_xthr<<<sh.B, kSelThreads, 0, s>>>(w, N, sh.k, sh.pool_cap, sh.scap, (int32_t)((N + kXStride - 1) / kXStride),
                                       sh.force_redo);
-  XScanArgs am{ix, queries, masks, w, sh.B, n_qb, (uint32_t)sh.pool_cap};
+  XScanArgs am{ix, queries, masks, w, sh.B, n_qb, (uint32_t)sh.pool_cap, sh.G};
   e = xscan_dim<false>(am, ix.dim, ix.sig_words, grid, s);
   if (e != hipSuccess) return e;
   return hipGetLastError();

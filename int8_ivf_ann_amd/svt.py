@@ -20,6 +20,7 @@ SVT_MAX_K = 2048
 SVT_MAX_SIG_WORDS = 2
 SVT_PATH_AUTO, SVT_PATH_QUERY, SVT_PATH_TILE, SVT_PATH_EXHAUSTIVE = 0, 1, 2, 3
 SVT_OPT_MERGE_FROM_SLOTS, SVT_OPT_FORCE_REDO = 1, 2
+SVT_MAX_MASK_GROUPS = 4
 SVT_NOALLOC_SCRATCH_BYTES = 256 << 20
 _PATHS = {"auto": SVT_PATH_AUTO, "query": SVT_PATH_QUERY, "tile": SVT_PATH_TILE}
 
@@ -54,18 +55,30 @@ class svt_search_options(ctypes.Structure):
         ("path", ctypes.c_int32),
         ("pool_keys", ctypes.c_int32),
         ("flags", ctypes.c_uint32),
-        ("reserved", ctypes.c_int32 * 5),
+        ("mask_groups", ctypes.c_int32),
+        ("reserved", ctypes.c_int32 * 4),
     ]
 
 
-def make_options(path="auto", pool_keys: int = 0, flags: int = 0) -> svt_search_options:
+def make_options(path="auto", pool_keys: int = 0, flags: int = 0, mask_groups: int = 0) -> svt_search_options:
     """Search options: path "auto" | "query" | "tile" (or an SVT_PATH_* value), pool_keys (tile path,
-    0 = default), flags (OR of SVT_OPT_*)."""
+    0 = default), flags (OR of SVT_OPT_*), mask_groups (masks per query, 0 or 1: one)."""
     o = svt_search_options()
     o.path = _PATHS[path] if isinstance(path, str) else int(path)
     o.pool_keys = int(pool_keys)
     o.flags = int(flags)
+    o.mask_groups = int(mask_groups)
     return o
+
+
+def _with_groups(opts, G: int):
+    """The options to pass for masks of G groups (a copy with mask_groups set; G must agree with it)."""
+    if opts is None:
+        return make_options(mask_groups=G) if G > 1 else None
+    have = max(1, int(opts.mask_groups))
+    if have != G:
+        raise ValueError(f"masks carry {G} groups per query but the options say mask_groups={opts.mask_groups}")
+    return opts
 
 
 _lib = None
@@ -274,7 +287,12 @@ def _search_tensors(handle, queries, masks, k, query_scales, out_ids, out_scores
     B = int(queries.shape[0])
     dev = queries.device
     _check_tensor("queries", queries, (torch.int8,), (B, dim))
-    _check_tensor("masks", masks, (torch.int64, torch.uint64), (B, W), dev)
+    if not hasattr(masks, "shape") or len(masks.shape) not in (2, 3):
+        raise ValueError("masks: expected a tensor [B, W] or [B, G, W]")
+    G = int(masks.shape[1]) if len(masks.shape) == 3 else 1
+    if not 1 <= G <= SVT_MAX_MASK_GROUPS:
+        raise ValueError(f"masks: {G} groups per query, at most {SVT_MAX_MASK_GROUPS}")
+    _check_tensor("masks", masks, (torch.int64, torch.uint64), (B, G, W) if len(masks.shape) == 3 else (B, W), dev)
     _check_tensor("query_scales", query_scales, (torch.float32,), (B,), dev, nullable=True)
     if out_ids is None:
         out_ids = torch.empty((B, k), dtype=torch.int64, device=dev)
@@ -291,7 +309,7 @@ def _search_tensors(handle, queries, masks, k, query_scales, out_ids, out_scores
     _check_tensor("out_fscores", out_fscores, (torch.float32,), (B, k), dev)
     _check_tensor("out_counts", out_counts, (torch.int32,), (B,), dev)
     _check_tensor("out_stats", out_stats, (torch.int64,), (B, 2), dev)
-    return B, dev, (out_ids, out_scores, out_fscores, out_counts, out_stats)
+    return B, dev, G, (out_ids, out_scores, out_fscores, out_counts, out_stats)
 
 
 def svt_search(handle, queries, masks, nprobe: int, k: int, query_scales=None, out_ids=None, out_scores=None,
@@ -301,8 +319,9 @@ def svt_search(handle, queries, masks, nprobe: int, k: int, query_scales=None, o
     outputs are allocated with torch unless passed in.  Asynchronous on ``stream``.  ``opts``: a
     svt_search_options (see make_options) or None."""
     import torch
-    B, dev, outs = _search_tensors(handle, queries, masks, k, query_scales, out_ids, out_scores, out_fscores,
-                                   out_counts, out_stats)
+    B, dev, G, outs = _search_tensors(handle, queries, masks, k, query_scales, out_ids, out_scores, out_fscores,
+                                      out_counts, out_stats)
+    opts = _with_groups(opts, G)
     if workspace is None:
         nbytes = svt_search_workspace_size(handle, B, nprobe, k, opts) if B > 0 else 0
         workspace = torch.empty((max(nbytes, 256),), dtype=torch.uint8, device=dev)
@@ -317,8 +336,9 @@ def svt_search_noalloc(handle, queries, masks, nprobe: int, k: int, query_scales
                        out_scores=None, out_fscores=None, out_counts=None, out_stats=None, stream=None, opts=None):
     """svt_search with the library's static scratch as workspace (the C call allocates no device memory;
     outputs not passed in are still allocated here, by torch).  Searches on one GPU must not overlap."""
-    B, dev, outs = _search_tensors(handle, queries, masks, k, query_scales, out_ids, out_scores, out_fscores,
-                                   out_counts, out_stats)
+    B, dev, G, outs = _search_tensors(handle, queries, masks, k, query_scales, out_ids, out_scores, out_fscores,
+                                      out_counts, out_stats)
+    opts = _with_groups(opts, G)
     _check(lib().svt_search_noalloc(handle, B, _t_ptr(queries), _t_ptr(masks), _t_ptr(query_scales), nprobe, k,
                                     *[_t_ptr(t) for t in outs], _opt_ptr(opts), _stream_ptr(stream)))
     return outs
@@ -363,6 +383,8 @@ class Index:
 
     def search(self, queries, masks, nprobe: int, k: int, query_scales=None, stream=None, opts=None, **outs):
         B = int(queries.shape[0])
+        if hasattr(masks, "shape") and len(masks.shape) == 3:
+            opts = _with_groups(opts, int(masks.shape[1]))
         ws = self.workspace(B, nprobe, k, opts) if B > 0 else None
         return svt_search(self.handle, queries, masks, nprobe, k, query_scales=query_scales, workspace=ws,
                           stream=stream, opts=opts, **outs)

@@ -61,7 +61,11 @@ def check_invariants(items, sigs, list_of, got, masks, queries, k, centroids=Non
         key = list(zip((-s).tolist(), i.tolist()))
         assert key == sorted(key)
         if n:
-            assert np.all((sigs[i] & masks[b]) == masks[b])
+            mb = masks[b] if masks.ndim == 3 else masks[b][None, :]   # eligible under any of the query's masks
+            ok = np.zeros(n, bool)
+            for m in mb:
+                ok |= np.all((sigs[i] & m) == m, axis=1)
+            assert np.all(ok)
             assert np.array_equal(items[i].astype(np.int64) @ queries[b].astype(np.int64), s)
             if orc is not None:
                 probes, _ = orc.coarse(centroids, queries[b], nprobe)

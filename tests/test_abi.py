@@ -113,17 +113,19 @@ def test_search_rejects_dead_index(L):
 
 
 def test_options_struct_layout():
-    # 8 words: path, pool_keys, flags, 5 reserved (must stay in step with include/svt.h)
+    # 8 words: path, pool_keys, flags, mask_groups, 4 reserved (must stay in step with include/svt.h)
     assert ctypes.sizeof(svt.svt_search_options) == 32
     o = svt.make_options("tile", 64, svt.SVT_OPT_FORCE_REDO)
     assert (o.path, o.pool_keys, o.flags) == (svt.SVT_PATH_TILE, 64, 2)
-    assert list(o.reserved) == [0] * 5
+    assert list(o.reserved) == [0] * 4 and o.mask_groups == 0
+    assert svt.make_options(mask_groups=3).mask_groups == 3
     hdr = open(os.path.join(ROOT, "include", "svt.h")).read()
     for name, v in (("SVT_PATH_AUTO", 0), ("SVT_PATH_QUERY", 1), ("SVT_PATH_TILE", 2), ("SVT_PATH_EXHAUSTIVE", 3)):
         assert re.search(rf"{name} = {v}\b", hdr), name
     assert re.search(r"#define SVT_OPT_MERGE_FROM_SLOTS 1u", hdr)
     assert re.search(r"#define SVT_OPT_FORCE_REDO 2u", hdr)
     assert re.search(r"SVT_ENOSPACE = -6", hdr) and svt.SVT_ENOSPACE == -6
+    assert re.search(r"#define SVT_MAX_MASK_GROUPS 4", hdr) and svt.SVT_MAX_MASK_GROUPS == 4
     assert re.search(r"#define SVT_NOALLOC_SCRATCH_BYTES \(\(size_t\)256 << 20\)", hdr)
     assert svt.SVT_NOALLOC_SCRATCH_BYTES == 256 << 20
 

@@ -67,6 +67,8 @@ def test_search_argument_errors(env):
         ("unknown path", dict(opts=svt.make_options(7)), svt.SVT_EINVAL),
         ("negative pool_keys", dict(opts=svt.make_options("tile", -1)), svt.SVT_EINVAL),
         ("unknown flag", dict(opts=svt.make_options("auto", 0, 8)), svt.SVT_EINVAL),
+        ("mask_groups = 5", dict(opts=svt.make_options("auto", 0, 0, 5)), svt.SVT_EINVAL),
+        ("mask_groups < 0", dict(opts=svt.make_options("tile", 0, 0, -1)), svt.SVT_EINVAL),
     ]
     o = svt.make_options()
     o.reserved[2] = 1

@@ -123,6 +123,22 @@ def test_exhaustive_several_query_blocks(svt, opts):
     _run(svt, opts, items, sigs, cl, cent, 2.0, q, masks, 20, 2048, "exh-70q-k2048")
 
 
+@pytest.mark.parametrize("G", [2, 3, 4])
+def test_several_masks_per_query(svt, opts, G):
+    # requests of G masks: an item is eligible when it passes any of them (one group of a query makes
+    # every item eligible, another query pads its last group with a mask that passes nothing)
+    rng = np.random.default_rng(40 + G)
+    items, sigs, cl, cent = P.small_catalogue(rng, n=9000, d=64, nlist=30, W=2, empty_clusters=3)
+    B = 37
+    q = rng.integers(-127, 128, (B, 64)).astype(np.int8)
+    masks = np.stack([P.random_masks(rng, B, 2, nbits_max=4) for _ in range(G)], axis=1)
+    masks[3, G - 1] = 0
+    masks[5, G - 1] = ~np.uint64(0)
+    o = svt.make_options(opts.path, opts.pool_keys, opts.flags, G)
+    for nprobe, k in ((4, 120), (30, 400)):
+        _run(svt, o, items, sigs, cl, cent, 2.0, q, masks, nprobe, k, f"groups{G}-{nprobe}-{k}")
+
+
 def test_large_k_many_candidates(svt, opts):
     # every query keeps ~40k candidates: LDS lists are cut many times and the merge selects
     rng = np.random.default_rng(7)

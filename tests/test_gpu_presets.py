@@ -50,18 +50,22 @@ class Preset:
         assert np.array_equal(masks, o_masks)
         return qs.queries, masks
 
-    def check(self, B, offset, nprobe=None, k=None, label="", paths=("query", "tile")):
+    def check(self, B, offset, nprobe=None, k=None, label="", paths=("query", "tile"), groups=1):
         from int8_ivf_ann_amd import svt as svt_mod
         nprobe = nprobe or self.cfg["nprobe"]
         k = k or self.cfg["k"]
-        q, masks = self.batch(B, offset)
+        q, masks = self.batch(B + groups - 1, offset)
+        if groups > 1:
+            # a request of several masks: query b also accepts the attribute sets of queries b + 1 ..
+            masks = np.stack([masks[g:g + B] for g in range(groups)], axis=1)
+        q = np.ascontiguousarray(q[:B])
         t = time.time()
         ref = oracle.Oracle().search(self.cat.items, self.sigs, self.cat.list_of, self.cat.centroids,
                                      self.cat.item_scale, q, masks, nprobe, k, n_threads=16)
         say(f"{label}: oracle on {B} queries {time.time() - t:.1f}s; eligible/query median "
             f"{int(np.median(ref[4][:, 1]))}")
         for path in paths:
-            opts = svt_mod.make_options(path)
+            opts = svt_mod.make_options(path, mask_groups=groups)
             t = time.time()
             got = gpu_search(self.ix, q, masks, nprobe, k, opts=opts)
             say(f"{label} [{path}]: B={B} gpu search {1e3 * (time.time() - t):.1f} ms (incl. copies)")
@@ -111,3 +115,7 @@ def test_10m_batch64_other(p10m):
 
 def test_10m_batch256(p10m):
     p10m.check(256, 10_000, label="10m-b256")
+
+
+def test_10m_batch256_three_masks(p10m):
+    p10m.check(256, 30_000, groups=3, label="10m-b256-groups3")
