@@ -88,6 +88,7 @@ struct svt_index {
   int32_t *d_perm = nullptr;
   int32_t *d_offsets = nullptr;
   int32_t *d_live = nullptr;
+  int32_t *d_slot_of = nullptr;                // [max(n_items, id_capacity)] slot of each id (-1: absent)
   int8_t *d_centroids = nullptr;
   int64_t n_live = 0;                          // items (not free slots)
   // updatable index: the host's record of the layout, which chooses every update's slot
@@ -112,6 +113,7 @@ static void free_index_memory(svt_index *ix) {
   if (ix->d_perm) (void)hipFree(ix->d_perm);
   if (ix->d_offsets) (void)hipFree(ix->d_offsets);
   if (ix->d_live) (void)hipFree(ix->d_live);
+  if (ix->d_slot_of) (void)hipFree(ix->d_slot_of);
   if (ix->d_centroids) (void)hipFree(ix->d_centroids);
   if (ix->d_stage) (void)hipFree(ix->d_stage);
 }
@@ -201,11 +203,9 @@ int upload(const svt_index_desc *d, bool updatable, int64_t id_capacity, int32_t
     ix->xscan_wgs = std::min(kMaxScanWGs, std::max(64, prop.multiProcessorCount * x_per_cu));
   }
 
-  int32_t *d_pos_of = nullptr;
   int8_t *stage_rows = nullptr;
   uint64_t *stage_sigs = nullptr;
   auto cleanup_fail = [&](hipError_t err, const char *what) {
-    if (d_pos_of) (void)hipFree(d_pos_of);
     if (stage_rows) (void)hipFree(stage_rows);
     if (stage_sigs) (void)hipFree(stage_sigs);
     free_index_memory(ix);
@@ -234,11 +234,18 @@ int upload(const svt_index_desc *d, bool updatable, int64_t id_capacity, int32_t
   if (n_slots > 0 &&
       (e = hipMemcpyAsync(ix->d_perm, perm.data(), (size_t)n_slots * sizeof(int32_t), hipMemcpyHostToDevice, s)) != hipSuccess)
     return cleanup_fail(e, "copy perm");
+  // id -> slot: the uploaded ids, then (updatable) the ids not yet used
+  const int64_t n_ids = std::max<int64_t>(n, updatable ? id_capacity : 0);
+  if ((e = hipMalloc(&ix->d_slot_of, (size_t)std::max<int64_t>(n_ids, 1) * sizeof(int32_t))) != hipSuccess)
+    return cleanup_fail(e, "hipMalloc(slot_of)");
+  if (n_ids > n &&
+      (e = hipMemsetAsync(ix->d_slot_of + n, 0xFF, (size_t)(n_ids - n) * sizeof(int32_t), s)) != hipSuccess)
+    return cleanup_fail(e, "fill slot_of");
+  if (n > 0 &&
+      (e = hipMemcpyAsync(ix->d_slot_of, pos_of.data(), (size_t)n * sizeof(int32_t), hipMemcpyHostToDevice, s)) != hipSuccess)
+    return cleanup_fail(e, "copy slot_of");
   if (n > 0) {
-    // rows and signatures: staged in bounded chunks, scattered on the device to their positions
-    if ((e = hipMalloc(&d_pos_of, (size_t)n * sizeof(int32_t))) != hipSuccess) return cleanup_fail(e, "hipMalloc(pos_of)");
-    if ((e = hipMemcpyAsync(d_pos_of, pos_of.data(), (size_t)n * sizeof(int32_t), hipMemcpyHostToDevice, s)) != hipSuccess)
-      return cleanup_fail(e, "copy pos_of");
+    // rows and signatures: staged in bounded chunks, scattered on the device to their slots
     const int64_t chunk = std::min<int64_t>(n, std::max<int64_t>(1, (int64_t(256) << 20) / dim));
     if ((e = hipMalloc(&stage_rows, (size_t)chunk * dim)) != hipSuccess) return cleanup_fail(e, "hipMalloc(stage)");
     if ((e = hipMalloc(&stage_sigs, (size_t)chunk * W * sizeof(uint64_t))) != hipSuccess) return cleanup_fail(e, "hipMalloc(stage)");
@@ -248,14 +255,13 @@ int upload(const svt_index_desc *d, bool updatable, int64_t id_capacity, int32_t
         return cleanup_fail(e, "copy rows");
       if ((e = hipMemcpyAsync(stage_sigs, d->sigs + (size_t)i0 * W, (size_t)m * W * sizeof(uint64_t), hipMemcpyHostToDevice, s)) != hipSuccess)
         return cleanup_fail(e, "copy sigs");
-      if ((e = launch_scatter_rows(stage_rows, stage_sigs, d_pos_of, i0, m, dim, W, ix->d_items, ix->d_sigs, s)) != hipSuccess)
+      if ((e = launch_scatter_rows(stage_rows, stage_sigs, ix->d_slot_of, i0, m, dim, W, ix->d_items, ix->d_sigs, s)) != hipSuccess)
         return cleanup_fail(e, "scatter rows");
       // the staging buffers are reused by the next chunk
       if ((e = hipStreamSynchronize(s)) != hipSuccess) return cleanup_fail(e, "upload sync");
     }
   }
   if ((e = hipStreamSynchronize(s)) != hipSuccess) return cleanup_fail(e, "upload sync");
-  if (d_pos_of) (void)hipFree(d_pos_of);
   if (stage_rows) (void)hipFree(stage_rows);
   if (stage_sigs) (void)hipFree(stage_sigs);
 
@@ -264,6 +270,8 @@ int upload(const svt_index_desc *d, bool updatable, int64_t id_capacity, int32_t
   ix->dev.perm = ix->d_perm;
   ix->dev.offsets = ix->d_offsets;
   ix->dev.live = ix->d_live;
+  ix->dev.slot_of = ix->d_slot_of;
+  ix->dev.n_ids = n_ids;
   ix->dev.centroids = ix->d_centroids;
   ix->dev.n_items = n_slots;
   ix->dev.dim = dim;
@@ -384,7 +392,7 @@ int apply_updates(svt_index *ix, const std::vector<UpdOp> &ops, const int8_t *ro
     return fail_hip(e, who);
   if (sigs && (e = hipMemcpyAsync(base + ob + rb, sigs, sb, hipMemcpyHostToDevice, s)) != hipSuccess)
     return fail_hip(e, who);
-  if ((e = launch_updates(ix->d_items, ix->d_sigs, ix->d_perm, ix->d_live, (const UpdOp *)base, n,
+  if ((e = launch_updates(ix->d_items, ix->d_sigs, ix->d_perm, ix->d_live, ix->d_slot_of, (const UpdOp *)base, n,
                           rows ? (const int8_t *)(base + ob) : nullptr,
                           sigs ? (const uint64_t *)(base + ob + rb) : nullptr, dim, W, s)) != hipSuccess)
     return fail_hip(e, who);
@@ -435,7 +443,7 @@ extern "C" int svt_index_delete(svt_index *ix, int32_t n, const int64_t *ids, vo
   for (int32_t i = 0; i < n; ++i) {
     const int32_t p = ix->slot_of[(size_t)ids[i]];
     const int32_t c = cluster_of_slot(ix, p);
-    ops[(size_t)i] = UpdOp{p, -1, c, kUpdDelete};
+    ops[(size_t)i] = UpdOp{p, (int32_t)ids[i], c, kUpdDelete};
     ix->slot_of[(size_t)ids[i]] = -1;
   }
   // freed slots go back on top of their clusters' stacks, lowest slot last pushed

@@ -54,8 +54,10 @@ struct DevIndex {
   const int32_t *perm;      // [n]         id of the item in each slot (-1: free)
   const int32_t *offsets;   // [nlist + 1]
   const int32_t *live;      // [nlist]     items (not free slots) of each cluster
+  const int32_t *slot_of;   // [n_ids]     slot of each id (-1: not in the index)
   const int8_t *centroids;  // [nlist][dim]
   int64_t n_items;          // slots
+  int64_t n_ids;            // ids: [0, n_ids)
   int32_t dim, sig_words, nlist;
   float item_scale;
 };
@@ -270,14 +272,15 @@ hipError_t launch_pool_merge(const DevIndex &ix, const float *query_scales, cons
 int scan_blocks_per_cu(int32_t dim, int32_t sig_words);
 int tscan_blocks_per_cu(int32_t dim, int32_t sig_words);
 int xscan_blocks_per_cu(int32_t dim, int32_t sig_words);
-// one update of an updatable index: the slot it writes, the item's id (insert), its cluster, the kind
+// one update of an updatable index: the slot it writes, the item's id, its cluster, the kind
 struct UpdOp {
   int32_t pos, id, cluster, kind;   // kind: kUpdInsert, kUpdDelete, kUpdResign
 };
 constexpr int32_t kUpdInsert = 0, kUpdDelete = 1, kUpdResign = 2;
 // applies n updates (rows[i] / sigs[i]: the payload of update i, where its kind has one)
-hipError_t launch_updates(int8_t *items, uint64_t *sigs, int32_t *perm, int32_t *live, const UpdOp *ops, int32_t n,
-                          const int8_t *rows, const uint64_t *new_sigs, int32_t dim, int32_t sig_words, hipStream_t s);
+hipError_t launch_updates(int8_t *items, uint64_t *sigs, int32_t *perm, int32_t *live, int32_t *slot_of,
+                          const UpdOp *ops, int32_t n, const int8_t *rows, const uint64_t *new_sigs, int32_t dim,
+                          int32_t sig_words, hipStream_t s);
 hipError_t launch_scatter_rows(const int8_t *src_rows, const uint64_t *src_sigs, const int32_t *pos_of,
                                int64_t i0, int64_t n, int32_t dim, int32_t sig_words, int8_t *dst_rows,
                                uint64_t *dst_sigs, hipStream_t s);

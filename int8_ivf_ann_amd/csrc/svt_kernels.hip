@@ -1586,7 +1586,7 @@ __global__ __launch_bounds__(256) void k_scatter_rows(const int8_t *__restrict__
 // the slot's signature is replaced.  Every update of one batch writes a different slot.
 __global__ __launch_bounds__(256) void k_updates(int8_t *__restrict__ items, uint64_t *__restrict__ sigs,
                                                  int32_t *__restrict__ perm, int32_t *__restrict__ live,
-                                                 const UpdOp *__restrict__ ops, int32_t n,
+                                                 int32_t *__restrict__ slot_of, const UpdOp *__restrict__ ops, int32_t n,
                                                  const int8_t *__restrict__ rows, const uint64_t *__restrict__ new_sigs,
                                                  int32_t chunks, int32_t sig_words) {
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -1605,9 +1605,11 @@ __global__ __launch_bounds__(256) void k_updates(int8_t *__restrict__ items, uin
   if (c == 0) {
     if (op.kind == kUpdInsert) {
       perm[p] = op.id;
+      slot_of[op.id] = (int32_t)p;
       atomicAdd(&live[op.cluster], 1);
     } else if (op.kind == kUpdDelete) {
       perm[p] = -1;
+      slot_of[op.id] = -1;
       atomicAdd(&live[op.cluster], -1);
     }
   }
@@ -1699,13 +1701,14 @@ hipError_t launch_merge(const DevIndex &ix, const float *query_scales, const Sea
   return hipGetLastError();
 }
 
-hipError_t launch_updates(int8_t *items, uint64_t *sigs, int32_t *perm, int32_t *live, const UpdOp *ops, int32_t n,
-                          const int8_t *rows, const uint64_t *new_sigs, int32_t dim, int32_t sig_words, hipStream_t s) {
+hipError_t launch_updates(int8_t *items, uint64_t *sigs, int32_t *perm, int32_t *live, int32_t *slot_of,
+                          const UpdOp *ops, int32_t n, const int8_t *rows, const uint64_t *new_sigs, int32_t dim,
+                          int32_t sig_words, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   const int32_t chunks = dim / 16;
   const int64_t threads = (int64_t)n * chunks;
-  k_updates<<<(unsigned)((threads + 255) / 256), 256, 0, s>>>(items, sigs, perm, live, ops, n, rows, new_sigs, chunks,
-                                                                sig_words);
+  k_updates<<<(unsigned)((threads + 255) / 256), 256, 0, s>>>(items, sigs, perm, live, slot_of, ops, n, rows, new_sigs,
+                                                                chunks, sig_words);
   return hipGetLastError();
 }
 
