@@ -255,6 +255,48 @@ int svt_search_noalloc(const svt_index *ix, int32_t n_queries, const int8_t *que
                        float *out_fscores, int32_t *out_counts, int64_t *out_stats, const svt_search_options *opts,
                        void *hip_stream);
 
+/*
+ * svt_rerank - re-score each query's retrieved candidates with a small gated mixture of experts over
+ * the query-candidate interaction, fused with the fetch of the candidates' rows and the final top-k
+ * ["SilverTorch - Index as Model", recommendation-quality section: retrieved candidates re-scored by
+ *  neural modules (MLP, mixture of logits, multi-task heads); "Meta Andromeda" summary, System section:
+ *  embedding fetch, interaction and scoring in one kernel with intermediates on chip].  The pages give no
+ * formula; this library computes, in float32, for query q and candidate row x:
+ *   q^ = q / query_scale, x^ = x / item_scale, z = q^ * x^ (elementwise)
+ *   g  = softmax(gate_w q^ + gate_b)                      (E experts)
+ *   r  = sum_e g_e (w2_e . relu(w1_e z + b1_e) + b2_e)    (hidden width H per expert)
+ * and returns the k_out best candidates by (r desc, id asc).
+ *   net           host struct of device pointers (float32, row-major): gate_w [E][dim], gate_b [E],
+ *                 w1 [E][H][dim], b1 [E][H], w2 [E][H], b2 [E]; 1 <= E <= SVT_RERANK_MAX_EXPERTS,
+ *                 H >= 1, E * H <= SVT_RERANK_MAX_UNITS
+ *   queries       device, [n_queries][dim] int8 (the search's queries)
+ *   query_scales  device, [n_queries] float > 0, or NULL to use the index's item_scale
+ *   cand_ids      device, [n_queries][n_cand] int64: the candidates of each query, e.g. svt_search's
+ *                 out_ids.  Entries that are negative or not an id present in the index are skipped; a
+ *                 repeated id is scored, and may be returned, once per occurrence.
+ *   n_cand        0 <= n_cand <= SVT_RERANK_MAX_CAND
+ *   k_out         1 <= k_out <= SVT_RERANK_MAX_OUT
+ *   out_ids       device, [n_queries][k_out] int64, best first; -1 past out_counts[b]
+ *   out_scores    device, [n_queries][k_out] float: r; -inf padding
+ *   out_counts    device, [n_queries] int32 or NULL: min(k_out, candidates scored)
+ * The index must not be updated while the call runs.  n_queries == 0 returns SVT_OK without enqueuing.
+ * Errors: SVT_EINVAL (NULL required pointer, n_queries < 0 or > 65535, n_cand, k_out, E or H out of
+ * range), SVT_ESTATE (freed index), SVT_EDEVICE (launch failure); on error nothing is enqueued.
+ * The call allocates no device memory; concurrent calls with their own outputs are safe.
+ */
+#define SVT_RERANK_MAX_EXPERTS 8
+#define SVT_RERANK_MAX_UNITS 64
+#define SVT_RERANK_MAX_CAND 4096
+#define SVT_RERANK_MAX_OUT 2048
+typedef struct {
+  int32_t n_experts;   /* E */
+  int32_t hidden;      /* H */
+  const float *gate_w, *gate_b, *w1, *b1, *w2, *b2;
+} svt_rerank_net;
+int svt_rerank(const svt_index *ix, int32_t n_queries, const int8_t *queries, const float *query_scales,
+               int32_t n_cand, const int64_t *cand_ids, const svt_rerank_net *net, int32_t k_out,
+               int64_t *out_ids, float *out_scores, int32_t *out_counts, void *hip_stream);
+
 /* svt_last_error - message of the last failed call on this thread ("" if none). */
 const char *svt_last_error(void);
 

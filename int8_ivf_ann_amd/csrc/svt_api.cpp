@@ -801,6 +801,34 @@ extern "C" size_t svt_search_workspace_size(const svt_index *ix, int32_t n_queri
   return layout(ix, n_queries, nprobe, k, opts).total;
 }
 
+extern "C" int svt_rerank(const svt_index *ix, int32_t B, const int8_t *queries, const float *query_scales,
+                          int32_t n_cand, const int64_t *cand_ids, const svt_rerank_net *net, int32_t k_out,
+                          int64_t *out_ids, float *out_scores, int32_t *out_counts, void *hip_stream) {
+  g_err.clear();
+  const char *who = "svt_rerank";
+  if (!ix || !is_live(ix) || ix->magic != kMagic) return fail(SVT_ESTATE, "%s: not a live index", who);
+  if (B < 0 || B > 65535) return fail(SVT_EINVAL, "%s: n_queries %d out of [0, 65535]", who, B);
+  if (n_cand < 0 || n_cand > SVT_RERANK_MAX_CAND)
+    return fail(SVT_EINVAL, "%s: n_cand %d out of [0, %d]", who, n_cand, SVT_RERANK_MAX_CAND);
+  if (k_out < 1 || k_out > SVT_RERANK_MAX_OUT)
+    return fail(SVT_EINVAL, "%s: k_out %d out of [1, %d]", who, k_out, SVT_RERANK_MAX_OUT);
+  if (!net) return fail(SVT_EINVAL, "%s: NULL net", who);
+  if (net->n_experts < 1 || net->n_experts > SVT_RERANK_MAX_EXPERTS)
+    return fail(SVT_EINVAL, "%s: n_experts %d out of [1, %d]", who, net->n_experts, SVT_RERANK_MAX_EXPERTS);
+  if (net->hidden < 1 || net->n_experts * net->hidden > SVT_RERANK_MAX_UNITS)
+    return fail(SVT_EINVAL, "%s: hidden %d: need 1 <= hidden and n_experts * hidden <= %d", who, net->hidden,
+                SVT_RERANK_MAX_UNITS);
+  if (B == 0) return SVT_OK;
+  if (!net->gate_w || !net->gate_b || !net->w1 || !net->b1 || !net->w2 || !net->b2)
+    return fail(SVT_EINVAL, "%s: NULL net weight", who);
+  if (!queries || !out_ids || !out_scores || (n_cand > 0 && !cand_ids))
+    return fail(SVT_EINVAL, "%s: NULL queries, cand_ids or outputs", who);
+  const hipError_t e = launch_rerank(ix->dev, B, queries, query_scales, n_cand, cand_ids, *net, k_out, out_ids,
+                                     out_scores, out_counts, (hipStream_t)hip_stream);
+  if (e != hipSuccess) return fail_hip(e, "launch_rerank");
+  return SVT_OK;
+}
+
 extern "C" int svt_search_path(const svt_index *ix, int32_t n_queries, int32_t nprobe, int32_t k,
                                const svt_search_options *opts) {
   g_err.clear();

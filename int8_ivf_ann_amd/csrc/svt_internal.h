@@ -281,6 +281,10 @@ constexpr int32_t kUpdInsert = 0, kUpdDelete = 1, kUpdResign = 2;
 hipError_t launch_updates(int8_t *items, uint64_t *sigs, int32_t *perm, int32_t *live, int32_t *slot_of,
                           const UpdOp *ops, int32_t n, const int8_t *rows, const uint64_t *new_sigs, int32_t dim,
                           int32_t sig_words, hipStream_t s);
+// rerank (svt_rerank.hip): one workgroup per query
+hipError_t launch_rerank(const DevIndex &ix, int32_t B, const int8_t *queries, const float *query_scales,
+                         int32_t n_cand, const int64_t *cand_ids, const svt_rerank_net &net, int32_t k_out,
+                         int64_t *out_ids, float *out_scores, int32_t *out_counts, hipStream_t s);
 hipError_t launch_scatter_rows(const int8_t *src_rows, const uint64_t *src_sigs, const int32_t *pos_of,
                                int64_t i0, int64_t n, int32_t dim, int32_t sig_words, int8_t *dst_rows,
                                uint64_t *dst_sigs, hipStream_t s);

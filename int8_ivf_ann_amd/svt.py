@@ -22,12 +22,13 @@ SVT_PATH_AUTO, SVT_PATH_QUERY, SVT_PATH_TILE, SVT_PATH_EXHAUSTIVE = 0, 1, 2, 3
 SVT_OPT_MERGE_FROM_SLOTS, SVT_OPT_FORCE_REDO = 1, 2
 SVT_MAX_MASK_GROUPS = 4
 SVT_NOALLOC_SCRATCH_BYTES = 256 << 20
+SVT_RERANK_MAX_EXPERTS, SVT_RERANK_MAX_UNITS, SVT_RERANK_MAX_CAND, SVT_RERANK_MAX_OUT = 8, 64, 4096, 2048
 _PATHS = {"auto": SVT_PATH_AUTO, "query": SVT_PATH_QUERY, "tile": SVT_PATH_TILE}
 
 #: every symbol include/svt.h declares
 EXPORTED = ("svt_index_upload", "svt_index_upload_updatable", "svt_index_insert", "svt_index_delete",
             "svt_index_resign", "svt_index_free", "svt_index_info", "svt_search_workspace_size", "svt_search_path",
-            "svt_search", "svt_search_noalloc", "svt_last_error", "svt_bloom_mask", "svt_bloom_sign", "svt_profile_enable", "svt_profile_read")
+            "svt_search", "svt_search_noalloc", "svt_rerank", "svt_last_error", "svt_bloom_mask", "svt_bloom_sign", "svt_profile_enable", "svt_profile_read")
 
 
 class SvtError(RuntimeError):
@@ -58,6 +59,12 @@ class svt_search_options(ctypes.Structure):
         ("mask_groups", ctypes.c_int32),
         ("reserved", ctypes.c_int32 * 4),
     ]
+
+
+class svt_rerank_net(ctypes.Structure):
+    _fields_ = [("n_experts", ctypes.c_int32), ("hidden", ctypes.c_int32), ("gate_w", ctypes.c_void_p),
+                ("gate_b", ctypes.c_void_p), ("w1", ctypes.c_void_p), ("b1", ctypes.c_void_p),
+                ("w2", ctypes.c_void_p), ("b2", ctypes.c_void_p)]
 
 
 def make_options(path="auto", pool_keys: int = 0, flags: int = 0, mask_groups: int = 0) -> svt_search_options:
@@ -106,6 +113,7 @@ def lib():
     L.svt_search_path.argtypes = [vp, i32, i32, i32, vp]
     L.svt_search.argtypes = [vp, i32, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.svt_search_noalloc.argtypes = [vp, i32, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp]
+    L.svt_rerank.argtypes = [vp, i32, vp, vp, i32, vp, ctypes.POINTER(svt_rerank_net), i32, vp, vp, vp, vp]
     L.svt_last_error.restype = ctypes.c_char_p
     L.svt_bloom_mask.argtypes = [vp, i32, i32, i32, vp]
     L.svt_bloom_sign.argtypes = [vp, i64, i32, i32, i32, vp, i32]
@@ -344,6 +352,49 @@ def svt_search_noalloc(handle, queries, masks, nprobe: int, k: int, query_scales
     return outs
 
 
+_NET_KEYS = ("gate_w", "gate_b", "w1", "b1", "w2", "b2")
+
+
+def svt_rerank(handle, queries, cand_ids, net, k_out: int, query_scales=None, out_ids=None, out_scores=None,
+               out_counts=None, stream=None):
+    """Re-score each query's candidates with a gated mixture of experts and keep the k_out best.
+    queries: int8 [B, d] cuda tensor; cand_ids: int64 [B, n_cand] cuda tensor (e.g. svt_search's ids;
+    -1 and ids not in the index are skipped); net: dict of float32 cuda tensors gate_w [E, d],
+    gate_b [E], w1 [E, H, d], b1 [E, H], w2 [E, H], b2 [E].  Returns (ids int64 [B, k_out],
+    scores float32 [B, k_out], counts int32 [B]); asynchronous on ``stream``."""
+    import torch
+    n, dim, W, _ = svt_index_info(handle)
+    if not hasattr(queries, "shape") or len(queries.shape) != 2:
+        raise ValueError("queries: expected a 2-D tensor [B, dim]")
+    if not hasattr(cand_ids, "shape") or len(cand_ids.shape) != 2:
+        raise ValueError("cand_ids: expected a 2-D tensor [B, n_cand]")
+    B, n_cand = int(queries.shape[0]), int(cand_ids.shape[1])
+    dev = queries.device
+    _check_tensor("queries", queries, (torch.int8,), (B, dim))
+    _check_tensor("cand_ids", cand_ids, (torch.int64,), (B, n_cand), dev)
+    _check_tensor("query_scales", query_scales, (torch.float32,), (B,), dev, nullable=True)
+    if not hasattr(net.get("w1"), "shape") or len(net["w1"].shape) != 3:
+        raise ValueError("net['w1']: expected a tensor [E, H, d]")
+    E, H = int(net["w1"].shape[0]), int(net["w1"].shape[1])
+    shapes = {"gate_w": (E, dim), "gate_b": (E,), "w1": (E, H, dim), "b1": (E, H), "w2": (E, H), "b2": (E,)}
+    for key in _NET_KEYS:
+        _check_tensor(f"net['{key}']", net.get(key), (torch.float32,), shapes[key], dev)
+    if out_ids is None:
+        out_ids = torch.empty((B, k_out), dtype=torch.int64, device=dev)
+    if out_scores is None:
+        out_scores = torch.empty((B, k_out), dtype=torch.float32, device=dev)
+    if out_counts is None:
+        out_counts = torch.empty((B,), dtype=torch.int32, device=dev)
+    _check_tensor("out_ids", out_ids, (torch.int64,), (B, k_out), dev)
+    _check_tensor("out_scores", out_scores, (torch.float32,), (B, k_out), dev)
+    _check_tensor("out_counts", out_counts, (torch.int32,), (B,), dev)
+    cnet = svt_rerank_net(E, H, *[net[key].data_ptr() for key in _NET_KEYS])
+    _check(lib().svt_rerank(handle, B, _t_ptr(queries), _t_ptr(query_scales), n_cand, _t_ptr(cand_ids),
+                            ctypes.byref(cnet), k_out, _t_ptr(out_ids), _t_ptr(out_scores), _t_ptr(out_counts),
+                            _stream_ptr(stream)))
+    return out_ids, out_scores, out_counts
+
+
 def svt_profile_enable(on) -> None:
     """False/0: off; True/1: every stage; 2: the scan stage only (two event records per search)."""
     _check(lib().svt_profile_enable(int(on)))
@@ -388,6 +439,10 @@ class Index:
         ws = self.workspace(B, nprobe, k, opts) if B > 0 else None
         return svt_search(self.handle, queries, masks, nprobe, k, query_scales=query_scales, workspace=ws,
                           stream=stream, opts=opts, **outs)
+
+    def rerank(self, queries, cand_ids, net, k_out: int, query_scales=None, stream=None, **outs):
+        return svt_rerank(self.handle, queries, cand_ids, net, k_out, query_scales=query_scales, stream=stream,
+                          **outs)
 
     def insert(self, ids, rows, sigs, list_of, stream=None):
         svt_index_insert(self.handle, ids, rows, sigs, list_of, stream)

@@ -103,6 +103,8 @@ def test_search_rejects_dead_index(L):
     assert L.svt_search_noalloc(bogus, 1, None, None, None, 1, 1, None, None, None, None, None, None,
                                 None) == svt.SVT_ESTATE
     assert L.svt_search_path(bogus, 1, 1, 1, None) == svt.SVT_ESTATE
+    net = svt.svt_rerank_net(1, 1)
+    assert L.svt_rerank(bogus, 1, None, None, 1, None, ctypes.byref(net), 1, None, None, None, None) == svt.SVT_ESTATE
     one = np.zeros(1, np.int64)
     assert L.svt_index_delete(bogus, 1, one.ctypes.data, None) == svt.SVT_ESTATE
     assert L.svt_index_resign(bogus, 1, one.ctypes.data, one.ctypes.data, None) == svt.SVT_ESTATE
@@ -128,6 +130,19 @@ def test_options_struct_layout():
     assert re.search(r"#define SVT_MAX_MASK_GROUPS 4", hdr) and svt.SVT_MAX_MASK_GROUPS == 4
     assert re.search(r"#define SVT_NOALLOC_SCRATCH_BYTES \(\(size_t\)256 << 20\)", hdr)
     assert svt.SVT_NOALLOC_SCRATCH_BYTES == 256 << 20
+
+
+def test_rerank_net_struct_layout():
+    # two int32 sizes, then six device pointers in the order gate_w, gate_b, w1, b1, w2, b2
+    assert ctypes.sizeof(svt.svt_rerank_net) == 8 + 6 * ctypes.sizeof(ctypes.c_void_p)
+    assert [f[0] for f in svt.svt_rerank_net._fields_] == ["n_experts", "hidden", "gate_w", "gate_b", "w1", "b1",
+                                                          "w2", "b2"]
+    hdr = open(os.path.join(ROOT, "include", "svt.h")).read()
+    assert re.search(r"int32_t n_experts;.*\n\s*int32_t hidden;.*\n\s*const float \*gate_w, \*gate_b, \*w1, \*b1, \*w2, \*b2;",
+                     hdr)
+    for name, v in (("SVT_RERANK_MAX_EXPERTS", svt.SVT_RERANK_MAX_EXPERTS), ("SVT_RERANK_MAX_UNITS", svt.SVT_RERANK_MAX_UNITS),
+                    ("SVT_RERANK_MAX_CAND", svt.SVT_RERANK_MAX_CAND), ("SVT_RERANK_MAX_OUT", svt.SVT_RERANK_MAX_OUT)):
+        assert re.search(rf"#define {name} {v}\b", hdr), name
 
 
 def test_binding_rejects_bad_tensors():
