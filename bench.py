@@ -59,6 +59,8 @@ def parse():
     ap.add_argument("--latency-queries", type=int, default=None,
                     help="searches timed one by one for latency percentiles (default: 1000 at batch 1, else 0)")
     ap.add_argument("--no-read-ceiling", action="store_true", help="skip the streaming-read probe")
+    ap.add_argument("--no-rerank", action="store_true", help="skip the rerank measurement")
+    ap.add_argument("--rerank-k", type=int, default=256, help="rerank: candidates kept per query")
     return ap.parse_args()
 
 
@@ -94,6 +96,59 @@ def read_ceiling_gbs(torch, gib: int = 4, reps: int = 5) -> float:
         best = max(best, x.numel() * 8 / (e0.elapsed_time(e1) * 1e-3) / 1e9)
     del x, s
     return best
+
+
+FP32_MATRIX_PEAK_TFLOPS = 157.3   # MI355X dense float32 matrix rate
+RERANK_EXPERTS, RERANK_HIDDEN = 4, 16
+
+
+def rerank_leg(args, torch, svt, ix, cat, bt, cand, d):
+    """Times svt_rerank over one batch's search results (the candidates) with a seeded random net;
+    the first layer (2 E H d flops per candidate) runs on the float32 matrix cores."""
+    import synth
+    rng = np.random.default_rng(2024)
+    net = synth.rerank_net(rng, d, RERANK_EXPERTS, RERANK_HIDDEN)
+    tnet = {key: torch.from_numpy(v).cuda() for key, v in net.items()}
+    B, n_cand = cand.shape
+    k_out = args.rerank_k
+    outs = dict(out_ids=torch.empty((B, k_out), dtype=torch.int64, device="cuda"),
+                out_scores=torch.empty((B, k_out), dtype=torch.float32, device="cuda"),
+                out_counts=torch.empty((B,), dtype=torch.int32, device="cuda"))
+    for _ in range(3):
+        ix.rerank(bt["q_d"], cand, tnet, k_out, **outs)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()   # on torch's current stream, the one the binding launches on
+    for _ in range(args.steps):
+        ix.rerank(bt["q_d"], cand, tnet, k_out, **outs)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    cand_h = cand.cpu().numpy()
+    n_valid = int((cand_h >= 0).sum())
+    U = RERANK_EXPERTS * RERANK_HIDDEN
+    flops = n_valid * 2.0 * U * d + B * 2.0 * RERANK_EXPERTS * d
+    achieved = flops / (ms * 1e-3) / 1e12
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import rerank as R
+        n_s = min(B, 16)
+        t0 = time.perf_counter()
+        R.rerank(cat.items, cat.item_scale, bt["q"][:n_s], None, cand_h[:n_s], net, k_out)
+        cs = time.perf_counter() - t0
+        nv_s = int((cand_h[:n_s] >= 0).sum())
+        cpu = {"value": nv_s / cs, "unit": "candidates/s", "cores": 1, "kind": "oracle",
+               "sample": f"first {n_s} queries of the batch ({nv_s} candidates, {cs:.2f} s, numpy float64)"}
+    res = {"kernel": "k_rerank", "candidates_per_s": n_valid / (ms * 1e-3), "ms_per_launch": ms,
+           "config": {"batch": B, "n_cand": n_cand, "k_out": k_out, "experts": RERANK_EXPERTS,
+                      "hidden": RERANK_HIDDEN, "dim": d, "candidates": "the search's top-k of the same batch"},
+           "roofline": {"bound": "mfma", "achieved": achieved, "peak": FP32_MATRIX_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": achieved / FP32_MATRIX_PEAK_TFLOPS, "flops_per_launch": flops,
+                        "traffic": None},
+           "cpu_baseline": cpu}
+    log(f"[bench] rerank {B}x{n_cand} -> {k_out}: {ms:.4f} ms/launch, {achieved:.1f} TFLOP/s "
+        f"({100 * achieved / FP32_MATRIX_PEAK_TFLOPS:.1f}% of fp32 matrix peak)")
+    return res
 
 
 def cpu_model() -> str:
@@ -272,6 +327,15 @@ def main():
             f"p99 {lat['device_ms']['p99']:.4f} ms")
         del ql_d, ml_d
 
+    rerank = None
+    if not args.no_rerank:
+        bt = batches[0]
+        cand = torch.empty((B, k), dtype=torch.int64, device="cuda")
+        svt.svt_search(ix.handle, bt["q_d"], bt["m_d"], nprobe, k, workspace=ws, opts=opts,
+                       **dict(outs, out_ids=cand))
+        rerank = rerank_leg(args, torch, svt, ix, cat, bt, cand, d)
+        del cand
+
     ceiling = None
     if not args.no_read_ceiling:
         ceiling = read_ceiling_gbs(torch)
@@ -386,6 +450,8 @@ def main():
     }
     if lat is not None:
         line["latency"] = lat
+    if rerank is not None:
+        line["rerank"] = rerank
     print(json.dumps(line), flush=True)
     ix.close()
 

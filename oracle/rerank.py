@@ -68,9 +68,3 @@ def rerank(items, item_scale, queries, query_scales, cand_ids, net, k_out):
         cnt[b] = n
     return out_ids, out_sc, cnt, out_abs
 
-
-def random_net(rng, d, E, H, scale=1.0):
-    """A net of random float32 weights (the library reads float32)."""
-    f = lambda *s: (rng.standard_normal(s) * scale).astype(np.float32)
-    return {"gate_w": f(E, d) / np.float32(np.sqrt(d)), "gate_b": f(E), "w1": f(E, H, d) / np.float32(np.sqrt(d)),
-            "b1": f(E, H) * np.float32(0.1), "w2": f(E, H) / np.float32(np.sqrt(H)), "b2": f(E) * np.float32(0.1)}

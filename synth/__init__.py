@@ -172,3 +172,11 @@ def queries(cat: Catalogue, n: int, offset: int = 0) -> QuerySet:
         lib.synth_queries(ctypes.byref(p), _ptr(cat.cent_f), ctypes.c_float(cat.item_scale), offset, n,
                           _ptr(q), _ptr(qc), _ptr(qt), _ptr(nr), _ptr(rt))
     return QuerySet(q, qc, qt, nr, rt)
+
+
+def rerank_net(rng: np.random.Generator, d: int, E: int, H: int, scale: float = 1.0) -> Dict[str, np.ndarray]:
+    """Random float32 weights of the rerank's gated mixture of experts (gate_w [E, d], gate_b [E],
+    w1 [E, H, d], b1 [E, H], w2 [E, H], b2 [E]): normal draws, fan-in scaled, small biases."""
+    f = lambda *s: (rng.standard_normal(s) * scale).astype(np.float32)
+    return {"gate_w": f(E, d) / np.float32(np.sqrt(d)), "gate_b": f(E), "w1": f(E, H, d) / np.float32(np.sqrt(d)),
+            "b1": f(E, H) * np.float32(0.1), "w2": f(E, H) / np.float32(np.sqrt(H)), "b2": f(E) * np.float32(0.1)}

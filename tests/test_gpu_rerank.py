@@ -28,6 +28,7 @@ import pytest
 
 import oracle_pins as P
 from gpu_common import say
+import synth
 from oracle import rerank as R
 
 pytestmark = pytest.mark.gpu
@@ -164,7 +165,7 @@ def test_rerank_matches_oracle(svt, shape, scaled):
         # some skipped entries: -1 (search padding), past the ids
         cand[rng.random((B, n_cand)) < 0.05] = -1
         cand[rng.random((B, n_cand)) < 0.02] = n + 5
-        net = R.random_net(rng, d, E, H)
+        net = synth.rerank_net(rng, d, E, H)
         say(f"rerank d={d} E={E} H={H} n_cand={n_cand} k_out={k_out} B={B} scaled={scaled}")
         got = gpu_rerank(ix, queries, cand, net, k_out, qs)
         check(items, scale, queries, qs, cand, net, k_out, got, f"d{d} E{E} H{H}")
@@ -181,7 +182,7 @@ def test_rerank_ties_duplicates_and_empty(svt):
     scale = 50.0
     ix = svt.Index(items, sigs, list_of, cent, scale)
     try:
-        net = R.random_net(rng, d, 2, 8)
+        net = synth.rerank_net(rng, d, 2, 8)
         q = rng.integers(-127, 128, size=(4, d)).astype(np.int8)
         cand = np.full((4, 40), -1, np.int64)
         cand[0, :6] = [30, 20, 10, 5, 5, 99]      # ties and a repeated id
@@ -228,7 +229,7 @@ def test_rerank_after_updates(svt):
         full[:n] = items
         full[new_ids] = new_rows
         present = np.setdiff1d(np.concatenate([np.arange(n), new_ids]), dead)
-        net = R.random_net(rng, d, 4, 4)
+        net = synth.rerank_net(rng, d, 4, 4)
         q = rng.integers(-127, 128, size=(5, d)).astype(np.int8)
         cand = np.concatenate([rng.integers(0, 100, size=(5, 40)), rng.integers(1000, 1040, size=(5, 40)),
                                rng.integers(800, 1000, size=(5, 10))], axis=1).astype(np.int64)
@@ -251,7 +252,7 @@ def test_rerank_of_search_results(svt):
         q = rng.integers(-127, 128, size=(B, d)).astype(np.int8)
         masks = P.random_masks(rng, B, 1, nbits_max=4)
         ids, _, _, _, _ = ix.search(_t(q, np.int8), _t(masks.view(np.int64)), 8, 512)
-        net = R.random_net(rng, d, 4, 16)
+        net = synth.rerank_net(rng, d, 4, 16)
         tnet = {k: _t(v, np.float32) for k, v in net.items()}
         rid, rsc, rcnt = ix.rerank(_t(q, np.int8), ids, tnet, 100)
         torch.cuda.synchronize()
@@ -294,5 +295,36 @@ def test_rerank_argument_errors(svt):
             ix.rerank(q, c, {"gate_w": torch.zeros((2, d + 1), device="cuda"), "gate_b": torch.zeros(2, device="cuda"),
                              "w1": torch.zeros((2, 3, d), device="cuda"), "b1": torch.zeros((2, 3), device="cuda"),
                              "w2": torch.zeros((2, 3), device="cuda"), "b2": torch.zeros(2, device="cuda")}, 4)
+    finally:
+        ix.close()
+
+
+@pytest.mark.parametrize("d,E,H", [(16, 1, 1), (128, 1, 1), (128, 4, 16)])
+def test_rerank_is_deterministic(svt, d, E, H):
+    """Repeated calls on the same inputs return identical bits (the shared-memory staging of the
+    weights has no lost writes: every entry is written once, by one thread), and the first matches the
+    oracle."""
+    import torch
+    rng = np.random.default_rng(11 + d + E)
+    n, B, n_cand, k_out = 5000, 96, 300, 40
+    items, sigs, list_of, cent = _catalogue(rng, n, d)
+    scale = 127.0 / 3.0
+    ix = svt.Index(items, sigs, list_of, cent, scale)
+    try:
+        q = rng.integers(-127, 128, size=(B, d)).astype(np.int8)
+        cand = rng.integers(0, n, size=(B, n_cand)).astype(np.int64)
+        net = synth.rerank_net(rng, d, E, H)
+        net["b1"][:] = np.abs(net["b1"]) + np.float32(0.05)   # positive biases: a lost weight changes scores
+        tnet = {k: _t(v, np.float32) for k, v in net.items()}
+        q_d, c_d = _t(q, np.int8), _t(cand, np.int64)
+        runs = []
+        for _ in range(12):
+            ids, sc, cnt = ix.rerank(q_d, c_d, tnet, k_out)
+            runs.append((ids.clone(), sc.clone(), cnt.clone()))
+        torch.cuda.synchronize()
+        for ids, sc, cnt in runs[1:]:
+            assert torch.equal(ids, runs[0][0]) and torch.equal(sc, runs[0][1]) and torch.equal(cnt, runs[0][2])
+        check(items, scale, q, None, cand, net, k_out,
+              tuple(t.cpu().numpy() for t in runs[0]), f"deterministic d{d} E{E} H{H}")
     finally:
         ix.close()

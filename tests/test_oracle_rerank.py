@@ -5,6 +5,7 @@ import math
 
 import numpy as np
 
+import synth
 from oracle import rerank as R
 
 
@@ -63,7 +64,7 @@ def test_negative_preactivation_is_cut():
 def test_query_scale_homogeneity():
     # without biases and with a constant gate the score is positively homogeneous in q^
     rng = np.random.default_rng(3)
-    net = R.random_net(rng, 4, 3, 5)
+    net = synth.rerank_net(rng, 4, 3, 5)
     for k in ("gate_w", "b1", "b2"):
         net[k][:] = 0
     r1, _ = R.rerank_scores(ITEMS, 3.0, Q[0], 2.0, np.array([0, 1]), net)
@@ -90,7 +91,7 @@ def test_order_ties_padding_and_ids():
 def test_error_bound_is_a_bound():
     # S_abs bounds |r|, with equality when every term is non-negative
     rng = np.random.default_rng(4)
-    net = R.random_net(rng, 4, 2, 3)
+    net = synth.rerank_net(rng, 4, 2, 3)
     r, s_abs = R.rerank_scores(ITEMS, 2.0, Q[0], 1.5, np.array([0, 1, 2]), net)
     assert np.all(np.abs(r) <= s_abs + 1e-12)
     pos = _net(1, 1, 4)
