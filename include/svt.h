@@ -13,8 +13,9 @@
  *         request with simple bit operations];
  *     3. score: int8 . int8 with int32 accumulation for eligible items only
  *        [same post, fused Int8 ANN paragraph and compute-cost-efficiency section ("dp4a")];
- *     4. select: the k best eligible items by (score desc, item id asc), k <= 2048, kept on chip and
- *        merged; only the final candidates are written out
+ *     4. select: the k best eligible items by (score desc, item id asc), kept on chip and merged for
+ *        k <= 2048 (larger k, up to SVT_MAX_K_LARGE: a radix select over repeated passes, see
+ *        SVT_PATH_LARGE_K); only the final candidates are written out
  *        [same post: no recall loss observed at 64 probes, top-2048; "Meta Andromeda" summary, System
  *         section: intermediates stay in registers and shared memory, targeting + scoring + top-K
  *         on one machine, only the final candidates return].
@@ -49,7 +50,8 @@ enum {
   SVT_ENOSPACE = -6      /* an insert finds no free slot in its cluster                              */
 };
 
-#define SVT_MAX_K 2048        /* largest top-k per query                                            */
+#define SVT_MAX_K 2048        /* largest top-k of the fused paths (per-workgroup lists in LDS)        */
+#define SVT_MAX_K_LARGE 16384 /* largest top-k per query: k > SVT_MAX_K takes the large-k path        */
 #define SVT_MAX_SIG_WORDS 2   /* signatures of 64 or 128 bits                                       */
 
 /* Opaque, library-owned index resident in HBM. */
@@ -151,8 +153,15 @@ int svt_index_info(const svt_index *ix, int64_t *n_items, int32_t *dim, int32_t 
  *                   query's items are kept in per-query pools; a query whose pool holds fewer than k
  *                   candidates (with a threshold above the minimum) or overflows is redone on the query
  *                   path, so the result stays exact whatever the data.
+ *   SVT_PATH_LARGE_K  any k up to SVT_MAX_K_LARGE (the path every search with k > SVT_MAX_K takes;
+ *                   also selectable for smaller k): an exact radix select over the eligible items'
+ *                   (score, id) keys, one 11-bit digit per pass over each query's probed items (at
+ *                   most 5 passes, a pass skipping the queries already decided), then one pass that
+ *                   keeps the keys at or above each query's threshold and an LDS sort of those
+ *                   ["SilverTorch - Index as Model", fused Int8 ANN paragraph and compute-cost table:
+ *                    top-k well beyond GPU FAISS's 2048].  Each pass reads the probed items again.
  */
-enum { SVT_PATH_AUTO = 0, SVT_PATH_QUERY = 1, SVT_PATH_TILE = 2, SVT_PATH_EXHAUSTIVE = 3 };
+enum { SVT_PATH_AUTO = 0, SVT_PATH_QUERY = 1, SVT_PATH_TILE = 2, SVT_PATH_EXHAUSTIVE = 3, SVT_PATH_LARGE_K = 4 };
 
 /* svt_search_options.flags */
 #define SVT_OPT_MERGE_FROM_SLOTS 1u  /* query path: the merge reads every chunk's slot instead of the keys
@@ -165,7 +174,8 @@ enum { SVT_PATH_AUTO = 0, SVT_PATH_QUERY = 1, SVT_PATH_TILE = 2, SVT_PATH_EXHAUS
  * Options of one search.  A NULL pointer, or a zero-initialised struct, selects the defaults.  The
  * workspace size depends on the options: pass the same options to svt_search_workspace_size and
  * svt_search.
- *   path       SVT_PATH_AUTO (default), SVT_PATH_QUERY or SVT_PATH_TILE
+ *   path       SVT_PATH_AUTO (default), SVT_PATH_QUERY, SVT_PATH_TILE or SVT_PATH_LARGE_K; with
+ *              k > SVT_MAX_K only SVT_PATH_AUTO and SVT_PATH_LARGE_K are accepted
  *   pool_keys  tile path: candidate keys kept per query (0 = default, 16 k rounded up to 4096); a
  *              smaller value makes more pools overflow (their queries are redone)
  *   flags      OR of SVT_OPT_* above
@@ -196,8 +206,9 @@ size_t svt_search_workspace_size(const svt_index *ix, int32_t n_queries, int32_t
                                  const svt_search_options *opts);
 
 /*
- * svt_search_path - the path a search with these sizes and options takes: SVT_PATH_QUERY, SVT_PATH_TILE
- * or SVT_PATH_EXHAUSTIVE (the tile path's MFMA scan of the whole catalogue, nprobe == nlist).  It depends
+ * svt_search_path - the path a search with these sizes and options takes: SVT_PATH_QUERY, SVT_PATH_TILE,
+ * SVT_PATH_EXHAUSTIVE (the tile path's MFMA scan of the whole catalogue, nprobe == nlist) or
+ * SVT_PATH_LARGE_K.  It depends
  * on the index, n_queries, nprobe and the options only, never on query values.  No device work.
  * Errors (negative return): those of svt_search_workspace_size's arguments (SVT_EINVAL, SVT_ESTATE).
  */
@@ -210,7 +221,7 @@ int svt_search_path(const svt_index *ix, int32_t n_queries, int32_t nprobe, int3
  *                 mask_groups, 1 by default), 8-byte aligned
  *   query_scales  device, [n_queries] float > 0, or NULL to use the index's item_scale
  *   nprobe        1 <= nprobe <= nlist
- *   k             1 <= k <= SVT_MAX_K
+ *   k             1 <= k <= SVT_MAX_K_LARGE (above SVT_MAX_K: the large-k path)
  *   out_ids       device, [n_queries][k] int64: item ids, best first; -1 past out_counts[b]
  *   out_scores    device, [n_queries][k] int32: exact int8 dot products; INT32_MIN past the count
  *   out_fscores   device, [n_queries][k] float or NULL: S / (item_scale * query_scale); -inf padding

@@ -13,7 +13,7 @@ ARCH = "gfx950"
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 # (source, holds device code); svt_api.cpp is host-only
 SOURCES = (("svt_kernels.hip", True), ("svt_tile.hip", True), ("svt_noalloc.hip", True), ("svt_rerank.hip", True),
-           ("svt_api.cpp", False))
+           ("svt_largek.hip", True), ("svt_api.cpp", False))
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result", "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 

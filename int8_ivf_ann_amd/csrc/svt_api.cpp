@@ -11,6 +11,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <functional>
 #include <mutex>
 #include <new>
 #include <set>
@@ -99,6 +100,7 @@ struct svt_index {
   std::vector<std::vector<int32_t>> free_h;    // free slots of each cluster (a stack, lowest slot on top)
   void *d_stage = nullptr;                     // device staging of an update batch
   size_t stage_bytes = 0;
+  std::vector<int64_t> top_slots;               // [nlist + 1] slots of the j largest clusters (a query's stream bound)
   int32_t scan_wgs;                 // persistent workgroups of the query-by-query scan
   int32_t tscan_wgs;                // persistent workgroups of the tile scan
   int32_t xscan_wgs;                // workgroups of the exhaustive MFMA scan
@@ -279,6 +281,13 @@ int upload(const svt_index_desc *d, bool updatable, int64_t id_capacity, int32_t
   ix->dev.nlist = nlist;
   ix->dev.item_scale = d->item_scale;
   ix->n_live = n;
+  {
+    std::vector<int64_t> sz((size_t)nlist);
+    for (int32_t c = 0; c < nlist; ++c) sz[(size_t)c] = (int64_t)offsets[c + 1] - offsets[c];
+    std::sort(sz.begin(), sz.end(), std::greater<int64_t>());
+    ix->top_slots.assign((size_t)nlist + 1, 0);
+    for (int32_t c = 0; c < nlist; ++c) ix->top_slots[(size_t)c + 1] = ix->top_slots[(size_t)c] + sz[(size_t)c];
+  }
   if (updatable) {
     ix->updatable = true;
     ix->id_capacity = id_capacity;
@@ -484,6 +493,7 @@ struct Layout {
   // tile and exhaustive paths (absent on the query path)
   size_t sthr, redo, pool_cnt, pool, gcnt, gfill, gstart, estart, uoff, mrec, entries, ctab, thdr, tblk, sbuf;
   size_t qdens, clog, ccost, cstart_u;
+  size_t lk_hist, lk_state, lk_cnt, lk_keys;   // large-k path
   size_t total;
   SearchShape sh;
 };
@@ -504,8 +514,9 @@ bool tile_fits(const svt_index *ix, int32_t B, int32_t nprobe, int32_t GT) {
   return ix->dev.n_items * blocks < kMaxUnion && (int64_t)B * nprobe * GT < kMaxUnion;
 }
 
-int resolve_path(const svt_index *ix, int32_t B, int32_t nprobe, const svt_search_options *o) {
+int resolve_path(const svt_index *ix, int32_t B, int32_t nprobe, int32_t k, const svt_search_options *o) {
   const int want = o ? o->path : SVT_PATH_AUTO;
+  if (want == SVT_PATH_LARGE_K || k > SVT_MAX_K) return kPathLargeK;
   if (want == SVT_PATH_QUERY || ix->dev.n_items == 0) return kPathQuery;
   const bool exh = nprobe == ix->dev.nlist;
   const int32_t GT = tile_groups(mask_groups(o));
@@ -521,7 +532,7 @@ int resolve_path(const svt_index *ix, int32_t B, int32_t nprobe, const svt_searc
 // SVT_OK or SVT_EINVAL (message set)
 int check_options(const svt_search_options *o, const char *who) {
   if (!o) return SVT_OK;
-  if (o->path != SVT_PATH_AUTO && o->path != SVT_PATH_QUERY && o->path != SVT_PATH_TILE)
+  if (o->path != SVT_PATH_AUTO && o->path != SVT_PATH_QUERY && o->path != SVT_PATH_TILE && o->path != SVT_PATH_LARGE_K)
     return fail(SVT_EINVAL, "%s: unknown path %d", who, o->path);
   if (o->pool_keys < 0) return fail(SVT_EINVAL, "%s: pool_keys %d < 0", who, o->pool_keys);
   if (o->flags & ~(SVT_OPT_MERGE_FROM_SLOTS | SVT_OPT_FORCE_REDO))
@@ -542,7 +553,7 @@ Layout layout(const svt_index *ix, int32_t B, int32_t nprobe, int32_t k, const s
   sh.k = k;
   sh.P = ix->scan_wgs;
   sh.max_chunks = max_chunks_for(B, ix->scan_wgs);
-  sh.path = resolve_path(ix, B, nprobe, o);
+  sh.path = resolve_path(ix, B, nprobe, k, o);
   sh.gather_cap = (o && (o->flags & SVT_OPT_MERGE_FROM_SLOTS)) ? 0 : kGatherCap;
   sh.force_redo = (o && (o->flags & SVT_OPT_FORCE_REDO)) ? 1 : 0;
   sh.TP = ix->tscan_wgs;
@@ -574,12 +585,19 @@ Layout layout(const svt_index *ix, int32_t B, int32_t nprobe, int32_t k, const s
   L.counter = take(8 * sizeof(uint32_t));
   L.slot_cnt = take(C * sizeof(int32_t));
   L.slot_min = take(C * sizeof(uint64_t));
-  L.slot_keys = take(C * (size_t)k * sizeof(uint64_t));
+  const bool lk = sh.path == kPathLargeK;
+  L.slot_keys = take(C * (size_t)(lk ? 1 : k) * sizeof(uint64_t));   // the large-k path keeps no slots
   L.mbound = take((size_t)B * sizeof(uint64_t));
   L.mcnt = take((size_t)B * sizeof(uint32_t));
   L.mkeys = take((size_t)B * kGatherCap * sizeof(uint64_t));
   L.stats = take((size_t)B * 2 * sizeof(int64_t));
-  if (sh.path != kPathQuery) {
+  if (lk) {
+    L.lk_hist = take((size_t)B * kLkBins * sizeof(uint32_t));
+    L.lk_state = take((size_t)B * sizeof(LkState));
+    L.lk_cnt = take((size_t)B * sizeof(uint32_t));
+    L.lk_keys = take((size_t)B * (size_t)k * sizeof(uint64_t));
+  }
+  if (sh.path == kPathTile || sh.path == kPathExh) {
     const int64_t def = std::max<int64_t>(4096, ((int64_t)16 * k + 4095) / 4096 * 4096);
     sh.pool_cap = (int32_t)((o && o->pool_keys > 0) ? o->pool_keys : def);
     L.sthr = take((size_t)B * sizeof(int32_t));
@@ -624,8 +642,12 @@ int check_search_args(const svt_index *ix, int32_t B, int32_t nprobe, int32_t k,
   if (!ix || !is_live(ix) || ix->magic != kMagic) return fail(SVT_ESTATE, "%s: not a live index", who);
   if (B < 0 || B > 65535) return fail(SVT_EINVAL, "%s: n_queries %d out of [0, 65535]", who, B);
   if (nprobe < 1 || nprobe > ix->dev.nlist) return fail(SVT_EINVAL, "%s: nprobe %d out of [1, %d]", who, nprobe, ix->dev.nlist);
-  if (k < 1 || k > SVT_MAX_K) return fail(SVT_EINVAL, "%s: k %d out of [1, %d]", who, k, SVT_MAX_K);
-  return check_options(o, who);
+  if (k < 1 || k > SVT_MAX_K_LARGE) return fail(SVT_EINVAL, "%s: k %d out of [1, %d]", who, k, SVT_MAX_K_LARGE);
+  const int rc = check_options(o, who);
+  if (rc != SVT_OK) return rc;
+  if (k > SVT_MAX_K && o && o->path != SVT_PATH_AUTO && o->path != SVT_PATH_LARGE_K)
+    return fail(SVT_EINVAL, "%s: k %d above %d needs the large-k path (path %d requested)", who, k, SVT_MAX_K, o->path);
+  return SVT_OK;
 }
 
 Work carve(const Layout &L, void *workspace, int64_t *out_stats) {
@@ -655,7 +677,13 @@ Work carve(const Layout &L, void *workspace, int64_t *out_stats) {
   w.mcnt = (uint32_t *)(base + L.mcnt);
   w.mkeys = (uint64_t *)(base + L.mkeys);
   w.stats = out_stats ? out_stats : (int64_t *)(base + L.stats);
-  if (sh.path != kPathQuery) {
+  if (sh.path == kPathLargeK) {
+    w.lk_hist = (uint32_t *)(base + L.lk_hist);
+    w.lk_state = (LkState *)(base + L.lk_state);
+    w.lk_cnt = (uint32_t *)(base + L.lk_cnt);
+    w.lk_keys = (uint64_t *)(base + L.lk_keys);
+  }
+  if (sh.path == kPathTile || sh.path == kPathExh) {
     w.sthr = (int32_t *)(base + L.sthr);
     w.redo = (int32_t *)(base + L.redo);
     w.pool_cnt = (uint32_t *)(base + L.pool_cnt);
@@ -711,7 +739,22 @@ int enqueue_search(const svt_index *ix, const SearchShape &sh, const Work &w, co
   if ((e = mark()) != hipSuccess) return fail_hip(e, "event");
   if ((e = launch_coarse_keys(dx, queries, sh.B, w, s)) != hipSuccess) return fail_hip(e, "launch coarse_keys");
   if ((e = mark()) != hipSuccess) return fail_hip(e, "event");
-  if ((e = launch_coarse_select(dx, queries, masks, sh, w, s)) != hipSuccess) return fail_hip(e, "launch coarse_select");
+  {
+    SearchShape cs = sh;   // the coarse stage of the large-k path is the query path's
+    cs.k = std::min(sh.k, (int32_t)SVT_MAX_K);
+    if ((e = launch_coarse_select(dx, queries, masks, cs, w, s)) != hipSuccess) return fail_hip(e, "launch coarse_select");
+  }
+  if (sh.path == kPathLargeK) {
+    for (int i = 0; i < 2; ++i)   // end of the select stage; no plan
+      if ((e = mark()) != hipSuccess) return fail_hip(e, "event");
+    if ((e = launch_large_k(dx, queries, masks, query_scales, sh, ix->top_slots[(size_t)sh.nprobe], w, out_ids,
+                            out_scores, out_fscores, out_counts, s)) != hipSuccess)
+      return fail_hip(e, "launch large-k passes");
+    for (int i = 0; i < 3; ++i)   // the passes are the scan stage; no fallback, no merge
+      if ((e = mark()) != hipSuccess) return fail_hip(e, "event");
+    if (prof) ++ps.searches;
+    return SVT_OK;
+  }
   if (sh.path == kPathQuery && (e = launch_plan(dx, sh, w, 0, s)) != hipSuccess) return fail_hip(e, "launch plan");
   if ((e = mark()) != hipSuccess) return fail_hip(e, "event");
   if (sh.path == kPathTile && (e = launch_tile_plan(dx, masks, sh, w, s)) != hipSuccess)
@@ -834,7 +877,8 @@ extern "C" int svt_search_path(const svt_index *ix, int32_t n_queries, int32_t n
   g_err.clear();
   const int rc = check_search_args(ix, n_queries, nprobe, k, opts, "svt_search_path");
   if (rc != SVT_OK) return rc;
-  switch (resolve_path(ix, n_queries, nprobe, opts)) {
+  switch (resolve_path(ix, n_queries, nprobe, k, opts)) {
+    case kPathLargeK: return SVT_PATH_LARGE_K;
     case kPathTile: return SVT_PATH_TILE;
     case kPathExh: return SVT_PATH_EXHAUSTIVE;
     default: return SVT_PATH_QUERY;

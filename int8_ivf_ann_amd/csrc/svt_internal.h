@@ -168,6 +168,18 @@ struct UEntry {                      // one entry of the union stream
 };
 
 // Per-search device workspace (carved by the host from the caller's buffer).
+// Searches with k above SVT_MAX_K (svt_largek.hip): a radix select over 55-bit keys, 11-bit digits from
+// bit 44 down, one counting pass over the probed items per digit, then a collect pass
+constexpr int kLkDigit = 11, kLkBins = 1 << kLkDigit, kLkTopShift = 44, kLkPasses = 5;
+constexpr int kLkChunk = 8192;   // stream positions per workgroup of a pass
+struct LkState {
+  uint64_t prefix;   // key bits fixed so far; once done, the threshold (0: every eligible key)
+  int32_t shift;     // lowest bit of the digit the next pass counts
+  int32_t need;      // keys still to take in the bucket the prefix names
+  int32_t done;
+  int32_t pad;
+};
+
 struct Work {
   int32_t *coarse_scores;   // [B][nlist]   coarse scores <query, centroid>
   int32_t *probes;          // [B][nprobe]  probed clusters, ascending cluster id
@@ -212,9 +224,14 @@ struct Work {
   int64_t *ccost;           // [nlist + 1]  prefix of the clusters' estimated costs
   int32_t *cstart_u;        // [max_tchunks + 1] union-stream offset where each chunk starts
   int32_t *sbuf;            // [B][scap]    exhaustive sample pass: per lane and run, the best eligible score
+  // searches with k > SVT_MAX_K (null otherwise)
+  uint32_t *lk_hist;        // [B][kLkBins] the current pass's digit counts
+  LkState *lk_state;        // [B]
+  uint32_t *lk_cnt;         // [B]          keys collected
+  uint64_t *lk_keys;        // [B][k]       the collected keys, unordered
 };
 
-enum { kPathQuery = 0, kPathTile = 1, kPathExh = 2 };
+enum { kPathQuery = 0, kPathTile = 1, kPathExh = 2, kPathLargeK = 3 };
 
 constexpr int kMaxGroups = 4;   // masks per query (SVT_MAX_MASK_GROUPS)
 
@@ -281,6 +298,11 @@ constexpr int32_t kUpdInsert = 0, kUpdDelete = 1, kUpdResign = 2;
 hipError_t launch_updates(int8_t *items, uint64_t *sigs, int32_t *perm, int32_t *live, int32_t *slot_of,
                           const UpdOp *ops, int32_t n, const int8_t *rows, const uint64_t *new_sigs, int32_t dim,
                           int32_t sig_words, hipStream_t s);
+// searches with k > SVT_MAX_K (svt_largek.hip), after the coarse stage; max_stream bounds any query's
+// stream (the nprobe largest clusters' slots)
+hipError_t launch_large_k(const DevIndex &ix, const int8_t *queries, const uint64_t *masks, const float *query_scales,
+                          const SearchShape &sh, int64_t max_stream, const Work &w, int64_t *out_ids,
+                          int32_t *out_scores, float *out_fscores, int32_t *out_counts, hipStream_t s);
 // rerank (svt_rerank.hip): one workgroup per query
 hipError_t launch_rerank(const DevIndex &ix, int32_t B, const int8_t *queries, const float *query_scales,
                          int32_t n_cand, const int64_t *cand_ids, const svt_rerank_net &net, int32_t k_out,

@@ -17,13 +17,14 @@ LIB_PATH = os.path.join(_HERE, "libsvt.so")
 
 SVT_OK, SVT_EINVAL, SVT_ENOMEM, SVT_EDEVICE, SVT_EUNSUPPORTED, SVT_ESTATE, SVT_ENOSPACE = 0, -1, -2, -3, -4, -5, -6
 SVT_MAX_K = 2048
+SVT_MAX_K_LARGE = 16384
 SVT_MAX_SIG_WORDS = 2
-SVT_PATH_AUTO, SVT_PATH_QUERY, SVT_PATH_TILE, SVT_PATH_EXHAUSTIVE = 0, 1, 2, 3
+SVT_PATH_AUTO, SVT_PATH_QUERY, SVT_PATH_TILE, SVT_PATH_EXHAUSTIVE, SVT_PATH_LARGE_K = 0, 1, 2, 3, 4
 SVT_OPT_MERGE_FROM_SLOTS, SVT_OPT_FORCE_REDO = 1, 2
 SVT_MAX_MASK_GROUPS = 4
 SVT_NOALLOC_SCRATCH_BYTES = 256 << 20
 SVT_RERANK_MAX_EXPERTS, SVT_RERANK_MAX_UNITS, SVT_RERANK_MAX_CAND, SVT_RERANK_MAX_OUT = 8, 64, 4096, 2048
-_PATHS = {"auto": SVT_PATH_AUTO, "query": SVT_PATH_QUERY, "tile": SVT_PATH_TILE}
+_PATHS = {"auto": SVT_PATH_AUTO, "query": SVT_PATH_QUERY, "tile": SVT_PATH_TILE, "large_k": SVT_PATH_LARGE_K}
 
 #: every symbol include/svt.h declares
 EXPORTED = ("svt_index_upload", "svt_index_upload_updatable", "svt_index_insert", "svt_index_delete",
@@ -68,7 +69,7 @@ class svt_rerank_net(ctypes.Structure):
 
 
 def make_options(path="auto", pool_keys: int = 0, flags: int = 0, mask_groups: int = 0) -> svt_search_options:
-    """Search options: path "auto" | "query" | "tile" (or an SVT_PATH_* value), pool_keys (tile path,
+    """Search options: path "auto" | "query" | "tile" | "large_k" (or an SVT_PATH_* value), pool_keys (tile path,
     0 = default), flags (OR of SVT_OPT_*), mask_groups (masks per query, 0 or 1: one)."""
     o = svt_search_options()
     o.path = _PATHS[path] if isinstance(path, str) else int(path)
@@ -282,7 +283,8 @@ def svt_search_path(handle, n_queries: int, nprobe: int, k: int, opts=None) -> s
     rc = lib().svt_search_path(handle, n_queries, nprobe, k, _opt_ptr(opts))
     if rc < 0:
         raise SvtError(rc, svt_last_error())
-    return {SVT_PATH_QUERY: "query", SVT_PATH_TILE: "tile", SVT_PATH_EXHAUSTIVE: "exhaustive"}[rc]
+    return {SVT_PATH_QUERY: "query", SVT_PATH_TILE: "tile", SVT_PATH_EXHAUSTIVE: "exhaustive",
+            SVT_PATH_LARGE_K: "large_k"}[rc]
 
 
 def _search_tensors(handle, queries, masks, k, query_scales, out_ids, out_scores, out_fscores, out_counts,

@@ -122,7 +122,8 @@ def test_options_struct_layout():
     assert list(o.reserved) == [0] * 4 and o.mask_groups == 0
     assert svt.make_options(mask_groups=3).mask_groups == 3
     hdr = open(os.path.join(ROOT, "include", "svt.h")).read()
-    for name, v in (("SVT_PATH_AUTO", 0), ("SVT_PATH_QUERY", 1), ("SVT_PATH_TILE", 2), ("SVT_PATH_EXHAUSTIVE", 3)):
+    for name, v in (("SVT_PATH_AUTO", 0), ("SVT_PATH_QUERY", 1), ("SVT_PATH_TILE", 2), ("SVT_PATH_EXHAUSTIVE", 3),
+                    ("SVT_PATH_LARGE_K", 4)):
         assert re.search(rf"{name} = {v}\b", hdr), name
     assert re.search(r"#define SVT_OPT_MERGE_FROM_SLOTS 1u", hdr)
     assert re.search(r"#define SVT_OPT_FORCE_REDO 2u", hdr)
@@ -130,6 +131,8 @@ def test_options_struct_layout():
     assert re.search(r"#define SVT_MAX_MASK_GROUPS 4", hdr) and svt.SVT_MAX_MASK_GROUPS == 4
     assert re.search(r"#define SVT_NOALLOC_SCRATCH_BYTES \(\(size_t\)256 << 20\)", hdr)
     assert svt.SVT_NOALLOC_SCRATCH_BYTES == 256 << 20
+    assert re.search(r"#define SVT_MAX_K 2048\b", hdr) and svt.SVT_MAX_K == 2048
+    assert re.search(r"#define SVT_MAX_K_LARGE 16384\b", hdr) and svt.SVT_MAX_K_LARGE == 16384
 
 
 def test_rerank_net_struct_layout():

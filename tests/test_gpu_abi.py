@@ -56,7 +56,9 @@ def test_search_argument_errors(env):
     nlist = 8
     cases = [
         ("k = 0", dict(k=0), svt.SVT_EINVAL),
-        ("k = 2049", dict(k=2049), svt.SVT_EINVAL),
+        ("k = SVT_MAX_K_LARGE + 1", dict(k=svt.SVT_MAX_K_LARGE + 1), svt.SVT_EINVAL),
+        ("k = 2049 on the query path", dict(k=2049, opts=svt.make_options("query")), svt.SVT_EINVAL),
+        ("k = 2049 on the tile path", dict(k=2049, opts=svt.make_options("tile")), svt.SVT_EINVAL),
         ("nprobe = 0", dict(nprobe=0), svt.SVT_EINVAL),
         ("nprobe = nlist + 1", dict(nprobe=nlist + 1), svt.SVT_EINVAL),
         ("n_queries < 0", dict(B=-1), svt.SVT_EINVAL),
@@ -86,7 +88,7 @@ def test_search_argument_errors(env):
 def test_workspace_size_errors(env):
     svt, ix, q, m, outs, ws, B, k = env
     L = svt.lib()
-    for args in ((B, 0, k), (B, 9, k), (B, 4, 0), (B, 4, 2049), (-1, 4, k), (70000, 4, k)):
+    for args in ((B, 0, k), (B, 9, k), (B, 4, 0), (B, 4, svt.SVT_MAX_K_LARGE + 1), (-1, 4, k), (70000, 4, k)):
         assert L.svt_search_workspace_size(ix.handle, *args, None) == 0, args
         assert svt.svt_last_error()
     assert L.svt_search_workspace_size(ix.handle, B, 4, k, ctypes.byref(svt.make_options(5))) == 0
