@@ -49,7 +49,11 @@ def parse():
     ap.add_argument("--workload", default="80m", help="preset: tiny, 1m, 10m, 80m, exh")
     ap.add_argument("--batch", type=int, default=None, help="queries per step (default: preset's largest)")
     ap.add_argument("--batches", type=int, default=4, help="distinct query batches cycled over the steps")
-    ap.add_argument("--path", default="auto", choices=["auto", "query", "tile"], help="search path")
+    ap.add_argument("--path", default="auto", choices=["auto", "query", "tile", "large_k"], help="search path")
+    ap.add_argument("--k", type=int, default=None, help="top-k (default: the preset's; above 2048: large-k path)")
+    ap.add_argument("--mask-groups", type=int, default=1,
+                    help="request masks per query (an item is eligible when any passes); group 0 is the query's own "
+                         "required tokens, group g those of another synthetic query")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU-seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic", default=None, help="traffic summary (profiles/); default by workload")
@@ -165,16 +169,24 @@ def cpu_model() -> str:
 def algorithmic_bytes(cat, sigs_sorted, offsets, queries, masks, nprobe, W, d):
     """Bytes the scan must move for one batch when every probed cluster is read once per batch:
     signatures of every item of the union of probed clusters, plus the row of every item eligible for
-    at least one query probing its cluster.  Also returns the number of eligible (query, item) pairs."""
+    at least one query probing its cluster.  Also returns the number of eligible (query, item) pairs.
+    masks: [B, W] or [B, G, W] (eligible when any group passes)."""
     nlist = cat.centroids.shape[0]
+    if masks.ndim == 2:
+        masks = masks[:, None, :]
+
+    def passes(sg, mb):   # items of sg passing any of the masks mb [G, W]
+        ok = np.zeros(sg.shape[0], bool)
+        for m in mb:
+            ok |= np.all((sg & m) == m, axis=1)
+        return ok
+
     if nprobe == nlist:
         # every query probes every cluster: one pass over the catalogue per query
         need = np.zeros(sigs_sorted.shape[0], bool)
         pairs = 0
         for b in range(queries.shape[0]):
-            ok = np.ones(sigs_sorted.shape[0], bool)
-            for w in range(W):
-                ok &= (sigs_sorted[:, w] & masks[b, w]) == masks[b, w]
+            ok = passes(sigs_sorted, masks[b])
             pairs += int(ok.sum())
             need |= ok
             if b % 8 == 7:
@@ -200,7 +212,7 @@ def algorithmic_bytes(cat, sigs_sorted, offsets, queries, masks, nprobe, W, d):
         sg = sigs_sorted[a:e]
         need = np.zeros(e - a, bool)
         for b in qs:
-            ok = np.all((sg & masks[b]) == masks[b], axis=1)
+            ok = passes(sg, masks[b])
             pairs += int(ok.sum())
             need |= ok
         sig_bytes += (e - a) * 8 * W
@@ -230,6 +242,8 @@ def main():
     cfg = cat.cfg
     W, h, d, nprobe, k = cfg["sig_words"], cfg["n_hashes"], cfg["dim"], cfg["nprobe"], cfg["k"]
     B = args.batch or max(cfg["batches"])
+    if args.k is not None:
+        k = args.k
     log(f"[bench] generated {name}: {cat.n_items} items d={d} nlist={cfg['nlist']} in {time.time() - t0:.1f}s")
     t0 = time.time()
     sigs = svt.svt_bloom_sign(cat.tokens, h, W)
@@ -242,11 +256,17 @@ def main():
     for i in range(args.batches):
         qs = synth.queries(cat, B, offset=i * B)
         masks = np.stack([svt.svt_bloom_mask(qs.required(b), h, W) for b in range(B)])
+        if args.mask_groups > 1:
+            groups = [masks]
+            for g in range(1, args.mask_groups):
+                alt = synth.queries(cat, B, offset=(args.batches * g + i) * B)
+                groups.append(np.stack([svt.svt_bloom_mask(alt.required(b), h, W) for b in range(B)]))
+            masks = np.ascontiguousarray(np.stack(groups, axis=1))   # [B, G, W]
         batches.append(dict(q=qs.queries, m=masks, q_d=torch.from_numpy(qs.queries).cuda(),
                             m_d=torch.from_numpy(masks.view(np.int64)).cuda()))
-    opts = svt.make_options(args.path)
+    opts = svt.make_options(args.path, mask_groups=args.mask_groups)
     path = svt.svt_search_path(ix.handle, B, nprobe, k, opts)
-    kernel = {"query": "k_scan", "tile": "k_tscan", "exhaustive": "k_xscan"}[path]
+    kernel = {"query": "k_scan", "tile": "k_tscan", "exhaustive": "k_xscan", "large_k": "k_lk_scan"}[path]
     ws = ix.workspace(B, nprobe, k, opts)
     log(f"[bench] workspace {ws.numel() / 2**20:.1f} MiB (path {args.path}: {path}, scan kernel {kernel})")
     outs = dict(out_ids=torch.empty((B, k), dtype=torch.int64, device="cuda"),
@@ -309,7 +329,7 @@ def main():
             ts = time.perf_counter()
             e0.record()
             svt.svt_search(ix.handle, ql_d[(i % n_lat) * B:(i % n_lat + 1) * B], ml_d[(i % n_lat) * B:(i % n_lat + 1) * B],
-                           nprobe, k, workspace=ws, out_stats=st_l, opts=opts, **outs)
+                           nprobe, k, workspace=ws, out_stats=st_l, opts=svt.make_options(args.path), **outs)
             e1.record()
             torch.cuda.synchronize()
             if i >= 5:   # the first searches of new queries warm the caches
@@ -415,7 +435,8 @@ def main():
 
     wl = (f"{name}: {cat.n_items} items, d={d}, nlist={cfg['nlist']} "
           f"({'Zipf ' + str(cfg['cluster_zipf']) if cfg['cluster_zipf'] else 'uniform'} cluster sizes), "
-          f"{64 * W}-bit Bloom signatures, nprobe={nprobe}, top-{k}, batch {B}")
+          f"{64 * W}-bit Bloom signatures, nprobe={nprobe}, top-{k}, batch {B}"
+          + (f", {args.mask_groups} masks per query (any passes)" if args.mask_groups > 1 else ""))
     line = {
         "metric": METRIC,
         "value": value,
@@ -430,7 +451,8 @@ def main():
         "dtype": "int8",
         "data": "synthetic (seeded generator; inputs resident in HBM)",
         "config": {"workload": wl, "preset": name, "batch": B, "n_items": cat.n_items, "dim": d,
-                   "nlist": cfg["nlist"], "nprobe": nprobe, "k": k, "sig_bits": 64 * W},
+                   "nlist": cfg["nlist"], "nprobe": nprobe, "k": k, "sig_bits": 64 * W,
+                   "mask_groups": args.mask_groups},
         "qps": B * args.steps / elapsed,
         "items_scanned_per_s": steps_scanned / elapsed,
         "stage_ms_per_step": {kname: v / max(n_stage, 1) for kname, v in stage_ms.items()},
@@ -442,6 +464,9 @@ def main():
                      "kernel": kernel, "path": path,
                      "algorithmic_bytes_per_launch": alg_per_launch,
                      "scan_ms": scan_ms,
+                     "scan_stage": ("the large-k path's passes: every digit-count pass and pick, the collect pass and "
+                                    "the sort (the algorithmic bytes are those of one pass)") if path == "large_k"
+                                   else "the scan kernel",
                      "step_achieved": alg_per_launch / (elapsed / args.steps) / 1e9,
                      "step_frac": alg_per_launch / (elapsed / args.steps) / 1e9 / HBM_PEAK_GBS,
                      "read_ceiling": ceiling,
