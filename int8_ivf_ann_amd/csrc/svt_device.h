@@ -131,7 +131,25 @@ __device__ uint64_t block_select(ForEach for_each, int need, SelScratch &sh) {
     const uint64_t m = hi_mask, p = prefix;
     const int s = shift;
     for_each([&](uint64_t key) {
-      if ((key & m) == p) atomicAdd(&sh.hist[(key >> s) & 255u], 1u);
+      // Keys cluster in a few buckets (scores are concentrated), and same-address LDS atomics of one
+      // wave serialise: the lanes of up to 4 buckets that at least 4 active lanes share add with one
+      // atomic per bucket, the rest one each.  Every key is counted once.
+      const bool in = (key & m) == p;
+      const uint32_t bin = (uint32_t)(key >> s) & 255u;
+      bool mine = in;
+      uint64_t act = __ballot(mine);
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        if (act == 0ull) break;
+        const int leader = __ffsll((long long)act) - 1;
+        const uint32_t b0 = __shfl(bin, leader);
+        const uint64_t same = __ballot(mine && bin == b0);
+        if (__popcll(same) < 4) break;
+        if (l == leader) atomicAdd(&sh.hist[b0], (uint32_t)__popcll(same));
+        if (mine && bin == b0) mine = false;
+        act &= ~same;
+      }
+      if (mine) atomicAdd(&sh.hist[bin], 1u);
     });
     __syncthreads();
     if (tid < 64) {

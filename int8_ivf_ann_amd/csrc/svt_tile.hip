@@ -960,7 +960,7 @@ struct PMergeArgs {
   int32_t *out_counts;
 };
 
-constexpr int kPoolLds = 12 * kSelThreads;   // pool keys merged in LDS (96 KB)
+constexpr int kPoolLds = 19 * kSelThreads;   // pool keys merged in LDS (152 KB of the 160 KB)
 static_assert(kPoolLds >= kMergeCap, "the LDS merge holds at least the staging capacity");
 
 // Keep the keys >= lo of cand[0..n) (n <= kPoolLds), in place, as (score, id) keys when to_id; returns
@@ -1039,45 +1039,51 @@ __global__ __launch_bounds__(kSelThreads) void k_pmerge(PMergeArgs a) {
       m = pool_keep(cand, n, 0ull, true, a.ix.perm, wave_tot);
     }
   } else {
-    // a pool larger than LDS: select in HBM
-    const uint64_t T = block_select<kSelThreads>(
-        [&](auto f) {
-          for (int i = tid; i < n; i += kSelThreads) f(pool[i]);
-        },
-        k, sel);
+    // a pool larger than LDS: select in HBM.  Every sweep over the pool loads 8 keys per thread before
+    // using any (pool_visit), so a sweep waits for the memory about n / (8 * kSelThreads) times.
+    auto pool_visit = [&](auto f) {
+      for (int i0 = tid; i0 < n; i0 += 8 * kSelThreads) {
+        uint64_t v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int i = i0 + u * kSelThreads;
+          v[u] = i < n ? pool[i] : 0ull;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (i0 + u * kSelThreads < n) f(i0 + u * kSelThreads, v[u]);
+      }
+    };
+    const uint64_t T = block_select<kSelThreads>([&](auto f) { pool_visit([&](int, uint64_t v) { f(v); }); }, k, sel);
     const uint64_t lo = (T >> 32) << 32;   // the smallest key with the k-th best score
     // keys at or above lo become (score, id) keys in place; their upper half, the score, is unchanged
-    for (int i = tid; i < n; i += kSelThreads) {
-      const uint64_t v = pool[i];
+    pool_visit([&](int i, uint64_t v) {
       if (v >= lo) pool[i] = make_key((int32_t)((uint32_t)(v >> 32) ^ 0x80000000u), (uint32_t)a.ix.perm[(uint32_t)v]);
-    }
+    });
     if (tid == 0) ncand = 0;
     __syncthreads();
-    for (int i = tid; i < n; i += kSelThreads) {
-      const uint64_t v = pool[i];
+    pool_visit([&](int, uint64_t v) {
       if (v >= lo) {
         const int o = atomicAdd(&ncand, 1);
         if (o < kPoolLds) cand[o] = v;
       }
-    }
+    });
     __syncthreads();
     m = ncand;
     if (m > kPoolLds) {
       // heavy ties at the k-th score: select among the converted keys in the pool
       const uint64_t Tk = block_select<kSelThreads>(
           [&](auto f) {
-            for (int i = tid; i < n; i += kSelThreads) {
-              const uint64_t v = pool[i];
+            pool_visit([&](int, uint64_t v) {
               if (v >= lo) f(v);
-            }
+            });
           },
           k, sel);
       if (tid == 0) ncand = 0;
       __syncthreads();
-      for (int i = tid; i < n; i += kSelThreads) {
-        const uint64_t v = pool[i];
+      pool_visit([&](int, uint64_t v) {
         if (v >= lo && v >= Tk) cand[atomicAdd(&ncand, 1)] = v;   // exactly k distinct keys
-      }
+      });
       __syncthreads();
       m = k;
     } else if (m > k) {

@@ -263,3 +263,26 @@ def test_nprobe_beyond_lds_probe_list(svt, opts):
     q = rng.integers(-127, 128, (6, 16)).astype(np.int8)
     masks = P.random_masks(rng, 6, 2, nbits_max=3)
     _run(svt, opts, items, sigs, cl, cent, 1.0, q, masks, 5_000, 300, "many-probes")
+
+
+@pytest.mark.parametrize("tie_heavy", [False, True])
+def test_tile_pool_beyond_lds(svt, tie_heavy):
+    """Pools larger than the merge's LDS stage (19456 keys): with 65536-key pools and streams the pool holds
+    whole, every eligible item is a candidate, so the pool merge selects in HBM.  With components in
+    {-1, 0, 1} the keys at the k-th best score alone exceed LDS (the heavy-ties branch)."""
+    rng = np.random.default_rng(77 + tie_heavy)
+    d, n, nlist, nprobe, B, k = (16, 60000, 4, 2, 5, 2048) if tie_heavy else (64, 60000, 4, 2, 5, 2048)
+    items, sigs, list_of, cent = P.small_catalogue(rng, n=n, d=d, nlist=nlist, W=2, tie_heavy=tie_heavy)
+    ix = svt.Index(items, sigs, list_of, cent, 1.0)
+    try:
+        q = rng.integers(-1, 2, size=(B, d)).astype(np.int8) if tie_heavy else \
+            rng.integers(-127, 128, size=(B, d)).astype(np.int8)
+        masks = np.zeros((B, 2), np.uint64)
+        masks[1, 0] = np.uint64(1) << np.uint64(3)   # about half the items
+        opts = svt.make_options("tile", 65536)
+        assert svt.svt_search_path(ix.handle, B, nprobe, k, opts) == "tile"
+        got = gpu_search(ix, q, masks, nprobe, k, opts=opts)
+        assert int(got[4][:, 1].max()) > 19456, "no pool beyond the LDS stage"
+        compare(got, oracle_search(items, sigs, list_of, cent, 1.0, q, masks, nprobe, k), k, "pool beyond LDS")
+    finally:
+        ix.close()
