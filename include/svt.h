@@ -154,10 +154,12 @@ int svt_index_info(const svt_index *ix, int64_t *n_items, int32_t *dim, int32_t 
  *                   candidates (with a threshold above the minimum) or overflows is redone on the query
  *                   path, so the result stays exact whatever the data.
  *   SVT_PATH_LARGE_K  any k up to SVT_MAX_K_LARGE (the path every search with k > SVT_MAX_K takes;
- *                   also selectable for smaller k): an exact radix select over the eligible items'
- *                   (score, id) keys, one 11-bit digit per pass over each query's probed items (at
- *                   most 5 passes, a pass skipping the queries already decided), then one pass that
- *                   keeps the keys at or above each query's threshold and an LDS sort of those
+ *                   also selectable for smaller k).  One scan keeps every eligible item whose score
+ *                   reaches a threshold estimated from the query's samples (about 2k of them) in a
+ *                   per-query pool; a pool that proves the top k is selected and sorted.  Any other
+ *                   query runs an exact radix select over its eligible items' (score, id) keys, one
+ *                   11-bit digit per pass over its probed items (at most 5 passes), then one pass that
+ *                   keeps the keys at or above its threshold and an LDS sort of those
  *                   ["SilverTorch - Index as Model", fused Int8 ANN paragraph and compute-cost table:
  *                    top-k well beyond GPU FAISS's 2048].  Each pass reads the probed items again.
  */
@@ -166,9 +168,10 @@ enum { SVT_PATH_AUTO = 0, SVT_PATH_QUERY = 1, SVT_PATH_TILE = 2, SVT_PATH_EXHAUS
 /* svt_search_options.flags */
 #define SVT_OPT_MERGE_FROM_SLOTS 1u  /* query path: the merge reads every chunk's slot instead of the keys
                                         gathered above each query's final bound (a test of that branch)  */
-#define SVT_OPT_FORCE_REDO 2u        /* tile path: every query's threshold is set above any score, so
-                                        every query with an eligible item is redone on the query path
-                                        (a test of that branch)                                         */
+#define SVT_OPT_FORCE_REDO 2u        /* tile and large-k paths: every query's threshold is set above any
+                                        score, so every query with an eligible item is redone on the
+                                        query path (tile) or goes through the digit passes (large k)
+                                        (a test of those branches)                                      */
 
 /*
  * Options of one search.  A NULL pointer, or a zero-initialised struct, selects the defaults.  The
@@ -176,8 +179,10 @@ enum { SVT_PATH_AUTO = 0, SVT_PATH_QUERY = 1, SVT_PATH_TILE = 2, SVT_PATH_EXHAUS
  * svt_search.
  *   path       SVT_PATH_AUTO (default), SVT_PATH_QUERY, SVT_PATH_TILE or SVT_PATH_LARGE_K; with
  *              k > SVT_MAX_K only SVT_PATH_AUTO and SVT_PATH_LARGE_K are accepted
- *   pool_keys  tile path: candidate keys kept per query (0 = default, 16 k rounded up to 4096); a
- *              smaller value makes more pools overflow (their queries are redone)
+ *   pool_keys  tile path: candidate keys kept per query (0 = default, 16 k rounded up to 4096); large-k
+ *              path: the same, default 8 k rounded up to 4096 (no pools when the batch's pools would
+ *              exceed 1 GiB); a smaller value makes more pools overflow (their queries are redone, or go
+ *              through the digit passes)
  *   flags      OR of SVT_OPT_* above
  *   mask_groups  G in [0, SVT_MAX_MASK_GROUPS]: each query brings G request masks ([B][G][sig_words]) and an
  *              item is eligible when its signature passes at least one of them (a targeting rule set as a

@@ -493,7 +493,7 @@ struct Layout {
   // tile and exhaustive paths (absent on the query path)
   size_t sthr, redo, pool_cnt, pool, gcnt, gfill, gstart, estart, uoff, mrec, entries, ctab, thdr, tblk, sbuf;
   size_t qdens, clog, ccost, cstart_u;
-  size_t lk_hist, lk_state, lk_cnt, lk_keys;   // large-k path
+  size_t lk_hist, lk_state, lk_cnt, lk_keys, lk_cstart;   // large-k path
   size_t total;
   SearchShape sh;
 };
@@ -592,10 +592,20 @@ Layout layout(const svt_index *ix, int32_t B, int32_t nprobe, int32_t k, const s
   L.mkeys = take((size_t)B * kGatherCap * sizeof(uint64_t));
   L.stats = take((size_t)B * 2 * sizeof(int64_t));
   if (lk) {
+    // pool mode: 8k keys per query (or the options' pool_keys), while the pools take at most 1 GiB
+    const int64_t def = ((int64_t)8 * k + 4095) / 4096 * 4096;
+    const int64_t cap = (o && o->pool_keys > 0) ? o->pool_keys : def;
+    sh.pool_cap = (int64_t)B * cap * 8 <= ((int64_t)1 << 30) ? (int32_t)cap : 0;
+    if (sh.pool_cap > 0) {
+      L.sthr = take((size_t)B * sizeof(int32_t));
+      L.pool_cnt = take((size_t)B * sizeof(uint32_t));
+      L.pool = take((size_t)B * (size_t)sh.pool_cap * sizeof(uint64_t));
+    }
     L.lk_hist = take((size_t)B * kLkBins * sizeof(uint32_t));
     L.lk_state = take((size_t)B * sizeof(LkState));
     L.lk_cnt = take((size_t)B * sizeof(uint32_t));
     L.lk_keys = take((size_t)B * (size_t)k * sizeof(uint64_t));
+    L.lk_cstart = take((size_t)(B + 1) * sizeof(int32_t));
   }
   if (sh.path == kPathTile || sh.path == kPathExh) {
     const int64_t def = std::max<int64_t>(4096, ((int64_t)16 * k + 4095) / 4096 * 4096);
@@ -678,10 +688,16 @@ Work carve(const Layout &L, void *workspace, int64_t *out_stats) {
   w.mkeys = (uint64_t *)(base + L.mkeys);
   w.stats = out_stats ? out_stats : (int64_t *)(base + L.stats);
   if (sh.path == kPathLargeK) {
+    if (sh.pool_cap > 0) {
+      w.sthr = (int32_t *)(base + L.sthr);
+      w.pool_cnt = (uint32_t *)(base + L.pool_cnt);
+      w.pool = (uint64_t *)(base + L.pool);
+    }
     w.lk_hist = (uint32_t *)(base + L.lk_hist);
     w.lk_state = (LkState *)(base + L.lk_state);
     w.lk_cnt = (uint32_t *)(base + L.lk_cnt);
     w.lk_keys = (uint64_t *)(base + L.lk_keys);
+    w.lk_cstart = (int32_t *)(base + L.lk_cstart);
   }
   if (sh.path == kPathTile || sh.path == kPathExh) {
     w.sthr = (int32_t *)(base + L.sthr);
@@ -740,8 +756,10 @@ int enqueue_search(const svt_index *ix, const SearchShape &sh, const Work &w, co
   if ((e = launch_coarse_keys(dx, queries, sh.B, w, s)) != hipSuccess) return fail_hip(e, "launch coarse_keys");
   if ((e = mark()) != hipSuccess) return fail_hip(e, "event");
   {
-    SearchShape cs = sh;   // the coarse stage of the large-k path is the query path's
-    cs.k = std::min(sh.k, (int32_t)SVT_MAX_K);
+    SearchShape cs = sh;
+    // large-k path: the threshold rank (for kAlpha * k candidates) is set for k / 2, so that a pool of 8k
+    // keys expects about 2k candidates
+    if (sh.path == kPathLargeK) cs.k = std::max(1, (sh.k + 1) / 2);
     if ((e = launch_coarse_select(dx, queries, masks, cs, w, s)) != hipSuccess) return fail_hip(e, "launch coarse_select");
   }
   if (sh.path == kPathLargeK) {

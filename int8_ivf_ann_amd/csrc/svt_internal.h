@@ -171,14 +171,16 @@ struct UEntry {                      // one entry of the union stream
 // Searches with k above SVT_MAX_K (svt_largek.hip): a radix select over 55-bit keys, 11-bit digits from
 // bit 44 down, one counting pass over the probed items per digit, then a collect pass
 constexpr int kLkDigit = 11, kLkBins = 1 << kLkDigit, kLkTopShift = 44, kLkPasses = 5;
-constexpr int kLkChunk = 8192;   // stream positions per workgroup of a pass
+constexpr int kLkChunk = 4096;   // stream positions per chunk of a pass
+constexpr int kLkScanWGs = 2048; // workgroups of a pass, walking the batch's chunks
 struct LkState {
   uint64_t prefix;   // key bits fixed so far; once done, the threshold (0: every eligible key)
   int32_t shift;     // lowest bit of the digit the next pass counts
   int32_t need;      // keys still to take in the bucket the prefix names
-  int32_t done;
+  int32_t done;      // 0: selecting; kLkDone: threshold final; kLkFromPool: the pool gave the k keys
   int32_t pad;
 };
+constexpr int32_t kLkDone = 1, kLkFromPool = 2;
 
 struct Work {
   int32_t *coarse_scores;   // [B][nlist]   coarse scores <query, centroid>
@@ -229,6 +231,7 @@ struct Work {
   LkState *lk_state;        // [B]
   uint32_t *lk_cnt;         // [B]          keys collected
   uint64_t *lk_keys;        // [B][k]       the collected keys, unordered
+  int32_t *lk_cstart;       // [B + 1]      first chunk of each query's stream (kLkChunk positions each)
 };
 
 enum { kPathQuery = 0, kPathTile = 1, kPathExh = 2, kPathLargeK = 3 };

@@ -1633,7 +1633,9 @@ hipError_t launch_coarse_keys(const DevIndex &ix, const int8_t *queries, int32_t
 
 hipError_t launch_coarse_select(const DevIndex &ix, const int8_t *queries, const uint64_t *masks,
                                 const SearchShape &sh, const Work &w, hipStream_t s) {
-  const int thr_mode = sh.path != kPathTile ? 0 : (sh.force_redo ? 2 : 1);
+  // speculative thresholds for the tile path's pools and the large-k path's (when it has them)
+  const bool pools = sh.path == kPathTile || (sh.path == kPathLargeK && sh.pool_cap > 0);
+  const int thr_mode = pools ? (sh.force_redo ? 2 : 1) : 0;
   k_coarse_select<<<sh.B, kSelThreads, 0, s>>>(ix, queries, masks, sh.G, sh.B, sh.nprobe, sh.k, sh.pool_cap,
                                                 thr_mode, w);
   return hipGetLastError();

@@ -1,8 +1,10 @@
-"""Searches with k above the fused paths' 2048 (the large-k path: a radix select over repeated passes,
-then a collect pass and an LDS sort) against the CPU oracle, element by element: ids, int32 scores,
-counts, scan statistics and dequantised scores.  Also: the path forced for small k equals the fused
-paths, heavy ties, fewer eligible items than k, several masks per query, an updated index, the
-no-allocation entry point and a 10M-item catalogue."""
+"""Searches with k above the fused paths' 2048 (the large-k path: one scan into per-query pools above a
+sampled threshold, else a radix select over repeated passes; a collect pass and an LDS sort) against the
+CPU oracle, element by element: ids, int32 scores, counts, scan statistics and dequantised scores.  Each
+case runs with pools (the default), with every query sent through the passes (thresholds above every
+score) and with pools too small to prove k.  Also: the path forced for small k equals the fused paths,
+heavy ties, fewer eligible items than k, several masks per query, an updated index, the no-allocation
+entry point and a 10M-item catalogue."""
 import numpy as np
 import pytest
 
@@ -23,6 +25,14 @@ def svt():
     return m
 
 
+MODES = {"pool": {}, "passes": {"flags": 2}, "overflow": {"pool_keys": 4096}}
+
+
+def _opts(svt, mode, G=1):
+    kw = dict(MODES[mode])
+    return svt.make_options("auto", kw.get("pool_keys", 0), kw.get("flags", 0), G)
+
+
 def _masks(rng, B, W, G, nbits_max=3):
     if G == 1:
         return P.random_masks(rng, B, W, nbits_max)
@@ -38,8 +48,9 @@ CASES = [  # d, W, n, nlist, nprobe, k, B, G, scaled
 ]
 
 
+@pytest.mark.parametrize("mode", list(MODES))
 @pytest.mark.parametrize("case", CASES, ids=[f"d{c[0]}_w{c[1]}_n{c[2]}_p{c[4]}_k{c[5]}_g{c[7]}" for c in CASES])
-def test_large_k_matches_oracle(svt, case):
+def test_large_k_matches_oracle(svt, case, mode):
     d, W, n, nlist, nprobe, k, B, G, scaled = case
     rng = np.random.default_rng(500 + d + k)
     items, sigs, list_of, cent = P.small_catalogue(rng, n=n, d=d, nlist=nlist, W=W)
@@ -50,8 +61,8 @@ def test_large_k_matches_oracle(svt, case):
         masks = _masks(rng, B, W, G)
         qs = rng.uniform(20.0, 60.0, size=B).astype(np.float32) if scaled else None
         assert svt.svt_search_path(ix.handle, B, nprobe, k) == "large_k"
-        say(f"large-k d={d} W={W} n={n} nprobe={nprobe}/{nlist} k={k} B={B} G={G}")
-        got = gpu_search(ix, q, masks, nprobe, k, query_scales=qs, opts=svt.make_options(mask_groups=G))
+        say(f"large-k {mode} d={d} W={W} n={n} nprobe={nprobe}/{nlist} k={k} B={B} G={G}")
+        got = gpu_search(ix, q, masks, nprobe, k, query_scales=qs, opts=_opts(svt, mode, G))
         ref = oracle_search(items, sigs, list_of, cent, scale, q, masks, nprobe, k, query_scales=qs)
         compare(got, ref, k, f"large-k {case}")
     finally:
@@ -77,7 +88,8 @@ def test_large_k_path_equals_fused_paths(svt, k):
         ix.close()
 
 
-def test_large_k_heavy_ties(svt):
+@pytest.mark.parametrize("mode", list(MODES))
+def test_large_k_heavy_ties(svt, mode):
     # components in {-1, 0, 1}: a handful of distinct scores, so the selection runs into the id digits
     rng = np.random.default_rng(7)
     d, n, nlist, nprobe, B, k = 16, 30000, 12, 7, 4, 4000
@@ -87,13 +99,14 @@ def test_large_k_heavy_ties(svt):
         q = rng.integers(-1, 2, size=(B, d)).astype(np.int8)
         masks = np.zeros((B, 1), np.uint64)
         masks[1, 0] = np.uint64(1) << np.uint64(5)
-        got = gpu_search(ix, q, masks, nprobe, k)
-        compare(got, oracle_search(items, sigs, list_of, cent, 1.0, q, masks, nprobe, k), k, "large-k ties")
+        got = gpu_search(ix, q, masks, nprobe, k, opts=_opts(svt, mode))
+        compare(got, oracle_search(items, sigs, list_of, cent, 1.0, q, masks, nprobe, k), k, f"large-k ties {mode}")
     finally:
         ix.close()
 
 
-def test_large_k_after_updates(svt):
+@pytest.mark.parametrize("mode", ["pool", "passes"])
+def test_large_k_after_updates(svt, mode):
     rng = np.random.default_rng(8)
     d, W, n, nlist, nprobe, B, k = 32, 2, 12000, 10, 4, 5, 6000
     items, sigs, list_of, cent = P.small_catalogue(rng, n=n, d=d, nlist=nlist, W=W)
@@ -115,7 +128,7 @@ def test_large_k_after_updates(svt):
         all_cl = np.concatenate([list_of[keep], new_cl])[order]
         q = rng.integers(-127, 128, size=(B, d)).astype(np.int8)
         masks = P.random_masks(rng, B, W)
-        got = list(gpu_search(ix, q, masks, nprobe, k))
+        got = list(gpu_search(ix, q, masks, nprobe, k, opts=_opts(svt, mode)))
         ref = list(oracle_search(all_items, all_sigs, all_cl, cent, 20.0, q, masks, nprobe, k))
         ref[0] = np.where(ref[0] >= 0, ids[np.maximum(ref[0], 0)], -1)   # oracle rows -> ids
         compare(tuple(got), tuple(ref), k, "large-k updated")
@@ -155,9 +168,10 @@ def test_large_k_10m_batch8(svt):
         qs = synth.queries(cat, B, offset=4096)
         masks = np.stack([svt.svt_bloom_mask(qs.required(b), h, W) for b in range(B)])
         say(f"large-k 10m: {cat.n_items} items, nprobe {nprobe}, k {k}, B {B}")
-        got = gpu_search(ix, qs.queries, masks, nprobe, k)
         ref = oracle_search(cat.items, sigs, cat.list_of, cat.centroids, cat.item_scale, qs.queries, masks, nprobe, k)
-        compare(got, ref, k, "large-k 10m")
+        for mode in MODES:
+            got = gpu_search(ix, qs.queries, masks, nprobe, k, opts=_opts(svt, mode))
+            compare(got, ref, k, f"large-k 10m {mode}")
         say(f"large-k 10m: counts {got[3].tolist()}, eligible {got[4][:, 1].tolist()}")
     finally:
         ix.close()
