@@ -143,12 +143,19 @@ def rerank_leg(args, torch, svt, ix, cat, bt, cand, d):
         nv_s = int((cand_h[:n_s] >= 0).sum())
         cpu = {"value": nv_s / cs, "unit": "candidates/s", "cores": 1, "kind": "oracle",
                "sample": f"first {n_s} queries of the batch ({nv_s} candidates, {cs:.2f} s, numpy float64)"}
+    traffic = None   # fabric bytes per launch from the committed summary, when taken on these sources
+    tpath = os.path.join(ROOT, "profiles", f"traffic_k_rerank_{args.workload}_b{B}.md")
+    if os.path.exists(tpath):
+        from int8_ivf_ann_amd.rocprof_summary import read_traffic
+        tj = read_traffic(tpath)
+        if tj.get("kernel_source_sha") == kernel_source_hash():
+            traffic = float(tj["hbm_bytes_per_launch"])
     res = {"kernel": "k_rerank", "candidates_per_s": n_valid / (ms * 1e-3), "ms_per_launch": ms,
            "config": {"batch": B, "n_cand": n_cand, "k_out": k_out, "experts": RERANK_EXPERTS,
                       "hidden": RERANK_HIDDEN, "dim": d, "candidates": "the search's top-k of the same batch"},
            "roofline": {"bound": "mfma", "achieved": achieved, "peak": FP32_MATRIX_PEAK_TFLOPS, "unit": "TFLOP/s",
                         "frac": achieved / FP32_MATRIX_PEAK_TFLOPS, "flops_per_launch": flops,
-                        "traffic": None},
+                        "traffic": traffic},
            "cpu_baseline": cpu}
     log(f"[bench] rerank {B}x{n_cand} -> {k_out}: {ms:.4f} ms/launch, {achieved:.1f} TFLOP/s "
         f"({100 * achieved / FP32_MATRIX_PEAK_TFLOPS:.1f}% of fp32 matrix peak)")
