@@ -240,7 +240,8 @@ int svt_search_path(const svt_index *ix, int32_t n_queries, int32_t nprobe, int3
  * Result rows are sorted by (score desc, id asc) and identical for any batch composition and path.
  * n_queries == 0 returns SVT_OK without enqueuing anything.
  * Errors: SVT_EINVAL (NULL required pointer, n_queries < 0 or > 65535, nprobe or k out of range,
- * misaligned queries, masks or workspace, workspace too small, invalid options), SVT_ESTATE (freed
+ * misaligned queries, masks, workspace, outputs or query_scales (each aligned to its element size),
+ * workspace too small, invalid options), SVT_ESTATE (freed
  * index), SVT_EDEVICE (launch failure).  On any error nothing is enqueued and no output is written.
  * Concurrency: the index is read-only; concurrent calls are safe if each uses its own workspace and
  * outputs.  Outputs are valid once hip_stream has been synchronised.
@@ -297,7 +298,8 @@ int svt_search_noalloc(const svt_index *ix, int32_t n_queries, const int8_t *que
  *   out_counts    device, [n_queries] int32 or NULL: min(k_out, candidates scored)
  * The index must not be updated while the call runs.  n_queries == 0 returns SVT_OK without enqueuing.
  * Errors: SVT_EINVAL (NULL required pointer, n_queries < 0 or > 65535, n_cand, k_out, E or H out of
- * range), SVT_ESTATE (freed index), SVT_EDEVICE (launch failure); on error nothing is enqueued.
+ * range, a pointer not aligned to its element size), SVT_ESTATE (freed index), SVT_EDEVICE (launch
+ * failure); on error nothing is enqueued.
  * The call allocates no device memory; concurrent calls with their own outputs are safe.
  */
 #define SVT_RERANK_MAX_EXPERTS 8

@@ -811,6 +811,8 @@ int check_search_ptrs(const int8_t *queries, const uint64_t *masks, const int64_
     return fail(SVT_EINVAL, "%s: NULL queries, masks, out_ids or out_scores", who);
   if (((uintptr_t)queries & 15) != 0) return fail(SVT_EINVAL, "%s: queries not 16-byte aligned", who);
   if (((uintptr_t)masks & 7) != 0) return fail(SVT_EINVAL, "%s: masks not 8-byte aligned", who);
+  if (((uintptr_t)out_ids & 7) != 0 || ((uintptr_t)out_scores & 3) != 0)
+    return fail(SVT_EINVAL, "%s: out_ids not 8-byte or out_scores not 4-byte aligned", who);
   return SVT_OK;
 }
 
@@ -843,6 +845,9 @@ int search_into(const svt_index *ix, int32_t B, const int8_t *queries, const uin
   if (rc != SVT_OK) return rc;
   if (B == 0) return SVT_OK;
   if ((rc = check_search_ptrs(queries, masks, out_ids, out_scores, who)) != SVT_OK) return rc;
+  if (((uintptr_t)out_fscores & 3) || ((uintptr_t)out_counts & 3) || ((uintptr_t)out_stats & 7) ||
+      ((uintptr_t)query_scales & 3))
+    return fail(SVT_EINVAL, "%s: misaligned out_fscores, out_counts, out_stats or query_scales", who);
   if (!workspace) return fail(SVT_EINVAL, "%s: NULL workspace", who);
   if (((uintptr_t)workspace & 255) != 0) return fail(SVT_EINVAL, "%s: workspace not 256-byte aligned", who);
   const Layout L = layout(ix, B, nprobe, k, opts);
@@ -884,6 +889,11 @@ extern "C" int svt_rerank(const svt_index *ix, int32_t B, const int8_t *queries,
     return fail(SVT_EINVAL, "%s: NULL net weight", who);
   if (!queries || !out_ids || !out_scores || (n_cand > 0 && !cand_ids))
     return fail(SVT_EINVAL, "%s: NULL queries, cand_ids or outputs", who);
+  if (((uintptr_t)cand_ids & 7) || ((uintptr_t)out_ids & 7) || ((uintptr_t)out_scores & 3) ||
+      ((uintptr_t)out_counts & 3) || ((uintptr_t)query_scales & 3))
+    return fail(SVT_EINVAL, "%s: misaligned cand_ids, outputs or query_scales", who);
+  for (const float *wp : {net->gate_w, net->gate_b, net->w1, net->b1, net->w2, net->b2})
+    if ((uintptr_t)wp & 3) return fail(SVT_EINVAL, "%s: misaligned net weight", who);
   const hipError_t e = launch_rerank(ix->dev, B, queries, query_scales, n_cand, cand_ids, *net, k_out, out_ids,
                                      out_scores, out_counts, (hipStream_t)hip_stream);
   if (e != hipSuccess) return fail_hip(e, "launch_rerank");

@@ -550,7 +550,6 @@ __global__ __launch_bounds__(kScanThreads, kTOcc) void k_tscan(TScanArgs a) {
     auto more_steps = [&]() { return cw < e_n; };
     // the walk; each iteration: filter the step in flight, request the next step's signatures and the next
     // batch's rows, score the batch requested one iteration earlier
-    int nb = 0;           // rows of the batch in flight
     for (int u = 0; u < R; ++u) mb[u] = 0u;   // the first iteration scores an empty batch
     uint32_t bh_prev = 0;
     auto iteration = [&](int4 (&xr)[R], uint32_t (&mr)[R], const int4 (&xs)[R], const uint32_t (&ms)[R]) -> bool {
@@ -562,7 +561,6 @@ __global__ __launch_bounds__(kScanThreads, kTOcc) void k_tscan(TScanArgs a) {
       const uint32_t bh_s = bh_prev;
       const int nr = request_rows(xr, mr);
       bh_prev = bhead;
-      nb = nr;
       score_rows(xs, ms, bh_s);   // also an empty batch: every path reads the rows it requested
       return !sg_live && nr == 0 && head == tail && !more_steps();
     };

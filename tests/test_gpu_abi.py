@@ -34,12 +34,14 @@ def env():
     ix.close()
 
 
-def _call(svt, ix, q, m, outs, ws, B, nprobe, k, opts=None, ws_bytes=None, ws_off=0, qp=None):
+def _call(svt, ix, q, m, outs, ws, B, nprobe, k, opts=None, ws_bytes=None, ws_off=0, qp=None, off=None, qs=None):
+    """off: byte offsets added to output pointers by name (misaligned outputs)."""
     L = svt.lib()
     p = lambda t: ctypes.c_void_p(t.data_ptr())
+    po = lambda name: ctypes.c_void_p(outs[name].data_ptr() + (off or {}).get(name, 0))
     optp = None if opts is None else ctypes.byref(opts)
-    return L.svt_search(ix.handle, B, qp if qp is not None else p(q), p(m), None, nprobe, k, p(outs["ids"]),
-                        p(outs["sc"]), p(outs["fs"]), p(outs["cnt"]), p(outs["st"]), optp,
+    return L.svt_search(ix.handle, B, qp if qp is not None else p(q), p(m), qs, nprobe, k, po("ids"),
+                        po("sc"), po("fs"), po("cnt"), po("st"), optp,
                         ctypes.c_void_p(ws.data_ptr() + ws_off),
                         ws.numel() - ws_off if ws_bytes is None else ws_bytes, None)
 
@@ -66,6 +68,11 @@ def test_search_argument_errors(env):
         ("workspace misaligned", dict(ws_off=8), svt.SVT_EINVAL),
         ("queries misaligned", dict(qp=ctypes.c_void_p(q.data_ptr() + 1)), svt.SVT_EINVAL),
         ("NULL queries", dict(qp=ctypes.c_void_p(0)), svt.SVT_EINVAL),
+        ("out_ids misaligned", dict(off={"ids": 4}), svt.SVT_EINVAL),
+        ("out_scores misaligned", dict(off={"sc": 2}), svt.SVT_EINVAL),
+        ("out_fscores misaligned", dict(off={"fs": 2}), svt.SVT_EINVAL),
+        ("out_counts misaligned", dict(off={"cnt": 1}), svt.SVT_EINVAL),
+        ("out_stats misaligned", dict(off={"st": 4}), svt.SVT_EINVAL),
         ("unknown path", dict(opts=svt.make_options(7)), svt.SVT_EINVAL),
         ("negative pool_keys", dict(opts=svt.make_options("tile", -1)), svt.SVT_EINVAL),
         ("unknown flag", dict(opts=svt.make_options("auto", 0, 8)), svt.SVT_EINVAL),

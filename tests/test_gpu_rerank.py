@@ -277,16 +277,17 @@ def test_rerank_argument_errors(svt):
         w = torch.zeros(8 * 64 * d, dtype=torch.float32, device="cuda")
         p = w.data_ptr()
 
-        def call(E=2, H=4, n_cand=8, k_out=8, B=2, ptrs=None, qp=q.data_ptr(), cp=c.data_ptr()):
+        def call(E=2, H=4, n_cand=8, k_out=8, B=2, ptrs=None, qp=q.data_ptr(), cp=c.data_ptr(), ip=oid.data_ptr(),
+                 sp=osc.data_ptr()):
             net = svt.svt_rerank_net(E, H, *(ptrs or [p] * 6))
-            return L.svt_rerank(ix.handle, B, qp, None, n_cand, cp, ctypes.byref(net), k_out, oid.data_ptr(),
-                                osc.data_ptr(), None, None)
+            return L.svt_rerank(ix.handle, B, qp, None, n_cand, cp, ctypes.byref(net), k_out, ip, sp, None, None)
 
         assert call() == svt.SVT_OK
         torch.cuda.synchronize()
         for kw in ({"E": 0}, {"E": 9}, {"H": 0}, {"E": 4, "H": 17}, {"n_cand": -1}, {"n_cand": 4097},
                    {"k_out": 0}, {"k_out": 2049}, {"B": -1}, {"ptrs": [p, p, 0, p, p, p]}, {"qp": None},
-                   {"cp": None}):
+                   {"cp": None}, {"cp": c.data_ptr() + 4}, {"ip": oid.data_ptr() + 4}, {"sp": osc.data_ptr() + 2},
+                   {"ptrs": [p, p, p + 2, p, p, p]}):
             assert call(**kw) == svt.SVT_EINVAL, kw
         assert call(B=0, qp=None) == svt.SVT_OK
         assert L.svt_rerank(ix.handle, 2, q.data_ptr(), None, 8, c.data_ptr(), None, 8, oid.data_ptr(),
