@@ -50,7 +50,7 @@ class Preset:
         assert np.array_equal(masks, o_masks)
         return qs.queries, masks
 
-    def check(self, B, offset, nprobe=None, k=None, label="", paths=("query", "tile"), groups=1):
+    def check(self, B, offset, nprobe=None, k=None, label="", paths=("query", "tile"), groups=1, flags=0):
         from int8_ivf_ann_amd import svt as svt_mod
         nprobe = nprobe or self.cfg["nprobe"]
         k = k or self.cfg["k"]
@@ -65,7 +65,7 @@ class Preset:
         say(f"{label}: oracle on {B} queries {time.time() - t:.1f}s; eligible/query median "
             f"{int(np.median(ref[4][:, 1]))}")
         for path in paths:
-            opts = svt_mod.make_options(path, mask_groups=groups)
+            opts = svt_mod.make_options(path, 0, flags, groups)
             t = time.time()
             got = gpu_search(self.ix, q, masks, nprobe, k, opts=opts)
             say(f"{label} [{path}]: B={B} gpu search {1e3 * (time.time() - t):.1f} ms (incl. copies)")
