@@ -596,6 +596,10 @@ Layout layout(const svt_index *ix, int32_t B, int32_t nprobe, int32_t k, const s
     const int64_t def = ((int64_t)8 * k + 4095) / 4096 * 4096;
     const int64_t cap = (o && o->pool_keys > 0) ? o->pool_keys : def;
     sh.pool_cap = (int64_t)B * cap * 8 <= ((int64_t)1 << 30) ? (int32_t)cap : 0;
+    // the tile scan fills the pools for batches the tile path would take (at least kTileMinBatch queries,
+    // a union plan that fits, not every cluster probed); otherwise the large-k path's own pooled scan
+    sh.lk_tile = sh.pool_cap > 0 && B >= kTileMinBatch && nprobe < (int32_t)nlist && ix->dev.n_items > 0 &&
+                         tile_fits(ix, B, nprobe, sh.GT) ? 1 : 0;
     if (sh.pool_cap > 0) {
       L.sthr = take((size_t)B * sizeof(int32_t));
       L.pool_cnt = take((size_t)B * sizeof(uint32_t));
@@ -615,7 +619,7 @@ Layout layout(const svt_index *ix, int32_t B, int32_t nprobe, int32_t k, const s
     L.pool_cnt = take((size_t)B * sizeof(uint32_t));
     L.pool = take((size_t)B * (size_t)sh.pool_cap * sizeof(uint64_t));
   }
-  if (sh.path == kPathTile) {
+  if (sh.path == kPathTile || sh.lk_tile) {
     const int64_t blocks = ((int64_t)B * sh.GT + kTMembers - 1) / kTMembers;
     sh.max_entries =
         (int32_t)std::max<int64_t>(1, std::min<int64_t>((int64_t)nlist * blocks, (int64_t)B * nprobe * sh.GT));
@@ -705,7 +709,7 @@ Work carve(const Layout &L, void *workspace, int64_t *out_stats) {
     w.pool_cnt = (uint32_t *)(base + L.pool_cnt);
     w.pool = (uint64_t *)(base + L.pool);
   }
-  if (sh.path == kPathTile) {
+  if (sh.path == kPathTile || sh.lk_tile) {
     w.gcnt = (int32_t *)(base + L.gcnt);
     w.gfill = (int32_t *)(base + L.gfill);
     w.gstart = (int32_t *)(base + L.gstart);
@@ -763,8 +767,10 @@ int enqueue_search(const svt_index *ix, const SearchShape &sh, const Work &w, co
     if ((e = launch_coarse_select(dx, queries, masks, cs, w, s)) != hipSuccess) return fail_hip(e, "launch coarse_select");
   }
   if (sh.path == kPathLargeK) {
-    for (int i = 0; i < 2; ++i)   // end of the select stage; no plan
-      if ((e = mark()) != hipSuccess) return fail_hip(e, "event");
+    if ((e = mark()) != hipSuccess) return fail_hip(e, "event");   // end of the select stage
+    if (sh.lk_tile && (e = launch_tile_plan(dx, masks, sh, w, s)) != hipSuccess) return fail_hip(e, "launch tile plan");
+    if ((e = mark()) != hipSuccess) return fail_hip(e, "event");   // end of the plan stage
+    if (sh.lk_tile && (e = launch_tscan(dx, queries, sh, w, s)) != hipSuccess) return fail_hip(e, "launch tile scan");
     if ((e = launch_large_k(dx, queries, masks, query_scales, sh, ix->top_slots[(size_t)sh.nprobe], w, out_ids,
                             out_scores, out_fscores, out_counts, s)) != hipSuccess)
       return fail_hip(e, "launch large-k passes");

@@ -253,6 +253,7 @@ struct SearchShape {
   int32_t G;            // request masks per query (masks [B][G][sig_words])
   int32_t GT;           // tile path: members per (query, probed cluster), G rounded up to 1, 2 or 4 (a power of
                         // two dividing kTMembers, so that a query's members never straddle two entries)
+  int32_t lk_tile;      // large-k path: the pools are filled by the tile scan ((score, slot) keys)
 };
 
 // most chunks a search can produce.  The costs of the queries add up to at most 4 P Tc.  Without a tail

@@ -291,14 +291,18 @@ __global__ __launch_bounds__(kLkThreads) void k_lk_pick(int32_t B, Work w) {
 // was filled without a threshold, holds every key at or above the query's k-th best: the k best of it
 // (a radix select over the pool, 8 loads in flight per thread) become the collected keys and the query
 // is marked kLkFromPool.  Any other query is left to the passes.
-__global__ __launch_bounds__(kLkEmitThreads) void k_lk_pool(int32_t k, uint32_t cap, Work w) {
+// slot_keys: the pool holds the tile scan's (score, slot) keys.  Their k-th best fixes the k-th best score;
+// every key at that score or above becomes a (score, id) key in place and every other key 0, and the
+// select then runs over those (ties at the k-th score go to the lower ids).
+__global__ __launch_bounds__(kLkEmitThreads) void k_lk_pool(int32_t k, uint32_t cap, int32_t slot_keys,
+                                                           const int32_t *perm, Work w) {
   __shared__ SelScratch sel;
   __shared__ int wave_tot[kLkEmitThreads / 64 + 1];
   const int b = blockIdx.x, tid = threadIdx.x;
   const uint32_t n = w.pool_cnt[b];
   const int32_t thr = w.sthr[b];
   if (n > cap || (n < (uint32_t)k && thr != INT32_MIN)) return;
-  const uint64_t *pool = w.pool + (size_t)b * cap;
+  uint64_t *pool = w.pool + (size_t)b * cap;
   const int nn = (int)n;
   auto visit = [&](auto f) {
     for (int i0 = tid; i0 < nn; i0 += 8 * kLkEmitThreads) {
@@ -313,8 +317,34 @@ __global__ __launch_bounds__(kLkEmitThreads) void k_lk_pool(int32_t k, uint32_t 
         if (i0 + u * kLkEmitThreads < nn) f(v[u]);
     }
   };
-  // the k-th best key (keys are distinct); every key when the pool holds at most k
-  const uint64_t T = nn > k ? block_select<kLkEmitThreads>(visit, k, sel) : 0ull;
+  if (slot_keys) {
+    // the smallest (score, slot) key with the k-th best score (0: every key), then the conversion
+    const uint64_t T1 = nn > k ? block_select<kLkEmitThreads>(visit, k, sel) : 0ull;
+    const uint64_t lo = (T1 >> 32) << 32;
+    for (int i0 = tid; i0 < nn; i0 += 8 * kLkEmitThreads) {
+      uint64_t v[8];
+      int32_t id[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = i0 + u * kLkEmitThreads;
+        v[u] = i < nn ? pool[i] : 0ull;
+        id[u] = (i < nn && v[u] >= lo) ? perm[(uint32_t)v[u]] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = i0 + u * kLkEmitThreads;
+        if (i < nn) pool[i] = v[u] >= lo ? lk_key(key_score(v[u]), id[u]) : 0ull;
+      }
+    }
+    __syncthreads();   // the converted pool, for every thread of the workgroup
+  }
+  // the k-th best key (keys are distinct; 0 marks a key below the k-th best score); every key when the
+  // pool holds at most k
+  const uint64_t T = nn > k ? block_select<kLkEmitThreads>([&](auto f) {
+    visit([&](uint64_t v) {
+      if (v) f(v);
+    });
+  }, k, sel) : 1ull;
   uint64_t *keys = w.lk_keys + (size_t)b * k;
   int base = 0;
   for (int i0 = 0; i0 < nn; i0 += 8 * kLkEmitThreads) {   // in the pool's order, 8 keys per thread a round
@@ -324,14 +354,14 @@ __global__ __launch_bounds__(kLkEmitThreads) void k_lk_pool(int32_t k, uint32_t 
     for (int u = 0; u < 8; ++u) {
       const int i = i0 + u * kLkEmitThreads + tid;
       v[u] = i < nn ? pool[i] : 0ull;
-      take += (i < nn && v[u] >= T) ? 1 : 0;
+      take += (i < nn && v[u] >= T && v[u] != 0ull) ? 1 : 0;
     }
     int tot;
     int off = base + block_excl_scan<kLkEmitThreads>(take, wave_tot, &tot);   // barriers inside
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int i = i0 + u * kLkEmitThreads + tid;
-      if (i < nn && v[u] >= T && off < k) keys[off++] = v[u];
+      if (i < nn && v[u] >= T && v[u] != 0ull && off < k) keys[off++] = v[u];
     }
     base += tot;
   }
@@ -473,9 +503,9 @@ hipError_t launch_large_k(const DevIndex &ix, const int8_t *queries, const uint6
     return hipSuccess;
   };
   hipError_t e;
-  if (sh.pool_cap > 0) {
-    if ((e = scan(kLkPool)) != hipSuccess) return e;
-    k_lk_pool<<<sh.B, kLkEmitThreads, 0, s>>>(sh.k, (uint32_t)sh.pool_cap, w);
+  if (sh.pool_cap > 0) {   // the pools: filled here, or by the tile scan before this call
+    if (!sh.lk_tile && (e = scan(kLkPool)) != hipSuccess) return e;
+    k_lk_pool<<<sh.B, kLkEmitThreads, 0, s>>>(sh.k, (uint32_t)sh.pool_cap, sh.lk_tile, ix.perm, w);
   }
   for (int pass = 0; pass <= kLkPasses; ++pass) {
     const bool collect = pass == kLkPasses;

@@ -175,3 +175,21 @@ def test_large_k_10m_batch8(svt):
         say(f"large-k 10m: counts {got[3].tolist()}, eligible {got[4][:, 1].tolist()}")
     finally:
         ix.close()
+
+
+@pytest.mark.parametrize("mode", list(MODES))
+def test_large_k_large_batch_tile_pools(svt, mode):
+    """Batches of at least 128 queries fill the large-k pools with the tile scan ((score, slot) keys,
+    converted to (score, id) keys at the k-th best score); every query compared."""
+    rng = np.random.default_rng(42)
+    d, W, n, nlist, nprobe, B, k = 64, 2, 60000, 32, 6, 130, 3000
+    items, sigs, list_of, cent = P.small_catalogue(rng, n=n, d=d, nlist=nlist, W=W)
+    ix = svt.Index(items, sigs, list_of, cent, 30.0)
+    try:
+        q = rng.integers(-127, 128, size=(B, d)).astype(np.int8)
+        masks = P.random_masks(rng, B, W, nbits_max=2)
+        assert svt.svt_search_path(ix.handle, B, nprobe, k) == "large_k"
+        got = gpu_search(ix, q, masks, nprobe, k, opts=_opts(svt, mode))
+        compare(got, oracle_search(items, sigs, list_of, cent, 30.0, q, masks, nprobe, k), k, f"large-k B={B} {mode}")
+    finally:
+        ix.close()

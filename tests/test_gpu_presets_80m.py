@@ -58,3 +58,7 @@ def test_80m_rerank_of_batch256(p80):
     got = (r_ids.cpu().numpy()[sample], r_sc.cpu().numpy()[sample], r_cnt.cpu().numpy()[sample])
     say(f"80m rerank: {int((cand >= 0).sum())} candidates of {len(sample)} sampled queries")
     rerank_check(p80.cat.items, p80.cat.item_scale, q[sample], None, cand, net, k_out, got, "80m rerank")
+
+
+def test_80m_batch256_top16384(p80):
+    p80.check(256, 0, k=16384, label="80m-b256-k16384", paths=("auto",))
