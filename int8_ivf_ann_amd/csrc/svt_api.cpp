@@ -489,7 +489,7 @@ namespace {
 
 struct Layout {
   size_t coarse_scores, probes, seg, pb, qlen, qcost, qtail, cstart, chunks, order, cband, thr, hlo, hshift, ghist, counter,
-      slot_cnt, slot_min, slot_keys, mbound, mcnt, mkeys, stats;
+      slot_cnt, slot_min, slot_keys, mcnt, mkeys, stats;
   // tile and exhaustive paths (absent on the query path)
   size_t sthr, redo, pool_cnt, pool, gcnt, gfill, gstart, estart, uoff, mrec, entries, ctab, thdr, tblk, sbuf;
   size_t qdens, clog, ccost, cstart_u;
@@ -587,7 +587,6 @@ Layout layout(const svt_index *ix, int32_t B, int32_t nprobe, int32_t k, const s
   L.slot_min = take(C * sizeof(uint64_t));
   const bool lk = sh.path == kPathLargeK;
   L.slot_keys = take(C * (size_t)(lk ? 1 : k) * sizeof(uint64_t));   // the large-k path keeps no slots
-  L.mbound = take((size_t)B * sizeof(uint64_t));
   L.mcnt = take((size_t)B * sizeof(uint32_t));
   L.mkeys = take((size_t)B * kGatherCap * sizeof(uint64_t));
   L.stats = take((size_t)B * 2 * sizeof(int64_t));
@@ -687,7 +686,6 @@ Work carve(const Layout &L, void *workspace, int64_t *out_stats) {
   w.slot_cnt = (int32_t *)(base + L.slot_cnt);
   w.slot_min = (uint64_t *)(base + L.slot_min);
   w.slot_keys = (uint64_t *)(base + L.slot_keys);
-  w.mbound = (uint64_t *)(base + L.mbound);
   w.mcnt = (uint32_t *)(base + L.mcnt);
   w.mkeys = (uint64_t *)(base + L.mkeys);
   w.stats = out_stats ? out_stats : (int64_t *)(base + L.stats);

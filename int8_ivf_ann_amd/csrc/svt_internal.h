@@ -92,6 +92,7 @@ static_assert(kMergeCap >= kMaxK && kMergeCap % kSelThreads == 0,
 constexpr int kSelSegLds = 4096;            // probe lists up to this long are searched in LDS
 constexpr int64_t kMinChunkCost = 16 << 10; // smallest chunk, in estimated bytes moved
 constexpr int kPlanBands = 256;             // cluster-id bands of the scan's queue order
+constexpr int kPlanSmallBatch = 4;          // query path: batches up to this size plan in one workgroup
 // The queue ends with the chunks of the highest bands.  Items of a query's probed clusters in bands
 // kTailBand and above are cut into chunks kTailDiv times shorter, so that the workgroups taking the last
 // chunks finish closer together.  kTailBand == kPlanBands: no shorter chunks.
@@ -202,8 +203,8 @@ struct Work {
   int32_t *slot_cnt;        // [max_chunks] candidates each chunk left
   uint64_t *slot_min;       // [max_chunks] smallest key of a slot holding k keys, else 0
   uint64_t *slot_keys;      // [max_chunks][k] those candidates (score/id keys)
-  uint64_t *mbound;         // [B]          the query's final proven bound, as the smallest key it admits
-  uint32_t *mcnt;           // [B]          slot keys at or above it (more than kGatherCap: not all kept)
+  uint32_t *mcnt;           // [B]          slot keys at or above the query's final proven bound (more than
+                            //              kGatherCap: not all kept)
   uint64_t *mkeys;          // [B][kGatherCap] those keys, gathered from the query's slots
   int64_t *stats;           // [B][2] scanned / eligible (caller buffer or workspace)
   // tile path (null on the query path)
@@ -268,13 +269,14 @@ hipError_t launch_coarse_keys(const DevIndex &ix, const int8_t *queries, int32_t
 // k_coarse_select: probes, stream layout, samples; tile path: speculative thresholds
 hipError_t launch_coarse_select(const DevIndex &ix, const int8_t *queries, const uint64_t *masks,
                                 const SearchShape &sh, const Work &w, hipStream_t s);
-// the query path's work list (k_plan_count, k_plan_chunks, k_plan_order); redo != 0 (tile path): the
-// queries whose pools cannot prove their top k are marked in w.redo, and only those get chunks
+// the query path's work list (k_plan_count, k_plan_chunks, k_plan_order; k_plan_small for batches of at
+// most kPlanSmallBatch queries); redo != 0 (tile path): the queries whose pools cannot prove their top k
+// are marked in w.redo, and only those get chunks
 hipError_t launch_plan(const DevIndex &ix, const SearchShape &sh, const Work &w, int redo, hipStream_t s);
 // k_scan; fallback != 0: the redo of the tile path (per-query statistics are not counted again)
 hipError_t launch_scan(const DevIndex &ix, const int8_t *queries, const uint64_t *masks, const SearchShape &sh,
                        const Work &w, int fallback, hipStream_t s);
-// k_merge_bound, k_merge_gather, k_merge; fallback != 0: only the queries marked for redo, merged from
+// k_merge_gather, k_merge; fallback != 0: only the queries marked for redo, merged from
 // their chunks' slots (k_merge alone)
 hipError_t launch_merge(const DevIndex &ix, const float *query_scales, const SearchShape &sh, const Work &w,
                         int fallback, int64_t *out_ids, int32_t *out_scores, float *out_fscores,

@@ -298,6 +298,7 @@ __global__ __launch_bounds__(kSelThreads) void k_coarse_select(DevIndex ix, cons
     if (in_lds) seg_lds[nprobe] = run;
     w.qlen[b] = run;
     w.thr[b] = INT32_MIN;
+    w.mcnt[b] = 0u;
     if (w.pool_cnt) w.pool_cnt[b] = 0u;
     if (w.stats) { w.stats[2 * (size_t)b] = (int64_t)live_s; w.stats[2 * (size_t)b + 1] = 0; }
   }
@@ -460,14 +461,15 @@ __global__ __launch_bounds__(kSelThreads) void k_coarse_select(DevIndex ix, cons
 // cluster it starts in and that cluster's band (1/256 of the cluster ids).  k_plan_order (one workgroup): the queue,
 // chunks grouped by band, so that chunks of different queries that read the same clusters run at about
 // the same time and the second reader finds the data in cache (Infinity Cache: every XCD works through
-// the same bands at the same time).
+// the same bands at the same time).  k_plan_small runs the three in one workgroup for batches of a few
+// queries, where the launches, not the work, set the stage's time.
 
 // Tile path (redo != 0): a pool proves its query's top k when it holds every candidate it was offered and
 // either its threshold admitted every eligible item or at least k candidates reached it (then the k-th
 // best score is at or above the threshold, so the top k are all in the pool); every other query is marked
 // for redo and only those get chunks.
-__global__ __launch_bounds__(kSelThreads) void k_plan_count(int32_t B, int32_t P, Work w, int32_t redo, int32_t k,
-                                                             uint32_t pool_cap) {
+__device__ __forceinline__ void plan_count(int32_t B, int32_t P, const Work &w, int32_t redo, int32_t k,
+                                           uint32_t pool_cap) {
   __shared__ int wave_tot[kSelThreads / 64 + 1];
   __shared__ int64_t wave_tot64[kSelThreads / 64 + 1];
   const int tid = threadIdx.x;
@@ -532,9 +534,15 @@ __global__ __launch_bounds__(kSelThreads) void k_plan_count(int32_t B, int32_t P
   if (tid == 0) w.cstart[B] = carry;
 }
 
-__global__ __launch_bounds__(256) void k_plan_chunks(int32_t B, int32_t nprobe, int32_t nlist, Work w) {
-  __shared__ int32_t sseg[kSelSegLds + 1];   // the query's stream offsets, when they fit
-  const int q = blockIdx.x, tid = threadIdx.x;
+__global__ __launch_bounds__(kSelThreads) void k_plan_count(int32_t B, int32_t P, Work w, int32_t redo, int32_t k,
+                                                             uint32_t pool_cap) {
+  plan_count(B, P, w, redo, k, pool_cap);
+}
+
+// the chunks of query q, by the NT threads of the workgroup; sseg: kSelSegLds + 1 ints of LDS
+template <int NT>
+__device__ __forceinline__ void plan_chunks(int q, int32_t nprobe, int32_t nlist, const Work &w, int32_t *sseg) {
+  const int tid = threadIdx.x;
   const int32_t c0 = w.cstart[q], nch = w.cstart[q + 1] - c0;
   if (nch == 0) return;
   const int64_t len = w.qlen[q], ta = w.qtail[2 * (size_t)q];
@@ -543,13 +551,13 @@ __global__ __launch_bounds__(256) void k_plan_chunks(int32_t B, int32_t nprobe, 
   const int32_t *pq = w.probes + (size_t)q * nprobe;
   const bool in_lds = nprobe <= kSelSegLds;
   if (in_lds)
-    for (int i = tid; i <= nprobe; i += 256) sseg[i] = sq[i];
+    for (int i = tid; i <= nprobe; i += NT) sseg[i] = sq[i];
   __syncthreads();
   // Each region holds its chunks of ceil(region length / chunks) items: none is empty, since that never
   // exceeds the length chosen for the region.
   const int64_t cla = na > 0 ? (ta + na - 1) / na : 0;
   const int64_t clb = nb > 0 ? (len - ta + nb - 1) / nb : 0;
-  for (int i = tid; i < nch; i += 256) {
+  for (int i = tid; i < nch; i += NT) {
     int64_t l0, l1;
     if (i < na) {
       l0 = (int64_t)i * cla;
@@ -571,6 +579,11 @@ __global__ __launch_bounds__(256) void k_plan_chunks(int32_t B, int32_t nprobe, 
   }
 }
 
+__global__ __launch_bounds__(256) void k_plan_chunks(int32_t B, int32_t nprobe, int32_t nlist, Work w) {
+  __shared__ int32_t sseg[kSelSegLds + 1];   // the query's stream offsets, when they fit
+  plan_chunks<256>(blockIdx.x, nprobe, nlist, w, sseg);
+}
+
 // The queue: a counting sort of the chunks by band.  Inside a band the chunks follow a scattered order
 // (scatter_index), which interleaves the queries: consecutive queue entries then belong to different
 // queries, so the workgroups running at the same time read the same clusters for different queries
@@ -579,7 +592,7 @@ __global__ __launch_bounds__(256) void k_plan_chunks(int32_t B, int32_t nprobe, 
 // counts their chunks per band, every (wave, band) gets its start from the band totals and the counts of
 // the waves before it, and the wave places its chunks, ranking the lanes of a 64-position group that
 // share a band with ballots on the band's bits.
-__global__ __launch_bounds__(kSelThreads) void k_plan_order(int32_t B, Work w) {
+__device__ __forceinline__ void plan_order(int32_t B, const Work &w) {
   constexpr int NWV = kSelThreads / 64;
   constexpr int BB = 8;                              // bits of a band
   static_assert(kPlanBands == 1 << BB, "bands are ranked with one ballot per band bit");
@@ -629,6 +642,24 @@ __global__ __launch_bounds__(kSelThreads) void k_plan_order(int32_t B, Work w) {
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
+}
+
+__global__ __launch_bounds__(kSelThreads) void k_plan_order(int32_t B, Work w) { plan_order(B, w); }
+
+// The whole work list of a small batch (query path) in one workgroup: counts, each query's chunks in
+// turn, the queue.  Each phase reads what the one before wrote to global memory; the workgroup barrier
+// between them orders those accesses, since every thread of a workgroup sees global memory through the
+// same compute unit.
+__global__ __launch_bounds__(kSelThreads) void k_plan_small(int32_t B, int32_t P, int32_t nprobe, int32_t nlist,
+                                                             int32_t k, Work w) {
+  __shared__ int32_t sseg[kSelSegLds + 1];
+  plan_count(B, P, w, 0, k, 0u);
+  __syncthreads();
+  for (int q = 0; q < B; ++q) {
+    plan_chunks<kSelThreads>(q, nprobe, nlist, w, sseg);
+    __syncthreads();   // sseg is reused by the next query
+  }
+  plan_order(B, w);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -1261,16 +1292,19 @@ __global__ __launch_bounds__(kScanThreads, kScanOcc) void k_scan(ScanArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------------
-// Before the merge.  k_merge_bound (one wave per query): every chunk has pushed the candidates it
-// accepted to its query's score histogram, so the histogram is final; the lower edge of the highest bin at
-// which at least k counted candidates lie at or above is a proven bound on the k-th score (at least k items
-// score that much), as is the query's running bound.  k_merge_gather (persistent workgroups, one slot at a
-// time): the keys of every slot at or above its query's bound, compacted per query with one atomic per slot.
-// A query's top k is among them: its true top k all score at least the bound.
+// Before the merge.  k_merge_gather (persistent workgroups, one slot at a time): the keys of every slot
+// at or above its query's final bound, compacted per query with one atomic per slot (the counts start at
+// zero from the coarse select).  Every chunk has pushed the candidates it accepted to its query's score
+// histogram, so the histogram is final; the lower edge of the highest bin at which at least k counted
+// candidates lie at or above is a proven bound on the k-th score (at least k items score that much), as
+// is the query's running bound.  A query's top k is among the gathered keys: its true top k all score at
+// least the bound.
 
-__global__ __launch_bounds__(64) void k_merge_bound(Work w, int32_t k) {
+// The final bound of query q as the smallest key it admits (0: none), by one whole wave; every lane
+// returns it.
+__device__ __forceinline__ uint64_t merge_bound_key(const Work &w, int q, int32_t k) {
   constexpr int HPB = kQHistBins / 64;
-  const int q = blockIdx.x, l = threadIdx.x;
+  const int l = lane_id();
   const uint32_t *gh = w.ghist + (size_t)q * kQHistBins;
   uint32_t h[HPB], sum = 0;
 #pragma unroll
@@ -1298,31 +1332,35 @@ __global__ __launch_bounds__(64) void k_merge_bound(Work w, int32_t k) {
   }
   const int32_t g = w.thr[q];
   bound = g > bound ? g : bound;
-  if (l == 0) {
-    w.mbound[q] = bound == INT32_MIN ? 0ull : make_key(bound, 0xFFFFFFFFu);   // smallest key of that score
-    w.mcnt[q] = 0u;
-  }
+  return bound == INT32_MIN ? 0ull : make_key(bound, 0xFFFFFFFFu);   // smallest key of that score
 }
 
 __global__ __launch_bounds__(256) void k_merge_gather(Work w, int32_t B, int32_t k, uint32_t cap) {
   constexpr int PER = kMaxK / 256;   // a slot holds at most k <= kMaxK keys: one pass of PER per thread
   __shared__ int wave_tot[256 / 64 + 1];
   __shared__ uint32_t sbase;
+  __shared__ unsigned long long sbound;
   const int tid = threadIdx.x;
   const int n = w.cstart[B];
   for (int c = blockIdx.x; c < n; c += gridDim.x) {
     const int q = w.chunks[c].q;
     const int cnt = w.slot_cnt[c];
-    const uint64_t T = w.mbound[q];
     const uint64_t *keys = w.slot_keys + (size_t)c * k;
     uint64_t v[PER];
-    int take = 0;
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int i = u * 256 + tid;
       v[u] = i < cnt ? keys[i] : 0ull;   // valid keys are never 0
-      take += v[u] >= T && v[u] != 0ull ? 1 : 0;
     }
+    if (tid < 64) {   // wave 0: the query's bound, while the slot's keys arrive
+      const uint64_t b = merge_bound_key(w, q, k);
+      if (tid == 0) sbound = b;
+    }
+    __syncthreads();
+    const uint64_t T = sbound;
+    int take = 0;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) take += v[u] >= T && v[u] != 0ull ? 1 : 0;
     int tot;
     int off = block_excl_scan<256>(take, wave_tot, &tot);   // barriers inside
     if (tid == 0) sbase = tot > 0 ? atomicAdd(&w.mcnt[q], (uint32_t)tot) : 0u;
@@ -1642,6 +1680,10 @@ hipError_t launch_coarse_select(const DevIndex &ix, const int8_t *queries, const
 }
 
 hipError_t launch_plan(const DevIndex &ix, const SearchShape &sh, const Work &w, int redo, hipStream_t s) {
+  if (!redo && sh.B <= kPlanSmallBatch) {
+    k_plan_small<<<1, kSelThreads, 0, s>>>(sh.B, sh.P, sh.nprobe, ix.nlist, sh.k, w);
+    return hipGetLastError();
+  }
   k_plan_count<<<1, kSelThreads, 0, s>>>(sh.B, sh.P, w, redo, sh.k, (uint32_t)sh.pool_cap);
   k_plan_chunks<<<sh.B, 256, 0, s>>>(sh.B, sh.nprobe, ix.nlist, w);
   k_plan_order<<<1, kSelThreads, 0, s>>>(sh.B, w);
@@ -1695,7 +1737,6 @@ hipError_t launch_merge(const DevIndex &ix, const float *query_scales, const Sea
   MergeArgs a{w, query_scales, ix.item_scale, sh.B, sh.k, sh.P, fallback, (uint32_t)sh.gather_cap, out_ids,
               out_scores, out_fscores, out_counts};
   if (!fallback) {   // the redo of the tile path (rare) merges straight from the chunks' slots
-    k_merge_bound<<<sh.B, 64, 0, s>>>(w, sh.k);
     const int g = sh.max_chunks < kMergeGatherWGs ? sh.max_chunks : kMergeGatherWGs;
     k_merge_gather<<<g, 256, 0, s>>>(w, sh.B, sh.k, (uint32_t)sh.gather_cap);
   }
