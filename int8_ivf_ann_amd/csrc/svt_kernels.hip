@@ -340,25 +340,35 @@ __global__ __launch_bounds__(kSelThreads) void k_coarse_select(DevIndex ix, cons
       mk[g][1] = (g < G && ix.sig_words == 2) ? masks[((size_t)b * G + g) * ix.sig_words + 1] : 0ull;
     }
     uint64_t sgv[kSampleMax][2];
+    int32_t sc0 = 0;
 #pragma unroll
     for (int i = 0; i < kSampleMax; ++i) {
-      // sample j = i * kSelThreads + tid of n_samp; samples past m repeat the thread's first position
-      const int j = (i < m ? i : 0) * kSelThreads + tid;
-      const int32_t t = (int32_t)((int64_t)j * run / n_samp);
-      if (nprobe == nlist) {
-        pos[i] = t;   // every cluster probed, in id order: the stream is the position order
-      } else {
-        int lo = 0, hi = nprobe - 1;   // largest j with seg[j] <= t
-        while (lo < hi) {
-          const int mid = (lo + hi + 1) >> 1;
-          const int32_t sv = in_lds ? seg_lds[mid] : seg[mid];
-          if (sv <= t) lo = mid; else hi = mid - 1;
+      if (i == 0 || i < m) {
+        // sample j = i * kSelThreads + tid of n_samp
+        const int j = i * kSelThreads + tid;
+        const int32_t t = (int32_t)((int64_t)j * run / n_samp);
+        if (nprobe == nlist) {
+          pos[i] = t;   // every cluster probed, in id order: the stream is the position order
+        } else {
+          int lo = 0, hi = nprobe - 1;   // largest j with seg[j] <= t
+          while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            const int32_t sv = in_lds ? seg_lds[mid] : seg[mid];
+            if (sv <= t) lo = mid; else hi = mid - 1;
+          }
+          pos[i] = (in_lds ? su.pb[lo] : pb[lo]) + t;
         }
-        pos[i] = (in_lds ? su.pb[lo] : pb[lo]) + t;
+        const uint64_t *sg = ix.sigs + (size_t)pos[i] * ix.sig_words;
+        sgv[i][0] = sg[0];
+        sgv[i][1] = ix.sig_words == 2 ? sg[1] : 0ull;
+        // query path: its one sample is scored whether it passes or not; the row is requested together
+        // with the signature
+        if (i == 0 && thr_mode == 0) sc0 = score_at(pos[0]);
+      } else {   // a thread draws m samples; the rest are never tested
+        pos[i] = pos[0];
+        sgv[i][0] = sgv[0][0];
+        sgv[i][1] = sgv[0][1];
       }
-      const uint64_t *sg = ix.sigs + (size_t)pos[i] * ix.sig_words;
-      sgv[i][0] = sg[0];
-      sgv[i][1] = ix.sig_words == 2 ? sg[1] : 0ull;
     }
 #pragma unroll
     for (int i = 0; i < kSampleMax; ++i) {
@@ -370,10 +380,9 @@ __global__ __launch_bounds__(kSelThreads) void k_coarse_select(DevIndex ix, cons
       hitm |= ok ? 1u << i : 0u;
     }
     if (thr_mode == 0) {   // query path: every sample scored
-      const int32_t sc = score_at(pos[0]);
       have = 1;
-      ssum_t = sc;
-      mx = sc;
+      ssum_t = sc0;
+      mx = sc0;
     }
   }
   const int hit = __popc(hitm);
@@ -926,16 +935,23 @@ __global__ __launch_bounds__(kScanThreads, kScanOcc) void k_scan(ScanArgs a) {
   const int tid = threadIdx.x, l = lane_id(), wv = tid / 64, sub = l % LPR;
   const int k = a.k;
   const int n_chunks = a.w.cstart[a.B];
-  if (tid == 0) sm.next = (int)atomicAdd(&a.w.counter[1], 1u);
+  // Persistent workgroups take chunks from the work list until it is empty.  Queue positions: the first
+  // two of workgroup i are i and P + i (P workgroups), later ones P * 2 + the counter's next value.  Fixed
+  // first claims keep every workgroup from waiting on one counter address at the start, where the
+  // atomics of all P workgroups would arrive together and be served one after another.
+  const int P = (int)gridDim.x;
+  if (tid == 0) sm.next = (int)blockIdx.x;
   __syncthreads();
-  // persistent workgroups take chunks from the work list until it is empty
+  int claims = 1;   // positions claimed so far (uniform)
   for (;;) {
     const int qpos = __builtin_amdgcn_readfirstlane(sm.next);
     if (qpos >= n_chunks) break;
     const int c = a.w.order[qpos];
     // the chunk after this one, requested now so the request is answered by the time it is needed
     int next_c = 0;
-    if (tid == 0) next_c = (int)atomicAdd(&a.w.counter[1], 1u);
+    if (tid == 0)
+      next_c = claims == 1 ? P + (int)blockIdx.x : 2 * P + (int)atomicAdd(&a.w.counter[1], 1u);
+    ++claims;
     const Chunk ch = a.w.chunks[c];
     const int q = ch.q;
     const int32_t ra = ch.lo, rb = ch.hi;

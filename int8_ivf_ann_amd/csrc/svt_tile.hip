@@ -326,10 +326,19 @@ __global__ __launch_bounds__(kScanThreads, kTOcc) void k_tscan(TScanArgs a) {
     wave_lds_sync();
     stage_n = 0;
   };
+  // Chunk claims: the first two of wave i (of NW waves) are i and NW + i, later ones NW * 2 + the
+  // counter's next value, so that the waves do not all wait on one counter address at the start.
+  const int NW = (int)gridDim.x * kTWaves, gw = (int)blockIdx.x * kTWaves + wv;
+  int claims = 0;   // chunks claimed so far (uniform across the wave)
   for (;;) {
     int ci = 0;
-    if (l == 0) ci = (int)atomicAdd(&a.w.counter[3], 1u);
-    ci = __builtin_amdgcn_readfirstlane(__shfl(ci, 0));
+    if (claims < 2) {
+      ci = claims * NW + gw;
+    } else {
+      if (l == 0) ci = 2 * NW + (int)atomicAdd(&a.w.counter[3], 1u);
+      ci = __builtin_amdgcn_readfirstlane(__shfl(ci, 0));
+    }
+    ++claims;
     if (ci >= n_chunks) break;
     const int32_t ra = a.w.cstart_u[ci], rb = a.w.cstart_u[ci + 1];
     if (ra >= rb) continue;
