@@ -270,8 +270,8 @@ hipError_t launch_coarse_keys(const DevIndex &ix, const int8_t *queries, int32_t
 hipError_t launch_coarse_select(const DevIndex &ix, const int8_t *queries, const uint64_t *masks,
                                 const SearchShape &sh, const Work &w, hipStream_t s);
 // the query path's work list (k_plan_count, k_plan_chunks, k_plan_order; k_plan_small for batches of at
-// most kPlanSmallBatch queries); redo != 0 (tile path): the queries whose pools cannot prove their top k
-// are marked in w.redo, and only those get chunks
+// most kPlanSmallBatch queries); redo != 0 (tile path, k_plan_redo): the queries whose pools cannot prove
+// their top k are marked in w.redo, and only those get chunks
 hipError_t launch_plan(const DevIndex &ix, const SearchShape &sh, const Work &w, int redo, hipStream_t s);
 // k_scan; fallback != 0: the redo of the tile path (per-query statistics are not counted again)
 hipError_t launch_scan(const DevIndex &ix, const int8_t *queries, const uint64_t *masks, const SearchShape &sh,

@@ -104,7 +104,7 @@ constexpr int kSelTwoLevel = kSelSegLds / 2 / kSelKR;   // largest nprobe the tw
 // score (every query with an eligible item is then redone on the query path)
 __global__ __launch_bounds__(kSelThreads) void k_coarse_select(DevIndex ix, const int8_t *__restrict__ queries,
                                                                 const uint64_t *__restrict__ masks, int32_t G,
-                                                                int32_t B, int32_t nprobe, int32_t k,
+                                                                int32_t GT, int32_t B, int32_t nprobe, int32_t k,
                                                                 int32_t pool_cap, int32_t thr_mode, Work w) {
   constexpr int NWV = kSelThreads / 64;
   __shared__ SelScratch sel;
@@ -461,6 +461,18 @@ __global__ __launch_bounds__(kSelThreads) void k_coarse_select(DevIndex ix, cons
     w.hlo[b] = lo;
     w.hshift[b] = shift;
   }
+  // Tile path (w.gcnt set): the query's GT members of each probed cluster are counted, and the log of
+  // the fraction of the cluster's items the query does not accept (its sampled density; members taken
+  // as independent) is added to the cluster's.  gcnt and clog are zeroed by k_coarse_keys.
+  if (w.gcnt) {
+    const float dens = (float)((double)hits / n_samp);
+    const float lg = log1pf(-(dens < 0.999f ? dens : 0.999f));
+    for (int j = tid; j < nprobe; j += kSelThreads) {
+      const int c = probes[j];
+      atomicAdd(&w.gcnt[c], GT);
+      atomicAdd(&w.clog[c], lg);
+    }
+  }
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -548,20 +560,24 @@ __global__ __launch_bounds__(kSelThreads) void k_plan_count(int32_t B, int32_t P
   plan_count(B, P, w, redo, k, pool_cap);
 }
 
-// the chunks of query q, by the NT threads of the workgroup; sseg: kSelSegLds + 1 ints of LDS
-template <int NT>
-__device__ __forceinline__ void plan_chunks(int q, int32_t nprobe, int32_t nlist, const Work &w, int32_t *sseg) {
-  const int tid = threadIdx.x;
+// The chunks of query q, by NT threads (tid: this thread's index among them).  STAGED: all threads of the
+// workgroup call it, and the query's stream offsets are staged in sseg (kSelSegLds + 1 ints of LDS) when
+// they fit; otherwise (one wave) they are searched in global memory and no barrier is met.
+template <int NT, bool STAGED>
+__device__ __forceinline__ void plan_chunks(int q, int tid, int32_t nprobe, int32_t nlist, const Work &w,
+                                            int32_t *sseg) {
   const int32_t c0 = w.cstart[q], nch = w.cstart[q + 1] - c0;
   if (nch == 0) return;
   const int64_t len = w.qlen[q], ta = w.qtail[2 * (size_t)q];
   const int32_t na = w.qtail[2 * (size_t)q + 1], nb = nch - na;
   const int32_t *sq = w.seg + (size_t)q * (nprobe + 1);
   const int32_t *pq = w.probes + (size_t)q * nprobe;
-  const bool in_lds = nprobe <= kSelSegLds;
-  if (in_lds)
-    for (int i = tid; i <= nprobe; i += NT) sseg[i] = sq[i];
-  __syncthreads();
+  const bool in_lds = STAGED && nprobe <= kSelSegLds;
+  if (STAGED) {
+    if (in_lds)
+      for (int i = tid; i <= nprobe; i += NT) sseg[i] = sq[i];
+    __syncthreads();
+  }
   // Each region holds its chunks of ceil(region length / chunks) items: none is empty, since that never
   // exceeds the length chosen for the region.
   const int64_t cla = na > 0 ? (ta + na - 1) / na : 0;
@@ -590,7 +606,7 @@ __device__ __forceinline__ void plan_chunks(int q, int32_t nprobe, int32_t nlist
 
 __global__ __launch_bounds__(256) void k_plan_chunks(int32_t B, int32_t nprobe, int32_t nlist, Work w) {
   __shared__ int32_t sseg[kSelSegLds + 1];   // the query's stream offsets, when they fit
-  plan_chunks<256>(blockIdx.x, nprobe, nlist, w, sseg);
+  plan_chunks<256, true>(blockIdx.x, threadIdx.x, nprobe, nlist, w, sseg);
 }
 
 // The queue: a counting sort of the chunks by band.  Inside a band the chunks follow a scattered order
@@ -665,9 +681,32 @@ __global__ __launch_bounds__(kSelThreads) void k_plan_small(int32_t B, int32_t P
   plan_count(B, P, w, 0, k, 0u);
   __syncthreads();
   for (int q = 0; q < B; ++q) {
-    plan_chunks<kSelThreads>(q, nprobe, nlist, w, sseg);
+    plan_chunks<kSelThreads, true>(q, threadIdx.x, nprobe, nlist, w, sseg);
     __syncthreads();   // sseg is reused by the next query
   }
+  plan_order(B, w);
+}
+
+// The tile path's redo work list in one workgroup: the queries whose pools cannot prove their top k are
+// marked and counted (plan_count), each wave cuts the chunks of the marked queries among its share
+// (queries wave + 16 j), one at a time, and the queue is built.  Usually no query is marked, and this one
+// launch replaces three.
+__global__ __launch_bounds__(kSelThreads) void k_plan_redo(int32_t B, int32_t P, int32_t nprobe, int32_t nlist,
+                                                            int32_t k, uint32_t pool_cap, Work w) {
+  constexpr int NWV = kSelThreads / 64;
+  const int l = lane_id(), wv = threadIdx.x / 64;
+  plan_count(B, P, w, 1, k, pool_cap);
+  __syncthreads();
+  for (int base = 0; base < B; base += NWV * 64) {
+    const int qi = base + l * NWV + wv;
+    uint64_t m = __ballot(qi < B && w.redo[qi] != 0);
+    while (m) {
+      const int bit = __ffsll((long long)m) - 1;
+      m &= m - 1ull;
+      plan_chunks<64, false>(base + bit * NWV + wv, l, nprobe, nlist, w, nullptr);
+    }
+  }
+  __syncthreads();
   plan_order(B, w);
 }
 
@@ -1690,13 +1729,17 @@ hipError_t launch_coarse_select(const DevIndex &ix, const int8_t *queries, const
   // speculative thresholds for the tile path's pools and the large-k path's (when it has them)
   const bool pools = sh.path == kPathTile || (sh.path == kPathLargeK && sh.pool_cap > 0);
   const int thr_mode = pools ? (sh.force_redo ? 2 : 1) : 0;
-  k_coarse_select<<<sh.B, kSelThreads, 0, s>>>(ix, queries, masks, sh.G, sh.B, sh.nprobe, sh.k, sh.pool_cap,
-                                                thr_mode, w);
+  k_coarse_select<<<sh.B, kSelThreads, 0, s>>>(ix, queries, masks, sh.G, sh.GT, sh.B, sh.nprobe, sh.k,
+                                                sh.pool_cap, thr_mode, w);
   return hipGetLastError();
 }
 
 hipError_t launch_plan(const DevIndex &ix, const SearchShape &sh, const Work &w, int redo, hipStream_t s) {
-  if (!redo && sh.B <= kPlanSmallBatch) {
+  if (redo) {
+    k_plan_redo<<<1, kSelThreads, 0, s>>>(sh.B, sh.P, sh.nprobe, ix.nlist, sh.k, (uint32_t)sh.pool_cap, w);
+    return hipGetLastError();
+  }
+  if (sh.B <= kPlanSmallBatch) {
     k_plan_small<<<1, kSelThreads, 0, s>>>(sh.B, sh.P, sh.nprobe, ix.nlist, sh.k, w);
     return hipGetLastError();
   }

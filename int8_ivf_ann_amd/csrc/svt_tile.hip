@@ -1,10 +1,11 @@
 // svt_tile.hip - gfx950 kernels of the tile search path: each probed cluster is read once per batch for
 // every query that probes it.
 //
-//   k_gcount, k_tplan1, k_tplan2, k_gfill, k_tentries, k_tchunks
+//   k_tplan1, k_tplan2, k_tfill
 //             the union stream: every probed cluster, in cluster order, once per block of at most
 //             kTMembers of the queries probing it (an entry); its members (mask, threshold, query); the
-//             stream cut into chunks of equal estimated cost
+//             stream cut into chunks of equal estimated cost (the members per cluster are counted by
+//             k_coarse_select)
 //   k_tscan   persistent workgroups take chunks from a queue and walk them in steps; each item of an
 //             entry is tested against the masks of all the entry's members, the rows any member accepts
 //             are gathered once and scored (v_dot4) for each member that accepts them; a score at or
@@ -37,20 +38,8 @@ namespace svt {
 // ------------------------------------------------------------------------------------------------
 // the union stream
 
-// queries probing each cluster, and the log of the fraction of the cluster's items no member accepts
-// (members taken as independent, each with its sampled density); gcnt, gfill and clog are zeroed by
-// k_coarse_keys
-__global__ __launch_bounds__(256) void k_gcount(const int32_t *__restrict__ probes, int32_t nprobe, int32_t GT,
-                                                Work w) {
-  const int b = blockIdx.x;
-  const float dens = w.qdens[b];
-  const float lg = log1pf(-(dens < 0.999f ? dens : 0.999f));
-  for (int j = threadIdx.x; j < nprobe; j += 256) {
-    const int c = probes[(size_t)b * nprobe + j];
-    atomicAdd(&w.gcnt[c], GT);   // one member per mask (GT of them, see k_gfill)
-    atomicAdd(&w.clog[c], lg);
-  }
-}
+// The members of each probed cluster and the log of the fraction of its items no member accepts are
+// counted by k_coarse_select (gcnt, clog).
 
 // Each cluster's members in mrec (gstart), its first entry (estart), the union-stream offset of that entry
 // (uoff) and the prefix of the clusters' estimated costs (ccost): prefix sums over the clusters in two
@@ -137,8 +126,7 @@ __global__ __launch_bounds__(kSelThreads) void k_tplan2(DevIndex ix, int32_t P, 
 // Chunk i of the union stream starts where the estimated cost reaches i / n of the total: inside the
 // cluster whose cost range holds that point, at the same fraction of the cluster's union items (rounded
 // down to 64).  The starts ascend with i; a chunk may be empty.  ctab[i]: the entry holding the start.
-__global__ __launch_bounds__(256) void k_tchunks(DevIndex ix, int32_t max_tchunks, Work w) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
+__device__ __forceinline__ void tile_chunk(const DevIndex &ix, int32_t max_tchunks, const Work &w, int i) {
   const int n = w.thdr[2];
   const int32_t U = w.thdr[1];
   if (i > n || i > max_tchunks) return;
@@ -173,9 +161,8 @@ __global__ __launch_bounds__(256) void k_tchunks(DevIndex ix, int32_t max_tchunk
 // mask (masks past the query's G pass nothing: every bit set), with the query's speculative threshold and
 // index.  The slots of a query's members start at a multiple of GT, and GT divides kTMembers, so they lie
 // in one entry, aligned.  The order of the queries inside a cluster is arbitrary; it changes no result.
-__global__ __launch_bounds__(256) void k_gfill(const int32_t *__restrict__ probes, const uint64_t *__restrict__ masks,
-                                               int32_t nprobe, int32_t W, int32_t G, int32_t GT, Work w) {
-  const int b = blockIdx.x;
+__device__ __forceinline__ void tile_members(const int32_t *__restrict__ probes, const uint64_t *__restrict__ masks,
+                                             int32_t nprobe, int32_t W, int32_t G, int32_t GT, const Work &w, int b) {
   const int32_t thr = w.sthr[b];
   for (int j = threadIdx.x; j < nprobe; j += 256) {
     const int c = probes[(size_t)b * nprobe + j];
@@ -189,8 +176,7 @@ __global__ __launch_bounds__(256) void k_gfill(const int32_t *__restrict__ probe
 }
 
 // entry e: the cluster whose entries hold e and its member block
-__global__ __launch_bounds__(256) void k_tentries(DevIndex ix, int32_t max_entries, Work w) {
-  const int e = blockIdx.x * 256 + threadIdx.x;
+__device__ __forceinline__ void tile_entry(const DevIndex &ix, int32_t max_entries, const Work &w, int e) {
   const int n_e = w.thdr[0];
   if (e >= n_e || e >= max_entries) return;
   const int nlist = ix.nlist;
@@ -207,6 +193,21 @@ __global__ __launch_bounds__(256) void k_tentries(DevIndex ix, int32_t max_entri
   const int mc = nq - bi * kTMembers < kTMembers ? nq - bi * kTMembers : kTMembers;
   const int ms = w.gstart[c] + bi * kTMembers;
   w.entries[e] = UEntry{useg, size, pos0, ms, mc, 0, 0, 0};
+}
+
+// The three independent steps after the prefix sums, in one launch: workgroups [0, B) place the members
+// of query blockIdx.x, the next ne_blocks write the entries, the rest cut the chunks.
+__global__ __launch_bounds__(256) void k_tfill(DevIndex ix, const int32_t *__restrict__ probes,
+                                               const uint64_t *__restrict__ masks, int32_t B, int32_t nprobe,
+                                               int32_t G, int32_t GT, int32_t max_entries, int32_t ne_blocks,
+                                               int32_t max_tchunks, Work w) {
+  const int blk = blockIdx.x;
+  if (blk < B)
+    tile_members(probes, masks, nprobe, ix.sig_words, G, GT, w, blk);
+  else if (blk < B + ne_blocks)
+    tile_entry(ix, max_entries, w, (blk - B) * 256 + threadIdx.x);
+  else
+    tile_chunk(ix, max_tchunks, w, (blk - B - ne_blocks) * 256 + threadIdx.x);
 }
 
 // Order of LDS accesses between the lanes of one wave (its LDS operations complete in order; this keeps
@@ -1112,12 +1113,11 @@ __global__ __launch_bounds__(kSelThreads) void k_pmerge(PMergeArgs a) {
 
 hipError_t launch_tile_plan(const DevIndex &ix, const uint64_t *masks, const SearchShape &sh, const Work &w,
                             hipStream_t s) {
-  k_gcount<<<sh.B, 256, 0, s>>>(w.probes, sh.nprobe, sh.GT, w);
   k_tplan1<<<(ix.nlist + kSelThreads - 1) / kSelThreads, kSelThreads, 0, s>>>(ix, w);
   k_tplan2<<<(ix.nlist + kSelThreads - 1) / kSelThreads + 1, kSelThreads, 0, s>>>(ix, sh.TP, w);
-  k_gfill<<<sh.B, 256, 0, s>>>(w.probes, masks, sh.nprobe, ix.sig_words, sh.G, sh.GT, w);
-  k_tentries<<<(sh.max_entries + 255) / 256, 256, 0, s>>>(ix, sh.max_entries, w);
-  k_tchunks<<<(sh.max_tchunks + 256) / 256, 256, 0, s>>>(ix, sh.max_tchunks, w);
+  const int ne_blocks = (sh.max_entries + 255) / 256, nc_blocks = (sh.max_tchunks + 256) / 256;
+  k_tfill<<<sh.B + ne_blocks + nc_blocks, 256, 0, s>>>(ix, w.probes, masks, sh.B, sh.nprobe, sh.G, sh.GT,
+                                                       sh.max_entries, ne_blocks, sh.max_tchunks, w);
   return hipGetLastError();
 }
 
