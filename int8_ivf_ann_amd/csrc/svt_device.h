@@ -207,13 +207,15 @@ __device__ __forceinline__ uint64_t pos_key(int32_t score, int32_t pos) {
   return ((uint64_t)((uint32_t)score ^ 0x80000000u) << 32) | (uint64_t)(uint32_t)pos;
 }
 
-// The n best ordering keys of a query, cand[0..n) in LDS (room for 2 NT keys), sorted best first and
+// The n best ordering keys of a query, cand[0..n) in LDS (room for 4 NT keys), sorted best first and
 // written as row q: ids, int32 scores and scores dequantised as S / (item_scale * query_scale) in double,
 // rounded once to float.  Entries nout..k-1 are padding.  All NT threads of the block call it;
 // nout <= n <= k <= 2 NT.
 // The sort is a bitonic network over 2 NT keys (missing keys are 0, below every real key), two per
 // thread (elements 2t and 2t + 1): strides up to 64 pair lanes of one wave and run on shuffles, larger
-// strides exchange through LDS.
+// strides exchange through LDS, alternating between two halves of cand: a thread reads its partner's
+// keys after one barrier, and the next exchange writes the other half, so no second barrier is needed
+// (the exchange after that one, which reuses this half, comes after the next exchange's barrier).
 template <int NT>
 __device__ void emit_sorted(uint64_t *cand, int n, int nout, int q, int k, const float *query_scales,
                             float item_scale, int64_t *out_ids, int32_t *out_scores, float *out_fscores) {
@@ -223,6 +225,7 @@ __device__ void emit_sorted(uint64_t *cand, int n, int nout, int q, int k, const
 #pragma unroll
   for (int e = 0; e < 2; ++e) v[e] = 2 * tid + e < n ? cand[2 * tid + e] : 0ull;
   __syncthreads();
+  int half = 0;   // the half of cand the next exchange writes
   for (int size = 2; size <= N; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
       const bool desc = ((2 * tid) & size) == 0;   // the run holding this thread's elements sorts descending
@@ -237,12 +240,13 @@ __device__ void emit_sorted(uint64_t *cand, int n, int nout, int q, int k, const
 #pragma unroll
         for (int e = 0; e < 2; ++e) p[e] = __shfl_xor(v[e], h);
       } else {
+        uint64_t *x = cand + half * N;
 #pragma unroll
-        for (int e = 0; e < 2; ++e) cand[2 * tid + e] = v[e];
+        for (int e = 0; e < 2; ++e) x[2 * tid + e] = v[e];
         __syncthreads();
 #pragma unroll
-        for (int e = 0; e < 2; ++e) p[e] = cand[2 * (tid ^ h) + e];
-        __syncthreads();
+        for (int e = 0; e < 2; ++e) p[e] = x[2 * (tid ^ h) + e];
+        half ^= 1;
       }
       const bool lower = (tid & h) == 0;   // this thread holds the lower index of each pair
       const bool keep_max = lower == desc;

@@ -1650,6 +1650,7 @@ __global__ __launch_bounds__(kSelThreads) void k_merge(MergeArgs a) {
     n = tot;
   }
   // 4. sort the n (= nout) winners and write the query's row
+  static_assert(kMergeCap >= 4 * kSelThreads, "emit_sorted needs room for 4 keys per thread");
   emit_sorted<kSelThreads>(cand, n, nout, q, k, a.query_scales, a.item_scale, a.out_ids, a.out_scores, a.out_fscores);
   if (tid == 0 && a.out_counts) a.out_counts[q] = nout;
 }

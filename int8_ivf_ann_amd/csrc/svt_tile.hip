@@ -1103,6 +1103,7 @@ __global__ __launch_bounds__(kSelThreads) void k_pmerge(PMergeArgs a) {
       m = pool_keep(cand, m, Tk, false, a.ix.perm, wave_tot);
     }
   }
+  static_assert(kPoolLds >= 4 * kSelThreads, "emit_sorted needs room for 4 keys per thread");
   emit_sorted<kSelThreads>(cand, m, nout, q, k, a.query_scales, a.item_scale, a.out_ids, a.out_scores,
                            a.out_fscores);
   if (tid == 0 && a.out_counts) a.out_counts[q] = nout;
