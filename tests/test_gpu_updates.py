@@ -77,7 +77,7 @@ def test_update_stream_matches_oracle(env):
             ix.delete(dels)
             for i in dels.tolist():
                 del model.rows[i], model.sigs[i], model.cl[i]
-            # inserts, within each cluster's free slots (new ids and, from round 2, ids deleted before)
+            # inserts, within each cluster's free slots (new ids and, from the second update round on, ids deleted before)
             free = {c: int(model.cap[c] - model.live(c)) for c in range(NLIST)}
             new_ids, new_cl = [], []
             reuse = [i for i in range(6000) if i not in model.rows][:50] if rnd >= 2 else []
