@@ -8,6 +8,8 @@
 2. The redo plan's split of the marked queries among the 16 waves of its one workgroup (k_plan_redo):
    wave w, lane l of pass p looks at query p * 1024 + l * 16 + w.  Every query must be looked at by
    exactly one (wave, lane, pass).
+3. The query path's cut of a query's stream into chunks (lengths from k_plan_count, ranges from
+   k_plan_chunks): the chunks must cover the stream in order, none empty, at most 2048 per query.
 """
 import random
 
@@ -76,3 +78,47 @@ def test_redo_split_covers_every_query_once():
                     if qi < B:
                         seen.append(qi)
         assert sorted(seen) == list(range(B)), B
+
+
+def _cdiv(a, b):
+    return -(-a // b)
+
+
+def query_chunks(length, ta, cost, tc, max_chunks=2048, tail_div=2):
+    """The query path's cut of one query's stream (k_plan_count's lengths, k_plan_chunks' ranges): a
+    regular region [0, ta) and a tail region [ta, length) of chunks tail_div times shorter."""
+    per = max_chunks // 2 if ta < length else max_chunks
+    cl_min = _cdiv(length, per)
+    cl = max(_cdiv(tc * length, cost), cl_min)
+    cl = min(_cdiv(cl, 64) * 64, length)
+    na = _cdiv(ta, cl) if ta > 0 else 0
+    nb = 0
+    if ta < length:
+        clb = max(_cdiv(_cdiv(cl, tail_div), 64) * 64, cl_min)
+        nb = _cdiv(length - ta, clb)
+    cla = _cdiv(ta, na) if na else 0
+    clb2 = _cdiv(length - ta, nb) if nb else 0
+    out = []
+    for i in range(na + nb):
+        if i < na:
+            l0 = i * cla
+            out.append((l0, min(l0 + cla, ta)))
+        else:
+            l0 = ta + (i - na) * clb2
+            out.append((l0, min(l0 + clb2, length)))
+    return out
+
+
+def test_query_chunks_tile_the_stream():
+    """Every query's chunks cover its stream exactly, in order, none empty, at most 2048 of them."""
+    rng = random.Random(3)
+    for _ in range(3000):
+        length = rng.choice([1, 63, 64, 65, 1000, rng.randint(1, 5_000_000)])
+        ta = rng.choice([0, length, rng.randint(0, length)])
+        cost = length * rng.randint(17, 200)
+        tc = rng.choice([16 << 10, rng.randint(1, 1 << 24)])
+        ch = query_chunks(length, ta, cost, tc)
+        assert 1 <= len(ch) <= 2048
+        assert ch[0][0] == 0 and ch[-1][1] == length
+        assert all(a < b for a, b in ch), "empty chunk"
+        assert all(ch[i][1] == ch[i + 1][0] for i in range(len(ch) - 1))
