@@ -105,6 +105,12 @@ def test_1m_batch64(p1m):
     p1m.check(64, 300, label="1m-b64")
 
 
+def test_10m_small_batches(p10m):
+    """Batches of 2 to 4 queries plan their chunks in one workgroup; 5 takes the three-launch plan."""
+    for B in (2, 3, 4, 5):
+        p10m.check(B, 60_000 + 10 * B, label=f"10m-b{B}")
+
+
 def test_10m_batch64(p10m):
     p10m.check(64, 0, label="10m-b64")
 

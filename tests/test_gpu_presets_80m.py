@@ -34,6 +34,10 @@ def test_80m_batch1(p80):
         p80.check(1, off, label=f"80m-b1-{off}")
 
 
+def test_80m_batch4(p80):
+    p80.check(4, 50_000, label="80m-b4")
+
+
 def test_80m_batch32_top16384(p80):
     for flags, what in ((0, "pools"), (2, "passes")):
         p80.check(32, 60_000, k=16384, label=f"80m-b32-k16384-{what}", paths=("auto",), flags=flags)
